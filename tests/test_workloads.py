@@ -1,0 +1,76 @@
+"""Input generators: determinism, shapes, distributions, and the stored routing
+biases reproducing their targets under the oracle.  CPU only."""
+
+import json
+import os
+
+import numpy as np
+import torch
+
+from mixture_experts_ffn_05_amd import workloads as wl
+from oracle import moe_oracle as O
+
+
+def test_x_and_router_are_deterministic_and_decode_is_a_prefix():
+    a = wl.make_x(wl.V2L)
+    b = wl.make_x(wl.V2L)
+    assert torch.equal(a, b)
+    d = wl.make_x(wl.WORKLOADS["v2l_decode16"])
+    assert d.shape == (16, 2048) and torch.equal(d, a[:16])
+    assert torch.equal(wl.make_router(wl.V3), wl.make_router(wl.WORKLOADS["v3_decode64"]))
+
+
+def test_expert_weights_per_expert_keys_and_distribution():
+    cfg = wl.LayerConfig("t", "bf16", T=8, H=64, E=3, top_k=2, I=32, I_s=48, gated=True)
+    W1, W2 = wl.make_expert_weights(cfg)
+    W1b, _ = wl.make_expert_weights(cfg)
+    assert torch.equal(W1, W1b)
+    assert not torch.equal(W1[0], W1[1])
+    assert W1.dtype == torch.bfloat16 and W1.shape == (3, 64, 64) and W2.shape == (3, 32, 64)
+    big = wl.make_expert_weights(wl.LayerConfig("u", "bf16", T=8, H=512, E=1, top_k=1, I=512))[0].float()
+    assert abs(big.std().item() - 0.02) < 5e-4 and abs(big.mean().item()) < 5e-4
+    ws1, ws2, wg = wl.make_shared_weights(cfg)
+    assert ws1.shape == (64, 96) and ws2.shape == (48, 64) and wg.shape == (64,)
+
+
+def test_tiny_workload_fan_in_init():
+    stds = wl.weight_stds(wl.TINY)
+    assert stds["wr"] == 1 / 16 and stds["w1"] == 1 / 16 and abs(stds["w2"] - 128 ** -0.5) < 1e-15
+    x = wl.make_x(wl.TINY)
+    assert x.dtype == torch.float32 and x.shape == (128, 256)
+    ids, w = wl.all_duplicate_routes(wl.TINY_DUP)
+    assert (ids == 0).all() and (w == 0.5).all()
+
+
+def test_stored_bias_reproduces_scout_zipf_counts():
+    cfg = wl.SCOUT
+    L0 = O.router_logits(wl.make_x(cfg).float().numpy(), wl.make_router(cfg).float().numpy(),
+                         wl.load_route_bias(cfg))
+    counts = np.bincount(O.topk_select(L0, 1).reshape(-1), minlength=16)
+    target = [round(2048 / (e + 1) / sum(1 / (i + 1) for i in range(16))) for e in range(16)]
+    assert np.abs(counts - np.array(target)).max() <= 3
+    assert counts[0] > 550 and np.all(np.diff(counts) <= 0)
+
+
+def test_stored_bias_gives_v3_top4_quarter_share():
+    cfg = wl.V3
+    L0 = O.router_logits(wl.make_x(cfg).float().numpy(), wl.make_router(cfg).float().numpy(),
+                         wl.load_route_bias(cfg))
+    counts = np.bincount(O.topk_select(L0, 8).reshape(-1), minlength=256)
+    assert abs(counts[:4].sum() / (4096 * 8) - 0.25) < 0.002
+
+
+def test_qwen2_shared_gate_is_not_saturated():
+    """Saturation guard: a gate stuck at 0 or 1 would let a dropped gate multiply pass."""
+    cfg = wl.QWEN2
+    x = wl.make_x(cfg).double().numpy()
+    wg = wl.make_shared_weights(cfg)[2]
+    z = x @ wg.double().numpy()
+    gate = 1 / (1 + np.exp(-z))
+    assert gate.min() > 1e-6 and gate.max() < 1 - 1e-6
+
+
+def test_bias_file_is_well_formed():
+    path = os.path.join(os.path.dirname(wl.__file__), "route_bias.json")
+    data = json.load(open(path))
+    assert len(data["scout_zipf"]["bias"]) == 16 and len(data["v3_top4"]["bias"]) == 256
