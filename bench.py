@@ -1,0 +1,243 @@
+"""Benchmark: forward pass of one MoE FFN layer through libmoe on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload scout]
+                    [--no-cpu-baseline] [--cpu-sample TOKENS]
+
+One step = all six libmoe calls (route, scatter build, grouped fc1 + SwiGLU,
+grouped fc2, gather/combine, shared expert) over one batch of synthetic input
+already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
+between two stream synchronisations.  Prints ONE JSON line.
+
+Inside the timed steps, HIP events on the launch stream (torch's current
+stream, where every libmoe call is enqueued) bracket each call, giving the
+average duration of the dominant kernel (grouped fc1) for the roofline object.
+
+The CPU baseline runs the NumPy oracle (float32, bf16 contract mode) over the
+first --cpu-sample tokens of the same workload on the host cores, after the
+GPU timing, and compares the GPU's output on those tokens with it; a parity
+failure makes the run exit non-zero.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from mixture_experts_ffn_05_amd import binding as B  # noqa: E402
+from mixture_experts_ffn_05_amd import workloads as wl  # noqa: E402
+
+METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% bf16 MFMA peak; decode % HBM BW)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+CALLS = ("route", "scatter", "fc1", "fc2", "combine", "shared")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg, counts):
+    """FLOPs and bytes the layer must do for the realized routes (counts per expert)."""
+    T, H, E, k, I, I_s = cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s
+    R = int(counts.sum())
+    active = int((counts > 0).sum())
+    el = 2 if cfg.dtype == "bf16" else 4
+    fc1_flops = 4.0 * R * H * I
+    fc2_flops = 2.0 * R * I * H
+    fc1_bytes = active * H * 2 * I * el + R * H * el + R * I * el      # weights + X_s read + A write
+    fc2_bytes = active * I * H * el + R * I * el + R * H * 4            # weights + A read + Y_s write
+    shared_flops = 6.0 * T * H * I_s + (2.0 * T * H if cfg.gated else 0.0)
+    layer_flops = 2.0 * T * H * E + fc1_flops + fc2_flops + shared_flops
+    layer_bytes = (active * 3 * H * I * el + 3 * H * I_s * el + H * E * el + T * H * el + T * H * 4)
+    return {"R": R, "active_experts": active, "fc1_flops": fc1_flops, "fc2_flops": fc2_flops,
+            "fc1_bytes": fc1_bytes, "fc2_bytes": fc2_bytes, "shared_flops": shared_flops,
+            "layer_flops": layer_flops, "layer_bytes": layer_bytes}
+
+
+def roofline(flops, nbytes, seconds):
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if flops / nbytes >= ridge:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBPS, 4)}
+
+
+def run_step(layer, bufs, cfg, bias_t, events=None):
+    x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
+    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+    rec(0)
+    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits)
+    rec(1)
+    B.moe_build_scatter(x, bufs.topk_ids, cfg.E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
+                        bufs.status_words, bufs.x_scattered, bufs.scatter_ws)
+    rec(2)
+    B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
+    rec(3)
+    B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
+    rec(4)
+    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
+    rec(5)
+    if layer["shared"] is not None:
+        ws1, ws2, wg = layer["shared"]
+        B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True)
+    rec(6)
+
+
+def cpu_baseline(layer, cfg, bufs, sample_tokens):
+    """Time the oracle on the first `sample_tokens` tokens and check the GPU output against it."""
+    import threadpoolctl
+    from oracle import moe_oracle as O
+
+    S = min(sample_tokens, cfg.T)
+    f = lambda t: t.detach().float().cpu().numpy()
+    log(f"cpu baseline: copying inputs for {S} tokens to the host")
+    x = f(layer["x"][:S])
+    wr = f(layer["w_router"])
+    W1 = [f(layer["W1"][e]) for e in range(cfg.E)]
+    W2 = [f(layer["W2"][e]) for e in range(cfg.E)]
+    shared = None
+    if layer["shared"] is not None:
+        ws1, ws2, wg = layer["shared"]
+        shared = (f(ws1), f(ws2), f(wg) if wg is not None else None)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    log(f"cpu baseline: oracle over {S} tokens with {threads} BLAS threads")
+    t0 = time.perf_counter()
+    ref = O.moe_forward(x, wr, W1, W2, cfg.top_k, bias=layer["bias"], shared=shared, contract=True,
+                        dtype=np.float32)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {dt:.2f} s")
+    # parity of the GPU run on the same tokens
+    ids_gpu = bufs.topk_ids[:S].cpu().numpy()
+    logits_gpu = bufs.logits[:S].cpu().numpy()
+    topk_exact = bool(np.array_equal(ids_gpu, O.topk_select(logits_gpu, cfg.top_k)))
+    same_route = (ids_gpu == ref["ids"]).all(1)
+    y_gpu = bufs.y[:S].cpu().numpy()[same_route]
+    y_ref = ref["y"][same_route]
+    d = y_gpu.astype(np.float64) - y_ref
+    max_err = float(np.abs(d).max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(y_ref), 1e-30)) if d.size else 0.0
+    ok = topk_exact and max_err <= 2e-2 and rel <= 1e-2 and np.isfinite(y_gpu).all()
+    parity = {"topk_bit_exact_on_gpu_logits": topk_exact, "tokens_compared": int(same_route.sum()),
+              "near_tie_tokens_excluded": int((~same_route).sum()), "max_abs_err": max_err,
+              "rel_fro_err": rel, "pass": bool(ok)}
+    cores = threads
+    base = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full layer (routing, scatter, "
+                      f"routed experts, combine, shared expert), NumPy float32 with bf16 activation rounding, "
+                      f"one run of {dt:.2f} s"}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="scout", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=2048)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: libmoe has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.load()
+    dev = torch.device("cuda:0")
+    cfg = wl.WORKLOADS[args.workload]
+    log(f"workload {cfg}")
+    layer = wl.make_layer(cfg, dev)
+    bias_t = torch.from_numpy(layer["bias"]).to(dev) if layer["bias"] is not None else None
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(layer, bufs, cfg, bias_t)
+    torch.cuda.synchronize()
+    status = bufs.status_words.cpu().tolist()
+    if status[1] != 0:
+        raise RuntimeError(f"router produced {status[1]} out-of-range expert ids")
+    counts = np.diff(bufs.expert_offsets.cpu().numpy())
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(layer, bufs, cfg, bias_t, ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, c in enumerate(CALLS)}
+    log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
+
+    work = algorithmic_work(cfg, counts)
+    fc1_s = per_call["fc1"] / 1e3
+    fc2_s = per_call["fc2"] / 1e3
+    roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_bf16<SwiGLU> (moe_grouped_swiglu_fc1)"
+    gg_s = fc1_s + fc2_s
+    gg_tflops = (work["fc1_flops"] + work["fc2_flops"]) / gg_s / 1e12
+    gg_gbps = (work["fc1_bytes"] + work["fc2_bytes"]) / gg_s / 1e9
+    layer_s = ms_per_step / 1e3
+    t_roof = max(work["layer_flops"] / (PEAK_BF16_TFLOPS * 1e12), work["layer_bytes"] / (PEAK_HBM_GBPS * 1e9))
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normals; random-init weights of the layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.top_k, "I": cfg.I,
+                   "I_s": cfg.I_s, "shared_gate": cfg.gated, "routing": cfg.skew or "natural",
+                   "realized_rows_per_expert": counts.tolist()},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": round(gg_tflops, 2), "frac_mfma_peak": round(gg_tflops / PEAK_BF16_TFLOPS, 4),
+                         "gbps": round(gg_gbps, 1), "frac_hbm_peak": round(gg_gbps / PEAK_HBM_GBPS, 4),
+                         "fc1_ms": round(per_call["fc1"], 4), "fc2_ms": round(per_call["fc2"], 4)},
+        "layer": {"flops": work["layer_flops"], "bytes_alg": work["layer_bytes"],
+                  "tflops": round(work["layer_flops"] / layer_s / 1e12, 2),
+                  "gbps_alg": round(work["layer_bytes"] / layer_s / 1e9, 1),
+                  "frac_roofline": round(t_roof / layer_s, 4), "roofline_ms": round(t_roof * 1e3, 4),
+                  "active_experts": work["active_experts"]},
+        "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "cpu_baseline": None,
+    }
+    rc = 0
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(layer, cfg, bufs, args.cpu_sample)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+        if not parity["pass"]:
+            log(f"PARITY FAILURE: {parity}")
+            rc = 1
+    print(json.dumps(result), flush=True)
+    sys.exit(rc)
+
+
+if __name__ == "__main__":
+    main()

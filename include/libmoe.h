@@ -1,0 +1,207 @@
+/*
+ * libmoe -- forward pass of one Mixture-of-Experts FFN layer on an AMD MI355X
+ * (gfx950), as hand-written HIP kernels behind a plain C ABI.
+ *
+ * The layer (PLENA_Compiler PR #69 and PLENA_Simulator PR #97, sections
+ * "Group C -- shared experts" / "Part 2 -- Shared experts"):
+ *
+ *     y = shared(x) + sum_k route_weight_k * routed_expert_k(x)
+ *
+ * computed by six calls, normally in this order on one stream:
+ *
+ *     moe_route -> moe_build_scatter -> moe_grouped_swiglu_fc1 -> moe_grouped_fc2
+ *               -> moe_gather_combine(accumulate=0) -> moe_shared_expert(accumulate=1)
+ *
+ * (the shared branch may instead run first, with accumulate=0, and the combine
+ * after it with accumulate=1).
+ *
+ * Conventions for every call:
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major buffer
+ *    that the caller allocated and owns; the library never allocates, frees,
+ *    or synchronises.  Calls enqueue kernels on `stream` (a hipStream_t; NULL
+ *    is the default stream) and return; results are valid once the caller
+ *    has synchronised that stream.
+ *  - `dt` is the element type of x, the weights, the scattered rows and the
+ *    SwiGLU activation (MOE_F32 or MOE_BF16).  Logits, route weights, the
+ *    per-row expert outputs Y_s and the layer output y are always float32.
+ *  - All shape arguments are explicit; there are no global modes.  Arguments
+ *    are validated on the host before anything is launched: an invalid call
+ *    returns a non-zero status, launches nothing, and moe_last_error() names
+ *    the offending argument.
+ *  - Sizes: T tokens, H hidden, E routed experts, top_k slots per token,
+ *    R = T * top_k scattered rows, I routed intermediate size, I_s shared
+ *    intermediate size.
+ *  - Limits (MOE_ERR_UNSUPPORTED beyond them): E <= 1024, top_k <= 32,
+ *    H, I, I_s multiples of 8, T * top_k < 2^31 / 8.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, top_k > E, half-specified shared branch */
+  MOE_ERR_UNSUPPORTED = 2,      /* legal but beyond the implemented limits above */
+  MOE_ERR_WORKSPACE = 3,        /* workspace missing or smaller than the *_workspace_bytes query */
+  MOE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Name of a status code ("MOE_OK", ...).  Never NULL. */
+const char* moe_status_name(int status);
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local; "" if none).  Names the offending argument. */
+const char* moe_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int moe_version(void);
+
+/*
+ * moe_route -- router GEMM and top-k softmax.
+ *
+ * Source: PLENA_Compiler PR #69 section "Group E" (the router GEMM) and
+ * PLENA_Simulator PR #97 section "C_SET_TOPK_REG" (topk_softmax, generic in
+ * the expert count and k; k must be positive).
+ *
+ *   logits[t, e]   = sum_h x[t, h] * w_router[h, e]  (+ logit_bias[e])      fp32
+ *   topk_ids[t, :] = the top_k experts with the largest logits, in slot order:
+ *                    descending logit, ties to the lower expert index; NaN
+ *                    logits rank below every number
+ *   topk_weights   = softmax over the top_k selected logits (sums to 1)
+ *
+ * x [T, H] (dt), w_router [H, E] (dt), logit_bias [E] fp32 or NULL for none,
+ * topk_ids [T, top_k] int32 out, topk_weights [T, top_k] fp32 out,
+ * logits [T, E] fp32 out (required): the logits exactly as top-k saw them.
+ */
+moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                     int32_t T, int32_t H, int32_t E, int32_t top_k,
+                     int32_t* topk_ids, float* topk_weights, float* logits, void* stream);
+
+/* Workspace bytes moe_build_scatter needs for (T, top_k, E). */
+size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
+
+/*
+ * moe_build_scatter -- expert-grouped row layout and the scattered rows.
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", sections "Scatter/gather
+ * layout" (tokens [T, H] expand to [T*top_k, H] rows grouped by expert;
+ * scatter_index maps (token, slot) to its row) and "Duplicate top-k routes"
+ * (several slots of one token may name one expert, so a group can exceed T).
+ *
+ * Pairs p = t*top_k + j are laid out by a stable counting sort: group e holds
+ * rows [expert_offsets[e], expert_offsets[e+1]) in increasing p.
+ *
+ * topk_ids [T, top_k] int32 in (from moe_route or fed in; duplicates allowed);
+ * x [T, H] (dt) in.  Outputs: scatter_index [T, top_k] int32 (row of pair
+ * (t, j), or -1 when its expert id is outside [0, E)); row_token [R] int32
+ * (token of each row; -1 for rows past expert_offsets[E]); expert_offsets
+ * [E+1] int32; status_words [2] int32 = {largest group size, number of
+ * out-of-range expert ids} -- a non-zero second word means the routes were
+ * invalid and those pairs were dropped; x_scattered [R, H] (dt):
+ * x_scattered[r] = x[row_token[r]] for r < expert_offsets[E], other rows
+ * untouched.  workspace: device scratch of at least
+ * moe_build_scatter_workspace_bytes(T, top_k, E) bytes, contents undefined
+ * on entry and exit.
+ */
+moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_ids,
+                             int32_t T, int32_t H, int32_t E, int32_t top_k,
+                             int32_t* scatter_index, int32_t* row_token, int32_t* expert_offsets,
+                             int32_t* status_words, void* x_scattered,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu_fc1 -- per-expert gate/up projection and SwiGLU.
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", section "Backward grouped-GEMM
+ * launch bound" (a same-N/K grouped GEMM whose launch must cover the largest
+ * group, never just the token count); PLENA_Compiler PR #69 section "Group C"
+ * and PLENA_Simulator PR #97 section "Tests" (SwiGLU = silu(gate) * up).
+ *
+ * For every expert e and row r of its group:
+ *   g = x_scattered[r] @ w1[e][:, 0:I],  u = x_scattered[r] @ w1[e][:, I:2I]
+ *   act[r] = silu(g) * u,  silu(g) = g / (1 + exp(-g))   (fp32, stored as dt;
+ *            bf16 is round-to-nearest-even)
+ * The tile walk is derived on the device from expert_offsets, so every row of
+ * every group is computed whatever the group sizes are (a group may hold up to
+ * R rows); empty experts read no weights.
+ *
+ * x_scattered [R, H] (dt), expert_offsets [E+1] int32 (device),
+ * w1 [E, H, 2I] (dt; per expert row-major [H, 2I], gate columns first),
+ * act [R, I] (dt) out; rows past expert_offsets[E] are not written.
+ */
+moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
+                                  const void* w1, int32_t R, int32_t H, int32_t E, int32_t I,
+                                  void* act, void* stream);
+
+/*
+ * moe_grouped_fc2 -- per-expert down projection.
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", sections "Scatter/gather
+ * layout" and "Backward grouped-GEMM launch bound".
+ *
+ *   y_rows[r] = act[r] @ w2[e]   for r in group e, accumulated and stored fp32
+ *
+ * act [R, I] (dt), expert_offsets [E+1] int32, w2 [E, I, H] (dt),
+ * y_rows [R, H] fp32 out; rows past expert_offsets[E] are not written.
+ */
+moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_offsets,
+                           const void* w2, int32_t R, int32_t I, int32_t E, int32_t H,
+                           float* y_rows, void* stream);
+
+/*
+ * moe_gather_combine -- weighted gather of the routed outputs back to tokens.
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", section "Scatter/gather
+ * layout" (moe_gather sums routed outputs back to [tokens, hidden]); the
+ * hf-adapters PR #2 commit on the loop-on-topk decode combine (a per-token
+ * reduction over the k slots, free of the read-modify-write hazard that
+ * duplicate indices cause).
+ *
+ *   y[t] = (accumulate ? y[t] : 0) + sum_{j ascending} topk_weights[t, j] * y_rows[scatter_index[t, j]]
+ *
+ * Slots with scatter_index -1 add nothing.  y_rows [R, H] fp32,
+ * scatter_index [T, top_k] int32, topk_weights [T, top_k] fp32,
+ * y [T, H] fp32 in/out.  Each output element is written by exactly one thread.
+ */
+moe_status moe_gather_combine(const float* y_rows, const int32_t* scatter_index, const float* topk_weights,
+                              int32_t T, int32_t H, int32_t top_k, int32_t accumulate, float* y,
+                              void* stream);
+
+/* Workspace bytes moe_shared_expert needs (the [T, I_s] activation and the
+ * per-token gate). */
+size_t moe_shared_expert_workspace_bytes(moe_dtype dt, int32_t T, int32_t I_s);
+
+/*
+ * moe_shared_expert -- the shared expert, optionally sigmoid-gated.
+ *
+ * Source: PLENA_Compiler PR #69 section "Group C -- shared experts" (a dense
+ * FFN over every token, added unweighted; Qwen2-MoE scales it by
+ * sigmoid(x @ w_gate), one scalar per token; DeepSeek's n shared experts are
+ * one fused MLP of width moe_inter * n_shared).
+ *
+ *   a  = silu(x @ ws1[:, 0:I_s]) * (x @ ws1[:, I_s:2I_s])   (stored as dt)
+ *   ys = a @ ws2;   if w_gate: ys[t] *= 1 / (1 + exp(-(x[t] . w_gate)))
+ *   y  = (accumulate ? y : 0) + ys                           (fp32)
+ *
+ * x [T, H] (dt), ws1 [H, 2 I_s] (dt), ws2 [I_s, H] (dt), w_gate [H] (dt) or
+ * NULL for the ungated variant, y [T, H] fp32 in/out, workspace of at least
+ * moe_shared_expert_workspace_bytes(dt, T, I_s) bytes.
+ */
+moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const void* ws2,
+                             const void* w_gate, int32_t T, int32_t H, int32_t I_s,
+                             int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

@@ -1,0 +1,252 @@
+"""Thin ctypes binding of libmoe's C ABI (include/libmoe.h).
+
+Each function here has the name of the C call it wraps and only marshals
+arguments: it checks devices, dtypes, shapes and contiguity of torch tensors,
+passes their device pointers and the current HIP stream, and raises MoEError
+on a non-zero status.  Every step of the layer runs in libmoe's HIP kernels;
+there is no fallback of any kind.  If libmoe.so has not been built, load()
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "libmoe.h")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OK = 0
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+_c_int, _c_size, _vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "moe_status_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_version": (ctypes.c_int, []),
+    "moe_route": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "moe_build_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_build_scatter": (_c_int, [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _c_size, _vp]),
+    "moe_grouped_swiglu_fc1": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_gather_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_shared_expert_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_shared_expert": (_c_int, [_c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
+                                   _vp]),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/libmoe.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmoe.so (once) and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmoe.so not found at {p}: build it with "
+                           "`python -m mixture_experts_ffn_05_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        lib = load()
+        raise MoEError(status, f"{lib.moe_status_name(status).decode()}: {lib.moe_last_error().decode()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: libmoe takes float32 or bfloat16")
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
+
+
+def moe_route(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, stream=None):
+    lib = load()
+    T, H = x.shape
+    E = w_router.shape[1]
+    dev = x.device
+    args = (_dt(x), _ptr(x, "x"), _ptr(w_router, "w_router", x.dtype, (H, E), dev),
+            _ptr(logit_bias, "logit_bias", torch.float32, (E,), dev), T, H, E, int(top_k),
+            _ptr(topk_ids, "topk_ids", torch.int32, (T, top_k), dev),
+            _ptr(topk_weights, "topk_weights", torch.float32, (T, top_k), dev),
+            _ptr(logits, "logits", torch.float32, (T, E), dev), _stream(stream, dev))
+    _check(lib.moe_route(*args))
+
+
+def moe_build_scatter_workspace_bytes(T, top_k, E) -> int:
+    return int(load().moe_build_scatter_workspace_bytes(int(T), int(top_k), int(E)))
+
+
+def moe_build_scatter(x, topk_ids, num_experts, scatter_index, row_token, expert_offsets, status_words,
+                      x_scattered, workspace, stream=None):
+    lib = load()
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E = int(num_experts)
+    dev = x.device
+    args = (_dt(x), _ptr(x, "x"), _ptr(topk_ids, "topk_ids", torch.int32, (T, k), dev), T, H, E, k,
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev),
+            _ptr(row_token, "row_token", torch.int32, (T * k,), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(status_words, "status_words", torch.int32, (2,), dev),
+            _ptr(x_scattered, "x_scattered", x.dtype, (T * k, H), dev),
+            _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_build_scatter(*args))
+
+
+def moe_grouped_swiglu_fc1(x_scattered, expert_offsets, w1, act, stream=None):
+    lib = load()
+    R, H = x_scattered.shape
+    E, _, I2 = w1.shape
+    I = I2 // 2
+    dev = x_scattered.device
+    args = (_dt(x_scattered), _ptr(x_scattered, "x_scattered"),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", x_scattered.dtype, (E, H, 2 * I), dev), R, H, E, I,
+            _ptr(act, "act", x_scattered.dtype, (R, I), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1(*args))
+
+
+def moe_grouped_fc2(act, expert_offsets, w2, y_rows, stream=None):
+    lib = load()
+    R, I = act.shape
+    E, _, H = w2.shape
+    dev = act.device
+    args = (_dt(act), _ptr(act, "act"), _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2, "w2", act.dtype, (E, I, H), dev), R, I, E, H,
+            _ptr(y_rows, "y_rows", torch.float32, (R, H), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_fc2(*args))
+
+
+def moe_gather_combine(y_rows, scatter_index, topk_weights, y, accumulate=False, stream=None):
+    lib = load()
+    T, k = scatter_index.shape
+    H = y.shape[1]
+    dev = y.device
+    args = (_ptr(y_rows, "y_rows", torch.float32, None, dev),
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev),
+            _ptr(topk_weights, "topk_weights", torch.float32, (T, k), dev), T, H, k, int(bool(accumulate)),
+            _ptr(y, "y", torch.float32, (T, H), dev), _stream(stream, dev))
+    if y_rows.dim() != 2 or y_rows.shape[1] != H:
+        raise ValueError("y_rows must be [R, H]")
+    _check(lib.moe_gather_combine(*args))
+
+
+def moe_shared_expert_workspace_bytes(dtype, T, I_s) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_shared_expert_workspace_bytes(dt, int(T), int(I_s)))
+
+
+def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream=None):
+    lib = load()
+    T, H = x.shape
+    I_s = ws2.shape[0]
+    dev = x.device
+    args = (_dt(x), _ptr(x, "x"), _ptr(ws1, "ws1", x.dtype, (H, 2 * I_s), dev),
+            _ptr(ws2, "ws2", x.dtype, (I_s, H), dev), _ptr(w_gate, "w_gate", x.dtype, (H,), dev), T, H, I_s,
+            int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
+            _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_shared_expert(*args))
+
+
+class MoELayerBuffers:
+    """Device buffers for one layer forward of T tokens (allocated once, reused)."""
+
+    def __init__(self, T, H, E, top_k, I, I_s, dtype, device):
+        R = T * top_k
+        i32, f32 = torch.int32, torch.float32
+        self.T, self.H, self.E, self.top_k, self.I, self.I_s = T, H, E, top_k, I, I_s
+        self.logits = torch.empty((T, E), dtype=f32, device=device)
+        self.topk_ids = torch.empty((T, top_k), dtype=i32, device=device)
+        self.topk_weights = torch.empty((T, top_k), dtype=f32, device=device)
+        self.scatter_index = torch.empty((T, top_k), dtype=i32, device=device)
+        self.row_token = torch.empty((R,), dtype=i32, device=device)
+        self.expert_offsets = torch.empty((E + 1,), dtype=i32, device=device)
+        self.status_words = torch.zeros((2,), dtype=i32, device=device)
+        self.x_scattered = torch.empty((R, H), dtype=dtype, device=device)
+        self.act = torch.empty((R, I), dtype=dtype, device=device)
+        self.y_rows = torch.empty((R, H), dtype=f32, device=device)
+        self.y = torch.empty((T, H), dtype=f32, device=device)
+        self.scatter_ws = torch.empty((moe_build_scatter_workspace_bytes(T, top_k, E),), dtype=torch.uint8,
+                                      device=device)
+        self.shared_ws = (torch.empty((moe_shared_expert_workspace_bytes(dtype, T, I_s),), dtype=torch.uint8,
+                                      device=device) if I_s > 0 else None)
+
+
+def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=None, routes=None,
+                      stream=None):
+    """The six calls in order.  ``routes`` = (topk_ids int32, topk_weights fp32)
+    device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None)."""
+    T, H = x.shape
+    E, _, I2 = W1.shape
+    I_s = shared[1].shape[0] if shared is not None else 0
+    if bufs is None:
+        bufs = MoELayerBuffers(T, H, E, top_k, I2 // 2, I_s, x.dtype, x.device)
+    if routes is None:
+        moe_route(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, stream)
+        ids, w = bufs.topk_ids, bufs.topk_weights
+    else:
+        ids, w = routes
+    moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                      bufs.x_scattered, bufs.scatter_ws, stream)
+    moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream)
+    moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream)
+    moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, False, stream)
+    if shared is not None:
+        ws1, ws2, wg = shared
+        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True, stream)
+    return bufs

@@ -1,0 +1,271 @@
+// libmoe C ABI: argument validation (on the host, before any HIP call) and
+// dispatch to the kernel launchers.  Declarations and the contract of every
+// call are in include/libmoe.h.
+#include "libmoe.h"
+#include "moe_common.h"
+
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxRows = (int64_t)1 << 28;
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status hip_result(hipError_t err, const char* call) {
+  if (err == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: HIP error %d (%s)", call, (int)err, hipGetErrorString(err));
+}
+
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int elem_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+// Validation helpers: each returns MOE_OK or records a message naming the argument.
+#define MOE_CHECK(expr)                 \
+  do {                                  \
+    moe_status _st = (expr);            \
+    if (_st != MOE_OK) return _st;      \
+  } while (0)
+
+moe_status need_ptr(const void* p, const char* fn, const char* name) {
+  return p ? MOE_OK : fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s must not be NULL", fn, name);
+}
+
+moe_status need_pos(int64_t v, const char* fn, const char* name) {
+  return v >= 1 ? MOE_OK : fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s must be >= 1 (got %lld)", fn, name, (long long)v);
+}
+
+moe_status need_dtype(moe_dtype dt, const char* fn) {
+  return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK
+                                          : fail(MOE_ERR_INVALID_ARGUMENT, "%s: dt must be MOE_F32 or MOE_BF16 (got %d)",
+                                                 fn, (int)dt);
+}
+
+moe_status need_mult8(int64_t v, const char* fn, const char* name) {
+  return v % 8 == 0 ? MOE_OK
+                    : fail(MOE_ERR_UNSUPPORTED, "%s: %s must be a multiple of 8 (got %lld)", fn, name, (long long)v);
+}
+
+moe_status need_experts(int64_t E, const char* fn) {
+  MOE_CHECK(need_pos(E, fn, "E"));
+  return E <= moe::kMaxExperts ? MOE_OK
+                               : fail(MOE_ERR_UNSUPPORTED, "%s: E must be <= %d (got %lld)", fn, moe::kMaxExperts,
+                                      (long long)E);
+}
+
+moe_status need_topk(int64_t k, const char* fn) {
+  if (k < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: top_k must be positive (got %lld)", fn, (long long)k);
+  return k <= moe::kMaxTopK ? MOE_OK
+                            : fail(MOE_ERR_UNSUPPORTED, "%s: top_k must be <= %d (got %lld)", fn, moe::kMaxTopK,
+                                   (long long)k);
+}
+
+moe_status need_rows(int64_t rows, const char* fn, const char* what) {
+  return rows < kMaxRows ? MOE_OK
+                         : fail(MOE_ERR_UNSUPPORTED, "%s: %s must be < 2^28 (got %lld)", fn, what, (long long)rows);
+}
+
+moe_status need_flag(int32_t v, const char* fn, const char* name) {
+  return (v == 0 || v == 1) ? MOE_OK
+                            : fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s must be 0 or 1 (got %d)", fn, name, (int)v);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_name(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_STATUS_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_version(void) { return kVersion; }
+
+moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias, int32_t T, int32_t H,
+                     int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights, float* logits, void* stream) {
+  const char* fn = "moe_route";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(w_router, fn, "w_router"));
+  MOE_CHECK(need_ptr(topk_ids, fn, "topk_ids"));
+  MOE_CHECK(need_ptr(topk_weights, fn, "topk_weights"));
+  MOE_CHECK(need_ptr(logits, fn, "logits"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_topk(top_k, fn));
+  if (top_k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "moe_route: top_k (%d) exceeds E (%d)", top_k, E);
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  MOE_CHECK(need_rows((int64_t)T * E / 8, fn, "T*E/8"));
+  return hip_result(moe_launch::route((int)dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
+                                      (hipStream_t)stream),
+                    fn);
+}
+
+size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
+  if (T < 1 || top_k < 1 || E < 1) return 0;
+  return moe_launch::scatter_workspace_bytes(T, top_k, E);
+}
+
+moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_ids, int32_t T, int32_t H, int32_t E,
+                             int32_t top_k, int32_t* scatter_index, int32_t* row_token, int32_t* expert_offsets,
+                             int32_t* status_words, void* x_scattered, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const char* fn = "moe_build_scatter";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(topk_ids, fn, "topk_ids"));
+  MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
+  MOE_CHECK(need_ptr(row_token, fn, "row_token"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(status_words, fn, "status_words"));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_topk(top_k, fn));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  const size_t need = moe_launch::scatter_workspace_bytes(T, top_k, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_build_scatter: workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  return hip_result(moe_launch::build_scatter((int)dt, x, topk_ids, T, H, E, top_k, scatter_index, row_token,
+                                              expert_offsets, status_words, x_scattered, workspace,
+                                              (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets, const void* w1,
+                                  int32_t R, int32_t H, int32_t E, int32_t I, void* act, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x_scattered, expert_offsets, E, R, w1,
+                                                   (int64_t)H * 2 * I, H, I, act, cu_count(), (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2, int32_t R,
+                           int32_t I, int32_t E, int32_t H, float* y_rows, void* stream) {
+  const char* fn = "moe_grouped_fc2";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w2, fn, "w2"));
+  MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  return hip_result(moe_launch::grouped_fc2((int)dt, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H, y_rows,
+                                            nullptr, 0, 1, cu_count(), (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_gather_combine(const float* y_rows, const int32_t* scatter_index, const float* topk_weights, int32_t T,
+                              int32_t H, int32_t top_k, int32_t accumulate, float* y, void* stream) {
+  const char* fn = "moe_gather_combine";
+  MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
+  MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
+  MOE_CHECK(need_ptr(topk_weights, fn, "topk_weights"));
+  MOE_CHECK(need_ptr(y, fn, "y"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_topk(top_k, fn));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_flag(accumulate, fn, "accumulate"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  return hip_result(moe_launch::gather_combine(y_rows, scatter_index, topk_weights, T, H, top_k, accumulate, y,
+                                               (hipStream_t)stream),
+                    fn);
+}
+
+size_t moe_shared_expert_workspace_bytes(moe_dtype dt, int32_t T, int32_t I_s) {
+  if (T < 1 || I_s < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  return align256((size_t)T * I_s * elem_size(dt)) + align256((size_t)T * sizeof(float));
+}
+
+moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const void* ws2, const void* w_gate,
+                             int32_t T, int32_t H, int32_t I_s, int32_t accumulate, float* y, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_shared_expert";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(ws1, fn, "ws1"));
+  MOE_CHECK(need_ptr(ws2, fn, "ws2"));
+  MOE_CHECK(need_ptr(y, fn, "y"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I_s, fn, "I_s"));
+  MOE_CHECK(need_flag(accumulate, fn, "accumulate"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  const size_t need = moe_shared_expert_workspace_bytes(dt, T, I_s);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_shared_expert: workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* act = ws;
+  float* gate = w_gate ? (float*)(ws + align256((size_t)T * I_s * elem_size(dt))) : nullptr;
+  const int cus = cu_count();
+  if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate((int)dt, x, w_gate, T, H, gate, s), fn));
+  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act, cus, s), fn));
+  return hip_result(moe_launch::grouped_fc2((int)dt, act, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate, 0, cus, s),
+                    fn);
+}
+
+}  // extern "C"

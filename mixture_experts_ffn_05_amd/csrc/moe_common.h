@@ -1,0 +1,103 @@
+// Shared device and host helpers for libmoe's gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+// Raw 16-bit storage of a bfloat16 value.
+typedef uint16_t bf16_t;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// float32 -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float load_as_f32(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_as_f32(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ void store_from_f32(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_from_f32(bf16_t* p, int64_t i, float v) {
+  p[i] = (bf16_t)f32_to_bf16_rne(v);
+}
+
+// silu(g) * u with silu(g) = g / (1 + exp(-g)), in fp32.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Bits of lanes below the calling lane.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane_id() >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+}  // namespace moe
+
+// Host-side launchers implemented in the kernel translation units.  Each
+// returns hipSuccess or the launch error; arguments were validated by the API.
+namespace moe_launch {
+
+hipError_t route(int dt, const void* x, const void* w_router, const float* bias, int T, int H, int E,
+                 int top_k, int32_t* ids, float* weights, float* logits, hipStream_t s);
+
+size_t scatter_workspace_bytes(int T, int top_k, int E);
+hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H, int E, int top_k,
+                         int32_t* scatter_index, int32_t* row_token, int32_t* offsets,
+                         int32_t* status_words, void* x_scattered, void* workspace, hipStream_t s);
+
+// Grouped GEMMs.  `offsets` may be null: one group of `rows` rows.
+hipError_t grouped_swiglu_fc1(int dt, const void* a, const int32_t* offsets, int groups, int rows,
+                              const void* w1, int64_t w1_group_stride, int K, int I, void* act,
+                              int cu_count, hipStream_t s);
+hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int groups, int rows,
+                       const void* w2, int64_t w2_group_stride, int K, int N, float* out,
+                       const float* row_scale, int accumulate, int plain_store, int cu_count,
+                       hipStream_t s);
+
+hipError_t gather_combine(const float* y_rows, const int32_t* scatter_index, const float* weights,
+                          int T, int H, int top_k, int accumulate, float* y, hipStream_t s);
+hipError_t shared_gate(int dt, const void* x, const void* w_gate, int T, int H, float* gate,
+                       hipStream_t s);
+
+}  // namespace moe_launch

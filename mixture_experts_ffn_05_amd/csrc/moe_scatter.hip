@@ -1,0 +1,201 @@
+// Expert-grouped row layout (scatter build).
+//
+// VeOmni docs "Fused MoE Kernel Notes", section "Scatter/gather layout": the
+// routed pairs of [T, H] tokens expand to [T*k, H] rows grouped by expert, and
+// scatter_index maps each (token, slot) pair to its row.  Section "Duplicate
+// top-k routes": one token may send several slots to one expert, so a group can
+// hold more than T rows -- nothing below assumes a bound of T.
+//
+// The layout is a stable counting sort of the pairs p = t*k + j by expert id,
+// computed without atomics so that it is deterministic:
+//   scatter_count  each wave64 takes a chunk of 1024 consecutive pairs and counts
+//                  them per expert.  Lanes holding the same expert are found
+//                  with ceil(log2 E) ballots; one leader per expert adds the
+//                  group's popcount to an LDS histogram.
+//   scatter_scan   one workgroup: per expert, an exclusive scan of the chunk
+//                  counts (chunk bases); across experts, an exclusive scan of the
+//                  totals (expert_offsets), the largest group and the number of
+//                  out-of-range ids.
+//   scatter_rank   each wave replays its chunk; a pair's row is its chunk base
+//                  plus offsets[e] plus the number of lower lanes with the same
+//                  expert; a running per-expert cursor lives in LDS.
+//   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;              // pairs per wave
+constexpr int kIters = kChunk / kWave;    // ballot rounds per chunk
+constexpr int kWavesPerBlock = 4;
+
+// Lanes (bitmask) whose expert id equals the calling lane's.  All lanes of the
+// wave must call it; lanes with in_range == false get 0.
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool in_range, int nbits) {
+  uint64_t m = __ballot(in_range);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t on = __ballot(in_range && bit);
+    m &= bit ? on : ~on;
+  }
+  return in_range ? m : 0ull;
+}
+
+__global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__ ids, int R, int E, int nbits,
+                                                     int nchunks, int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ bad) {
+  extern __shared__ int32_t hist[];  // [4][E]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kWavesPerBlock * E; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * kWavesPerBlock + w;
+  int nbad = 0;
+  if (c < nchunks) {
+    int32_t* h = hist + w * E;
+    for (int it = 0; it < kIters; ++it) {
+      const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
+      const bool live = p < R;
+      const int e = live ? ids[p] : -1;
+      const bool in_range = live && e >= 0 && e < E;
+      nbad += __popcll(__ballot(live && !in_range));
+      const uint64_t m = same_expert_lanes(e, in_range, nbits);
+      if (in_range && lane == __ffsll((unsigned long long)m) - 1) h[e] += __popcll(m);
+    }
+  }
+  __syncthreads();
+  if (c < nchunks) {
+    for (int e = lane; e < E; e += kWave) cnt[(int64_t)c * E + e] = hist[w * E + e];
+    if (lane == 0) bad[c] = nbad;
+  }
+}
+
+__global__ __launch_bounds__(1024) void scatter_scan(int32_t* __restrict__ cnt, const int32_t* __restrict__ bad,
+                                                     int nchunks, int E, int R, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ status, int32_t* __restrict__ row_token) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t wmax[16];
+  __shared__ int32_t s_total;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int total_e = 0;
+  if (tid < E) {  // chunk bases of expert tid (each thread owns one column)
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t i = (int64_t)c * E + tid;
+      const int v = cnt[i];
+      cnt[i] = run;
+      run += v;
+    }
+    total_e = run;
+  }
+  const int incl = wave_inclusive_scan(total_e);
+  const int mx = wave_max(total_e);
+  if (lane == 63) wsum[w] = incl;
+  if (lane == 0) wmax[w] = mx;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  if (tid < E) offsets[tid] = base + incl - total_e;
+  if (tid == 0) {
+    int total = 0, maxg = 0, nbad = 0;
+    for (int i = 0; i < 16; ++i) {
+      total += wsum[i];
+      maxg = max(maxg, wmax[i]);
+    }
+    for (int c = 0; c < nchunks; ++c) nbad += bad[c];
+    offsets[E] = total;
+    status[0] = maxg;
+    status[1] = nbad;
+    s_total = total;
+  }
+  __syncthreads();
+  for (int r = s_total + tid; r < R; r += 1024) row_token[r] = -1;
+}
+
+__global__ __launch_bounds__(256) void scatter_rank(const int32_t* __restrict__ ids, int R, int E, int k, int nbits,
+                                                    int nchunks, const int32_t* __restrict__ chunk_base,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ scatter_index,
+                                                    int32_t* __restrict__ row_token) {
+  extern __shared__ int32_t cursor_all[];  // [4][E]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x * kWavesPerBlock + w;
+  if (c >= nchunks) return;  // whole wave; no workgroup barrier follows
+  int32_t* cursor = cursor_all + w * E;
+  for (int e = lane; e < E; e += kWave) cursor[e] = chunk_base[(int64_t)c * E + e] + offsets[e];
+  const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
+    const bool live = p < R;
+    const int e = live ? ids[p] : -1;
+    const bool in_range = live && e >= 0 && e < E;
+    const uint64_t m = same_expert_lanes(e, in_range, nbits);
+    int r = -1;
+    if (in_range) {
+      const int b = cursor[e];
+      r = b + __popcll(m & lanemask_lt());
+      if ((m & above) == 0ull) cursor[e] = b + __popcll(m);
+    }
+    if (live) scatter_index[p] = r;
+    if (in_range) row_token[r] = (int)(p / k);
+  }
+}
+
+constexpr int kCopyRows = 8;
+
+__global__ __launch_bounds__(256) void scatter_copy(const u32x4* __restrict__ x, const int32_t* __restrict__ row_token,
+                                                    const int32_t* __restrict__ offsets, int E, int R, int row_vecs,
+                                                    u32x4* __restrict__ xs) {
+  const int nvalid = offsets[E];
+  const int r0 = blockIdx.x * kCopyRows;
+  for (int rr = 0; rr < kCopyRows; ++rr) {
+    const int r = r0 + rr;
+    if (r >= nvalid || r >= R) break;
+    const int t = row_token[r];
+    const u32x4* src = x + (int64_t)t * row_vecs;
+    u32x4* dst = xs + (int64_t)r * row_vecs;
+    for (int v = threadIdx.x; v < row_vecs; v += 256) dst[v] = src[v];
+  }
+}
+
+int num_chunks(int R) { return (R + kChunk - 1) / kChunk; }
+
+}  // namespace
+}  // namespace moe
+
+namespace moe_launch {
+
+size_t scatter_workspace_bytes(int T, int top_k, int E) {
+  const int64_t R = (int64_t)T * top_k;
+  const int64_t nchunks = (R + moe::kChunk - 1) / moe::kChunk;
+  return (size_t)(nchunks * (E + 1) * 4 + 256);
+}
+
+hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H, int E, int top_k,
+                         int32_t* scatter_index, int32_t* row_token, int32_t* offsets, int32_t* status_words,
+                         void* x_scattered, void* workspace, hipStream_t s) {
+  using namespace moe;
+  const int R = T * top_k;
+  const int nchunks = num_chunks(R);
+  const int nblk = (nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  int32_t* cnt = (int32_t*)workspace;
+  int32_t* bad = cnt + (int64_t)nchunks * E;
+  const size_t lds = (size_t)kWavesPerBlock * E * sizeof(int32_t);
+  hipLaunchKernelGGL(scatter_count, dim3(nblk), dim3(256), lds, s, ids, R, E, nbits, nchunks, cnt, bad);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, cnt, (const int32_t*)bad, nchunks, E, R, offsets,
+                     status_words, row_token);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_rank, dim3(nblk), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
+                     (const int32_t*)cnt, (const int32_t*)offsets, scatter_index, row_token);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int elem = dt == 1 ? 2 : 4;
+  const int row_vecs = (int)((int64_t)H * elem / 16);
+  hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,
+                     (const int32_t*)row_token, (const int32_t*)offsets, E, R, row_vecs, (u32x4*)x_scattered);
+  return hipGetLastError();
+}
+
+}  // namespace moe_launch

@@ -67,6 +67,8 @@ __all__ = [
     "scatter_rows",
     "silu",
     "expert_ffn",
+    "grouped_swiglu_up",
+    "grouped_down",
     "grouped_experts",
     "gather_combine",
     "shared_expert",
@@ -242,6 +244,46 @@ def expert_ffn(xrows, w1, w2, *, contract: bool = False, dtype=np.float64):
     return a, a @ W2
 
 
+def _group_bounds(offsets, stale_row_bound=None):
+    off = np.asarray(offsets, np.int64)
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if stale_row_bound is not None:
+            hi = min(hi, lo + int(stale_row_bound))
+        yield e, lo, hi
+
+
+def grouped_swiglu_up(Xs, offsets, W1, *, contract: bool = False, dtype=np.float64,
+                      _stale_row_bound: int | None = None) -> np.ndarray:
+    """First half of every expert over its group: A[r] = silu(X_s[r] W1[e][:, :I]) * (X_s[r] W1[e][:, I:]).
+
+    Group e is rows [offsets[e], offsets[e+1]); rows outside every group stay NaN.
+    ``_stale_row_bound`` exists only for the mutation test (see grouped_experts).
+    """
+    Xs = np.asarray(Xs)
+    I = np.asarray(W1[0]).shape[1] // 2
+    A = np.full((Xs.shape[0], I), np.nan, dtype)
+    for e, lo, hi in _group_bounds(offsets, _stale_row_bound):
+        if hi > lo:
+            h = np.asarray(Xs[lo:hi], dtype) @ np.asarray(W1[e], dtype)
+            a = silu(h[:, :I]) * h[:, I:]
+            if contract:
+                a = bf16_rne(a.astype(np.float32)).astype(dtype)
+            A[lo:hi] = a
+    return A
+
+
+def grouped_down(A, offsets, W2, *, dtype=np.float64, _stale_row_bound: int | None = None) -> np.ndarray:
+    """Second half of every expert over its group: Y_s[r] = A[r] W2[e]; other rows stay NaN."""
+    A = np.asarray(A)
+    H = np.asarray(W2[0]).shape[1]
+    Ys = np.full((A.shape[0], H), np.nan, dtype)
+    for e, lo, hi in _group_bounds(offsets, _stale_row_bound):
+        if hi > lo:
+            Ys[lo:hi] = np.asarray(A[lo:hi], dtype) @ np.asarray(W2[e], dtype)
+    return Ys
+
+
 def grouped_experts(Xs, offsets, W1, W2, *, contract: bool = False, dtype=np.float64,
                     _stale_row_bound: int | None = None):
     """Per-expert FFN over the expert-grouped rows.
@@ -255,21 +297,9 @@ def grouped_experts(Xs, offsets, W1, W2, *, contract: bool = False, dtype=np.flo
     that many rows per group, emulating the stale bound that page describes.
     Returns (A [R, I], Y_s [R, H]).
     """
-    Xs = np.asarray(Xs)
-    off = np.asarray(offsets, np.int64)
-    R = Xs.shape[0]
-    I = np.asarray(W2[0]).shape[0]
-    H = np.asarray(W2[0]).shape[1]
-    A = np.full((R, I), np.nan, dtype)
-    Ys = np.full((R, H), np.nan, dtype)
-    for e in range(len(off) - 1):
-        lo, hi = int(off[e]), int(off[e + 1])
-        if _stale_row_bound is not None:
-            hi = min(hi, lo + int(_stale_row_bound))
-        if hi > lo:
-            a, y = expert_ffn(Xs[lo:hi], W1[e], W2[e], contract=contract, dtype=dtype)
-            A[lo:hi] = a
-            Ys[lo:hi] = y
+    A = grouped_swiglu_up(Xs, offsets, W1, contract=contract, dtype=dtype,
+                          _stale_row_bound=_stale_row_bound)
+    Ys = grouped_down(A, offsets, W2, dtype=dtype, _stale_row_bound=_stale_row_bound)
     return A, Ys
 
 

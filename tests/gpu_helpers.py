@@ -1,0 +1,65 @@
+"""Helpers shared by the GPU parity tests (comparison metrics and tolerances)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+U32 = 2.0 ** -24   # unit roundoff of float32
+
+# Output tolerances: bf16 workloads against the oracle in contract mode
+# (the SwiGLU output rounded to bf16 where the kernels round it), float32
+# workloads against the plain oracle.
+TOL = {"bf16": {"max_abs": 2e-2, "rel_fro": 1e-2}, "f32": {"max_abs": 1e-4, "rel_fro": 1e-4}}
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 (or integer) host copy of a device tensor."""
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def err_metrics(y, ref) -> tuple[float, float]:
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = y - ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+
+
+def assert_output_close(y, ref, dtype: str, what: str = "y"):
+    assert np.isfinite(y).all(), f"{what}: non-finite values"
+    mx, rel = err_metrics(y, ref)
+    tol = TOL[dtype]
+    assert mx <= tol["max_abs"] and rel <= tol["rel_fro"], \
+        f"{what}: max|err| {mx:.3e} (tol {tol['max_abs']}), rel_fro {rel:.3e} (tol {tol['rel_fro']})"
+    return mx, rel
+
+
+def logits_error_bound(x, w, bias=None):
+    """Bound on |fp32-accumulated logits - exact logits|, plus the oracle's own
+    rounding to float32 and the bias add: gamma_H * sum|x||w| (gamma_n =
+    n u / (1 - n u)) doubled for slack, plus two float32 ulps of the value."""
+    x = np.abs(np.asarray(x, np.float64))
+    w = np.abs(np.asarray(w, np.float64))
+    H = x.shape[1]
+    gamma = H * U32 / (1 - H * U32)
+    mag = x @ w
+    b = 0.0 if bias is None else np.abs(np.asarray(bias, np.float64))[None, :]
+    return 2.0 * gamma * mag + 4.0 * U32 * (mag + b) + 1e-30
+
+
+def check_routing(logits_gpu, ids_gpu, w_gpu, x, wr, bias, top_k, oracle):
+    """Route parity: logits within the certified bound of the oracle's; top-k
+    bit-exact against the oracle applied to the GPU's own logits; weights
+    within 1e-6 of the oracle's softmax of those logits."""
+    ref_logits = oracle.router_logits(x, wr, bias)
+    bound = logits_error_bound(x, wr, bias)
+    excess = np.abs(logits_gpu.astype(np.float64) - ref_logits) - bound
+    assert excess.max() <= 0, f"logits outside the certified bound by {excess.max():.3e}"
+    ids_ref = oracle.topk_select(logits_gpu, top_k)
+    assert np.array_equal(ids_gpu, ids_ref), f"top-k differs on {int((ids_gpu != ids_ref).any(1).sum())} tokens"
+    w_ref = oracle.route_weights(logits_gpu, ids_gpu)
+    assert np.max(np.abs(w_gpu - w_ref)) <= 1e-6
+    # how many tokens' routes would flip under the oracle's own logits (near ties)
+    return int((oracle.topk_select(ref_logits, top_k) != ids_gpu).any(1).sum())

@@ -1,0 +1,98 @@
+"""The C-ABI library: it builds for gfx950, loads, exports every call the header
+declares, and rejects invalid arguments on the host before touching a GPU.
+No kernel is launched here (CPU only)."""
+
+import ctypes
+
+import pytest
+
+from mixture_experts_ffn_05_amd import binding as B
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = B.header_functions()
+    assert {"moe_route", "moe_build_scatter", "moe_grouped_swiglu_fc1", "moe_grouped_fc2",
+            "moe_gather_combine", "moe_shared_expert"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B._SIGNATURES) == set(names)
+
+
+def test_status_names_and_version(lib):
+    assert lib.moe_status_name(0) == b"MOE_OK"
+    assert lib.moe_status_name(3) == b"MOE_ERR_WORKSPACE"
+    assert lib.moe_status_name(99) == b"MOE_STATUS_UNKNOWN"
+    assert lib.moe_version() == 100
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_route_validation(lib):
+    args = dict(dt=1, x=FAKE, w=FAKE, b=None, T=4, H=16, E=8, k=2, ids=FAKE, w_out=FAKE, logits=FAKE)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.moe_route(a["dt"], a["x"], a["w"], a["b"], a["T"], a["H"], a["E"], a["k"], a["ids"],
+                             a["w_out"], a["logits"], None)
+
+    assert call(x=None) == 1 and "x must not be NULL" in _err(lib)
+    assert call(k=0) == 1 and "top_k must be positive" in _err(lib)
+    assert call(k=9) == 1 and "exceeds E" in _err(lib)
+    assert call(T=0) == 1 and "T must be >= 1" in _err(lib)
+    assert call(H=12) == 2 and "H must be a multiple of 8" in _err(lib)
+    assert call(E=2048, k=2) == 2 and "E must be <=" in _err(lib)
+    assert call(E=64, k=40) == 2 and "top_k must be <=" in _err(lib)
+    assert call(dt=7) == 1 and "dt must be" in _err(lib)
+    assert call(logits=None) == 1 and "logits" in _err(lib)
+
+
+def test_scatter_validation_and_workspace(lib):
+    need = lib.moe_build_scatter_workspace_bytes(128, 2, 8)
+    assert need > 0
+    assert lib.moe_build_scatter_workspace_bytes(0, 2, 8) == 0
+
+    def call(ws=FAKE, ws_bytes=need, k=2, E=8):
+        return lib.moe_build_scatter(1, FAKE, FAKE, 128, 256, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(ws=None) == 3 and "workspace needs" in _err(lib)
+    assert call(ws_bytes=need - 1) == 3
+    assert call(k=0) == 1
+    assert call(E=0) == 1
+    assert lib.moe_build_scatter(1, FAKE, FAKE, 128, 256, 8, 2, FAKE, None, FAKE, FAKE, FAKE, FAKE, need,
+                                 None) == 1 and "row_token" in _err(lib)
+
+
+def test_grouped_gemm_validation(lib):
+    assert lib.moe_grouped_swiglu_fc1(1, FAKE, FAKE, FAKE, 256, 256, 8, 100, FAKE, None) == 2
+    assert "I must be a multiple of 8" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1(1, FAKE, None, FAKE, 256, 256, 8, 128, FAKE, None) == 1
+    assert "expert_offsets" in _err(lib)
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 0, 128, 8, 256, FAKE, None) == 1
+    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 256, 128, 8, 250, FAKE, None) == 2
+
+
+def test_combine_and_shared_validation(lib):
+    assert lib.moe_gather_combine(FAKE, FAKE, FAKE, 4, 16, 2, 2, FAKE, None) == 1
+    assert "accumulate must be 0 or 1" in _err(lib)
+    assert lib.moe_gather_combine(FAKE, FAKE, FAKE, 4, 16, 0, 0, FAKE, None) == 1
+    need = lib.moe_shared_expert_workspace_bytes(1, 64, 128)
+    assert need >= 64 * 128 * 2 + 64 * 4
+    # half-specified shared branch: a width without its weights
+    assert lib.moe_shared_expert(1, FAKE, FAKE, None, None, 64, 256, 128, 1, FAKE, FAKE, need, None) == 1
+    assert "ws2 must not be NULL" in _err(lib)
+    assert lib.moe_shared_expert(1, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, need - 1, None) == 3
+
+
+def test_build_compiles_all_kernels_for_gfx950():
+    import __graft_entry__ as ge
+    ge.build()
+    assert B.load() is not None
