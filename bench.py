@@ -79,7 +79,8 @@ def run_step(layer, bufs, cfg, bias_t, events=None):
     x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     rec(0)
-    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits)
+    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                bufs.route_ws)
     rec(1)
     B.moe_build_scatter(x, bufs.topk_ids, cfg.E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
                         bufs.status_words, bufs.x_scattered, bufs.scatter_ws)

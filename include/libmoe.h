@@ -80,10 +80,17 @@ int moe_version(void);
  * x [T, H] (dt), w_router [H, E] (dt), logit_bias [E] fp32 or NULL for none,
  * topk_ids [T, top_k] int32 out, topk_weights [T, top_k] fp32 out,
  * logits [T, E] fp32 out (required): the logits exactly as top-k saw them.
+ * workspace: device scratch of at least moe_route_workspace_bytes(dt, H, E)
+ * bytes (it receives the router weight transposed to [E rounded up to 16, H];
+ * may be NULL when that size is 0), contents undefined on entry and exit.
  */
 moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
                      int32_t T, int32_t H, int32_t E, int32_t top_k,
-                     int32_t* topk_ids, float* topk_weights, float* logits, void* stream);
+                     int32_t* topk_ids, float* topk_weights, float* logits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_route needs for (dt, H, E). */
+size_t moe_route_workspace_bytes(moe_dtype dt, int32_t H, int32_t E);
 
 /* Workspace bytes moe_build_scatter needs for (T, top_k, E). */
 size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E);

@@ -38,7 +38,9 @@ _SIGNATURES = {
     "moe_status_name": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_int, []),
-    "moe_route": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "moe_route": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size,
+                           _vp]),
+    "moe_route_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_build_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_build_scatter": (_c_int, [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_size, _vp]),
@@ -114,16 +116,23 @@ def _stream(stream, device):
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
 
 
-def moe_route(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, stream=None):
+def moe_route_workspace_bytes(dtype, H, E) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_route_workspace_bytes(dt, int(H), int(E)))
+
+
+def moe_route(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, workspace, stream=None):
     lib = load()
     T, H = x.shape
     E = w_router.shape[1]
     dev = x.device
+    ws_ptr = _ptr(workspace, "workspace", torch.uint8, None, dev) if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
     args = (_dt(x), _ptr(x, "x"), _ptr(w_router, "w_router", x.dtype, (H, E), dev),
             _ptr(logit_bias, "logit_bias", torch.float32, (E,), dev), T, H, E, int(top_k),
             _ptr(topk_ids, "topk_ids", torch.int32, (T, top_k), dev),
             _ptr(topk_weights, "topk_weights", torch.float32, (T, top_k), dev),
-            _ptr(logits, "logits", torch.float32, (T, E), dev), _stream(stream, dev))
+            _ptr(logits, "logits", torch.float32, (T, E), dev), ws_ptr, ws_bytes, _stream(stream, dev))
     _check(lib.moe_route(*args))
 
 
@@ -221,6 +230,8 @@ class MoELayerBuffers:
         self.act = torch.empty((R, I), dtype=dtype, device=device)
         self.y_rows = torch.empty((R, H), dtype=f32, device=device)
         self.y = torch.empty((T, H), dtype=f32, device=device)
+        rb = moe_route_workspace_bytes(dtype, H, E)
+        self.route_ws = torch.empty((max(rb, 1),), dtype=torch.uint8, device=device)
         self.scatter_ws = torch.empty((moe_build_scatter_workspace_bytes(T, top_k, E),), dtype=torch.uint8,
                                       device=device)
         self.shared_ws = (torch.empty((moe_shared_expert_workspace_bytes(dtype, T, I_s),), dtype=torch.uint8,
@@ -237,7 +248,8 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
     if bufs is None:
         bufs = MoELayerBuffers(T, H, E, top_k, I2 // 2, I_s, x.dtype, x.device)
     if routes is None:
-        moe_route(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, stream)
+        moe_route(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws,
+                  stream)
         ids, w = bufs.topk_ids, bufs.topk_weights
     else:
         ids, w = routes

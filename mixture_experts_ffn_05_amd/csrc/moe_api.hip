@@ -118,8 +118,14 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int moe_version(void) { return kVersion; }
 
+size_t moe_route_workspace_bytes(moe_dtype dt, int32_t H, int32_t E) {
+  if (H < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  return moe_launch::route_workspace_bytes((int)dt, H, E);
+}
+
 moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias, int32_t T, int32_t H,
-                     int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights, float* logits, void* stream) {
+                     int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights, float* logits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const char* fn = "moe_route";
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
@@ -135,8 +141,12 @@ moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const fl
   MOE_CHECK(need_mult8(H, fn, "H"));
   MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
   MOE_CHECK(need_rows((int64_t)T * E / 8, fn, "T*E/8"));
+  const size_t need = moe_launch::route_workspace_bytes((int)dt, H, E);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
   return hip_result(moe_launch::route((int)dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
-                                      (hipStream_t)stream),
+                                      workspace, (hipStream_t)stream),
                     fn);
 }
 
@@ -190,7 +200,7 @@ moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const i
   MOE_CHECK(need_mult8(I, fn, "I"));
   MOE_CHECK(need_rows(R, fn, "R"));
   return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x_scattered, expert_offsets, E, R, w1,
-                                                   (int64_t)H * 2 * I, H, I, act, cu_count(), (hipStream_t)stream),
+                                                   (int64_t)H * 2 * I, H, I, act, 0, cu_count(), (hipStream_t)stream),
                     fn);
 }
 
@@ -210,7 +220,7 @@ moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_
   MOE_CHECK(need_mult8(I, fn, "I"));
   MOE_CHECK(need_rows(R, fn, "R"));
   return hip_result(moe_launch::grouped_fc2((int)dt, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H, y_rows,
-                                            nullptr, 0, 1, cu_count(), (hipStream_t)stream),
+                                            nullptr, 0, 1, 0, cu_count(), (hipStream_t)stream),
                     fn);
 }
 
@@ -263,8 +273,8 @@ moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const
   float* gate = w_gate ? (float*)(ws + align256((size_t)T * I_s * elem_size(dt))) : nullptr;
   const int cus = cu_count();
   if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate((int)dt, x, w_gate, T, H, gate, s), fn));
-  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act, cus, s), fn));
-  return hip_result(moe_launch::grouped_fc2((int)dt, act, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate, 0, cus, s),
+  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act, 1, cus, s), fn));
+  return hip_result(moe_launch::grouped_fc2((int)dt, act, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate, 0, 1, cus, s),
                     fn);
 }
 

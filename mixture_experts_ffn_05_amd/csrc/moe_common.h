@@ -78,8 +78,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // returns hipSuccess or the launch error; arguments were validated by the API.
 namespace moe_launch {
 
+size_t route_workspace_bytes(int dt, int H, int E);
 hipError_t route(int dt, const void* x, const void* w_router, const float* bias, int T, int H, int E,
-                 int top_k, int32_t* ids, float* weights, float* logits, hipStream_t s);
+                 int top_k, int32_t* ids, float* weights, float* logits, void* workspace, hipStream_t s);
 
 size_t scatter_workspace_bytes(int T, int top_k, int E);
 hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H, int E, int top_k,
@@ -87,12 +88,14 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
                          int32_t* status_words, void* x_scattered, void* workspace, hipStream_t s);
 
 // Grouped GEMMs.  `offsets` may be null: one group of `rows` rows.
+// `role` (0 routed experts, 1 shared expert) only selects a separately named
+// kernel instantiation so that profiles tell the two apart.
 hipError_t grouped_swiglu_fc1(int dt, const void* a, const int32_t* offsets, int groups, int rows,
                               const void* w1, int64_t w1_group_stride, int K, int I, void* act,
-                              int cu_count, hipStream_t s);
+                              int role, int cu_count, hipStream_t s);
 hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int groups, int rows,
                        const void* w2, int64_t w2_group_stride, int K, int N, float* out,
-                       const float* row_scale, int accumulate, int plain_store, int cu_count,
+                       const float* row_scale, int accumulate, int plain_store, int role, int cu_count,
                        hipStream_t s);
 
 hipError_t gather_combine(const float* y_rows, const int32_t* scatter_index, const float* weights,

@@ -9,7 +9,29 @@
 // covered and an empty group reads no weights.  The host only sizes a
 // persistent grid from the worst case floor(R/128) + min(E, R) row tiles.
 //
-// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+// bf16 pipelined path (reduction size a multiple of 64; every configuration):
+//   * workgroup tile 128 rows x BN staged weight columns (BN = 128 or 256),
+//     reduction slice 64, 4 waves in a 2x2 arrangement, each owning 64 rows x
+//     BN/2 columns as 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, fp32
+//     accumulate).
+//   * operands travel HBM -> LDS with global_load_lds_dwordx4 (no register
+//     round trip) through a STAGES-deep ring of LDS buffers, so several
+//     reduction slices are in flight while the MFMAs consume an older one.
+//     Each lane's 16 bytes land at LDS base + 16*lane, so the XOR swizzles
+//     below are applied by choosing which 16-byte chunk each lane fetches.
+//   * activations ([rows, K], K-contiguous) sit in LDS as 128-byte rows with
+//     the 16-byte chunk index XORed by (row >> 1) & 7; an MFMA A fragment is
+//     one conflict-free ds_read_b128.
+//   * weights ([K, N] per expert, N-contiguous) sit in LDS in that natural
+//     layout (chunk index XORed by 4*(k & 3)); the B fragment (8 consecutive
+//     k of one column) is assembled from two ds_read_b64_tr_b16 transpose
+//     reads: within each 16-lane group, lane c receives element c%4 of the
+//     8-byte rows read by lanes c/4, c/4+4, c/4+8 and c/4+12, so lanes that
+//     read a 4 (k) x 16 (n) block get 4 consecutive k of their own column.
+//   * rows past a group's end and columns past N are fetched from clamped
+//     addresses; they only feed output rows/columns that are never stored.
+//
+// bf16 generic path (any multiple-of-8 sizes; register-staged):
 //   * workgroup tile 128 rows x 128 staged weight columns, reduction slice 64;
 //     4 waves in a 2x2 arrangement, each owning 64 rows x 64 columns
 //     (2x2 blocks of 32x32).  fc1 stages the gate columns [n0, n0+64) and the
@@ -28,6 +50,14 @@
 //     XCDs round-robin) and share its L2.
 // f32 path: one thread per output element (used by the float32 workload).
 #include "moe_common.h"
+
+// Build-time switches used when tuning (the defaults are the shipped configuration).
+#ifndef MOE_FRAG_PREFETCH
+#define MOE_FRAG_PREFETCH 1
+#endif
+#ifndef MOE_PIPE_VARIANT
+#define MOE_PIPE_VARIANT 0
+#endif
 
 namespace moe {
 namespace {
@@ -191,30 +221,28 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16(GemmParams<bf16_t> p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[kBM * kLds];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[kBNB * kLds];
-  __shared__ int32_t sOff[kMaxExperts + 1];
-  __shared__ int32_t sPre[kMaxExperts + 1];
-  __shared__ int32_t sWave[4];
-
+// Group bounds (clamped to [0, rows], so that no tile can leave the buffers)
+// and the exclusive prefix of row tiles per group, built in LDS by the whole
+// workgroup of NT threads.  Returns the number of row tiles.
+template <int BM, int NT, typename T>
+__device__ __forceinline__ int build_tile_prefix(const GemmParams<T>& p, int32_t* sOff, int32_t* sPre,
+                                                 int32_t* sWave) {
+  constexpr int kPer = (kMaxExperts + NT - 1) / NT;  // consecutive groups per thread
+  constexpr int kWaves = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.groups;
-  // Group bounds, clamped to [0, rows] so that no tile can leave the buffers.
-  for (int i = tid; i <= G; i += kThreads) {
-    int v = p.offsets ? p.offsets[i] : (i == 0 ? 0 : p.rows);
+  for (int i = tid; i <= G; i += NT) {
+    const int v = p.offsets ? p.offsets[i] : (i == 0 ? 0 : p.rows);
     sOff[i] = min(max(v, 0), p.rows);
   }
   __syncthreads();
-  // Exclusive prefix of row tiles per group (4 consecutive groups per thread).
-  int loc[4], s = 0;
+  int loc[kPer], s = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = tid * 4 + q;
+  for (int q = 0; q < kPer; ++q) {
+    const int g = tid * kPer + q;
     const int c = g < G ? max(sOff[g + 1] - sOff[g], 0) : 0;
     loc[q] = s;
-    s += (c + kBM - 1) / kBM;
+    s += (c + BM - 1) / BM;
   }
   const int incl = wave_inclusive_scan(s);
   if (lane == 63) sWave[wave] = incl;
@@ -223,30 +251,320 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16(GemmParams<bf16
   for (int i = 0; i < wave; ++i) base += sWave[i];
   const int excl = base + incl - s;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = tid * 4 + q;
+  for (int q = 0; q < kPer; ++q) {
+    const int g = tid * kPer + q;
     if (g < G) sPre[g] = excl + loc[q];
   }
-  if (tid == 0) sPre[G] = sWave[0] + sWave[1] + sWave[2] + sWave[3];
+  if (tid == 0) {
+    int total = 0;
+    for (int i = 0; i < kWaves; ++i) total += sWave[i];
+    sPre[G] = total;
+  }
   __syncthreads();
+  return sPre[G];
+}
 
-  const int64_t nt = p.n_tiles;
-  const int64_t total = (int64_t)sPre[G] * nt;
+struct TileCoord {
+  int g, row0, row_end, ntile;
+};
+
+// Tile ids run expert-major, then column tile, then row tile.
+template <int BM>
+__device__ __forceinline__ TileCoord decode_tile(int64_t id, int G, int64_t nt, const int32_t* sOff,
+                                                 const int32_t* sPre) {
+  int lo = 0, hi = G - 1;  // largest g with sPre[g]*nt <= id: a non-empty group
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)sPre[mid] * nt <= id) lo = mid; else hi = mid - 1;
+  }
+  const int64_t local = id - (int64_t)sPre[lo] * nt;
+  const int mt = sPre[lo + 1] - sPre[lo];
+  TileCoord c;
+  c.g = lo;
+  c.ntile = (int)(local / mt);
+  c.row0 = sOff[lo] + (int)(local % mt) * BM;
+  c.row_end = sOff[lo + 1];
+  return c;
+}
+
+// Consecutive slots run on one XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int xcd_slot() {
   const int nslot = gridDim.x;
-  const int slot = (blockIdx.x % kXcds) * (nslot / kXcds) + blockIdx.x / kXcds;
-  for (int64_t id = slot; id < total; id += nslot) {
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)sPre[mid] * nt <= id) lo = mid; else hi = mid - 1;
+  return (blockIdx.x % kXcds) * (nslot / kXcds) + blockIdx.x / kXcds;
+}
+
+template <int EPI, int ROLE>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_generic(GemmParams<bf16_t> p) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[kBM * kLds];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[kBNB * kLds];
+  __shared__ int32_t sOff[kMaxExperts + 1];
+  __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sWave[4];
+  const int mtiles = build_tile_prefix<kBM, kThreads>(p, sOff, sPre, sWave);
+  const int64_t nt = p.n_tiles;
+  const int64_t total = (int64_t)mtiles * nt;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const TileCoord c = decode_tile<kBM>(id, p.groups, nt, sOff, sPre);
+    run_tile_bf16<EPI>(p, c.g, c.row0, c.row_end, c.ntile * (EPI == kSwiGLU ? 64 : 128), sA, sB);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Pipelined bf16 path
+// ------------------------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define MOE_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+#define MOE_GLOBAL(T, ptr) ((const __attribute__((address_space(1))) T*)(ptr))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() (and a fence on LDS
+// alone) makes the compiler wait for every outstanding direct load first --
+// they count as vector-memory operations -- which would drain the ring.  The
+// ring's loads are waited for explicitly with wait_vmcnt before this barrier;
+// the "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Shape of one pipelined configuration: workgroup tile BM x BN (staged weight
+// columns), reduction slice BK, STAGES-deep LDS ring; WM x WN waves, each
+// owning (BM/WM) x (BN/WN) as 32x32 MFMA blocks.
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_ = 2, int WN_ = 2>
+struct PipeCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int NT = kWaves * kWave;
+  static constexpr int kARow = BK * 2;                  // bytes of one activation row in LDS
+  static constexpr int kAChunks = BK / 8;               // 16-byte chunks per activation row
+  static constexpr int kAStage = BM * kARow;
+  static constexpr int kBStage = BK * BN * 2;
+  static constexpr int kStage = kAStage + kBStage;
+  static constexpr int kALoads = kAStage / 1024 / kWaves;  // 1 KiB direct loads per wave per slice
+  static constexpr int kBLoads = kBStage / 1024 / kWaves;
+  static constexpr int kLoads = kALoads + kBLoads;
+  static constexpr int kARowsPerLoad = 1024 / kARow;
+  static constexpr int kBChunks = BN / 8;               // 16-byte chunks per weight row
+  static constexpr int kBRowsPerLoad = 64 / kBChunks;
+  static constexpr int kMB = BM / WM / 32;              // 32-row blocks per wave
+  static constexpr int kNB = BN / WN / 32;              // 32-column blocks per wave
+  static constexpr int kKS = BK / 16;                   // MFMA k-substeps per slice
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kWgsPerCu = (kLds <= 72 * 1024 && kWaves == 4) ? 2 : 1;
+  static_assert(kAStage % (1024 * kWaves) == 0 && kBStage % (1024 * kWaves) == 0,
+                "slices must split into 1 KiB loads per wave");
+  static_assert(kMB >= 1 && kNB >= 2 && kNB % 2 == 0, "wave tile must hold whole 32x32 blocks");
+  static_assert(kBChunks >= 16, "the weight swizzle needs at least 16 chunks per row");
+};
+
+// LDS swizzles of the ring (gfx950 LDS: 64 banks of 4 bytes; a 16-byte read
+// serves 16 lanes per cycle, an 8-byte read 32 lanes).
+//  * an A fragment read touches one 16-byte chunk of 16 consecutive
+//    activation rows per cycle.  A 256-byte bank window holds W = 256/rowbytes
+//    rows; XORing the chunk index with (row / W) mod chunks puts the 16 rows
+//    into 16 distinct bank groups.
+//  * a transpose read of 32 lanes touches 4 consecutive k rows x 32 columns
+//    (4 chunks per row); XORing the chunk index with 4 * (k & 3) sends the 4
+//    rows to disjoint 64-byte quarters of the bank window.
+template <class C>
+__device__ __forceinline__ int a_swizzle(int row) { return (row / (256 / C::kARow)) % C::kAChunks; }
+__device__ __forceinline__ int b_swizzle(int k) { return 4 * (k & 3); }
+
+template <int EPI, class C>
+__device__ __forceinline__ int pipe_col_base(int nb, int wn) {
+  // SwiGLU: blocks [0, kNB/2) are gate columns, [kNB/2, kNB) the matching up columns.
+  return EPI == kSwiGLU
+             ? ((nb < C::kNB / 2 ? 0 : C::BN / 2) + wn * (C::BN / 2 / C::WN) + 32 * (nb % (C::kNB / 2)))
+             : (wn * (C::BN / C::WN) + 32 * nb);
+}
+
+// Direct loads of one reduction slice (activations, then weights) into a ring stage.
+template <class C>
+__device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const bf16_t* a_k, const bf16_t* b_k,
+                                           const int64_t* a_off, const int* b_off) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i)
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                     MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i)
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                     MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, 0);
+}
+
+// One pipeline step: start the loads of a future slice into `wst`, then run
+// the MFMAs of the slice held in `rst`.  The two stages never coincide; the
+// __restrict__ qualifiers tell the compiler so, which lets it skip waiting
+// for the in-flight direct loads before the LDS reads below.
+template <int EPI, class C>
+__device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
+                                          bool issue, const bf16_t* a_k, const bf16_t* b_k, const int64_t* a_off,
+                                          const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm) {
+  const int lane = threadIdx.x & 63;
+  if (issue) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                       MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                       MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
+                                       0);
+  }
+  const unsigned char* As = rst;
+  const unsigned char* Bs = rst + C::kAStage;
+  const int grp = lane >> 4, s16 = lane & 15;
+  const int b_row_in = 8 * (grp >> 1) + (s16 >> 2);  // k row inside a 16-k substep; row & 3 == s16 >> 2
+  const int b_chunk_lo = (s16 & 3) >> 1;
+  const int b_byte = (s16 & 1) * 8;
+
+  auto load_frags = [&](int ks, u32x4 (&af)[C::kMB], u32x4 (&bfr)[C::kNB]) {
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb) {
+      const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+      const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(m);
+      af[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
     }
-    const int g = lo;
-    const int64_t local = id - (int64_t)sPre[g] * nt;
-    const int mt = sPre[g + 1] - sPre[g];
-    const int ntile = (int)(local / mt), mtile = (int)(local % mt);
-    const int row0 = sOff[g] + mtile * kBM;
-    const int n0 = ntile * (EPI == kSwiGLU ? 64 : 128);
-    run_tile_bf16<EPI>(p, g, row0, sOff[g + 1], n0, sA, sB);
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb) {
+      const int c0 = pipe_col_base<EPI, C>(nb, wn) + 16 * (grp & 1);
+      const int row = 16 * ks + b_row_in;
+      const int chunk = (c0 / 8 + b_chunk_lo) ^ b_swizzle(s16 >> 2);
+      const unsigned char* ptr = Bs + row * (2 * C::BN) + chunk * 16 + b_byte;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * (2 * C::BN)));
+      bfr[nb] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+    }
+  };
+  // Fragments of substep ks+1 are read while the MFMAs of substep ks run.
+  u32x4 af[2][C::kMB], bfr[2][C::kNB];
+  load_frags(0, af[0], bfr[0]);
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) {
+    if (ks + 1 < C::kKS) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[ks & 1][mb], bfr[ks & 1][nb], acc[mb][nb]);
+  }
+}
+
+template <int EPI, class C>
+__device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+                                              unsigned char* __restrict__ smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
+  const int K = p.K, ldb = p.ldb;
+
+  // Per-lane source offsets (elements) of this wave's direct loads, slice 0.
+  int64_t a_off[C::kALoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
+    const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
+    const int row = min(row0 + r, row_end - 1);
+    a_off[i] = (int64_t)row * K + chunk * 8;
+  }
+  int b_off[C::kBLoads];
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i) {
+    const int kr = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
+    const int chunk = (lane % C::kBChunks) ^ b_swizzle(kr);
+    int col;
+    if (EPI == kSwiGLU) {
+      const int half = C::kBChunks / 2;
+      const int nc = n0 + 8 * (chunk % half);
+      col = (nc < p.N ? nc : 0) + (chunk < half ? 0 : p.up_off);
+    } else {
+      const int nc = n0 + 8 * chunk;
+      col = nc < p.N ? nc : 0;
+    }
+    b_off[i] = kr * ldb + col;
+  }
+  const int nk = K / C::BK;
+
+  f32x16 acc[C::kMB][C::kNB];
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+  const bf16_t* a_base = p.a;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk)
+      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + (int64_t)s * C::BK * ldb, a_off, b_off);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    const int kn = kt + C::STAGES - 1;
+    pipe_step<EPI, C>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
+                      a_base + kn * C::BK, bg + (int64_t)kn * C::BK * ldb, a_off, b_off, acc, wn, wm);
+  }
+  lds_barrier();  // every wave is done with the ring before the next tile refills it
+
+  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = row0 + wm * (C::BM / C::WM) + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (row >= row_end) continue;
+      if (EPI == kSwiGLU) {
+#pragma unroll
+        for (int j = 0; j < C::kNB / 2; ++j) {
+          const int col = n0 + wn * (C::BN / 2 / C::WN) + 32 * j + (lane & 31);
+          if (col < p.N)
+            ((bf16_t*)p.out)[(int64_t)row * p.N + col] =
+                (bf16_t)f32_to_bf16_rne(swiglu(acc[mb][j][i], acc[mb][j + C::kNB / 2][i]));
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < C::kNB; ++nb) {
+          const int col = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
+          if (col >= p.N) continue;
+          float* o = (float*)p.out + (int64_t)row * p.N + col;
+          const float v = acc[mb][nb][i];
+          if (EPI == kStoreF32) {
+            *o = v;
+          } else {
+            const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
+            *o = (p.accumulate ? *o : 0.0f) + sc * v;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, class C, int ROLE>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(GemmParams<bf16_t> p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int32_t sOff[kMaxExperts + 1];
+  __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sWave[C::kWaves];
+  const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave);
+  const int64_t nt = p.n_tiles;
+  const int64_t total = (int64_t)mtiles * nt;
+  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
+    run_tile_pipe<EPI, C>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
   }
 }
 
@@ -291,8 +609,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmParams<float> p) {
   }
 }
 
-int persistent_grid(int64_t upper_tiles, int cu_count) {
-  int64_t g = upper_tiles < (int64_t)2 * cu_count ? upper_tiles : (int64_t)2 * cu_count;
+int persistent_grid(int64_t upper_tiles, int slots) {
+  int64_t g = upper_tiles < (int64_t)slots ? upper_tiles : (int64_t)slots;
   if (g < 1) g = 1;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)g;
@@ -302,50 +620,108 @@ int64_t upper_row_tiles(int rows, int groups) {
   return (int64_t)rows / kBM + (groups < rows ? groups : rows);
 }
 
+// Launch one pipelined instantiation (persistent grid, dynamic LDS ring).
+template <int EPI, class C, int ROLE>
+hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&grouped_gemm_bf16_pipe<EPI, C, ROLE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (attr != hipSuccess) return attr;
+  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  p.n_tiles = (p.N + out_cols - 1) / out_cols;
+  const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
+  const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
+  hipLaunchKernelGGL((grouped_gemm_bf16_pipe<EPI, C, ROLE>), dim3(grid), dim3(C::NT), C::kLds, s, p);
+  return hipGetLastError();
+}
+
+// Pipelined configurations (BM, BN, BK, STAGES).
+typedef PipeCfg<128, 128, 64, 2> Cfg1;
+typedef PipeCfg<128, 128, 32, 4> Cfg2;
+typedef PipeCfg<256, 256, 32, 4> Cfg3;
+typedef PipeCfg<256, 256, 64, 2> Cfg4;
+typedef PipeCfg<128, 256, 64, 3> Cfg5;
+typedef PipeCfg<256, 128, 32, 4> Cfg6;
+typedef PipeCfg<256, 256, 32, 4, 4, 2> Cfg7;   // 8 waves
+typedef PipeCfg<256, 256, 64, 2, 4, 2> Cfg8;   // 8 waves
+typedef PipeCfg<256, 128, 64, 2, 4, 2> Cfg9;   // 8 waves
+typedef PipeCfg<128, 256, 64, 2, 2, 4> Cfg10;  // 8 waves
+
+// Configuration for a problem, from the host-known sizes only: groups that
+// average 512 rows or more (the shared expert, dense prefill) take the
+// 256x256 tile with 8 waves, which halves the L2->LDS traffic per MFMA and
+// keeps two waves per SIMD; smaller or ragged groups (decode, skewed routing,
+// many experts) take the 128x128 tile with two workgroups per CU, which
+// wastes fewer MFMA rows on partial tiles.  (Measured on MI355X across the
+// Scout-, Qwen2-, DeepSeek-V2-Lite- and DeepSeek-V3-shaped layers.)
+int pick_pipe_variant(const GemmParams<bf16_t>& p, int epi) {
+  if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
+  (void)epi;
+  const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
+  return rows_per_group >= 512 ? 8 : 1;
+}
+
+template <int EPI, int ROLE>
+hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
+  if (p.K % 64 == 0) {
+    switch (pick_pipe_variant(p, EPI)) {
+      case 2: return launch_pipe<EPI, Cfg2, ROLE>(p, cu_count, s);
+      case 3: return launch_pipe<EPI, Cfg3, ROLE>(p, cu_count, s);
+      case 4: return launch_pipe<EPI, Cfg4, ROLE>(p, cu_count, s);
+      case 5: return launch_pipe<EPI, Cfg5, ROLE>(p, cu_count, s);
+      case 6: return launch_pipe<EPI, Cfg6, ROLE>(p, cu_count, s);
+      case 7: return launch_pipe<EPI, Cfg7, ROLE>(p, cu_count, s);
+      case 8: return launch_pipe<EPI, Cfg8, ROLE>(p, cu_count, s);
+      case 9: return launch_pipe<EPI, Cfg9, ROLE>(p, cu_count, s);
+      case 10: return launch_pipe<EPI, Cfg10, ROLE>(p, cu_count, s);
+      default: return launch_pipe<EPI, Cfg1, ROLE>(p, cu_count, s);
+    }
+  }
+  p.n_tiles = EPI == kSwiGLU ? (p.N + 63) / 64 : (p.N + 127) / 128;
+  const int grid = persistent_grid(upper_row_tiles(p.rows, p.groups) * p.n_tiles, 2 * cu_count);
+  hipLaunchKernelGGL((grouped_gemm_bf16_generic<EPI, ROLE>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace moe
 
 namespace moe_launch {
 
 hipError_t grouped_swiglu_fc1(int dt, const void* a, const int32_t* offsets, int groups, int rows, const void* w1,
-                              int64_t w1_group_stride, int K, int I, void* act, int cu_count, hipStream_t s) {
+                              int64_t w1_group_stride, int K, int I, void* act, int role, int cu_count,
+                              hipStream_t s) {
   using namespace moe;
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)a, offsets, groups, rows, K, I, (const bf16_t*)w1, w1_group_stride,
-                         2 * I, I, act, nullptr, 0, (I + 63) / 64};
-    const int grid = persistent_grid(upper_row_tiles(rows, groups) * p.n_tiles, cu_count);
-    hipLaunchKernelGGL(grouped_gemm_bf16<kSwiGLU>, dim3(grid), dim3(kThreads), 0, s, p);
-  } else {
-    GemmParams<float> p{(const float*)a, offsets, groups, rows, K, I, (const float*)w1, w1_group_stride,
-                        2 * I, I, act, nullptr, 0, 0};
-    const int64_t n = (int64_t)rows * I;
-    hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLU>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+                         2 * I, I, act, nullptr, 0, 0};
+    return role ? launch_bf16<kSwiGLU, 1>(p, cu_count, s) : launch_bf16<kSwiGLU, 0>(p, cu_count, s);
   }
+  GemmParams<float> p{(const float*)a, offsets, groups, rows, K, I, (const float*)w1, w1_group_stride,
+                      2 * I, I, act, nullptr, 0, 0};
+  const int64_t n = (int64_t)rows * I;
+  hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLU>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int groups, int rows, const void* w2,
                        int64_t w2_group_stride, int K, int N, float* out, const float* row_scale, int accumulate,
-                       int plain_store, int cu_count, hipStream_t s) {
+                       int plain_store, int role, int cu_count, hipStream_t s) {
   using namespace moe;
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)act, offsets, groups, rows, K, N, (const bf16_t*)w2, w2_group_stride,
-                         N, 0, out, row_scale, accumulate, (N + 127) / 128};
-    const int grid = persistent_grid(upper_row_tiles(rows, groups) * p.n_tiles, cu_count);
-    if (plain_store)
-      hipLaunchKernelGGL(grouped_gemm_bf16<kStoreF32>, dim3(grid), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(grouped_gemm_bf16<kScaleAdd>, dim3(grid), dim3(kThreads), 0, s, p);
-  } else {
-    GemmParams<float> p{(const float*)act, offsets, groups, rows, K, N, (const float*)w2, w2_group_stride,
-                        N, 0, out, row_scale, accumulate, 0};
-    const int64_t n = (int64_t)rows * N;
-    const dim3 grid((unsigned)((n + 255) / 256));
-    if (plain_store)
-      hipLaunchKernelGGL(grouped_gemm_f32<kStoreF32>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(grouped_gemm_f32<kScaleAdd>, grid, dim3(256), 0, s, p);
+                         N, 0, out, row_scale, accumulate, 0};
+    if (plain_store) return role ? launch_bf16<kStoreF32, 1>(p, cu_count, s) : launch_bf16<kStoreF32, 0>(p, cu_count, s);
+    return role ? launch_bf16<kScaleAdd, 1>(p, cu_count, s) : launch_bf16<kScaleAdd, 0>(p, cu_count, s);
   }
+  GemmParams<float> p{(const float*)act, offsets, groups, rows, K, N, (const float*)w2, w2_group_stride,
+                      N, 0, out, row_scale, accumulate, 0};
+  const int64_t n = (int64_t)rows * N;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (plain_store)
+    hipLaunchKernelGGL(grouped_gemm_f32<kStoreF32>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(grouped_gemm_f32<kScaleAdd>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

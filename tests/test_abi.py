@@ -42,7 +42,7 @@ def test_route_validation(lib):
     def call(**kw):
         a = {**args, **kw}
         return lib.moe_route(a["dt"], a["x"], a["w"], a["b"], a["T"], a["H"], a["E"], a["k"], a["ids"],
-                             a["w_out"], a["logits"], None)
+                             a["w_out"], a["logits"], a.get("ws", FAKE), a.get("ws_bytes", 1 << 20), None)
 
     assert call(x=None) == 1 and "x must not be NULL" in _err(lib)
     assert call(k=0) == 1 and "top_k must be positive" in _err(lib)
@@ -53,6 +53,10 @@ def test_route_validation(lib):
     assert call(E=64, k=40) == 2 and "top_k must be <=" in _err(lib)
     assert call(dt=7) == 1 and "dt must be" in _err(lib)
     assert call(logits=None) == 1 and "logits" in _err(lib)
+    assert lib.moe_route_workspace_bytes(1, 16, 8) == 16 * 16 * 2       # E rounded up to 16
+    assert lib.moe_route_workspace_bytes(0, 16, 8) == 0
+    assert call(ws=None) == 3 and "workspace needs" in _err(lib)
+    assert call(ws_bytes=16) == 3
 
 
 def test_scatter_validation_and_workspace(lib):

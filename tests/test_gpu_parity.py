@@ -23,6 +23,8 @@ CASES = [
     wl.LayerConfig("decode1_bf16", "bf16", T=1, H=256, E=64, top_k=6, I=128, I_s=128),
     wl.LayerConfig("wide_bf16", "bf16", T=96, H=384, E=256, top_k=8, I=64, I_s=64),
     wl.LayerConfig("ragged_f32", "f32", T=77, H=136, E=5, top_k=3, I=40, I_s=24, gated=True, fan_in_init=True),
+    # groups of >= 512 rows take the 256x256 tile configuration (routed and shared)
+    wl.LayerConfig("big_groups_bf16", "bf16", T=1100, H=512, E=2, top_k=1, I=320, I_s=192, gated=True),
 ]
 
 
@@ -64,7 +66,8 @@ def test_route_parity(cfg):
     bias = layer["bias"]
     bias_t = torch.from_numpy(bias).to(DEV) if bias is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
-    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits)
+    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                bufs.route_ws)
     torch.cuda.synchronize()
     check_routing(host(bufs.logits), host(bufs.topk_ids), host(bufs.topk_weights), host(x), host(wr), bias,
                   cfg.top_k, O)
@@ -76,7 +79,8 @@ def test_route_with_logit_bias_and_limits():
     wr = wl.make_router(cfg, DEV)
     bias = np.linspace(-1, 1, cfg.E).astype(np.float32)
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, 8, 0, x.dtype, DEV)
-    B.moe_route(x, wr, torch.from_numpy(bias).to(DEV), cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits)
+    B.moe_route(x, wr, torch.from_numpy(bias).to(DEV), cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                bufs.route_ws)
     torch.cuda.synchronize()
     check_routing(host(bufs.logits), host(bufs.topk_ids), host(bufs.topk_weights), host(x), host(wr), bias,
                   cfg.top_k, O)
@@ -89,7 +93,8 @@ def test_topk_ties_and_nan_on_identical_logits():
     x = torch.from_numpy(rng.integers(-1, 2, (T, H)).astype(np.float32)).to(torch.bfloat16).to(DEV)
     wr = torch.from_numpy(rng.integers(0, 2, (H, E)).astype(np.float32)).to(torch.bfloat16).to(DEV)
     bufs = B.MoELayerBuffers(T, H, E, k, 8, 0, torch.bfloat16, DEV)
-    B.moe_route(x, wr, None, k, bufs.topk_ids, bufs.topk_weights, bufs.logits)
+    B.moe_route(x, wr, None, k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                bufs.route_ws)
     torch.cuda.synchronize()
     L = host(bufs.logits)
     assert np.array_equal(L, O.router_logits(host(x), host(wr)))      # exact integer sums
