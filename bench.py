@@ -75,6 +75,22 @@ def roofline(flops, nbytes, seconds):
             "frac": round(a / PEAK_HBM_GBPS, 4)}
 
 
+def committed_traffic(workload):
+    """Calibrated HBM bytes per dispatch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on a different kernel source."""
+    import glob
+    import re
+    from mixture_experts_ffn_05_amd import prof_summary
+    for path in glob.glob(os.path.join(ROOT, "profiles", f"*{workload}*pmc*.md")):
+        m = re.search(r"^TRAFFIC_JSON (.*)$", open(path).read(), re.M)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec and rec.get("gemm_source_hash") == prof_summary.kernel_source_hash():
+            return rec
+    return None
+
+
 def run_step(layer, bufs, cfg, bias_t, events=None):
     x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
@@ -151,6 +167,8 @@ def main():
     ap.add_argument("--workload", default="scout", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--copy-reference-mb", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -167,6 +185,14 @@ def main():
     bias_t = torch.from_numpy(layer["bias"]).to(dev) if layer["bias"] is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, dev)
     torch.cuda.synchronize()
+    if args.copy_reference_mb > 0:
+        n = args.copy_reference_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy reference: {n} bytes read and {n} bytes written by one device copy")
+        del src, dst
 
     for _ in range(args.warmup):
         run_step(layer, bufs, cfg, bias_t)
@@ -192,8 +218,11 @@ def main():
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_bf16<SwiGLU> (moe_grouped_swiglu_fc1)"
+    tr = committed_traffic(cfg.name)
+    roof["traffic"] = round(tr["hbm_bytes_per_dispatch"] / 1e9, 4) if tr else None
+    roof["traffic_unit"] = "GB per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    roof["kernel"] = "grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1, routed experts)"
     gg_s = fc1_s + fc2_s
     gg_tflops = (work["fc1_flops"] + work["fc2_flops"]) / gg_s / 1e12
     gg_gbps = (work["fc1_bytes"] + work["fc2_bytes"]) / gg_s / 1e9

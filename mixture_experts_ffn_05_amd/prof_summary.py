@@ -1,0 +1,103 @@
+"""Summarise rocprofv3 CSV output into the short text kept under profiles/.
+
+    python -m mixture_experts_ffn_05_amd.prof_summary trace <kernel_stats.csv> <out.md> <command...>
+    python -m mixture_experts_ffn_05_amd.prof_summary pmc <fetch_dir> <write_dir> <copy_mib> <kernel_substr> \
+        <out.md> <command...>
+
+`trace` writes per-kernel call counts and average durations.  `pmc` reads two
+counter-collection runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+calibrates both against the device copy of <copy_mib> MiB that the profiled
+command performed first (its counters should read copy_mib*1024 KiB each),
+and writes the calibrated HBM bytes per dispatch of the kernels whose name
+contains <kernel_substr>, plus a JSON line that bench.py reads for the
+roofline object's `traffic` field.  The JSON line records a hash of the GEMM
+source, so a later change of the kernel voids the figure.
+"""
+
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("moe_gemm.hip", "moe_common.h"):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    name = name.replace("moe::(anonymous namespace)::", "")
+    return name if len(name) < 110 else name[:107] + "..."
+
+
+def trace(stats_csv: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# rocprofv3 kernel trace", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg us | total share % |", "|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(run_dir: str, counter: str):
+    path = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out_md: str, command: str) -> None:
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    fcopy = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if v > 0.5 * copy_kib]
+    wcopy = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if v > 0.5 * copy_kib]
+    f_scale = copy_kib / max(fcopy) if fcopy else None
+    w_scale = copy_kib / max(wcopy) if wcopy else None
+    lines = ["# rocprofv3 HBM counters (FETCH_SIZE, WRITE_SIZE)", "",
+             f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`", "",
+             f"Calibration: a device copy of {copy_mib:.0f} MiB reads FETCH_SIZE "
+             f"{max(fcopy) if fcopy else float('nan'):.0f} KiB and WRITE_SIZE "
+             f"{max(wcopy) if wcopy else float('nan'):.0f} KiB; scale factors "
+             f"{f_scale if f_scale else float('nan'):.4f} (fetch) and {w_scale if w_scale else float('nan'):.4f} (write).",
+             "", "| kernel | dispatches | FETCH KiB/dispatch | WRITE KiB/dispatch | calibrated HBM MB/dispatch |",
+             "|---|---|---|---|---|"]
+    record = None
+    for k in sorted(set(fetch) | set(write)):
+        if "moe::" not in k:
+            continue
+        fv, wv = fetch.get(k, []), write.get(k, [])
+        fa = sum(fv) / len(fv) if fv else 0.0
+        wa = sum(wv) / len(wv) if wv else 0.0
+        hbm = (fa * (f_scale or 1.0) + wa * (w_scale or 1.0)) * 1024 / 1e6
+        lines.append(f"| {short(k)} | {len(fv)} | {fa:.0f} | {wa:.0f} | {hbm:.1f} |")
+        if kernel_substr in k and record is None:
+            record = {"kernel": short(k), "fetch_kib": fa, "write_kib": wa, "fetch_scale": f_scale,
+                      "write_scale": w_scale, "hbm_bytes_per_dispatch": hbm * 1e6,
+                      "gemm_source_hash": kernel_source_hash()}
+    lines += ["", "Machine-readable record for the dominant kernel (read by bench.py):", "",
+              "TRAFFIC_JSON " + json.dumps(record)]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "trace":
+        trace(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif mode == "pmc":
+        pmc(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5], sys.argv[6], " ".join(sys.argv[7:]))
+    else:
+        raise SystemExit(__doc__)
