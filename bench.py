@@ -3,14 +3,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload scout]
                     [--no-cpu-baseline] [--cpu-sample TOKENS]
 
-One step = all six libmoe calls (route, scatter build, grouped fc1 + SwiGLU,
-grouped fc2, gather/combine, shared expert) over one batch of synthetic input
-already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
+One step = the whole layer through libmoe (route, scatter build, grouped fc1 +
+SwiGLU with the shared expert's fc1 in the same launch, grouped fc2 with the
+shared expert's fc2 and gate in the same launch, gather/combine) over one
+batch of synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
 between two stream synchronisations.  Prints ONE JSON line.
 
 Inside the timed steps, HIP events on the launch stream (torch's current
 stream, where every libmoe call is enqueued) bracket each call, giving the
-average duration of the dominant kernel (grouped fc1) for the roofline object.
+average duration of the dominant kernel (the fc1 launch) for the roofline object.
 
 The CPU baseline runs the NumPy oracle (float32, bf16 contract mode) over the
 first --cpu-sample tokens of the same workload on the host cores, after the
@@ -39,7 +40,7 @@ from mixture_experts_ffn_05_amd import workloads as wl  # noqa: E402
 METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% bf16 MFMA peak; decode % HBM BW)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-CALLS = ("route", "scatter", "fc1", "fc2", "combine", "shared")
+CALLS = ("route", "scatter", "fc1", "fc2", "combine")
 
 
 def log(msg):
@@ -52,12 +53,15 @@ def algorithmic_work(cfg, counts):
     R = int(counts.sum())
     active = int((counts > 0).sum())
     el = 2 if cfg.dtype == "bf16" else 4
-    fc1_flops = 4.0 * R * H * I
-    fc2_flops = 2.0 * R * I * H
-    fc1_bytes = active * H * 2 * I * el + R * H * el + R * I * el      # weights + X_s read + A write
-    fc2_bytes = active * I * H * el + R * I * el + R * H * 4            # weights + A read + Y_s write
+    # fc1/fc2 launches carry the routed groups and, when the layer has one, the shared expert
+    fc1_flops = 4.0 * R * H * I + 4.0 * T * H * I_s
+    fc2_flops = 2.0 * R * I * H + 2.0 * T * I_s * H
+    fc1_bytes = (active * H * 2 * I * el + R * H * el + R * I * el          # routed weights + X_s read + A write
+                 + (H * 2 * I_s * el + T * H * el + T * I_s * el if I_s else 0))
+    fc2_bytes = (active * I * H * el + R * I * el + R * H * 4               # routed weights + A read + Y_s write
+                 + (I_s * H * el + T * I_s * el + T * H * 4 if I_s else 0))
     shared_flops = 6.0 * T * H * I_s + (2.0 * T * H if cfg.gated else 0.0)
-    layer_flops = 2.0 * T * H * E + fc1_flops + fc2_flops + shared_flops
+    layer_flops = 2.0 * T * H * E + 4.0 * R * H * I + 2.0 * R * I * H + shared_flops
     layer_bytes = (active * 3 * H * I * el + 3 * H * I_s * el + H * E * el + T * H * el + T * H * 4)
     return {"R": R, "active_experts": active, "fc1_flops": fc1_flops, "fc2_flops": fc2_flops,
             "fc1_bytes": fc1_bytes, "fc2_bytes": fc2_bytes, "shared_flops": shared_flops,
@@ -92,25 +96,33 @@ def committed_traffic(workload):
 
 
 def run_step(layer, bufs, cfg, bias_t, events=None):
+    """One layer forward: route, scatter, fc1 (+ shared fc1), fc2 (+ shared fc2, gate), combine.
+    With `events`, records one HIP event before each call and one after the last."""
     x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+    shared = layer["shared"]
     rec(0)
-    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
-                bufs.route_ws)
+    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws)
     rec(1)
     B.moe_build_scatter(x, bufs.topk_ids, cfg.E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
                         bufs.status_words, bufs.x_scattered, bufs.scatter_ws)
     rec(2)
-    B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
-    rec(3)
-    B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
-    rec(4)
-    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
+    if shared is not None:
+        ws1, ws2, wg = shared
+        B.moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
+                                            bufs.act_shared)
+        rec(3)
+        B.moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
+                                     bufs.y, bufs.shared_ws, False)
+        rec(4)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
+    else:
+        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
+        rec(3)
+        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
+        rec(4)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
     rec(5)
-    if layer["shared"] is not None:
-        ws1, ws2, wg = layer["shared"]
-        B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True)
-    rec(6)
 
 
 def cpu_baseline(layer, cfg, bufs, sample_tokens):
@@ -202,7 +214,7 @@ def main():
         raise RuntimeError(f"router produced {status[1]} out-of-range expert ids")
     counts = np.diff(bufs.expert_offsets.cpu().numpy())
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -222,7 +234,8 @@ def main():
     roof["traffic"] = round(tr["hbm_bytes_per_dispatch"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = work["fc1_bytes"]
-    roof["kernel"] = "grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1, routed experts)"
+    roof["kernel"] = ("grouped_gemm_bf16_fused<SwiGLU> (moe_grouped_swiglu_fc1_and_shared: routed experts and "
+                      "shared expert)" if cfg.I_s else "grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1)")
     gg_s = fc1_s + fc2_s
     gg_tflops = (work["fc1_flops"] + work["fc2_flops"]) / gg_s / 1e12
     gg_gbps = (work["fc1_bytes"] + work["fc2_bytes"]) / gg_s / 1e9

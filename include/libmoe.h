@@ -207,6 +207,42 @@ moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const
                              int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * moe_grouped_swiglu_fc1_and_shared / moe_grouped_fc2_and_shared -- the routed
+ * expert FFNs and the shared expert computed together, one launch per half.
+ *
+ * Source: as for moe_grouped_swiglu_fc1, moe_grouped_fc2 and moe_shared_expert
+ * (VeOmni docs "Fused MoE Kernel Notes", "Backward grouped-GEMM launch bound";
+ * PLENA_Compiler PR #69, "Group C -- shared experts").  Routed groups stream
+ * expert weights that are read once, while the shared expert reuses one weight
+ * across all T tokens; interleaving both kinds of tiles in one persistent
+ * launch lets them overlap on every CU.
+ *
+ * fc1 half:  act        [R, I]   = SwiGLU of the routed rows (as moe_grouped_swiglu_fc1)
+ *            act_shared [T, I_s] = SwiGLU(x @ ws1)            (dt, caller buffer)
+ * fc2 half:  y_rows     [R, H]   = routed expert outputs, fp32 (as moe_grouped_fc2)
+ *            y          [T, H]   = (accumulate ? y : 0) + gate * (act_shared @ ws2), fp32,
+ *                                  gate = sigmoid(x . w_gate) per token, or 1 when w_gate is NULL
+ * The routed outputs are then added with moe_gather_combine(accumulate = 1).
+ * moe_grouped_fc2_and_shared needs a workspace of at least
+ * moe_shared_expert_workspace_bytes(dt, T, I_s) bytes (it holds the gate).
+ * Other arguments are those of the three separate calls.  Each call chooses
+ * from the shapes whether its two computations share one launch (bf16, H, I
+ * and I_s multiples of 64, and a shared expert whose FLOPs are small next to
+ * the routed weight bytes) or run one after the other; results are the same
+ * either way.
+ */
+moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
+                                             const void* w1, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
+                                             const void* x, const void* ws1, int32_t T, int32_t I_s,
+                                             void* act_shared, void* stream);
+
+moe_status moe_grouped_fc2_and_shared(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2,
+                                      int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
+                                      const void* act_shared, const void* ws2, const void* x, const void* w_gate,
+                                      int32_t T, int32_t I_s, int32_t accumulate, float* y, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

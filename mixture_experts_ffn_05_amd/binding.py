@@ -50,6 +50,10 @@ _SIGNATURES = {
     "moe_shared_expert_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_shared_expert": (_c_int, [_c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
                                    _vp]),
+    "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                                   _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                            _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -212,6 +216,40 @@ def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream
     _check(lib.moe_shared_expert(*args))
 
 
+def moe_grouped_swiglu_fc1_and_shared(x_scattered, expert_offsets, w1, act, x, ws1, act_shared, stream=None):
+    lib = load()
+    R, H = x_scattered.shape
+    E, _, I2 = w1.shape
+    I = I2 // 2
+    T = x.shape[0]
+    I_s = ws1.shape[1] // 2
+    dev = x.device
+    dt = x.dtype
+    args = (_dt(x), _ptr(x_scattered, "x_scattered", dt, (R, H), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", dt, (E, H, 2 * I), dev), R, H, E, I, _ptr(act, "act", dt, (R, I), dev),
+            _ptr(x, "x", dt, (T, H), dev), _ptr(ws1, "ws1", dt, (H, 2 * I_s), dev), T, I_s,
+            _ptr(act_shared, "act_shared", dt, (T, I_s), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_and_shared(*args))
+
+
+def moe_grouped_fc2_and_shared(act, expert_offsets, w2, y_rows, act_shared, ws2, x, w_gate, y, workspace,
+                               accumulate=False, stream=None):
+    lib = load()
+    R, I = act.shape
+    E, _, H = w2.shape
+    T, I_s = act_shared.shape
+    dev = act.device
+    dt = act.dtype
+    args = (_dt(act), _ptr(act, "act"), _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2, "w2", dt, (E, I, H), dev), R, I, E, H, _ptr(y_rows, "y_rows", torch.float32, (R, H), dev),
+            _ptr(act_shared, "act_shared", dt, (T, I_s), dev), _ptr(ws2, "ws2", dt, (I_s, H), dev),
+            _ptr(x, "x", dt, (T, H), dev), _ptr(w_gate, "w_gate", dt, (H,), dev), T, I_s, int(bool(accumulate)),
+            _ptr(y, "y", torch.float32, (T, H), dev), _ptr(workspace, "workspace", torch.uint8, None, dev),
+            workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_grouped_fc2_and_shared(*args))
+
+
 class MoELayerBuffers:
     """Device buffers for one layer forward of T tokens (allocated once, reused)."""
 
@@ -236,12 +274,17 @@ class MoELayerBuffers:
                                       device=device)
         self.shared_ws = (torch.empty((moe_shared_expert_workspace_bytes(dtype, T, I_s),), dtype=torch.uint8,
                                       device=device) if I_s > 0 else None)
+        self.act_shared = torch.empty((T, I_s), dtype=dtype, device=device) if I_s > 0 else None
 
 
 def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=None, routes=None,
-                      stream=None):
+                      stream=None, fused_shared=False):
     """The six calls in order.  ``routes`` = (topk_ids int32, topk_weights fp32)
-    device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None)."""
+    device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None).
+    With ``fused_shared`` and a shared expert, the routed experts and the shared
+    expert run together through moe_grouped_swiglu_fc1_and_shared and
+    moe_grouped_fc2_and_shared, and the combine adds the routed outputs onto the
+    shared ones."""
     T, H = x.shape
     E, _, I2 = W1.shape
     I_s = shared[1].shape[0] if shared is not None else 0
@@ -255,6 +298,14 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         ids, w = routes
     moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
                       bufs.x_scattered, bufs.scatter_ws, stream)
+    if fused_shared and shared is not None:
+        ws1, ws2, wg = shared
+        moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
+                                          bufs.act_shared, stream)
+        moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
+                                   bufs.y, bufs.shared_ws, False, stream)
+        moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, True, stream)
+        return bufs
     moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream)
     moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream)
     moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, False, stream)

@@ -278,4 +278,88 @@ moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const
                     fn);
 }
 
+moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
+                                             const void* w1, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
+                                             const void* x, const void* ws1, int32_t T, int32_t I_s,
+                                             void* act_shared, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1_and_shared";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(ws1, fn, "ws1"));
+  MOE_CHECK(need_ptr(act_shared, fn, "act_shared"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_mult8(I_s, fn, "I_s"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  hipStream_t s = (hipStream_t)stream;
+  const int cus = cu_count();
+  if (moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T))
+    return hip_result(moe_launch::fused_fc1(x_scattered, expert_offsets, E, R, w1, H, I, act, x, T, ws1, I_s,
+                                            act_shared, cus, s),
+                      fn);
+  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x_scattered, expert_offsets, E, R, w1,
+                                                      (int64_t)H * 2 * I, H, I, act, 0, cus, s),
+                       fn));
+  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act_shared, 1, cus, s),
+                    fn);
+}
+
+moe_status moe_grouped_fc2_and_shared(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2,
+                                      int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
+                                      const void* act_shared, const void* ws2, const void* x, const void* w_gate,
+                                      int32_t T, int32_t I_s, int32_t accumulate, float* y, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_grouped_fc2_and_shared";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w2, fn, "w2"));
+  MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
+  MOE_CHECK(need_ptr(act_shared, fn, "act_shared"));
+  MOE_CHECK(need_ptr(ws2, fn, "ws2"));
+  MOE_CHECK(need_ptr(y, fn, "y"));
+  if (w_gate) MOE_CHECK(need_ptr(x, fn, "x (needed for the gate)"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_mult8(I_s, fn, "I_s"));
+  MOE_CHECK(need_flag(accumulate, fn, "accumulate"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  const size_t need = moe_shared_expert_workspace_bytes(dt, T, I_s);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_fc2_and_shared: workspace needs %zu bytes (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  float* gate = w_gate ? (float*)((char*)workspace + align256((size_t)T * I_s * elem_size(dt))) : nullptr;
+  const int cus = cu_count();
+  if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate((int)dt, x, w_gate, T, H, gate, s), fn));
+  if (moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T))
+    return hip_result(moe_launch::fused_fc2(act, expert_offsets, E, R, w2, I, H, y_rows, act_shared, T, ws2, I_s,
+                                            gate, accumulate, y, cus, s),
+                      fn);
+  MOE_CHECK(hip_result(moe_launch::grouped_fc2((int)dt, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H, y_rows,
+                                               nullptr, 0, 1, 0, cus, s),
+                       fn));
+  return hip_result(moe_launch::grouped_fc2((int)dt, act_shared, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate,
+                                            0, 1, cus, s),
+                    fn);
+}
+
 }  // extern "C"

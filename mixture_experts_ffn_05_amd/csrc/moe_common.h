@@ -98,6 +98,17 @@ hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int grou
                        const float* row_scale, int accumulate, int plain_store, int role, int cu_count,
                        hipStream_t s);
 
+// Routed groups and the shared expert in one launch (bf16, reduction sizes
+// multiples of 64, and a shared expert that is light next to the routed
+// weights; fused_supported() decides from the shapes).
+bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T);
+hipError_t fused_fc1(const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
+                     void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
+                     hipStream_t s);
+hipError_t fused_fc2(const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
+                     float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
+                     int accumulate, float* y, int cu_count, hipStream_t s);
+
 hipError_t gather_combine(const float* y_rows, const int32_t* scatter_index, const float* weights,
                           int T, int H, int top_k, int accumulate, float* y, hipStream_t s);
 hipError_t shared_gate(int dt, const void* x, const void* w_gate, int T, int H, float* gate,

@@ -568,6 +568,39 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
   }
 }
 
+// Routed expert groups and the shared expert in one persistent launch.  The
+// routed tiles stream expert weights that are read once (HBM-bound when
+// groups are small); the shared-expert tiles reuse one weight over all T rows
+// (MFMA-bound).  Tile ids of the two problems are interleaved evenly
+// (position p is a shared tile when floor((p+1)*Ts/total) > floor(p*Ts/total)),
+// so every CU works on both kinds at once and each hides the other's stalls.
+template <int EPI_R, int EPI_S, class C>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(GemmParams<bf16_t> pr,
+                                                                                GemmParams<bf16_t> ps) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int32_t sOff[kMaxExperts + 1];
+  __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sWave[C::kWaves];
+  const int mtiles = build_tile_prefix<C::BM, C::NT>(pr, sOff, sPre, sWave);
+  const int64_t ntr = pr.n_tiles;
+  const int64_t tiles_r = (int64_t)mtiles * ntr;
+  const int64_t mts = (ps.rows + C::BM - 1) / C::BM;
+  const int64_t tiles_s = mts * ps.n_tiles;
+  const int64_t total = tiles_r + tiles_s;
+  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const int64_t s_before = id * tiles_s / total;
+    if ((id + 1) * tiles_s / total != s_before) {
+      const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
+      run_tile_pipe<EPI_S, C>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
+    } else {
+      const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
+      run_tile_pipe<EPI_R, C>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
+    }
+  }
+}
+
 // float32 path: one thread per output element.
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmParams<float> p) {
@@ -661,6 +694,34 @@ int pick_pipe_variant(const GemmParams<bf16_t>& p, int epi) {
   return rows_per_group >= 512 ? 8 : 1;
 }
 
+template <int EPI_R, int EPI_S, class C>
+hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (attr != hipSuccess) return attr;
+  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  pr.n_tiles = (pr.N + out_r - 1) / out_r;
+  ps.n_tiles = (ps.N + out_s - 1) / out_s;
+  const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
+  const int64_t tiles_s = (int64_t)((ps.rows + C::BM - 1) / C::BM) * ps.n_tiles;
+  const int grid = persistent_grid(ub_r + tiles_s, cu_count * C::kWgsPerCu);
+  hipLaunchKernelGGL((grouped_gemm_bf16_fused<EPI_R, EPI_S, C>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
+  return hipGetLastError();
+}
+
+// One configuration for both problems of a fused launch: the large tile only
+// when the routed groups and the shared expert both average >= 512 rows.
+template <int EPI_R, int EPI_S>
+hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, int cu_count,
+                             hipStream_t s) {
+  const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
+  if (MOE_PIPE_VARIANT == 8 || (MOE_PIPE_VARIANT == 0 && per_group >= 512 && ps.rows >= 512))
+    return launch_fused<EPI_R, EPI_S, Cfg8>(pr, ps, cu_count, s);
+  return launch_fused<EPI_R, EPI_S, Cfg1>(pr, ps, cu_count, s);
+}
+
 template <int EPI, int ROLE>
 hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   if (p.K % 64 == 0) {
@@ -723,6 +784,42 @@ hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int grou
   else
     hipLaunchKernelGGL(grouped_gemm_f32<kScaleAdd>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// One launch for both problems pays off when the shared expert's MFMA work is
+// small next to the routed weight stream (decode, many large experts): its
+// tiles then fill the gaps of the weight-bound routed tiles.  A large shared
+// expert (prefill with a wide shared MLP) runs faster in a launch of its own
+// with the large tile.  Measured on MI355X: one launch wins at a ratio of
+// shared FLOPs to routed weight bytes of ~2 (DeepSeek-V2-Lite-shaped decode)
+// and ~16 (DeepSeek-V3-shaped prefill) and loses from ~128 (Scout-shaped).
+bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T) {
+  if (!(dt == 1 && H % 64 == 0 && I % 64 == 0 && I_s % 64 == 0)) return false;
+  const double routed_bytes = (double)(E < R ? E : R) * 3.0 * H * I * 2.0;
+  const double shared_flops = 6.0 * T * H * I_s;
+  return shared_flops < 50.0 * routed_bytes;
+}
+
+hipError_t fused_fc1(const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
+                     void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
+                     hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> pr{(const bf16_t*)xs, offsets, E, R, H, I, (const bf16_t*)w1, (int64_t)H * 2 * I,
+                        2 * I, I, act, nullptr, 0, 0};
+  GemmParams<bf16_t> ps{(const bf16_t*)x, nullptr, 1, T, H, I_s, (const bf16_t*)ws1, 0,
+                        2 * I_s, I_s, act_s, nullptr, 0, 0};
+  return launch_fused_bf16<kSwiGLU, kSwiGLU>(pr, ps, cu_count, s);
+}
+
+hipError_t fused_fc2(const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
+                     float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
+                     int accumulate, float* y, int cu_count, hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> pr{(const bf16_t*)act, offsets, E, R, I, H, (const bf16_t*)w2, (int64_t)I * H,
+                        H, 0, y_rows, nullptr, 0, 0};
+  GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2, 0,
+                        H, 0, y, gate, accumulate, 0};
+  return launch_fused_bf16<kStoreF32, kScaleAdd>(pr, ps, cu_count, s);
 }
 
 }  // namespace moe_launch

@@ -96,6 +96,22 @@ def test_combine_and_shared_validation(lib):
     assert lib.moe_shared_expert(1, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, need - 1, None) == 3
 
 
+def test_fused_shared_calls_validation(lib):
+    assert lib.moe_grouped_swiglu_fc1_and_shared(1, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, FAKE, None, 64, 128,
+                                                 FAKE, None) == 1
+    assert "ws1 must not be NULL" in _err(lib)
+    need = lib.moe_shared_expert_workspace_bytes(1, 64, 128)
+    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
+                                          128, 0, FAKE, FAKE, need - 1, None) == 3
+    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
+                                          128, 3, FAKE, FAKE, need, None) == 1
+    assert "accumulate" in _err(lib)
+    # a gate needs x
+    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, None, FAKE, 64,
+                                          128, 0, FAKE, FAKE, need, None) == 1
+    assert "x (needed for the gate)" in _err(lib)
+
+
 def test_build_compiles_all_kernels_for_gfx950():
     import __graft_entry__ as ge
     ge.build()

@@ -1,5 +1,6 @@
 """Full-size GPU parity for every layer workload, in the launch configuration
-the benchmark times (the same binding calls on the same buffers).
+the benchmark times (the same binding calls on the same buffers: routed and
+shared experts through the *_and_shared calls).
 
 Checked on each workload:
   * routing: logits within the certified fp32 bound of the oracle's; top-k
@@ -52,7 +53,8 @@ def test_full_size_layer(name):
     bias_t = torch.from_numpy(bias).to(DEV) if bias is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.y_rows.fill_(float("nan"))
-    B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs)
+    B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
+                        fused_shared=True)
     torch.cuda.synchronize()
 
     # routing

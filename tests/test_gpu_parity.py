@@ -25,6 +25,8 @@ CASES = [
     wl.LayerConfig("ragged_f32", "f32", T=77, H=136, E=5, top_k=3, I=40, I_s=24, gated=True, fan_in_init=True),
     # groups of >= 512 rows take the 256x256 tile configuration (routed and shared)
     wl.LayerConfig("big_groups_bf16", "bf16", T=1100, H=512, E=2, top_k=1, I=320, I_s=192, gated=True),
+    # a light shared expert next to >= 512-row routed groups: one launch with the 256x256 tile
+    wl.LayerConfig("fused_big_bf16", "bf16", T=1024, H=512, E=2, top_k=1, I=2048, I_s=64, gated=True),
 ]
 
 
@@ -184,17 +186,21 @@ def test_grouped_gemms_per_call(cfg):
     assert mx <= 1e-5, f"fc2 relative max error {mx:.3e} against the oracle on the same activation"
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused_shared"])
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
-def test_layer_end_to_end(cfg):
-    """All six calls; y against the oracle fed the GPU's routes (which were
-    themselves checked against the oracle's top-k of the GPU logits)."""
+def test_layer_end_to_end(cfg, fused):
+    """All six calls (or, with fused_shared, the routed and shared experts
+    together through the *_and_shared calls); y against the oracle fed the
+    GPU's routes (which were themselves checked against the oracle's top-k of
+    the GPU logits)."""
     layer = _layer(cfg)
     x, wr = layer["x"], layer["w_router"]
     bias_t = torch.from_numpy(layer["bias"]).to(DEV) if layer["bias"] is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.act.fill_(float("nan"))
     bufs.y_rows.fill_(float("nan"))
-    B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs)
+    B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
+                        fused_shared=fused)
     torch.cuda.synchronize()
     ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
     check_routing(host(bufs.logits), ids, w, host(x), host(wr), layer["bias"], cfg.top_k, O)
@@ -282,13 +288,14 @@ def test_combine_accumulate_and_skipped_slots():
     assert_output_close(host(y), ref, "f32")
 
 
-def test_two_runs_bit_identical():
-    cfg = CASES[2]
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused_shared"])
+def test_two_runs_bit_identical(fused):
+    cfg = CASES[6]
     layer = _layer(cfg)
     outs = []
     for _ in range(2):
         bufs = B.moe_layer_forward(layer["x"], layer["w_router"], None, layer["W1"], layer["W2"], cfg.top_k,
-                                   shared=layer["shared"])
+                                   shared=layer["shared"], fused_shared=fused)
         torch.cuda.synchronize()
         outs.append((host(bufs.y).copy(), host(bufs.scatter_index).copy(), host(bufs.y_rows).copy()))
     for a, b in zip(*outs):
