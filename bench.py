@@ -3,10 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload scout]
                     [--no-cpu-baseline] [--cpu-sample TOKENS]
 
-One step = the whole layer through libmoe (route, scatter build, grouped fc1 +
-SwiGLU with the shared expert's fc1 in the same launch, grouped fc2 with the
-shared expert's fc2 and gate in the same launch, gather/combine) over one
-batch of synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
+One step = the whole layer through libmoe (routing and scatter build in one
+call, grouped fc1 + SwiGLU with the shared expert's fc1 in the same launch,
+grouped fc2 with the shared expert's fc2 and gate in the same launch,
+gather/combine) over one batch of synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
 between two stream synchronisations.  Prints ONE JSON line.
 
 Inside the timed steps, HIP events on the launch stream (torch's current
@@ -40,26 +40,28 @@ from mixture_experts_ffn_05_amd import workloads as wl  # noqa: E402
 METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% bf16 MFMA peak; decode % HBM BW)"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
-CALLS = ("route", "scatter", "fc1", "fc2", "combine")
+CALLS = ("route_scatter", "fc1", "fc2", "combine")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_work(cfg, counts):
-    """FLOPs and bytes the layer must do for the realized routes (counts per expert)."""
+def algorithmic_work(cfg, counts, shared_in_gemms=True):
+    """FLOPs and bytes the layer must do for the realized routes (counts per expert).
+    fc1/fc2 figures cover what the timed fc1/fc2 launches carry: the routed
+    groups and, with shared_in_gemms and a shared expert, the shared expert."""
     T, H, E, k, I, I_s = cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s
     R = int(counts.sum())
     active = int((counts > 0).sum())
     el = 2 if cfg.dtype == "bf16" else 4
-    # fc1/fc2 launches carry the routed groups and, when the layer has one, the shared expert
-    fc1_flops = 4.0 * R * H * I + 4.0 * T * H * I_s
-    fc2_flops = 2.0 * R * I * H + 2.0 * T * I_s * H
+    S = I_s if shared_in_gemms else 0
+    fc1_flops = 4.0 * R * H * I + 4.0 * T * H * S
+    fc2_flops = 2.0 * R * I * H + 2.0 * T * S * H
     fc1_bytes = (active * H * 2 * I * el + R * H * el + R * I * el          # routed weights + X_s read + A write
-                 + (H * 2 * I_s * el + T * H * el + T * I_s * el if I_s else 0))
+                 + (H * 2 * S * el + T * H * el + T * S * el if S else 0))
     fc2_bytes = (active * I * H * el + R * I * el + R * H * 4               # routed weights + A read + Y_s write
-                 + (I_s * H * el + T * I_s * el + T * H * 4 if I_s else 0))
+                 + (S * H * el + T * S * el + T * H * 4 if S else 0))
     shared_flops = 6.0 * T * H * I_s + (2.0 * T * H if cfg.gated else 0.0)
     layer_flops = 2.0 * T * H * E + 4.0 * R * H * I + 2.0 * R * I * H + shared_flops
     layer_bytes = (active * 3 * H * I * el + 3 * H * I_s * el + H * E * el + T * H * el + T * H * 4)
@@ -95,34 +97,55 @@ def committed_traffic(workload):
     return None
 
 
-def run_step(layer, bufs, cfg, bias_t, events=None):
-    """One layer forward: route, scatter, fc1 (+ shared fc1), fc2 (+ shared fc2, gate), combine.
-    With `events`, records one HIP event before each call and one after the last."""
+def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
+    """One layer forward: route + scatter, fc1 (+ shared fc1), fc2 (+ shared fc2, gate), combine.
+    With `side` (a second stream) and a shared expert, the shared expert runs on
+    `side` (y = shared(x)) while routing and the routed experts run on the
+    current stream, which waits for it before the combine adds onto y.
+    With `events`, records one HIP event before each call on the current stream
+    and one after the last."""
     x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     shared = layer["shared"]
+    if side is not None and shared is not None:
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        ws1, ws2, wg = shared
+        B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, stream=side)
+        rec(0)
+        B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                                bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                                bufs.x_scattered, bufs.route_scatter_ws)
+        rec(1)
+        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
+        rec(2)
+        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
+        rec(3)
+        main.wait_stream(side)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
+        rec(4)
+        return
     rec(0)
-    B.moe_route(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws)
+    B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                            bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                            bufs.x_scattered, bufs.route_scatter_ws)
     rec(1)
-    B.moe_build_scatter(x, bufs.topk_ids, cfg.E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
-                        bufs.status_words, bufs.x_scattered, bufs.scatter_ws)
-    rec(2)
     if shared is not None:
         ws1, ws2, wg = shared
         B.moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
                                             bufs.act_shared)
-        rec(3)
+        rec(2)
         B.moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
                                      bufs.y, bufs.shared_ws, False)
-        rec(4)
+        rec(3)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
     else:
         B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
-        rec(3)
+        rec(2)
         B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
-        rec(4)
+        rec(3)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
-    rec(5)
+    rec(4)
 
 
 def cpu_baseline(layer, cfg, bufs, sample_tokens):
@@ -179,6 +202,11 @@ def main():
     ap.add_argument("--workload", default="scout", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time graph replays (launch-bound decode shapes)")
+    ap.add_argument("--shared", choices=("fused", "overlap"), default="fused",
+                    help="shared expert inside the routed fc1/fc2 launches (fused, the default: measured faster "
+                         "on every workload) or on a second stream concurrent with routing (overlap)")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -206,8 +234,12 @@ def main():
         log(f"copy reference: {n} bytes read and {n} bytes written by one device copy")
         del src, dst
 
+    mode = args.shared
+    if not cfg.I_s:
+        mode = "none"
+    side = torch.cuda.Stream() if mode == "overlap" else None
     for _ in range(args.warmup):
-        run_step(layer, bufs, cfg, bias_t)
+        run_step(layer, bufs, cfg, bias_t, side=side)
     torch.cuda.synchronize()
     status = bufs.status_words.cpu().tolist()
     if status[1] != 0:
@@ -216,17 +248,38 @@ def main():
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(layer, bufs, cfg, bias_t, ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.graph:
+        # Per-call times come from an eager pass with events; the timed steps replay a captured graph.
+        for s in range(args.steps):
+            run_step(layer, bufs, cfg, bias_t, ev[s], side=side)
+        torch.cuda.synchronize()
+        capture_stream = torch.cuda.Stream()
+        capture_stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(capture_stream):
+            with torch.cuda.graph(graph, stream=capture_stream):
+                run_step(layer, bufs, cfg, bias_t, side=side)
+        torch.cuda.current_stream().wait_stream(capture_stream)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            run_step(layer, bufs, cfg, bias_t, ev[s], side=side)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                 for i, c in enumerate(CALLS)}
     log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
 
-    work = algorithmic_work(cfg, counts)
+    work = algorithmic_work(cfg, counts, shared_in_gemms=(mode == "fused"))
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
@@ -235,7 +288,8 @@ def main():
     roof["traffic_unit"] = "GB per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = work["fc1_bytes"]
     roof["kernel"] = ("grouped_gemm_bf16_fused<SwiGLU> (moe_grouped_swiglu_fc1_and_shared: routed experts and "
-                      "shared expert)" if cfg.I_s else "grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1)")
+                      "shared expert)" if mode == "fused" else
+                      "grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1: routed experts)")
     gg_s = fc1_s + fc2_s
     gg_tflops = (work["fc1_flops"] + work["fc2_flops"]) / gg_s / 1e12
     gg_gbps = (work["fc1_bytes"] + work["fc2_bytes"]) / gg_s / 1e9
@@ -268,6 +322,11 @@ def main():
                   "frac_roofline": round(t_roof / layer_s, 4), "roofline_ms": round(t_roof * 1e3, 4),
                   "active_experts": work["active_experts"]},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "timing": "hip graph replay" if args.graph else "eager launches",
+        "shared_expert": {"fused": "inside the routed fc1/fc2 launches",
+                          "overlap": "moe_shared_expert on a second stream, concurrent with routing and the "
+                                     "routed experts; the combine waits for it",
+                          "none": "layer has no shared expert"}[mode],
         "cpu_baseline": None,
     }
     rc = 0

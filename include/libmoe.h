@@ -80,17 +80,18 @@ int moe_version(void);
  * x [T, H] (dt), w_router [H, E] (dt), logit_bias [E] fp32 or NULL for none,
  * topk_ids [T, top_k] int32 out, topk_weights [T, top_k] fp32 out,
  * logits [T, E] fp32 out (required): the logits exactly as top-k saw them.
- * workspace: device scratch of at least moe_route_workspace_bytes(dt, H, E)
- * bytes (it receives the router weight transposed to [E rounded up to 16, H];
- * may be NULL when that size is 0), contents undefined on entry and exit.
+ * workspace: device scratch of at least moe_route_workspace_bytes(dt, T, H, E)
+ * bytes (it receives the router weight transposed to [E rounded up to 16, H]
+ * and partial sums over slices of H; may be NULL when that size is 0),
+ * contents undefined on entry and exit.
  */
 moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
                      int32_t T, int32_t H, int32_t E, int32_t top_k,
                      int32_t* topk_ids, float* topk_weights, float* logits,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes moe_route needs for (dt, H, E). */
-size_t moe_route_workspace_bytes(moe_dtype dt, int32_t H, int32_t E);
+/* Workspace bytes moe_route needs for (dt, T, H, E). */
+size_t moe_route_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E);
 
 /* Workspace bytes moe_build_scatter needs for (T, top_k, E). */
 size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
@@ -123,6 +124,31 @@ moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_id
                              int32_t* scatter_index, int32_t* row_token, int32_t* expert_offsets,
                              int32_t* status_words, void* x_scattered,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_and_scatter -- moe_route followed by moe_build_scatter on its
+ * topk_ids, in one call.
+ *
+ * Sources: those of moe_route and moe_build_scatter above.  Every output is
+ * the one the two calls produce (same bits), so the same arguments carry the
+ * same meaning, layout and ownership; logits is required as in moe_route.
+ * For few tokens (bf16, T <= 16, E a multiple of 8) the top-k and the whole
+ * scatter build, including the row copy when the rows are few, run in one
+ * workgroup after the router product, which saves kernel launches at decode;
+ * otherwise the call runs the two calls' kernels back to back.
+ * workspace: device scratch of at least
+ * moe_route_and_scatter_workspace_bytes(dt, T, H, E, top_k) bytes, contents
+ * undefined on entry and exit.  Errors: those of both calls.
+ */
+moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                                 int32_t T, int32_t H, int32_t E, int32_t top_k,
+                                 int32_t* topk_ids, float* topk_weights, float* logits,
+                                 int32_t* scatter_index, int32_t* row_token, int32_t* expert_offsets,
+                                 int32_t* status_words, void* x_scattered,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_route_and_scatter needs for (dt, T, H, E, top_k); 0 for invalid sizes. */
+size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E, int32_t top_k);
 
 /*
  * moe_grouped_swiglu_fc1 -- per-expert gate/up projection and SwiGLU.

@@ -40,8 +40,11 @@ _SIGNATURES = {
     "moe_version": (ctypes.c_int, []),
     "moe_route": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size,
                            _vp]),
-    "moe_route_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_route_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "moe_build_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "moe_route_and_scatter": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "moe_route_and_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_build_scatter": (_c_int, [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_size, _vp]),
     "moe_grouped_swiglu_fc1": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
@@ -120,9 +123,9 @@ def _stream(stream, device):
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
 
 
-def moe_route_workspace_bytes(dtype, H, E) -> int:
+def moe_route_workspace_bytes(dtype, T, H, E) -> int:
     dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
-    return int(load().moe_route_workspace_bytes(dt, int(H), int(E)))
+    return int(load().moe_route_workspace_bytes(dt, int(T), int(H), int(E)))
 
 
 def moe_route(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, workspace, stream=None):
@@ -159,6 +162,32 @@ def moe_build_scatter(x, topk_ids, num_experts, scatter_index, row_token, expert
             _ptr(x_scattered, "x_scattered", x.dtype, (T * k, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_build_scatter(*args))
+
+
+def moe_route_and_scatter_workspace_bytes(dtype, T, H, E, top_k) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_route_and_scatter_workspace_bytes(dt, int(T), int(H), int(E), int(top_k)))
+
+
+def moe_route_and_scatter(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, scatter_index, row_token,
+                          expert_offsets, status_words, x_scattered, workspace, stream=None):
+    lib = load()
+    T, H = x.shape
+    E = w_router.shape[1]
+    k = int(top_k)
+    dev = x.device
+    args = (_dt(x), _ptr(x, "x"), _ptr(w_router, "w_router", x.dtype, (H, E), dev),
+            _ptr(logit_bias, "logit_bias", torch.float32, (E,), dev), T, H, E, k,
+            _ptr(topk_ids, "topk_ids", torch.int32, (T, k), dev),
+            _ptr(topk_weights, "topk_weights", torch.float32, (T, k), dev),
+            _ptr(logits, "logits", torch.float32, (T, E), dev),
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev),
+            _ptr(row_token, "row_token", torch.int32, (T * k,), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(status_words, "status_words", torch.int32, (2,), dev),
+            _ptr(x_scattered, "x_scattered", x.dtype, (T * k, H), dev),
+            _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_route_and_scatter(*args))
 
 
 def moe_grouped_swiglu_fc1(x_scattered, expert_offsets, w1, act, stream=None):
@@ -268,36 +297,55 @@ class MoELayerBuffers:
         self.act = torch.empty((R, I), dtype=dtype, device=device)
         self.y_rows = torch.empty((R, H), dtype=f32, device=device)
         self.y = torch.empty((T, H), dtype=f32, device=device)
-        rb = moe_route_workspace_bytes(dtype, H, E)
+        rb = moe_route_workspace_bytes(dtype, T, H, E)
         self.route_ws = torch.empty((max(rb, 1),), dtype=torch.uint8, device=device)
         self.scatter_ws = torch.empty((moe_build_scatter_workspace_bytes(T, top_k, E),), dtype=torch.uint8,
                                       device=device)
+        self.route_scatter_ws = torch.empty((moe_route_and_scatter_workspace_bytes(dtype, T, H, E, top_k),),
+                                            dtype=torch.uint8, device=device)
         self.shared_ws = (torch.empty((moe_shared_expert_workspace_bytes(dtype, T, I_s),), dtype=torch.uint8,
                                       device=device) if I_s > 0 else None)
         self.act_shared = torch.empty((T, I_s), dtype=dtype, device=device) if I_s > 0 else None
 
 
 def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=None, routes=None,
-                      stream=None, fused_shared=False):
+                      stream=None, fused_shared=False, fused_route=False, side_stream=None):
     """The six calls in order.  ``routes`` = (topk_ids int32, topk_weights fp32)
     device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None).
     With ``fused_shared`` and a shared expert, the routed experts and the shared
     expert run together through moe_grouped_swiglu_fc1_and_shared and
     moe_grouped_fc2_and_shared, and the combine adds the routed outputs onto the
-    shared ones."""
+    shared ones.  With ``fused_route`` (and no fed-in routes), routing and the
+    scatter build run through moe_route_and_scatter.  With ``side_stream`` (a
+    torch.cuda.Stream; not with ``fused_shared``) and a shared expert, the shared
+    expert runs there first (y = shared(x)), concurrently with routing and the
+    routed experts, and the combine waits for it and adds onto y."""
     T, H = x.shape
     E, _, I2 = W1.shape
     I_s = shared[1].shape[0] if shared is not None else 0
     if bufs is None:
         bufs = MoELayerBuffers(T, H, E, top_k, I2 // 2, I_s, x.dtype, x.device)
-    if routes is None:
-        moe_route(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws,
-                  stream)
-        ids, w = bufs.topk_ids, bufs.topk_weights
+    if routes is None and fused_route:
+        moe_route_and_scatter(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                              bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                              bufs.x_scattered, bufs.route_scatter_ws, stream)
+        w = bufs.topk_weights
     else:
-        ids, w = routes
-    moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                      bufs.x_scattered, bufs.scatter_ws, stream)
+        if routes is None:
+            moe_route(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws,
+                      stream)
+            ids, w = bufs.topk_ids, bufs.topk_weights
+        else:
+            ids, w = routes
+        moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                          bufs.x_scattered, bufs.scatter_ws, stream)
+    if side_stream is not None and shared is not None and not fused_shared:
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            raise ValueError("side_stream needs stream to be None or a torch.cuda.Stream")
+        main = torch.cuda.current_stream(x.device) if stream is None else stream
+        side_stream.wait_stream(main)
+        ws1, ws2, wg = shared
+        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, side_stream)
     if fused_shared and shared is not None:
         ws1, ws2, wg = shared
         moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
@@ -308,6 +356,10 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         return bufs
     moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream)
     moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream)
+    if side_stream is not None and shared is not None:
+        main.wait_stream(side_stream)
+        moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, True, stream)
+        return bufs
     moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, False, stream)
     if shared is not None:
         ws1, ws2, wg = shared

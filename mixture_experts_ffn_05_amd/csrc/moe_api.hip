@@ -118,9 +118,9 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int moe_version(void) { return kVersion; }
 
-size_t moe_route_workspace_bytes(moe_dtype dt, int32_t H, int32_t E) {
-  if (H < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
-  return moe_launch::route_workspace_bytes((int)dt, H, E);
+size_t moe_route_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E) {
+  if (T < 1 || H < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  return moe_launch::route_workspace_bytes((int)dt, T, H, E);
 }
 
 moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias, int32_t T, int32_t H,
@@ -141,13 +141,67 @@ moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const fl
   MOE_CHECK(need_mult8(H, fn, "H"));
   MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
   MOE_CHECK(need_rows((int64_t)T * E / 8, fn, "T*E/8"));
-  const size_t need = moe_launch::route_workspace_bytes((int)dt, H, E);
+  const size_t need = moe_launch::route_workspace_bytes((int)dt, T, H, E);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL pointer");
   return hip_result(moe_launch::route((int)dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
                                       workspace, (hipStream_t)stream),
                     fn);
+}
+
+size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E, int32_t top_k) {
+  if (T < 1 || H < 1 || E < 1 || top_k < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  const size_t r = moe_launch::route_workspace_bytes((int)dt, T, H, E);
+  const size_t sc = moe_launch::scatter_workspace_bytes(T, top_k, E);
+  return r > sc ? r : sc;
+}
+
+moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                                 int32_t T, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids,
+                                 float* topk_weights, float* logits, int32_t* scatter_index, int32_t* row_token,
+                                 int32_t* expert_offsets, int32_t* status_words, void* x_scattered, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_route_and_scatter";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(w_router, fn, "w_router"));
+  MOE_CHECK(need_ptr(topk_ids, fn, "topk_ids"));
+  MOE_CHECK(need_ptr(topk_weights, fn, "topk_weights"));
+  MOE_CHECK(need_ptr(logits, fn, "logits"));
+  MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
+  MOE_CHECK(need_ptr(row_token, fn, "row_token"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(status_words, fn, "status_words"));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_topk(top_k, fn));
+  if (top_k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: top_k (%d) exceeds E (%d)", fn, top_k, E);
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  MOE_CHECK(need_rows((int64_t)T * E / 8, fn, "T*E/8"));
+  const size_t need = moe_route_and_scatter_workspace_bytes(dt, T, H, E, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  const hipStream_t s = (hipStream_t)stream;
+  if (moe_launch::router_small((int)dt, T, E) && moe_launch::route_scatter_fusable(T, top_k, E)) {
+    int nsplit = 0;
+    hipError_t err = moe_launch::route_partials_small(x, w_router, T, H, E, workspace, &nsplit, s);
+    if (err == hipSuccess)
+      err = moe_launch::route_scatter_fused((int)dt, (const float*)workspace, nsplit, logit_bias, logits, T, H, E,
+                                            top_k, topk_ids, topk_weights, x, scatter_index, row_token,
+                                            expert_offsets, status_words, x_scattered, s);
+    return hip_result(err, fn);
+  }
+  hipError_t err = moe_launch::route((int)dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights,
+                                     logits, workspace, s);
+  if (err == hipSuccess)
+    err = moe_launch::build_scatter((int)dt, x, topk_ids, T, H, E, top_k, scatter_index, row_token, expert_offsets,
+                                    status_words, x_scattered, workspace, s);
+  return hip_result(err, fn);
 }
 
 size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {

@@ -51,12 +51,19 @@
 // f32 path: one thread per output element (used by the float32 workload).
 #include "moe_common.h"
 
-// Build-time switches used when tuning (the defaults are the shipped configuration).
+// Build-time switches used when tuning (the defaults are the shipped
+// configuration; MOE_TUNING makes every numbered configuration reachable).
 #ifndef MOE_FRAG_PREFETCH
 #define MOE_FRAG_PREFETCH 1
 #endif
 #ifndef MOE_PIPE_VARIANT
 #define MOE_PIPE_VARIANT 0
+#endif
+#ifndef MOE_DECODE_FC1
+#define MOE_DECODE_FC1 13
+#endif
+#ifndef MOE_DECODE_FC2
+#define MOE_DECODE_FC2 13
 #endif
 
 namespace moe {
@@ -333,12 +340,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Shape of one pipelined configuration: workgroup tile BM x BN (staged weight
-// columns), reduction slice BK, STAGES-deep LDS ring; WM x WN waves, each
-// owning (BM/WM) x (BN/WN) as 32x32 MFMA blocks.
-template <int BM_, int BN_, int BK_, int STAGES_, int WM_ = 2, int WN_ = 2>
+// columns), reduction slice BK, STAGES-deep LDS ring; WM x WN x KW waves.
+// Each (WM, WN) position owns (BM/WM) x (BN/WN) as 32x32 MFMA blocks; with
+// KW > 1, KW waves share one position and split every slice's 16-deep MFMA
+// substeps between them, and their accumulators are added in a fixed order
+// through LDS before the epilogue (more waves and more bytes in flight per
+// tile when a tile holds few rows).
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_ = 2, int WN_ = 2, int KW_ = 1>
 struct PipeCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
-  static constexpr int kWaves = WM * WN;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_, KW = KW_;
+  static constexpr int kPos = WM * WN;                  // wave positions in the tile
+  static constexpr int kWaves = kPos * KW;
   static constexpr int NT = kWaves * kWave;
   static constexpr int kARow = BK * 2;                  // bytes of one activation row in LDS
   static constexpr int kAChunks = BK / 8;               // 16-byte chunks per activation row
@@ -354,12 +366,18 @@ struct PipeCfg {
   static constexpr int kMB = BM / WM / 32;              // 32-row blocks per wave
   static constexpr int kNB = BN / WN / 32;              // 32-column blocks per wave
   static constexpr int kKS = BK / 16;                   // MFMA k-substeps per slice
+  static constexpr int kKSW = kKS / KW;                 // substeps per wave
   static constexpr int kLds = STAGES * kStage;
-  static constexpr int kWgsPerCu = (kLds <= 72 * 1024 && kWaves == 4) ? 2 : 1;
+  static constexpr int kRed = (KW - 1) * kPos * kMB * kNB * 16 * kWave * 4;  // split-K partials
+  // Workgroups per CU that fit the 160 KiB of LDS (ring + ~9 KiB of tile tables).
+  static constexpr int kFit = (160 * 1024) / (kLds + 9 * 1024);
+  static constexpr int kWgsPerCu = kFit < 1 ? 1 : (kFit > 4 ? 4 : kFit);
   static_assert(kAStage % (1024 * kWaves) == 0 && kBStage % (1024 * kWaves) == 0,
                 "slices must split into 1 KiB loads per wave");
   static_assert(kMB >= 1 && kNB >= 2 && kNB % 2 == 0, "wave tile must hold whole 32x32 blocks");
-  static_assert(kBChunks >= 16, "the weight swizzle needs at least 16 chunks per row");
+  static_assert(kBChunks == 8 || kBChunks >= 16, "the weight swizzle needs 8 or at least 16 chunks per row");
+  static_assert(kKS % KW == 0, "substeps must split evenly between the split-K waves");
+  static_assert(kRed <= kLds, "split-K partials must fit in the ring");
 };
 
 // LDS swizzles of the ring (gfx950 LDS: 64 banks of 4 bytes; a 16-byte read
@@ -369,11 +387,14 @@ struct PipeCfg {
 //    rows; XORing the chunk index with (row / W) mod chunks puts the 16 rows
 //    into 16 distinct bank groups.
 //  * a transpose read of 32 lanes touches 4 consecutive k rows x 32 columns
-//    (4 chunks per row); XORing the chunk index with 4 * (k & 3) sends the 4
-//    rows to disjoint 64-byte quarters of the bank window.
+//    (4 chunks per row).  With 256-byte rows (16+ chunks) all 4 rows sit on
+//    one bank window and XORing the chunk index with 4 * (k & 3) sends them to
+//    disjoint 64-byte quarters; with 128-byte rows (8 chunks) rows k and k+2
+//    collide, and XORing with 4 * ((k >> 1) & 1) separates them.
 template <class C>
 __device__ __forceinline__ int a_swizzle(int row) { return (row / (256 / C::kARow)) % C::kAChunks; }
-__device__ __forceinline__ int b_swizzle(int k) { return 4 * (k & 3); }
+template <class C>
+__device__ __forceinline__ int b_swizzle(int k) { return C::kBChunks >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 
 template <int EPI, class C>
 __device__ __forceinline__ int pipe_col_base(int nb, int wn) {
@@ -405,7 +426,7 @@ __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const
 template <int EPI, class C>
 __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
                                           bool issue, const bf16_t* a_k, const bf16_t* b_k, const int64_t* a_off,
-                                          const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm) {
+                                          const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw) {
   const int lane = threadIdx.x & 63;
   if (issue) {
     const int wave = threadIdx.x >> 6;
@@ -437,7 +458,7 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
     for (int nb = 0; nb < C::kNB; ++nb) {
       const int c0 = pipe_col_base<EPI, C>(nb, wn) + 16 * (grp & 1);
       const int row = 16 * ks + b_row_in;
-      const int chunk = (c0 / 8 + b_chunk_lo) ^ b_swizzle(s16 >> 2);
+      const int chunk = (c0 / 8 + b_chunk_lo) ^ b_swizzle<C>(s16 >> 2);
       const unsigned char* ptr = Bs + row * (2 * C::BN) + chunk * 16 + b_byte;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * (2 * C::BN)));
@@ -447,16 +468,17 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
                       (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
     }
   };
-  // Fragments of substep ks+1 are read while the MFMAs of substep ks run.
+  // This wave's substeps are kw, kw+KW, ...; the fragments of the next one
+  // are read while the MFMAs of the current one run.
   u32x4 af[2][C::kMB], bfr[2][C::kNB];
-  load_frags(0, af[0], bfr[0]);
+  load_frags(kw, af[0], bfr[0]);
 #pragma unroll
-  for (int ks = 0; ks < C::kKS; ++ks) {
-    if (ks + 1 < C::kKS) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+  for (int j = 0; j < C::kKSW; ++j) {
+    if (j + 1 < C::kKSW) load_frags(kw + (j + 1) * C::KW, af[(j + 1) & 1], bfr[(j + 1) & 1]);
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[ks & 1][mb], bfr[ks & 1][nb], acc[mb][nb]);
+      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[j & 1][mb], bfr[j & 1][nb], acc[mb][nb]);
   }
 }
 
@@ -464,7 +486,8 @@ template <int EPI, class C>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int kw = wave / C::kPos, wpos = wave % C::kPos;
+  const int wm = wpos / C::WN, wn = wpos % C::WN;
   const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
   const int K = p.K, ldb = p.ldb;
 
@@ -481,7 +504,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i) {
     const int kr = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
-    const int chunk = (lane % C::kBChunks) ^ b_swizzle(kr);
+    const int chunk = (lane % C::kBChunks) ^ b_swizzle<C>(kr);
     int col;
     if (EPI == kSwiGLU) {
       const int half = C::kBChunks / 2;
@@ -514,9 +537,39 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
     lds_barrier();
     const int kn = kt + C::STAGES - 1;
     pipe_step<EPI, C>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
-                      a_base + kn * C::BK, bg + (int64_t)kn * C::BK * ldb, a_off, b_off, acc, wn, wm);
+                      a_base + kn * C::BK, bg + (int64_t)kn * C::BK * ldb, a_off, b_off, acc, wn, wm, kw);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
+
+  if constexpr (C::KW > 1) {
+    // Split-K partials through the (now idle) ring: waves kw >= 1 store theirs,
+    // wave kw == 0 of each position adds them in the order kw = 1, 2, ... and
+    // runs the epilogue.
+    float* red = (float*)smem;
+    auto slot = [&](int q, int mb, int nb, int i) {
+      return ((((q - 1) * C::kPos + wpos) * C::kMB + mb) * C::kNB + nb) * 16 * kWave + i * kWave + lane;
+    };
+    if (kw > 0) {
+#pragma unroll
+      for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[slot(kw, mb, nb, i)] = acc[mb][nb][i];
+    }
+    lds_barrier();
+    if (kw == 0) {
+      for (int q = 1; q < C::KW; ++q)
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][nb][i] += red[slot(q, mb, nb, i)];
+    }
+    lds_barrier();  // partials consumed before the next tile refills the ring
+    if (kw > 0) return;
+  }
 
   // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
 #pragma unroll
@@ -656,6 +709,7 @@ int64_t upper_row_tiles(int rows, int groups) {
 // Launch one pipelined instantiation (persistent grid, dynamic LDS ring).
 template <int EPI, class C, int ROLE>
 hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
+  if (p.K % C::BK != 0) return launch_pipe<EPI, PipeCfg<128, 128, 64, 2>, ROLE>(p, cu_count, s);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_bf16_pipe<EPI, C, ROLE>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -668,7 +722,8 @@ hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Pipelined configurations (BM, BN, BK, STAGES).
+// Pipelined configurations (BM, BN, BK, STAGES, WM, WN, KW), numbered for
+// tuning builds.
 typedef PipeCfg<128, 128, 64, 2> Cfg1;
 typedef PipeCfg<128, 128, 32, 4> Cfg2;
 typedef PipeCfg<256, 256, 32, 4> Cfg3;
@@ -679,23 +734,76 @@ typedef PipeCfg<256, 256, 32, 4, 4, 2> Cfg7;   // 8 waves
 typedef PipeCfg<256, 256, 64, 2, 4, 2> Cfg8;   // 8 waves
 typedef PipeCfg<256, 128, 64, 2, 4, 2> Cfg9;   // 8 waves
 typedef PipeCfg<128, 256, 64, 2, 2, 4> Cfg10;  // 8 waves
+// Few rows per group (decode): 32-row tiles, narrow columns, split-K waves.
+typedef PipeCfg<32, 64, 64, 5, 1, 1, 4> Cfg11;
+typedef PipeCfg<32, 64, 64, 8, 1, 1, 4> Cfg12;
+typedef PipeCfg<32, 128, 64, 4, 1, 2, 2> Cfg13;
+typedef PipeCfg<32, 64, 64, 3, 1, 1, 4> Cfg14;
+typedef PipeCfg<32, 64, 128, 4, 1, 1, 4> Cfg15;
+typedef PipeCfg<32, 128, 64, 6, 1, 2, 2> Cfg16;
+typedef PipeCfg<32, 128, 128, 3, 1, 2, 4> Cfg17;  // 8 waves
+typedef PipeCfg<32, 128, 64, 3, 1, 2, 2> Cfg18;
 
-// Configuration for a problem, from the host-known sizes only: groups that
-// average 512 rows or more (the shared expert, dense prefill) take the
-// 256x256 tile with 8 waves, which halves the L2->LDS traffic per MFMA and
-// keeps two waves per SIMD; smaller or ragged groups (decode, skewed routing,
-// many experts) take the 128x128 tile with two workgroups per CU, which
-// wastes fewer MFMA rows on partial tiles.  (Measured on MI355X across the
-// Scout-, Qwen2-, DeepSeek-V2-Lite- and DeepSeek-V3-shaped layers.)
-int pick_pipe_variant(const GemmParams<bf16_t>& p, int epi) {
+template <int V> struct CfgOf { typedef Cfg1 type; };
+#define MOE_CFG(V) template <> struct CfgOf<V> { typedef Cfg##V type; };
+MOE_CFG(2) MOE_CFG(3) MOE_CFG(4) MOE_CFG(5) MOE_CFG(6) MOE_CFG(7) MOE_CFG(8) MOE_CFG(9) MOE_CFG(10)
+MOE_CFG(11) MOE_CFG(12) MOE_CFG(13) MOE_CFG(14) MOE_CFG(15) MOE_CFG(16) MOE_CFG(17) MOE_CFG(18)
+#undef MOE_CFG
+
+// Calls f(Cfg{}) for configuration number v.  The shipped build instantiates
+// only the configurations that the selection below can return; a build with
+// MOE_TUNING instantiates all of them for sweeps.
+template <class F>
+hipError_t with_cfg(int v, F&& f) {
+#ifdef MOE_TUNING
+  switch (v) {
+#define MOE_CASE(V) case V: return f(typename CfgOf<V>::type{});
+    MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8) MOE_CASE(9)
+    MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
+    MOE_CASE(17) MOE_CASE(18)
+#undef MOE_CASE
+    default: return f(Cfg1{});
+  }
+#else
+  if (v == 8) return f(Cfg8{});
+  if (v == MOE_DECODE_FC1) return f(typename CfgOf<MOE_DECODE_FC1>::type{});
+  if (v == MOE_DECODE_FC2) return f(typename CfgOf<MOE_DECODE_FC2>::type{});
+  return f(Cfg1{});
+#endif
+}
+
+// Configuration for a problem, from the host-known sizes only (measured on
+// MI355X across the Scout-, Qwen2-, DeepSeek-V2-Lite- and DeepSeek-V3-shaped
+// layers):
+//  * groups that average 512 rows or more (the shared expert, dense prefill)
+//    take the 256x256 tile with 8 waves, which halves the L2->LDS traffic per
+//    MFMA and keeps two waves per SIMD;
+//  * groups of at most 32 rows (decode) take a 32-row tile whose waves split
+//    the reduction, so that many more tiles, each with several weight slices
+//    in flight, stream the expert weights;
+//  * everything else (skewed routing, many mid-sized groups) takes the
+//    128x128 tile with two workgroups per CU, which wastes fewer MFMA rows on
+//    partial tiles.
+int64_t rows_per_active_group(const GemmParams<bf16_t>& p) {
+  const int64_t active = p.groups < p.rows ? p.groups : p.rows;  // at most one group per row
+  return (int64_t)p.rows / (active > 0 ? active : 1);
+}
+
+constexpr int64_t kDecodeRows = 32;
+
+template <int EPI>
+constexpr int decode_variant() { return EPI == kSwiGLU ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
+
+int pick_pipe_variant(const GemmParams<bf16_t>& p, int decode_v) {
   if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
-  (void)epi;
+  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_v;
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   return rows_per_group >= 512 ? 8 : 1;
 }
 
 template <int EPI_R, int EPI_S, class C>
 hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
+  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, Cfg1>(pr, ps, cu_count, s);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -712,32 +820,29 @@ hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_cou
 }
 
 // One configuration for both problems of a fused launch: the large tile only
-// when the routed groups and the shared expert both average >= 512 rows.
+// when the routed groups and the shared expert both average >= 512 rows, the
+// decode tile when the routed groups are small and the shared expert has at
+// most 64 rows.
 template <int EPI_R, int EPI_S>
 hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, int cu_count,
                              hipStream_t s) {
   const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
-  if (MOE_PIPE_VARIANT == 8 || (MOE_PIPE_VARIANT == 0 && per_group >= 512 && ps.rows >= 512))
-    return launch_fused<EPI_R, EPI_S, Cfg8>(pr, ps, cu_count, s);
-  return launch_fused<EPI_R, EPI_S, Cfg1>(pr, ps, cu_count, s);
+  int v = 1;
+  if (MOE_PIPE_VARIANT != 0)
+    v = MOE_PIPE_VARIANT;
+  else if (per_group >= 512 && ps.rows >= 512)
+    v = 8;
+  else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
+           ps.K % 128 == 0)
+    v = decode_variant<EPI_R>();
+  return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c)>(pr, ps, cu_count, s); });
 }
 
 template <int EPI, int ROLE>
 hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  if (p.K % 64 == 0) {
-    switch (pick_pipe_variant(p, EPI)) {
-      case 2: return launch_pipe<EPI, Cfg2, ROLE>(p, cu_count, s);
-      case 3: return launch_pipe<EPI, Cfg3, ROLE>(p, cu_count, s);
-      case 4: return launch_pipe<EPI, Cfg4, ROLE>(p, cu_count, s);
-      case 5: return launch_pipe<EPI, Cfg5, ROLE>(p, cu_count, s);
-      case 6: return launch_pipe<EPI, Cfg6, ROLE>(p, cu_count, s);
-      case 7: return launch_pipe<EPI, Cfg7, ROLE>(p, cu_count, s);
-      case 8: return launch_pipe<EPI, Cfg8, ROLE>(p, cu_count, s);
-      case 9: return launch_pipe<EPI, Cfg9, ROLE>(p, cu_count, s);
-      case 10: return launch_pipe<EPI, Cfg10, ROLE>(p, cu_count, s);
-      default: return launch_pipe<EPI, Cfg1, ROLE>(p, cu_count, s);
-    }
-  }
+  if (p.K % 64 == 0)
+    return with_cfg(pick_pipe_variant(p, decode_variant<EPI>()),
+                    [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE>(p, cu_count, s); });
   p.n_tiles = EPI == kSwiGLU ? (p.N + 63) / 64 : (p.N + 127) / 128;
   const int grid = persistent_grid(upper_row_tiles(p.rows, p.groups) * p.n_tiles, 2 * cu_count);
   hipLaunchKernelGGL((grouped_gemm_bf16_generic<EPI, ROLE>), dim3(grid), dim3(kThreads), 0, s, p);

@@ -5,15 +5,21 @@
 // topk_softmax is generic in the expert count and in k.
 //
 // Kernels:
+//   router_logits_valu     up to 16 tokens (bf16, E a multiple of 8): x @ W_r on the
+//                          vector ALUs straight from W_r's [H,E] layout, H split
+//                          across workgroups; partial sums land in the workspace.
 //   router_transpose_bf16  W_r [H,E] -> [E_pad,H] in the caller's workspace, so that
 //                          both operands of the router product are K-contiguous.
 //   router_logits_mfma     x[T,H] @ W_r on MFMA (16x16x32 bf16, fp32 accumulate),
-//                          16 tokens x 64 experts per workgroup, split-K over its
-//                          4 waves with a fixed-order reduction, optional fp32 bias.
+//                          16 tokens x 64 experts per workgroup, H split across
+//                          workgroups (grid.z) and across each workgroup's 4 waves;
+//                          partial sums land in the workspace.
 //   route_logits_f32       the same product for float32 inputs, one thread per logit.
-//   topk_softmax       one wave64 per token: k rounds of a wave arg-max under the
-//                      key (logit descending, index ascending, NaN lowest), then
-//                      a softmax over the k selected logits.
+//   topk_softmax           one wave64 per token: adds the partial sums in a fixed
+//                          order (+ bias) into the logits, then topk_wave: k rounds
+//                          of a wave arg-max under the key (logit descending, index
+//                          ascending, NaN lowest) and a softmax over the k selected
+//                          logits.
 #include "moe_common.h"
 
 #include <math.h>
@@ -44,20 +50,24 @@ __global__ __launch_bounds__(256) void router_transpose_bf16(const bf16_t* __res
   }
 }
 
-// logits[t, e] for 16 tokens x 64 experts per workgroup.  Both MFMA operands are
-// K-contiguous (x rows and the transposed router rows), so each lane loads its
-// 16x16x32 fragments straight from global memory; the 4 waves split H into
-// quarters and their partial sums are added in a fixed order through LDS.
+// Partial logits over one slice of H for 16 tokens x 64 experts per
+// workgroup.  Both MFMA operands are K-contiguous (x rows and the transposed
+// router rows), so each lane loads its 16x16x32 fragments straight from global
+// memory, four k-substeps (128 k) at a time so that many loads are in flight.
+// The 4 waves split the workgroup's slice; their sums are added in a fixed
+// order through LDS.  grid.z splits H into `ksplit` slices; partial[z][t][e]
+// is summed over z in a fixed order by topk_softmax, so the result does not
+// depend on scheduling.
 __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ wt,
-                                                          const float* __restrict__ bias, int T, int H, int E,
-                                                          int E_pad, float* __restrict__ logits) {
+                                                          const bf16_t* __restrict__ wt, int T, int H, int E_pad,
+                                                          int kslice, float* __restrict__ partial) {
   __shared__ float red[4][kRtTok][kRtExp + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
   const int nblk = min(4, (E_pad - e0) / 16);
-  const int kq = ((H + 127) / 128) * 32;   // per-wave share of H, a multiple of 32
-  const int kbeg = wave * kq, kend = min(H, kbeg + kq);
+  const int zbeg = blockIdx.z * kslice, zend = min(H, zbeg + kslice);
+  const int kq = ((kslice + 127) / 128) * 32;   // per-wave share of the slice, a multiple of 32
+  const int kbeg = zbeg + wave * kq, kend = min(zend, kbeg + kq);
   const int row = t0 + (lane & 15);
   const int koff = (lane >> 4) * 8;
   const bool row_ok = row < T;
@@ -65,19 +75,25 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restri
   f32x4 acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = kbeg; k < kend; k += 32) {
-    const int kk = k + koff;
-    const bool k_ok = kk < kend;
-    const u32x4 a = (row_ok && k_ok) ? *(const u32x4*)(xr + kk) : u32x4{0u, 0u, 0u, 0u};
+  for (int k = kbeg; k < kend; k += 128) {
+    u32x4 a[4], b[4][4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      if (nb < nblk) {
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k + 32 * u + koff;
+      const bool k_ok = kk < kend;
+      a[u] = (row_ok && k_ok) ? *(const u32x4*)(xr + kk) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
         const int e = e0 + nb * 16 + (lane & 15);
-        const u32x4 b = k_ok ? *(const u32x4*)(wt + (int64_t)e * H + kk) : u32x4{0u, 0u, 0u, 0u};
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          __builtin_bit_cast(bf16x8, b), acc[nb], 0, 0, 0);
+        b[u][nb] = (k_ok && nb < nblk) ? *(const u32x4*)(wt + (int64_t)e * H + kk) : u32x4{0u, 0u, 0u, 0u};
       }
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                          __builtin_bit_cast(bf16x8, b[u][nb]), acc[nb], 0, 0, 0);
   }
   // 16x16 accumulator layout: row = 4*(lane/16) + r, column = lane%16.
 #pragma unroll
@@ -85,13 +101,12 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restri
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][nb * 16 + (lane & 15)] = acc[nb][r];
   __syncthreads();
+  float* out = partial + (int64_t)blockIdx.z * T * E_pad;
   for (int i = tid; i < kRtTok * kRtExp; i += 256) {
     const int tt = i / kRtExp, ee = i % kRtExp;
     const int t = t0 + tt, e = e0 + ee;
-    if (t < T && e < E) {
-      const float v = ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
-      logits[(int64_t)t * E + e] = bias ? v + bias[e] : v;
-    }
+    if (t < T && e < E_pad)
+      out[(int64_t)t * E_pad + e] = ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
   }
 }
 
@@ -108,54 +123,101 @@ __global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict_
 }
 
 // True if candidate (v, e) ranks before (bv, be): larger value, then lower index.
-__device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
+// Small token counts: partial logits over one slice of H for up to kVTok
+// tokens and every expert, reading W_r in its [H, E] layout (E a multiple of
+// 8), so no transposed copy is made.  Thread (hl, o) owns experts [8o, 8o+8)
+// (one 16-byte load per row) and rows hl, hl + nh, ... of the slice; the
+// tokens' x values of the slice are staged in LDS as [row][token] floats.  The
+// nh row lanes' sums are added in a fixed order through LDS.
+constexpr int kVTok = 4;
+constexpr int kVMaxSlice = 1024;
+
+__global__ __launch_bounds__(256) void router_logits_valu(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                          int T, int H, int E, int kslice,
+                                                          float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) float xs[kVMaxSlice * kVTok];
+  extern __shared__ float red[];  // [nh][kVTok][E]
+  const int tid = threadIdx.x;
+  const int O = E / 8, nh = 256 / O;
+  const int t0 = blockIdx.x * kVTok, nt = min(kVTok, T - t0);
+  const int h0 = blockIdx.y * kslice, hn = min(kslice, H - h0);
+  for (int i = tid; i < hn * kVTok; i += 256) {
+    const int hh = i / kVTok, tt = i % kVTok;
+    xs[i] = tt < nt ? bf16_to_f32(x[(int64_t)(t0 + tt) * H + h0 + hh]) : 0.f;
+  }
+  __syncthreads();
+  const int o = tid % O, hl = tid / O;
+  if (hl < nh) {
+    float acc[kVTok][8];
+#pragma unroll
+    for (int t = 0; t < kVTok; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[t][j] = 0.f;
+    const bf16_t* wp = w + (int64_t)h0 * E + 8 * o;
+#pragma unroll 8
+    for (int hh = hl; hh < hn; hh += nh) {
+      const u32x4 wv = *(const u32x4*)(wp + (int64_t)hh * E);
+      const f32x4 xv = *(const f32x4*)(xs + hh * kVTok);
+      float wf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wf[2 * j] = __uint_as_float(wv[j] << 16);
+        wf[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int t = 0; t < kVTok; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] = fmaf(xv[t], wf[j], acc[t][j]);
+    }
+#pragma unroll
+    for (int t = 0; t < kVTok; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[(hl * kVTok + t) * E + 8 * o + j] = acc[t][j];
+  }
+  __syncthreads();
+  float* out = partial + (int64_t)blockIdx.y * T * E;
+  for (int i = tid; i < nt * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    float v = 0.f;
+    for (int q = 0; q < nh; ++q) v += red[(q * kVTok + tt) * E + e];
+    out[(int64_t)(t0 + tt) * E + e] = v;
+  }
 }
 
-__global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int T, int E, int k,
-                                                    int32_t* __restrict__ ids, float* __restrict__ weights) {
-  constexpr int kPer = kMaxExperts / kWave;
+// One wave64 per token.  With `partial` set, the logits are first assembled
+// as the fixed-order sum of `nsplit` partial products (+ bias) and written to
+// `logits`; otherwise `logits` already holds them.
+__global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ partial, int nsplit, int stride_e,
+                                                    const float* __restrict__ bias, float* __restrict__ logits,
+                                                    int T, int E, int k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
-  float key[kPer];
+  float* row = logits + (int64_t)t * E;
+  float raw[kTopkPer];
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) {
+  for (int q = 0; q < kTopkPer; ++q) {
     const int e = lane + kWave * q;
-    const float v = e < E ? row[e] : -INFINITY;
-    key[q] = (v != v) ? -INFINITY : v;
-  }
-  uint32_t taken = 0;
-  float my_sel = 0.f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int e = lane + kWave * q;
-      if (e < E && !((taken >> q) & 1u) && ranks_before(key[q], e, bv, be)) {
-        bv = key[q];
-        be = e;
+    float v = -INFINITY;
+    if (e < E) {
+      if (partial) {
+        v = sum_slices(partial + (int64_t)t * stride_e + e, (int64_t)T * stride_e, nsplit);
+        if (bias) v += bias[e];
+        row[e] = v;
+      } else {
+        v = row[e];
       }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oe = __shfl_xor(be, d, kWave);
-      if (ranks_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == 0) ids[(int64_t)t * k + j] = be;
-    if (lane == j) my_sel = row[be];
+    raw[q] = v;
   }
-  const float m = __shfl(my_sel, 0, kWave);
-  const float ex = lane < k ? expf(my_sel - m) : 0.f;
-  const float s = wave_sum(ex);
-  if (lane < k) weights[(int64_t)t * k + lane] = ex / s;
+  int id;
+  float wgt;
+  topk_wave(raw, E, k, id, wgt);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = id;
+    weights[(int64_t)t * k + lane] = wgt;
+  }
 }
 
 }  // namespace
@@ -163,33 +225,93 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 
 namespace moe_launch {
 
-size_t route_workspace_bytes(int dt, int H, int E) {
+// Small-T router (bf16, E a multiple of 8, at most 16 tokens): at most eight
+// slices of H per token group (more only when H exceeds 8192).
+bool router_small(int dt, int T, int E) { return dt == 1 && E % 8 == 0 && T <= 16; }
+
+struct Split {
+  int nz, kslice;
+};
+
+Split router_valu_split(int T, int H) {
+  using namespace moe;
+  const int chunks = (T + kVTok - 1) / kVTok;
+  int nz = (512 + chunks - 1) / chunks;
+  if (nz > 8) nz = 8;  // one batch of eight partial loads per logit in the top-k pass
+  const int min_nz = (H + kVMaxSlice - 1) / kVMaxSlice;
+  if (nz < min_nz) nz = min_nz;
+  int kslice = ((H + nz - 1) / nz + 7) / 8 * 8;
+  if (kslice > kVMaxSlice) kslice = kVMaxSlice;
+  return Split{(H + kslice - 1) / kslice, kslice};
+}
+
+// MFMA router: slices of H (multiples of 128) so that the grid covers about
+// 512 workgroups.
+Split router_mfma_split(int T, int H, int E) {
+  using namespace moe;
+  const int tiles = ((T + kRtTok - 1) / kRtTok) * ((padded_experts(E) + kRtExp - 1) / kRtExp);
+  int ks = (512 + tiles - 1) / tiles;
+  const int max_ks = (H + 127) / 128;
+  if (ks > max_ks) ks = max_ks;
+  if (ks < 1) ks = 1;
+  const int kslice = ((H + ks - 1) / ks + 127) / 128 * 128;
+  return Split{(H + kslice - 1) / kslice, kslice};
+}
+
+size_t wt_bytes(int H, int E) {
+  return ((size_t)moe::padded_experts(E) * H * sizeof(moe::bf16_t) + 255) & ~(size_t)255;
+}
+
+size_t route_workspace_bytes(int dt, int T, int H, int E) {
   if (dt != 1) return 0;
-  return (size_t)moe::padded_experts(E) * H * sizeof(moe::bf16_t);
+  if (router_small(dt, T, E)) return (size_t)router_valu_split(T, H).nz * T * E * sizeof(float);
+  return wt_bytes(H, E) + (size_t)router_mfma_split(T, H, E).nz * T * moe::padded_experts(E) * sizeof(float);
+}
+
+hipError_t route_partials_small(const void* x, const void* w_router, int T, int H, int E, void* workspace,
+                                int* nsplit, hipStream_t s) {
+  using namespace moe;
+  const Split sp = router_valu_split(T, H);
+  const size_t lds = (size_t)(256 / (E / 8)) * kVTok * E * sizeof(float);
+  hipLaunchKernelGGL(router_logits_valu, dim3((T + kVTok - 1) / kVTok, sp.nz), dim3(256), lds, s,
+                     (const bf16_t*)x, (const bf16_t*)w_router, T, H, E, sp.kslice, (float*)workspace);
+  *nsplit = sp.nz;
+  return hipGetLastError();
 }
 
 hipError_t route(int dt, const void* x, const void* w_router, const float* bias, int T, int H, int E,
                  int top_k, int32_t* ids, float* weights, float* logits, void* workspace, hipStream_t s) {
   using namespace moe;
+  hipError_t err;
+  if (router_small(dt, T, E)) {
+    int nz = 0;
+    if ((err = route_partials_small(x, w_router, T, H, E, workspace, &nz, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)workspace, nz, E, bias,
+                       logits, T, E, top_k, ids, weights);
+    return hipGetLastError();
+  }
   if (dt == 1) {
     const int E_pad = padded_experts(E);
+    const Split sp = router_mfma_split(T, H, E);
     bf16_t* wt = (bf16_t*)workspace;
+    float* partial = (float*)((char*)workspace + wt_bytes(H, E));
     hipLaunchKernelGGL(router_transpose_bf16, dim3((H + 63) / 64, (E_pad + 63) / 64), dim3(256), 0, s,
                        (const bf16_t*)w_router, H, E, E_pad, wt);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    dim3 grid((T + kRtTok - 1) / kRtTok, (E_pad + kRtExp - 1) / kRtExp);
-    hipLaunchKernelGGL(router_logits_mfma, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, bias, T, H,
-                       E, E_pad, logits);
-  } else {
-    const int64_t n = (int64_t)T * E;
-    hipLaunchKernelGGL(route_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float*)x, (const float*)w_router, bias, T, H, E, logits);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    dim3 grid((T + kRtTok - 1) / kRtTok, (E_pad + kRtExp - 1) / kRtExp, sp.nz);
+    hipLaunchKernelGGL(router_logits_mfma, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
+                       E_pad, sp.kslice, partial);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, sp.nz, E_pad, bias,
+                       logits, T, E, top_k, ids, weights);
+    return hipGetLastError();
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)logits, T, E, top_k,
-                     ids, weights);
+  const int64_t n = (int64_t)T * E;
+  hipLaunchKernelGGL(route_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     (const float*)x, (const float*)w_router, bias, T, H, E, logits);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)nullptr, 0, E, nullptr, logits,
+                     T, E, top_k, ids, weights);
   return hipGetLastError();
 }
 

@@ -20,6 +20,9 @@
 //                  plus offsets[e] plus the number of lower lanes with the same
 //                  expert; a running per-expert cursor lives in LDS.
 //   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies.
+// Up to 16 chunks (decode, and prefill up to 16384 pairs) take scatter_small,
+// which runs count, scan and rank in one workgroup of 16 waves, and for at
+// most 256 rows of at most 256 KiB in all also the row copy.
 #include "moe_common.h"
 
 namespace moe {
@@ -41,6 +44,44 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool in_range, int 
   return in_range ? m : 0ull;
 }
 
+// The expert ids of one chunk, kIters per lane, all loads issued before any is used.
+__device__ __forceinline__ void load_chunk(const int32_t* ids, int R, int c, int lane,
+                                           int (&ev)[kIters]) {
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
+    ev[it] = p < R ? ids[p] : -1;
+  }
+}
+
+// Rows of one chunk's pairs: a pair's row is the running cursor of its expert
+// plus the number of lower lanes with the same expert; the highest such lane
+// advances the cursor.
+__device__ __forceinline__ void rank_chunk(const int (&ev)[kIters], int R, int E, int k, int nbits, int c, int lane,
+                                           int32_t* cursor, int32_t* __restrict__ scatter_index,
+                                           int32_t* __restrict__ row_token, int32_t* lds_row_token = nullptr) {
+  const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
+  for (int it = 0; it < kIters; ++it) {
+    if ((int64_t)c * kChunk + it * kWave >= R) break;  // the rest of the chunk is past R
+    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
+    const bool live = p < R;
+    const int e = ev[it];
+    const bool in_range = live && e >= 0 && e < E;
+    const uint64_t m = same_expert_lanes(e, in_range, nbits);
+    int r = -1;
+    if (in_range) {
+      const int b = cursor[e];
+      r = b + __popcll(m & lanemask_lt());
+      if ((m & above) == 0ull) cursor[e] = b + __popcll(m);
+    }
+    if (live) scatter_index[p] = r;
+    if (in_range) {
+      row_token[r] = (int)(p / k);
+      if (lds_row_token) lds_row_token[r] = (int)(p / k);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__ ids, int R, int E, int nbits,
                                                      int nchunks, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ bad) {
@@ -52,10 +93,12 @@ __global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__
   int nbad = 0;
   if (c < nchunks) {
     int32_t* h = hist + w * E;
+    int ev[kIters];
+    load_chunk(ids, R, c, lane, ev);
     for (int it = 0; it < kIters; ++it) {
       const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
       const bool live = p < R;
-      const int e = live ? ids[p] : -1;
+      const int e = ev[it];
       const bool in_range = live && e >= 0 && e < E;
       nbad += __popcll(__ballot(live && !in_range));
       const uint64_t m = same_expert_lanes(e, in_range, nbits);
@@ -121,23 +164,177 @@ __global__ __launch_bounds__(256) void scatter_rank(const int32_t* __restrict__ 
   const int c = blockIdx.x * kWavesPerBlock + w;
   if (c >= nchunks) return;  // whole wave; no workgroup barrier follows
   int32_t* cursor = cursor_all + w * E;
+  int ev[kIters];
+  load_chunk(ids, R, c, lane, ev);
   for (int e = lane; e < E; e += kWave) cursor[e] = chunk_base[(int64_t)c * E + e] + offsets[e];
-  const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
-    const bool live = p < R;
-    const int e = live ? ids[p] : -1;
-    const bool in_range = live && e >= 0 && e < E;
-    const uint64_t m = same_expert_lanes(e, in_range, nbits);
-    int r = -1;
-    if (in_range) {
-      const int b = cursor[e];
-      r = b + __popcll(m & lanemask_lt());
-      if ((m & above) == 0ull) cursor[e] = b + __popcll(m);
+  rank_chunk(ev, R, E, k, nbits, c, lane, cursor, scatter_index, row_token);
+}
+
+// Pairs up to 16 chunks (16384 pairs) in one workgroup of 4 waves (up to 4
+// chunks) or 16 waves: count, scan and rank in one launch, with each wave's
+// chunk held in registers between the count and the rank.  hist holds
+// nchunks x E counts, then cursors.  With fold set (at most kFoldRows rows),
+// the same workgroup also copies the rows, reading row_token from LDS.
+constexpr int kSmallWaves = 16;
+constexpr int kFoldRows = 256;
+constexpr int64_t kFoldBytes = 256 * 1024;
+
+struct BlockLds {
+  int32_t* hist;        // [nchunks][E]
+  int32_t* wsum;        // [NW]
+  int32_t* wmax;        // [NW]
+  int32_t* wbad;        // [NW]
+  int32_t* row_token;   // [kFoldRows]
+};
+
+// The whole scatter build of R <= NW * 1024 pairs (one chunk per wave) by one
+// workgroup of NW waves; ids may point to global memory or to LDS.
+template <int NW>
+__device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, int k, int nbits, int nchunks,
+                                              int32_t* __restrict__ scatter_index, int32_t* __restrict__ row_token,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ status,
+                                              int fold, const u32x4* __restrict__ x, int row_vecs,
+                                              u32x4* __restrict__ xs, const BlockLds& L) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < nchunks * E; i += NT) L.hist[i] = 0;
+  __syncthreads();
+  const bool has = w < nchunks;
+  int ev[kIters];
+  int nbad = 0;
+  if (has) {
+    load_chunk(ids, R, w, lane, ev);
+    int32_t* h = L.hist + w * E;
+    for (int it = 0; it < kIters; ++it) {
+      if ((int64_t)w * kChunk + it * kWave >= R) break;  // the rest of the chunk is past R
+      const int64_t p = (int64_t)w * kChunk + it * kWave + lane;
+      const bool live = p < R;
+      const int e = ev[it];
+      const bool in_range = live && e >= 0 && e < E;
+      nbad += __popcll(__ballot(live && !in_range));
+      const uint64_t m = same_expert_lanes(e, in_range, nbits);
+      if (in_range && lane == __ffsll((unsigned long long)m) - 1) h[e] += __popcll(m);
     }
-    if (live) scatter_index[p] = r;
-    if (in_range) row_token[r] = (int)(p / k);
   }
+  if (lane == 0) L.wbad[w] = nbad;
+  __syncthreads();
+  // Per expert: chunk bases, then the exclusive scan of the totals.  Thread
+  // tid owns experts tid, tid + NT, ...; the scan runs over the experts in
+  // index order, one block of NT experts after the other.
+  int carry = 0, maxg = 0;
+  for (int e0 = 0; e0 < E; e0 += NT) {
+    const int e = e0 + tid;
+    int total_e = 0;
+    if (e < E) {
+      int run = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        const int v = L.hist[c * E + e];
+        L.hist[c * E + e] = run;
+        run += v;
+      }
+      total_e = run;
+    }
+    const int incl = wave_inclusive_scan(total_e);
+    const int mx = wave_max(total_e);
+    if (lane == 63) L.wsum[w] = incl;
+    if (lane == 0) L.wmax[w] = mx;
+    __syncthreads();
+    int base = carry;
+    for (int i = 0; i < w; ++i) base += L.wsum[i];
+    if (e < E) {
+      const int excl = base + incl - total_e;
+      offsets[e] = excl;
+      for (int c = 0; c < nchunks; ++c) L.hist[c * E + e] += excl;
+    }
+    for (int i = 0; i < NW; ++i) {
+      carry += L.wsum[i];
+      maxg = max(maxg, L.wmax[i]);
+    }
+    __syncthreads();  // wsum / wmax are rewritten by the next block of experts
+  }
+  if (tid == 0) {
+    int bad = 0;
+    for (int i = 0; i < NW; ++i) bad += L.wbad[i];
+    offsets[E] = carry;
+    status[0] = maxg;
+    status[1] = bad;
+  }
+  const int total = carry;
+  for (int r = total + tid; r < R; r += NT) row_token[r] = -1;
+  if (has)
+    rank_chunk(ev, R, E, k, nbits, w, lane, L.hist + w * E, scatter_index, row_token, fold ? L.row_token : nullptr);
+  if (fold) {
+    __syncthreads();
+    const int n = total * row_vecs;
+    for (int i = tid; i < n; i += NT) {
+      const int r = i / row_vecs, v = i - r * row_vecs;
+      xs[(int64_t)r * row_vecs + v] = x[(int64_t)L.row_token[r] * row_vecs + v];
+    }
+  }
+}
+
+#define MOE_BLOCK_LDS(NW)                                                                        \
+  extern __shared__ int32_t hist[];                                                              \
+  __shared__ int32_t wsum[NW], wmax[NW], wbad[NW];                                               \
+  __shared__ int32_t s_row_token[kFoldRows];                                                     \
+  const BlockLds lds{hist, wsum, wmax, wbad, s_row_token};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void scatter_small(const int32_t* __restrict__ ids, int R, int E, int k,
+                                                         int nbits, int nchunks, int32_t* __restrict__ scatter_index,
+                                                         int32_t* __restrict__ row_token,
+                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ status,
+                                                         int fold, const u32x4* __restrict__ x, int row_vecs,
+                                                         u32x4* __restrict__ xs) {
+  MOE_BLOCK_LDS(NW)
+  scatter_block<NW>(ids, R, E, k, nbits, nchunks, scatter_index, row_token, offsets, status, fold, x, row_vecs, xs,
+                    lds);
+}
+
+// Routing and scatter of at most kRsTokens tokens (and kRsLogits logits) in
+// one workgroup: the workgroup first assembles every logit (fixed-order sum of
+// the partial logits + bias) into the logits output and LDS; each wave then
+// runs topk_wave for its tokens from the LDS copy, the selections go to global
+// memory and to LDS, and the workgroup builds the scatter from the LDS copy.
+constexpr int kRsTokens = 16;
+constexpr int kRsLogits = 4096;
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void route_scatter_small(
+    const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, float* __restrict__ logits,
+    int T, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int nbits, int nchunks,
+    int32_t* __restrict__ scatter_index, int32_t* __restrict__ row_token, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ status, int fold, const u32x4* __restrict__ x, int row_vecs, u32x4* __restrict__ xs) {
+  MOE_BLOCK_LDS(NW)
+  __shared__ int32_t s_ids[kRsTokens * kMaxTopK];
+  __shared__ float s_logits[kRsLogits];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < T * E; i += NW * kWave) {
+    float v = sum_slices(partial + i, (int64_t)T * E, nsplit);
+    if (bias) v += bias[i % E];
+    logits[i] = v;
+    s_logits[i] = v;
+  }
+  __syncthreads();
+  for (int t = w; t < T; t += NW) {
+    float raw[kTopkPer];
+#pragma unroll
+    for (int q = 0; q < kTopkPer; ++q) {
+      const int e = lane + kWave * q;
+      raw[q] = e < E ? s_logits[t * E + e] : -INFINITY;
+    }
+    int id;
+    float wgt;
+    topk_wave(raw, E, k, id, wgt);
+    if (lane < k) {
+      topk_ids[(int64_t)t * k + lane] = id;
+      topk_weights[(int64_t)t * k + lane] = wgt;
+      s_ids[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  scatter_block<NW>(s_ids, T * k, E, k, nbits, nchunks, scatter_index, row_token, offsets, status, fold, x,
+                          row_vecs, xs, lds);
 }
 
 constexpr int kCopyRows = 8;
@@ -158,6 +355,7 @@ __global__ __launch_bounds__(256) void scatter_copy(const u32x4* __restrict__ x,
 }
 
 int num_chunks(int R) { return (R + kChunk - 1) / kChunk; }
+constexpr int kSmallHist = 8192;  // LDS counters of the one-workgroup path (32 KiB)
 
 }  // namespace
 }  // namespace moe
@@ -179,20 +377,70 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
   const int nblk = (nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  int32_t* cnt = (int32_t*)workspace;
-  int32_t* bad = cnt + (int64_t)nchunks * E;
-  const size_t lds = (size_t)kWavesPerBlock * E * sizeof(int32_t);
-  hipLaunchKernelGGL(scatter_count, dim3(nblk), dim3(256), lds, s, ids, R, E, nbits, nchunks, cnt, bad);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, cnt, (const int32_t*)bad, nchunks, E, R, offsets,
-                     status_words, row_token);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_rank, dim3(nblk), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
-                     (const int32_t*)cnt, (const int32_t*)offsets, scatter_index, row_token);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err;
   const int elem = dt == 1 ? 2 : 4;
   const int row_vecs = (int)((int64_t)H * elem / 16);
+  if (nchunks <= kSmallWaves && nchunks * E <= kSmallHist) {
+    const int fold = R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
+    const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
+    if (nchunks <= 4)
+      hipLaunchKernelGGL(scatter_small<4>, dim3(1), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
+                         scatter_index, row_token, offsets, status_words, fold, (const u32x4*)x, row_vecs,
+                         (u32x4*)x_scattered);
+    else
+      hipLaunchKernelGGL(scatter_small<kSmallWaves>, dim3(1), dim3(kSmallWaves * 64), lds, s, ids, R, E, top_k,
+                         nbits, nchunks, scatter_index, row_token, offsets, status_words, fold, (const u32x4*)x,
+                         row_vecs, (u32x4*)x_scattered);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (fold) return hipSuccess;
+  } else {
+    int32_t* cnt = (int32_t*)workspace;
+    int32_t* bad = cnt + (int64_t)nchunks * E;
+    const size_t lds = (size_t)kWavesPerBlock * E * sizeof(int32_t);
+    hipLaunchKernelGGL(scatter_count, dim3(nblk), dim3(256), lds, s, ids, R, E, nbits, nchunks, cnt, bad);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, cnt, (const int32_t*)bad, nchunks, E, R, offsets,
+                       status_words, row_token);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(scatter_rank, dim3(nblk), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
+                       (const int32_t*)cnt, (const int32_t*)offsets, scatter_index, row_token);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,
+                     (const int32_t*)row_token, (const int32_t*)offsets, E, R, row_vecs, (u32x4*)x_scattered);
+  return hipGetLastError();
+}
+
+bool route_scatter_fusable(int T, int top_k, int E) {
+  using namespace moe;
+  const int R = T * top_k;
+  return T <= kRsTokens && T * E <= kRsLogits && top_k <= kMaxTopK && num_chunks(R) <= 4 &&
+         num_chunks(R) * E <= kSmallHist;
+}
+
+hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const float* bias, float* logits, int T,
+                               int H, int E, int top_k, int32_t* ids, float* weights, const void* x,
+                               int32_t* scatter_index, int32_t* row_token, int32_t* offsets, int32_t* status_words,
+                               void* x_scattered, hipStream_t s) {
+  using namespace moe;
+  const int R = T * top_k;
+  const int nchunks = num_chunks(R);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int elem = dt == 1 ? 2 : 4;
+  const int row_vecs = (int)((int64_t)H * elem / 16);
+  const int fold = R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
+  const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
+  if (T <= 4)  // one token per wave
+    hipLaunchKernelGGL(route_scatter_small<4>, dim3(1), dim3(256), lds, s, partial, nsplit, bias, logits, T, E,
+                       top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets, status_words, fold,
+                       (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
+  else
+    hipLaunchKernelGGL(route_scatter_small<kSmallWaves>, dim3(1), dim3(kSmallWaves * 64), lds, s, partial, nsplit,
+                       bias, logits, T, E, top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets,
+                       status_words, fold, (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || fold) return err;
   hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,
                      (const int32_t*)row_token, (const int32_t*)offsets, E, R, row_vecs, (u32x4*)x_scattered);
   return hipGetLastError();

@@ -53,10 +53,30 @@ def test_route_validation(lib):
     assert call(E=64, k=40) == 2 and "top_k must be <=" in _err(lib)
     assert call(dt=7) == 1 and "dt must be" in _err(lib)
     assert call(logits=None) == 1 and "logits" in _err(lib)
-    assert lib.moe_route_workspace_bytes(1, 16, 8) == 16 * 16 * 2       # E rounded up to 16
-    assert lib.moe_route_workspace_bytes(0, 16, 8) == 0
+    assert lib.moe_route_workspace_bytes(1, 4, 16, 8) >= 4 * 8 * 4                  # partial sums
+    assert lib.moe_route_workspace_bytes(1, 32, 16, 8) >= 16 * 16 * 2 + 32 * 16 * 4  # W_r^T, E rounded up to 16
+    assert lib.moe_route_workspace_bytes(0, 4, 16, 8) == 0
     assert call(ws=None) == 3 and "workspace needs" in _err(lib)
     assert call(ws_bytes=16) == 3
+
+
+def test_route_and_scatter_validation(lib):
+    need = lib.moe_route_and_scatter_workspace_bytes(1, 4, 64, 16, 2)
+    assert need >= max(lib.moe_route_workspace_bytes(1, 4, 64, 16), lib.moe_build_scatter_workspace_bytes(4, 2, 16))
+    assert lib.moe_route_and_scatter_workspace_bytes(1, 0, 64, 16, 2) == 0
+
+    def call(**kw):
+        a = dict(dt=1, x=FAKE, w=FAKE, T=4, H=64, E=16, k=2, logits=FAKE, rt=FAKE, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.moe_route_and_scatter(a["dt"], a["x"], a["w"], None, a["T"], a["H"], a["E"], a["k"], FAKE, FAKE,
+                                         a["logits"], FAKE, a["rt"], FAKE, FAKE, FAKE, a["ws"], a["wsb"], None)
+
+    assert call(logits=None) == 1 and "logits must not be NULL" in _err(lib)
+    assert call(rt=None) == 1 and "row_token" in _err(lib)
+    assert call(k=17) == 1 and "exceeds E" in _err(lib)
+    assert call(H=60) == 2 and "multiple of 8" in _err(lib)
+    assert call(ws=None) == 3 and "workspace needs" in _err(lib)
+    assert call(wsb=need - 1) == 3
 
 
 def test_scatter_validation_and_workspace(lib):

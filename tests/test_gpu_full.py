@@ -1,6 +1,7 @@
 """Full-size GPU parity for every layer workload, in the launch configuration
-the benchmark times (the same binding calls on the same buffers: routed and
-shared experts through the *_and_shared calls).
+the benchmark times (the same binding calls on the same buffers: routing and
+scatter through moe_route_and_scatter; routed and shared experts through the
+*_and_shared calls).
 
 Checked on each workload:
   * routing: logits within the certified fp32 bound of the oracle's; top-k
@@ -54,7 +55,7 @@ def test_full_size_layer(name):
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.y_rows.fill_(float("nan"))
     B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
-                        fused_shared=True)
+                        fused_shared=True, fused_route=True)
     torch.cuda.synchronize()
 
     # routing

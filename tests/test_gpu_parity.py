@@ -88,6 +88,43 @@ def test_route_with_logit_bias_and_limits():
                   cfg.top_k, O)
 
 
+@pytest.mark.parametrize("T,H,E,k,with_bias", [
+    (1, 2048, 64, 6, False),      # vector-ALU router, W_r read in place
+    (3, 136, 24, 5, True),        # 3 experts per 8-wide slot group; row lanes not a power of two
+    (16, 7168, 256, 8, False),    # largest token count of the vector-ALU router
+    (17, 520, 64, 4, True),       # first token count of the MFMA router
+    (2, 264, 1024, 32, True),     # most experts: two row lanes per workgroup
+    (5, 264, 60, 4, False),       # E not a multiple of 8 at a small token count: MFMA router
+    (2, 40000, 8, 2, False),      # more H slices than one group of eight partial loads
+])
+def test_route_small_token_paths(T, H, E, k, with_bias):
+    cfg = wl.LayerConfig("route_small", "bf16", T=T, H=H, E=E, top_k=k, I=8)
+    print(f"[route-small] T={T} H={H} E={E} k={k} bias={with_bias}", flush=True)
+    x = wl.make_x(cfg, DEV)
+    wr = wl.make_router(cfg, DEV)
+    bias = np.linspace(-0.5, 0.5, E).astype(np.float32) if with_bias else None
+    bias_t = torch.from_numpy(bias).to(DEV) if with_bias else None
+    bufs = B.MoELayerBuffers(T, H, E, k, 8, 0, x.dtype, DEV)
+    B.moe_route(x, wr, bias_t, k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws)
+    torch.cuda.synchronize()
+    check_routing(host(bufs.logits), host(bufs.topk_ids), host(bufs.topk_weights), host(x), host(wr), bias, k, O)
+
+
+@pytest.mark.parametrize("T", [4, 64])
+def test_topk_ties_on_integer_logits(T):
+    """Exact integer router products at both router paths: logits and ties bit-exact."""
+    H, E, k = 64, 16, 5
+    rng = np.random.default_rng(T)
+    x = torch.from_numpy(rng.integers(-1, 2, (T, H)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    wr = torch.from_numpy(rng.integers(0, 2, (H, E)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    bufs = B.MoELayerBuffers(T, H, E, k, 8, 0, torch.bfloat16, DEV)
+    B.moe_route(x, wr, None, k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws)
+    torch.cuda.synchronize()
+    L = host(bufs.logits)
+    assert np.array_equal(L, O.router_logits(host(x), host(wr)))
+    assert np.array_equal(host(bufs.topk_ids), O.topk_select(L, k))
+
+
 def test_topk_ties_and_nan_on_identical_logits():
     """Top-k bit-exactness where ties decide: integer-valued router products."""
     T, H, E, k = 64, 64, 20, 5
@@ -126,7 +163,8 @@ def _check_scatter(b, ids_np, x_np, E):
 
 @pytest.mark.parametrize("T,E,k,dup", [(128, 8, 2, "all0"), (128, 8, 2, "balanced"), (1, 64, 6, "rand"),
                                        (4096, 256, 8, "rand"), (3000, 60, 4, "rand"), (2500, 1024, 32, "rand"),
-                                       (777, 3, 5, "rand")])
+                                       (777, 3, 5, "rand"), (4096, 128, 4, "rand"), (4097, 8, 4, "rand"),
+                                       (100, 1024, 8, "rand"), (64, 300, 16, "rand")])
 def test_scatter_bit_exact(T, E, k, dup):
     rng = np.random.default_rng(T + E + k)
     if dup == "all0":
@@ -149,6 +187,46 @@ def test_scatter_out_of_range_ids_are_counted():
     _check_scatter(b, ids, host(x), 3)
     assert host(b.status_words)[1] == 3
     assert (host(b.scatter_index)[ids >= 3] == -1).all()
+
+
+@pytest.mark.parametrize("T,H,E,k,with_bias", [
+    (1, 2048, 64, 6, False),      # one workgroup: top-k, scatter and row copy
+    (4, 264, 1024, 32, True),     # one workgroup at the largest expert count
+    (16, 256, 256, 32, True),     # one workgroup at the most logits (T*E = 4096); too many rows to copy there
+    (16, 7168, 256, 8, False),    # one workgroup for the layout, rows too many bytes to copy there
+    (16, 256, 1024, 32, False),   # T*E past the one-workgroup path: the separate kernels
+    (9, 264, 60, 4, True),        # E not a multiple of 8: the separate kernels
+    (17, 520, 64, 6, False),      # first token count past the one-workgroup path
+    (300, 264, 7, 2, False),      # f32 below
+])
+def test_route_and_scatter_matches_the_two_calls(T, H, E, k, with_bias):
+    dtype = "f32" if E == 7 else "bf16"
+    cfg = wl.LayerConfig("route_scatter", dtype, T=T, H=H, E=E, top_k=k, I=8)
+    print(f"[route+scatter] {dtype} T={T} H={H} E={E} k={k} bias={with_bias}", flush=True)
+    x = wl.make_x(cfg, DEV)
+    wr = wl.make_router(cfg, DEV)
+    bias = np.linspace(-0.5, 0.5, E).astype(np.float32) if with_bias else None
+    bias_t = torch.from_numpy(bias).to(DEV) if with_bias else None
+    a = B.MoELayerBuffers(T, H, E, k, 8, 0, x.dtype, DEV)
+    b = B.MoELayerBuffers(T, H, E, k, 8, 0, x.dtype, DEV)
+    for buf in (a, b):
+        buf.x_scattered.fill_(0)
+        buf.row_token.fill_(-7)
+    B.moe_route(x, wr, bias_t, k, a.topk_ids, a.topk_weights, a.logits, a.route_ws)
+    B.moe_build_scatter(x, a.topk_ids, E, a.scatter_index, a.row_token, a.expert_offsets, a.status_words,
+                        a.x_scattered, a.scatter_ws)
+    B.moe_route_and_scatter(x, wr, bias_t, k, b.topk_ids, b.topk_weights, b.logits, b.scatter_index, b.row_token,
+                            b.expert_offsets, b.status_words, b.x_scattered, b.route_scatter_ws)
+    torch.cuda.synchronize()
+    for name in ("logits", "topk_ids", "topk_weights", "scatter_index", "row_token", "expert_offsets",
+                 "status_words", "x_scattered"):
+        assert torch.equal(getattr(a, name).view(torch.uint8) if getattr(a, name).dtype == torch.bfloat16
+                           else getattr(a, name), getattr(b, name).view(torch.uint8)
+                           if getattr(b, name).dtype == torch.bfloat16 else getattr(b, name)), name
+    # and against the oracle
+    ids = host(b.topk_ids)
+    check_routing(host(b.logits), ids, host(b.topk_weights), host(x), host(wr), bias, k, O)
+    _check_scatter(b, ids, host(x), E)
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
@@ -186,11 +264,14 @@ def test_grouped_gemms_per_call(cfg):
     assert mx <= 1e-5, f"fc2 relative max error {mx:.3e} against the oracle on the same activation"
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused_shared"])
+@pytest.mark.parametrize("mode", ["separate", "fused", "overlap"])
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
-def test_layer_end_to_end(cfg, fused):
-    """All six calls (or, with fused_shared, the routed and shared experts
-    together through the *_and_shared calls); y against the oracle fed the
+def test_layer_end_to_end(cfg, mode):
+    """All six calls; or, fused: routing and scatter through
+    moe_route_and_scatter and the routed and shared experts together through
+    the *_and_shared calls; or, overlap: routing and scatter through
+    moe_route_and_scatter, the shared expert on a second stream.  y against
+    the oracle fed the
     GPU's routes (which were themselves checked against the oracle's top-k of
     the GPU logits)."""
     layer = _layer(cfg)
@@ -200,7 +281,8 @@ def test_layer_end_to_end(cfg, fused):
     bufs.act.fill_(float("nan"))
     bufs.y_rows.fill_(float("nan"))
     B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
-                        fused_shared=fused)
+                        fused_shared=mode == "fused", fused_route=mode != "separate",
+                        side_stream=torch.cuda.Stream() if mode == "overlap" else None)
     torch.cuda.synchronize()
     ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
     check_routing(host(bufs.logits), ids, w, host(x), host(wr), layer["bias"], cfg.top_k, O)
@@ -288,14 +370,16 @@ def test_combine_accumulate_and_skipped_slots():
     assert_output_close(host(y), ref, "f32")
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused_shared"])
-def test_two_runs_bit_identical(fused):
+@pytest.mark.parametrize("mode", ["separate", "fused", "overlap"])
+def test_two_runs_bit_identical(mode):
     cfg = CASES[6]
     layer = _layer(cfg)
     outs = []
     for _ in range(2):
         bufs = B.moe_layer_forward(layer["x"], layer["w_router"], None, layer["W1"], layer["W2"], cfg.top_k,
-                                   shared=layer["shared"], fused_shared=fused)
+                                   shared=layer["shared"], fused_shared=mode == "fused",
+                                   fused_route=mode != "separate",
+                                   side_stream=torch.cuda.Stream() if mode == "overlap" else None)
         torch.cuda.synchronize()
         outs.append((host(bufs.y).copy(), host(bufs.scatter_index).copy(), host(bufs.y_rows).copy()))
     for a, b in zip(*outs):
