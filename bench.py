@@ -98,6 +98,7 @@ def committed_traffic(workload):
 
 
 def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
+    lay = layer["layout"]
     """One layer forward: route + scatter, fc1 (+ shared fc1), fc2 (+ shared fc2, gate), combine.
     With `side` (a second stream) and a shared expert, the shared expert runs on
     `side` (y = shared(x)) while routing and the routed experts run on the
@@ -111,15 +112,15 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
         main = torch.cuda.current_stream()
         side.wait_stream(main)
         ws1, ws2, wg = shared
-        B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, stream=side)
+        B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, stream=side, layout=lay)
         rec(0)
         B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                                 bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
                                 bufs.x_scattered, bufs.route_scatter_ws)
         rec(1)
-        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
+        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, layout=lay)
         rec(2)
-        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
+        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, layout=lay)
         rec(3)
         main.wait_stream(side)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
@@ -133,16 +134,16 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
     if shared is not None:
         ws1, ws2, wg = shared
         B.moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
-                                            bufs.act_shared)
+                                            bufs.act_shared, layout=lay)
         rec(2)
         B.moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
-                                     bufs.y, bufs.shared_ws, False)
+                                     bufs.y, bufs.shared_ws, False, layout=lay)
         rec(3)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
     else:
-        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act)
+        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, layout=lay)
         rec(2)
-        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)
+        B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, layout=lay)
         rec(3)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
     rec(4)
@@ -155,15 +156,17 @@ def cpu_baseline(layer, cfg, bufs, sample_tokens):
 
     S = min(sample_tokens, cfg.T)
     f = lambda t: t.detach().float().cpu().numpy()
+    # the oracle takes each weight as the K x N matrix of x @ W
+    fw = (lambda t: np.ascontiguousarray(f(t).T)) if layer["layout"] == B.MOE_W_NK else f
     log(f"cpu baseline: copying inputs for {S} tokens to the host")
     x = f(layer["x"][:S])
     wr = f(layer["w_router"])
-    W1 = [f(layer["W1"][e]) for e in range(cfg.E)]
-    W2 = [f(layer["W2"][e]) for e in range(cfg.E)]
+    W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
+    W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
     shared = None
     if layer["shared"] is not None:
         ws1, ws2, wg = layer["shared"]
-        shared = (f(ws1), f(ws2), f(wg) if wg is not None else None)
+        shared = (fw(ws1), fw(ws2), f(wg) if wg is not None else None)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     log(f"cpu baseline: oracle over {S} tokens with {threads} BLAS threads")
@@ -207,6 +210,9 @@ def main():
     ap.add_argument("--shared", choices=("fused", "overlap"), default="fused",
                     help="shared expert inside the routed fc1/fc2 launches (fused, the default: measured faster "
                          "on every workload) or on a second stream concurrent with routing (overlap)")
+    ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
+                    help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default: measured "
+                         "as fast or faster on every workload), nk = [N, K] (torch.nn.Linear layout)")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -222,6 +228,15 @@ def main():
     cfg = wl.WORKLOADS[args.workload]
     log(f"workload {cfg}")
     layer = wl.make_layer(cfg, dev)
+    layer["layout"] = B.MOE_W_NK if args.layout == "nk" else B.MOE_W_KN
+    if args.layout == "nk":  # the same matrices, stored [N, K]
+        t = lambda w: w.transpose(-1, -2).contiguous()
+        for key in ("W1", "W2"):
+            layer[key] = t(layer[key])
+            torch.cuda.empty_cache()
+        if layer["shared"] is not None:
+            ws1, ws2, wg = layer["shared"]
+            layer["shared"] = (t(ws1), t(ws2), wg)
     bias_t = torch.from_numpy(layer["bias"]).to(dev) if layer["bias"] is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, dev)
     torch.cuda.synchronize()
@@ -323,6 +338,7 @@ def main():
                   "active_experts": work["active_experts"]},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
         "timing": "hip graph replay" if args.graph else "eager launches",
+        "weight_layout": "[N, K] per expert (torch.nn.Linear)" if args.layout == "nk" else "[K, N] per expert",
         "shared_expert": {"fused": "inside the routed fc1/fc2 launches",
                           "overlap": "moe_shared_expert on a second stream, concurrent with routing and the "
                                      "routed experts; the combine waits for it",

@@ -54,6 +54,16 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage of an expert weight W that maps K inputs to N outputs (the layer
+ * computes x @ W with W a K x N matrix in the pages' notation):
+ *   MOE_W_KN: row-major [K, N], N contiguous (the pages' x @ W form);
+ *   MOE_W_NK: row-major [N, K], K contiguous (the layout of a torch.nn.Linear
+ *             weight; both MFMA operands are then K-contiguous, so weight
+ *             tiles are read from LDS like activation tiles).
+ * The values are the same matrix either way; results are identical up to
+ * the fp32 accumulation order within a tile. */
+typedef enum moe_weight_layout { MOE_W_KN = 0, MOE_W_NK = 1 } moe_weight_layout;
+
 /* Name of a status code ("MOE_OK", ...).  Never NULL. */
 const char* moe_status_name(int status);
 
@@ -167,12 +177,13 @@ size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H,
  * R rows); empty experts read no weights.
  *
  * x_scattered [R, H] (dt), expert_offsets [E+1] int32 (device),
- * w1 [E, H, 2I] (dt; per expert row-major [H, 2I], gate columns first),
+ * w1 (dt): wl = MOE_W_KN: [E, H, 2I] (per expert [H, 2I], gate columns
+ * first); wl = MOE_W_NK: [E, 2I, H] (per expert [2I, H], gate rows first),
  * act [R, I] (dt) out; rows past expert_offsets[E] are not written.
  */
-moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
-                                  const void* w1, int32_t R, int32_t H, int32_t E, int32_t I,
-                                  void* act, void* stream);
+moe_status moe_grouped_swiglu_fc1(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                  const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
+                                  int32_t E, int32_t I, void* act, void* stream);
 
 /*
  * moe_grouped_fc2 -- per-expert down projection.
@@ -182,10 +193,11 @@ moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const i
  *
  *   y_rows[r] = act[r] @ w2[e]   for r in group e, accumulated and stored fp32
  *
- * act [R, I] (dt), expert_offsets [E+1] int32, w2 [E, I, H] (dt),
- * y_rows [R, H] fp32 out; rows past expert_offsets[E] are not written.
+ * act [R, I] (dt), expert_offsets [E+1] int32, w2 (dt): [E, I, H] for
+ * MOE_W_KN, [E, H, I] for MOE_W_NK, y_rows [R, H] fp32 out; rows past
+ * expert_offsets[E] are not written.
  */
-moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_offsets,
+moe_status moe_grouped_fc2(moe_dtype dt, moe_weight_layout wl, const void* act, const int32_t* expert_offsets,
                            const void* w2, int32_t R, int32_t I, int32_t E, int32_t H,
                            float* y_rows, void* stream);
 
@@ -224,11 +236,12 @@ size_t moe_shared_expert_workspace_bytes(moe_dtype dt, int32_t T, int32_t I_s);
  *   ys = a @ ws2;   if w_gate: ys[t] *= 1 / (1 + exp(-(x[t] . w_gate)))
  *   y  = (accumulate ? y : 0) + ys                           (fp32)
  *
- * x [T, H] (dt), ws1 [H, 2 I_s] (dt), ws2 [I_s, H] (dt), w_gate [H] (dt) or
- * NULL for the ungated variant, y [T, H] fp32 in/out, workspace of at least
+ * x [T, H] (dt), ws1 (dt) [H, 2 I_s] (MOE_W_KN) or [2 I_s, H] (MOE_W_NK),
+ * ws2 (dt) [I_s, H] or [H, I_s], w_gate [H] (dt) or NULL for the ungated
+ * variant, y [T, H] fp32 in/out, workspace of at least
  * moe_shared_expert_workspace_bytes(dt, T, I_s) bytes.
  */
-moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const void* ws2,
+moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, const void* ws1, const void* ws2,
                              const void* w_gate, int32_t T, int32_t H, int32_t I_s,
                              int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
                              void* stream);
@@ -252,22 +265,23 @@ moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const
  * The routed outputs are then added with moe_gather_combine(accumulate = 1).
  * moe_grouped_fc2_and_shared needs a workspace of at least
  * moe_shared_expert_workspace_bytes(dt, T, I_s) bytes (it holds the gate).
- * Other arguments are those of the three separate calls.  Each call chooses
+ * Other arguments (wl covers w1/w2 and ws1/ws2 alike) are those of the
+ * three separate calls.  Each call chooses
  * from the shapes whether its two computations share one launch (bf16, H, I
  * and I_s multiples of 64, and a shared expert whose FLOPs are small next to
  * the routed weight bytes) or run one after the other; results are the same
  * either way.
  */
-moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
-                                             const void* w1, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
-                                             const void* x, const void* ws1, int32_t T, int32_t I_s,
-                                             void* act_shared, void* stream);
+moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                             const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
+                                             int32_t E, int32_t I, void* act, const void* x, const void* ws1,
+                                             int32_t T, int32_t I_s, void* act_shared, void* stream);
 
-moe_status moe_grouped_fc2_and_shared(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2,
-                                      int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
-                                      const void* act_shared, const void* ws2, const void* x, const void* w_gate,
-                                      int32_t T, int32_t I_s, int32_t accumulate, float* y, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const void* act,
+                                      const int32_t* expert_offsets, const void* w2, int32_t R, int32_t I, int32_t E,
+                                      int32_t H, float* y_rows, const void* act_shared, const void* ws2,
+                                      const void* x, const void* w_gate, int32_t T, int32_t I_s, int32_t accumulate,
+                                      float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

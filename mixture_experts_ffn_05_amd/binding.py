@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "libmoe.h")
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_W_KN, MOE_W_NK = 0, 1   # expert weights as [K, N] (x @ W) or [N, K] (torch.nn.Linear)
 MOE_OK = 0
 
 _lib = None
@@ -47,16 +48,16 @@ _SIGNATURES = {
     "moe_route_and_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_build_scatter": (_c_int, [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_size, _vp]),
-    "moe_grouped_swiglu_fc1": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
-    "moe_grouped_fc2": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_swiglu_fc1": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_gather_combine": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_shared_expert_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
-    "moe_shared_expert": (_c_int, [_c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
-                                   _vp]),
-    "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
-                                                   _vp, _vp, _c_int, _c_int, _vp, _vp]),
-    "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
-                                            _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "moe_shared_expert": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                   _c_size, _vp]),
+    "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                                   _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                            _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -190,26 +191,38 @@ def moe_route_and_scatter(x, w_router, logit_bias, top_k, topk_ids, topk_weights
     _check(lib.moe_route_and_scatter(*args))
 
 
-def moe_grouped_swiglu_fc1(x_scattered, expert_offsets, w1, act, stream=None):
+def _fc1_sizes(w1, layout):
+    """(E, H, I) of a stacked fc1 weight in the given layout."""
+    if layout == MOE_W_NK:
+        E, I2, H = w1.shape
+    else:
+        E, H, I2 = w1.shape
+    return E, H, I2 // 2
+
+
+def moe_grouped_swiglu_fc1(x_scattered, expert_offsets, w1, act, stream=None, layout=MOE_W_KN):
     lib = load()
     R, H = x_scattered.shape
-    E, _, I2 = w1.shape
-    I = I2 // 2
+    E, _, I = _fc1_sizes(w1, layout)
     dev = x_scattered.device
-    args = (_dt(x_scattered), _ptr(x_scattered, "x_scattered"),
+    wshape = (E, 2 * I, H) if layout == MOE_W_NK else (E, H, 2 * I)
+    args = (_dt(x_scattered), int(layout), _ptr(x_scattered, "x_scattered"),
             _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
-            _ptr(w1, "w1", x_scattered.dtype, (E, H, 2 * I), dev), R, H, E, I,
+            _ptr(w1, "w1", x_scattered.dtype, wshape, dev), R, H, E, I,
             _ptr(act, "act", x_scattered.dtype, (R, I), dev), _stream(stream, dev))
     _check(lib.moe_grouped_swiglu_fc1(*args))
 
 
-def moe_grouped_fc2(act, expert_offsets, w2, y_rows, stream=None):
+def moe_grouped_fc2(act, expert_offsets, w2, y_rows, stream=None, layout=MOE_W_KN):
     lib = load()
     R, I = act.shape
-    E, _, H = w2.shape
+    E = w2.shape[0]
+    H = w2.shape[1] if layout == MOE_W_NK else w2.shape[2]
     dev = act.device
-    args = (_dt(act), _ptr(act, "act"), _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
-            _ptr(w2, "w2", act.dtype, (E, I, H), dev), R, I, E, H,
+    wshape = (E, H, I) if layout == MOE_W_NK else (E, I, H)
+    args = (_dt(act), int(layout), _ptr(act, "act"),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2, "w2", act.dtype, wshape, dev), R, I, E, H,
             _ptr(y_rows, "y_rows", torch.float32, (R, H), dev), _stream(stream, dev))
     _check(lib.moe_grouped_fc2(*args))
 
@@ -233,46 +246,56 @@ def moe_shared_expert_workspace_bytes(dtype, T, I_s) -> int:
     return int(load().moe_shared_expert_workspace_bytes(dt, int(T), int(I_s)))
 
 
-def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream=None):
+def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream=None, layout=MOE_W_KN):
     lib = load()
     T, H = x.shape
-    I_s = ws2.shape[0]
+    nk = layout == MOE_W_NK
+    I_s = ws2.shape[1] if nk else ws2.shape[0]
     dev = x.device
-    args = (_dt(x), _ptr(x, "x"), _ptr(ws1, "ws1", x.dtype, (H, 2 * I_s), dev),
-            _ptr(ws2, "ws2", x.dtype, (I_s, H), dev), _ptr(w_gate, "w_gate", x.dtype, (H,), dev), T, H, I_s,
+    args = (_dt(x), int(layout), _ptr(x, "x"),
+            _ptr(ws1, "ws1", x.dtype, (2 * I_s, H) if nk else (H, 2 * I_s), dev),
+            _ptr(ws2, "ws2", x.dtype, (H, I_s) if nk else (I_s, H), dev),
+            _ptr(w_gate, "w_gate", x.dtype, (H,), dev), T, H, I_s,
             int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_shared_expert(*args))
 
 
-def moe_grouped_swiglu_fc1_and_shared(x_scattered, expert_offsets, w1, act, x, ws1, act_shared, stream=None):
+def moe_grouped_swiglu_fc1_and_shared(x_scattered, expert_offsets, w1, act, x, ws1, act_shared, stream=None,
+                                      layout=MOE_W_KN):
     lib = load()
     R, H = x_scattered.shape
-    E, _, I2 = w1.shape
-    I = I2 // 2
+    E, _, I = _fc1_sizes(w1, layout)
+    nk = layout == MOE_W_NK
     T = x.shape[0]
-    I_s = ws1.shape[1] // 2
+    I_s = (ws1.shape[0] if nk else ws1.shape[1]) // 2
     dev = x.device
     dt = x.dtype
-    args = (_dt(x), _ptr(x_scattered, "x_scattered", dt, (R, H), dev),
+    args = (_dt(x), int(layout), _ptr(x_scattered, "x_scattered", dt, (R, H), dev),
             _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
-            _ptr(w1, "w1", dt, (E, H, 2 * I), dev), R, H, E, I, _ptr(act, "act", dt, (R, I), dev),
-            _ptr(x, "x", dt, (T, H), dev), _ptr(ws1, "ws1", dt, (H, 2 * I_s), dev), T, I_s,
+            _ptr(w1, "w1", dt, (E, 2 * I, H) if nk else (E, H, 2 * I), dev), R, H, E, I,
+            _ptr(act, "act", dt, (R, I), dev), _ptr(x, "x", dt, (T, H), dev),
+            _ptr(ws1, "ws1", dt, (2 * I_s, H) if nk else (H, 2 * I_s), dev), T, I_s,
             _ptr(act_shared, "act_shared", dt, (T, I_s), dev), _stream(stream, dev))
     _check(lib.moe_grouped_swiglu_fc1_and_shared(*args))
 
 
 def moe_grouped_fc2_and_shared(act, expert_offsets, w2, y_rows, act_shared, ws2, x, w_gate, y, workspace,
-                               accumulate=False, stream=None):
+                               accumulate=False, stream=None, layout=MOE_W_KN):
     lib = load()
     R, I = act.shape
-    E, _, H = w2.shape
+    nk = layout == MOE_W_NK
+    E = w2.shape[0]
+    H = w2.shape[1] if nk else w2.shape[2]
     T, I_s = act_shared.shape
     dev = act.device
     dt = act.dtype
-    args = (_dt(act), _ptr(act, "act"), _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
-            _ptr(w2, "w2", dt, (E, I, H), dev), R, I, E, H, _ptr(y_rows, "y_rows", torch.float32, (R, H), dev),
-            _ptr(act_shared, "act_shared", dt, (T, I_s), dev), _ptr(ws2, "ws2", dt, (I_s, H), dev),
+    args = (_dt(act), int(layout), _ptr(act, "act"),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2, "w2", dt, (E, H, I) if nk else (E, I, H), dev), R, I, E, H,
+            _ptr(y_rows, "y_rows", torch.float32, (R, H), dev),
+            _ptr(act_shared, "act_shared", dt, (T, I_s), dev),
+            _ptr(ws2, "ws2", dt, (H, I_s) if nk else (I_s, H), dev),
             _ptr(x, "x", dt, (T, H), dev), _ptr(w_gate, "w_gate", dt, (H,), dev), T, I_s, int(bool(accumulate)),
             _ptr(y, "y", torch.float32, (T, H), dev), _ptr(workspace, "workspace", torch.uint8, None, dev),
             workspace.numel(), _stream(stream, dev))
@@ -309,7 +332,7 @@ class MoELayerBuffers:
 
 
 def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=None, routes=None,
-                      stream=None, fused_shared=False, fused_route=False, side_stream=None):
+                      stream=None, fused_shared=False, fused_route=False, side_stream=None, layout=MOE_W_KN):
     """The six calls in order.  ``routes`` = (topk_ids int32, topk_weights fp32)
     device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None).
     With ``fused_shared`` and a shared expert, the routed experts and the shared
@@ -319,12 +342,13 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
     scatter build run through moe_route_and_scatter.  With ``side_stream`` (a
     torch.cuda.Stream; not with ``fused_shared``) and a shared expert, the shared
     expert runs there first (y = shared(x)), concurrently with routing and the
-    routed experts, and the combine waits for it and adds onto y."""
+    routed experts, and the combine waits for it and adds onto y.  ``layout``
+    (MOE_W_KN or MOE_W_NK) is the storage of W1, W2 and the shared weights."""
     T, H = x.shape
-    E, _, I2 = W1.shape
-    I_s = shared[1].shape[0] if shared is not None else 0
+    E, _, I = _fc1_sizes(W1, layout)
+    I_s = (shared[1].shape[1] if layout == MOE_W_NK else shared[1].shape[0]) if shared is not None else 0
     if bufs is None:
-        bufs = MoELayerBuffers(T, H, E, top_k, I2 // 2, I_s, x.dtype, x.device)
+        bufs = MoELayerBuffers(T, H, E, top_k, I, I_s, x.dtype, x.device)
     if routes is None and fused_route:
         moe_route_and_scatter(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                               bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
@@ -345,17 +369,17 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         main = torch.cuda.current_stream(x.device) if stream is None else stream
         side_stream.wait_stream(main)
         ws1, ws2, wg = shared
-        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, side_stream)
+        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, side_stream, layout=layout)
     if fused_shared and shared is not None:
         ws1, ws2, wg = shared
         moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
-                                          bufs.act_shared, stream)
+                                          bufs.act_shared, stream, layout=layout)
         moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
-                                   bufs.y, bufs.shared_ws, False, stream)
+                                   bufs.y, bufs.shared_ws, False, stream, layout=layout)
         moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, True, stream)
         return bufs
-    moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream)
-    moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream)
+    moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream, layout=layout)
+    moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream, layout=layout)
     if side_stream is not None and shared is not None:
         main.wait_stream(side_stream)
         moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, True, stream)
@@ -363,5 +387,5 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
     moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, False, stream)
     if shared is not None:
         ws1, ws2, wg = shared
-        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True, stream)
+        moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True, stream, layout=layout)
     return bufs

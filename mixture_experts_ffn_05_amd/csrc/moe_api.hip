@@ -70,6 +70,12 @@ moe_status need_dtype(moe_dtype dt, const char* fn) {
                                                  fn, (int)dt);
 }
 
+moe_status need_layout(moe_weight_layout wl, const char* fn) {
+  return (wl == MOE_W_KN || wl == MOE_W_NK)
+             ? MOE_OK
+             : fail(MOE_ERR_INVALID_ARGUMENT, "%s: weight layout must be MOE_W_KN or MOE_W_NK (got %d)", fn, (int)wl);
+}
+
 moe_status need_mult8(int64_t v, const char* fn, const char* name) {
   return v % 8 == 0 ? MOE_OK
                     : fail(MOE_ERR_UNSUPPORTED, "%s: %s must be a multiple of 8 (got %lld)", fn, name, (long long)v);
@@ -238,10 +244,12 @@ moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_id
                     fn);
 }
 
-moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets, const void* w1,
-                                  int32_t R, int32_t H, int32_t E, int32_t I, void* act, void* stream) {
+moe_status moe_grouped_swiglu_fc1(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                  const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H, int32_t E,
+                                  int32_t I, void* act, void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1";
   MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w1, fn, "w1"));
@@ -253,15 +261,16 @@ moe_status moe_grouped_swiglu_fc1(moe_dtype dt, const void* x_scattered, const i
   MOE_CHECK(need_mult8(H, fn, "H"));
   MOE_CHECK(need_mult8(I, fn, "I"));
   MOE_CHECK(need_rows(R, fn, "R"));
-  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x_scattered, expert_offsets, E, R, w1,
+  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x_scattered, expert_offsets, E, R, w1,
                                                    (int64_t)H * 2 * I, H, I, act, 0, cu_count(), (hipStream_t)stream),
                     fn);
 }
 
-moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2, int32_t R,
-                           int32_t I, int32_t E, int32_t H, float* y_rows, void* stream) {
+moe_status moe_grouped_fc2(moe_dtype dt, moe_weight_layout wl, const void* act, const int32_t* expert_offsets,
+                           const void* w2, int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows, void* stream) {
   const char* fn = "moe_grouped_fc2";
   MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w2, fn, "w2"));
@@ -273,8 +282,8 @@ moe_status moe_grouped_fc2(moe_dtype dt, const void* act, const int32_t* expert_
   MOE_CHECK(need_mult8(H, fn, "H"));
   MOE_CHECK(need_mult8(I, fn, "I"));
   MOE_CHECK(need_rows(R, fn, "R"));
-  return hip_result(moe_launch::grouped_fc2((int)dt, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H, y_rows,
-                                            nullptr, 0, 1, 0, cu_count(), (hipStream_t)stream),
+  return hip_result(moe_launch::grouped_fc2((int)dt, (int)wl, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H,
+                                            y_rows, nullptr, 0, 1, 0, cu_count(), (hipStream_t)stream),
                     fn);
 }
 
@@ -301,11 +310,12 @@ size_t moe_shared_expert_workspace_bytes(moe_dtype dt, int32_t T, int32_t I_s) {
   return align256((size_t)T * I_s * elem_size(dt)) + align256((size_t)T * sizeof(float));
 }
 
-moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const void* ws2, const void* w_gate,
-                             int32_t T, int32_t H, int32_t I_s, int32_t accumulate, float* y, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, const void* ws1, const void* ws2,
+                             const void* w_gate, int32_t T, int32_t H, int32_t I_s, int32_t accumulate, float* y,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "moe_shared_expert";
   MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(ws1, fn, "ws1"));
   MOE_CHECK(need_ptr(ws2, fn, "ws2"));
@@ -327,17 +337,20 @@ moe_status moe_shared_expert(moe_dtype dt, const void* x, const void* ws1, const
   float* gate = w_gate ? (float*)(ws + align256((size_t)T * I_s * elem_size(dt))) : nullptr;
   const int cus = cu_count();
   if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate((int)dt, x, w_gate, T, H, gate, s), fn));
-  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act, 1, cus, s), fn));
-  return hip_result(moe_launch::grouped_fc2((int)dt, act, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate, 0, 1, cus, s),
-                    fn);
+  MOE_CHECK(hip_result(
+      moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, nullptr, 1, T, ws1, 0, H, I_s, act, 1, cus, s), fn));
+  return hip_result(
+      moe_launch::grouped_fc2((int)dt, (int)wl, act, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate, 0, 1, cus, s),
+      fn);
 }
 
-moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, const void* x_scattered, const int32_t* expert_offsets,
-                                             const void* w1, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
-                                             const void* x, const void* ws1, int32_t T, int32_t I_s,
-                                             void* act_shared, void* stream) {
+moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                             const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
+                                             int32_t E, int32_t I, void* act, const void* x, const void* ws1,
+                                             int32_t T, int32_t I_s, void* act_shared, void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1_and_shared";
   MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w1, fn, "w1"));
@@ -359,23 +372,24 @@ moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, const void* x_scatter
   hipStream_t s = (hipStream_t)stream;
   const int cus = cu_count();
   if (moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T))
-    return hip_result(moe_launch::fused_fc1(x_scattered, expert_offsets, E, R, w1, H, I, act, x, T, ws1, I_s,
-                                            act_shared, cus, s),
+    return hip_result(moe_launch::fused_fc1((int)wl, x_scattered, expert_offsets, E, R, w1, H, I, act, x, T, ws1,
+                                            I_s, act_shared, cus, s),
                       fn);
-  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x_scattered, expert_offsets, E, R, w1,
+  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x_scattered, expert_offsets, E, R, w1,
                                                       (int64_t)H * 2 * I, H, I, act, 0, cus, s),
                        fn));
-  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, x, nullptr, 1, T, ws1, 0, H, I_s, act_shared, 1, cus, s),
-                    fn);
+  return hip_result(
+      moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, nullptr, 1, T, ws1, 0, H, I_s, act_shared, 1, cus, s), fn);
 }
 
-moe_status moe_grouped_fc2_and_shared(moe_dtype dt, const void* act, const int32_t* expert_offsets, const void* w2,
-                                      int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
-                                      const void* act_shared, const void* ws2, const void* x, const void* w_gate,
-                                      int32_t T, int32_t I_s, int32_t accumulate, float* y, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const void* act,
+                                      const int32_t* expert_offsets, const void* w2, int32_t R, int32_t I, int32_t E,
+                                      int32_t H, float* y_rows, const void* act_shared, const void* ws2,
+                                      const void* x, const void* w_gate, int32_t T, int32_t I_s, int32_t accumulate,
+                                      float* y, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "moe_grouped_fc2_and_shared";
   MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w2, fn, "w2"));
@@ -405,14 +419,14 @@ moe_status moe_grouped_fc2_and_shared(moe_dtype dt, const void* act, const int32
   const int cus = cu_count();
   if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate((int)dt, x, w_gate, T, H, gate, s), fn));
   if (moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T))
-    return hip_result(moe_launch::fused_fc2(act, expert_offsets, E, R, w2, I, H, y_rows, act_shared, T, ws2, I_s,
-                                            gate, accumulate, y, cus, s),
+    return hip_result(moe_launch::fused_fc2((int)wl, act, expert_offsets, E, R, w2, I, H, y_rows, act_shared, T,
+                                            ws2, I_s, gate, accumulate, y, cus, s),
                       fn);
-  MOE_CHECK(hip_result(moe_launch::grouped_fc2((int)dt, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H, y_rows,
-                                               nullptr, 0, 1, 0, cus, s),
+  MOE_CHECK(hip_result(moe_launch::grouped_fc2((int)dt, (int)wl, act, expert_offsets, E, R, w2, (int64_t)I * H, I, H,
+                                               y_rows, nullptr, 0, 1, 0, cus, s),
                        fn));
-  return hip_result(moe_launch::grouped_fc2((int)dt, act_shared, nullptr, 1, T, ws2, 0, I_s, H, y, gate, accumulate,
-                                            0, 1, cus, s),
+  return hip_result(moe_launch::grouped_fc2((int)dt, (int)wl, act_shared, nullptr, 1, T, ws2, 0, I_s, H, y, gate,
+                                            accumulate, 0, 1, cus, s),
                     fn);
 }
 

@@ -168,10 +168,11 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
 // Grouped GEMMs.  `offsets` may be null: one group of `rows` rows.
 // `role` (0 routed experts, 1 shared expert) only selects a separately named
 // kernel instantiation so that profiles tell the two apart.
-hipError_t grouped_swiglu_fc1(int dt, const void* a, const int32_t* offsets, int groups, int rows,
+// bt: weight layout, 0 = [K, N] per group (N contiguous), 1 = [N, K] (K contiguous).
+hipError_t grouped_swiglu_fc1(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
                               const void* w1, int64_t w1_group_stride, int K, int I, void* act,
                               int role, int cu_count, hipStream_t s);
-hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int groups, int rows,
+hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, int groups, int rows,
                        const void* w2, int64_t w2_group_stride, int K, int N, float* out,
                        const float* row_scale, int accumulate, int plain_store, int role, int cu_count,
                        hipStream_t s);
@@ -180,10 +181,10 @@ hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int grou
 // multiples of 64, and a shared expert that is light next to the routed
 // weights; fused_supported() decides from the shapes).
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T);
-hipError_t fused_fc1(const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
+hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
                      void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
                      hipStream_t s);
-hipError_t fused_fc2(const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
+hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
                      float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
                      int accumulate, float* y, int cu_count, hipStream_t s);
 

@@ -62,6 +62,12 @@
 #ifndef MOE_DECODE_FC1
 #define MOE_DECODE_FC1 13
 #endif
+#ifndef MOE_MID_FC1
+#define MOE_MID_FC1 10
+#endif
+#ifndef MOE_FUSE_POLICY
+#define MOE_FUSE_POLICY 0  // tuning: 0 by shape, 1 always, 2 never
+#endif
 #ifndef MOE_DECODE_FC2
 #define MOE_DECODE_FC2 13
 #endif
@@ -94,6 +100,7 @@ struct GemmParams {
   const float* row_scale;   // kScaleAdd: per-row factor, or null for 1
   int accumulate;           // kScaleAdd: add into out instead of overwriting
   int n_tiles;              // output column tiles per group
+  int bt;                   // 0: b rows are k ([K, ldb], N contiguous); 1: b rows are n ([N, ldb = K], K contiguous)
 };
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -113,7 +120,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
   const int wm = wave >> 1, wn = wave & 1;
   const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
 
-  // This thread's weight octet: columns [c, c+8) of the staged tile.
+  // [K, N] weights: this thread's weight octet is columns [c, c+8) of the staged tile.
   const int co = tid & 15, kq = tid >> 4;
   int bcol;
   bool bcol_ok;
@@ -147,6 +154,25 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
       const int row = row0 + r, k = k0 + ko * 8;
       ra[i] = (row < row_end && k < p.K) ? *(const u32x4*)(p.a + (int64_t)row * p.K + k) : u32x4{0u, 0u, 0u, 0u};
     }
+    if (p.bt) {  // [N, K] weights: 8 consecutive k of one staged column, like the activations
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = tid + kThreads * i, c = v >> 3, ko = v & 7;
+        const int k = k0 + ko * 8;
+        int nrow;
+        bool ok;
+        if (EPI == kSwiGLU) {
+          const int nc = n0 + (c & 63);
+          nrow = (c < 64 ? 0 : p.up_off) + nc;
+          ok = nc < p.N;
+        } else {
+          nrow = n0 + c;
+          ok = nrow < p.N;
+        }
+        rb[i] = (ok && k < p.K) ? *(const u32x4*)(bg + (int64_t)nrow * p.ldb + k) : u32x4{0u, 0u, 0u, 0u};
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = k0 + kq * 4 + i;
@@ -159,6 +185,14 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
     for (int i = 0; i < 4; ++i) {
       const int v = tid + kThreads * i, r = v >> 3, ko = v & 7;
       *(u32x4*)(sA + r * kLds + ko * 8) = ra[i];
+    }
+    if (p.bt) {  // k-octet ko of column c lands at octet ko ^ ((c >> 3) & 7) of the column's LDS row
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = tid + kThreads * i, c = v >> 3, ko = v & 7;
+        *(u32x4*)(sB + c * kLds + 8 * (ko ^ ((c >> 3) & 7))) = rb[i];
+      }
+      return;
     }
 #pragma unroll
     for (int cl = 0; cl < 8; ++cl) {
@@ -423,7 +457,7 @@ __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const
 // the MFMAs of the slice held in `rst`.  The two stages never coincide; the
 // __restrict__ qualifiers tell the compiler so, which lets it skip waiting
 // for the in-flight direct loads before the LDS reads below.
-template <int EPI, class C>
+template <int EPI, class C, bool BT>
 __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
                                           bool issue, const bf16_t* a_k, const bf16_t* b_k, const int64_t* a_off,
                                           const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw) {
@@ -456,6 +490,12 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
     }
 #pragma unroll
     for (int nb = 0; nb < C::kNB; ++nb) {
+      if constexpr (BT) {  // [n][k] tile: one 16-byte read of 8 consecutive k, as for the activations
+        const int n = pipe_col_base<EPI, C>(nb, wn) + (lane & 31);
+        const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(n);
+        bfr[nb] = *(const u32x4*)(Bs + n * C::kARow + chunk * 16);
+        continue;
+      }
       const int c0 = pipe_col_base<EPI, C>(nb, wn) + 16 * (grp & 1);
       const int row = 16 * ks + b_row_in;
       const int chunk = (c0 / 8 + b_chunk_lo) ^ b_swizzle<C>(s16 >> 2);
@@ -482,7 +522,7 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
   }
 }
 
-template <int EPI, class C>
+template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -503,6 +543,22 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
   int b_off[C::kBLoads];
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i) {
+    if constexpr (BT) {
+      // [N, K] weights stage like the activations: LDS row r is staged column r.
+      const int r = (wave * C::kBLoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
+      const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
+      int nrow;
+      if (EPI == kSwiGLU) {
+        const int half = C::BN / 2;
+        const int nc = n0 + r % half;
+        nrow = (nc < p.N ? nc : 0) + (r < half ? 0 : p.up_off);
+      } else {
+        const int nc = n0 + r;
+        nrow = nc < p.N ? nc : 0;
+      }
+      b_off[i] = nrow * ldb + chunk * 8;
+      continue;
+    }
     const int kr = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
     const int chunk = (lane % C::kBChunks) ^ b_swizzle<C>(kr);
     int col;
@@ -516,6 +572,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
     }
     b_off[i] = kr * ldb + col;
   }
+  const int64_t b_step = BT ? (int64_t)C::BK : (int64_t)C::BK * ldb;  // elements per reduction slice
   const int nk = K / C::BK;
 
   f32x16 acc[C::kMB][C::kNB];
@@ -530,14 +587,14 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
     if (s < nk)
-      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + (int64_t)s * C::BK * ldb, a_off, b_off);
+      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off);
 
   for (int kt = 0; kt < nk; ++kt) {
     if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
     lds_barrier();
     const int kn = kt + C::STAGES - 1;
-    pipe_step<EPI, C>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
-                      a_base + kn * C::BK, bg + (int64_t)kn * C::BK * ldb, a_off, b_off, acc, wn, wm, kw);
+    pipe_step<EPI, C, BT>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
+                          a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
 
@@ -605,7 +662,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
   }
 }
 
-template <int EPI, class C, int ROLE>
+template <int EPI, class C, int ROLE, bool BT>
 __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(GemmParams<bf16_t> p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int32_t sOff[kMaxExperts + 1];
@@ -617,7 +674,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
   const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
-    run_tile_pipe<EPI, C>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
+    run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
   }
 }
 
@@ -627,7 +684,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
 // (MFMA-bound).  Tile ids of the two problems are interleaved evenly
 // (position p is a shared tile when floor((p+1)*Ts/total) > floor(p*Ts/total)),
 // so every CU works on both kinds at once and each hides the other's stalls.
-template <int EPI_R, int EPI_S, class C>
+template <int EPI_R, int EPI_S, class C, bool BT>
 __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(GemmParams<bf16_t> pr,
                                                                                 GemmParams<bf16_t> ps) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -646,10 +703,10 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(G
     const int64_t s_before = id * tiles_s / total;
     if ((id + 1) * tiles_s / total != s_before) {
       const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
-      run_tile_pipe<EPI_S, C>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
+      run_tile_pipe<EPI_S, C, BT>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
     } else {
       const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
-      run_tile_pipe<EPI_R, C>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
+      run_tile_pipe<EPI_R, C, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
     }
   }
 }
@@ -674,17 +731,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmParams<float> p) {
   }
   const float* bg = p.b + (int64_t)g * p.b_stride;
   const float* ar = p.a + (int64_t)row * p.K;
+  // element (k, n) of the group's weight
+  auto w = [&](int k, int n) { return p.bt ? bg[(int64_t)n * p.ldb + k] : bg[(int64_t)k * p.ldb + n]; };
   if (EPI == kSwiGLU) {
     float gs = 0.f, us = 0.f;
     for (int k = 0; k < p.K; ++k) {
       const float av = ar[k];
-      gs = fmaf(av, bg[(int64_t)k * p.ldb + col], gs);
-      us = fmaf(av, bg[(int64_t)k * p.ldb + p.up_off + col], us);
+      gs = fmaf(av, w(k, col), gs);
+      us = fmaf(av, w(k, p.up_off + col), us);
     }
     ((float*)p.out)[(int64_t)row * p.N + col] = swiglu(gs, us);
   } else {
     float v = 0.f;
-    for (int k = 0; k < p.K; ++k) v = fmaf(ar[k], bg[(int64_t)k * p.ldb + col], v);
+    for (int k = 0; k < p.K; ++k) v = fmaf(ar[k], w(k, col), v);
     float* o = (float*)p.out + (int64_t)row * p.N + col;
     if (EPI == kStoreF32) {
       *o = v;
@@ -707,18 +766,18 @@ int64_t upper_row_tiles(int rows, int groups) {
 }
 
 // Launch one pipelined instantiation (persistent grid, dynamic LDS ring).
-template <int EPI, class C, int ROLE>
+template <int EPI, class C, int ROLE, bool BT>
 hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  if (p.K % C::BK != 0) return launch_pipe<EPI, PipeCfg<128, 128, 64, 2>, ROLE>(p, cu_count, s);
+  if (p.K % C::BK != 0) return launch_pipe<EPI, PipeCfg<128, 128, 64, 2>, ROLE, BT>(p, cu_count, s);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&grouped_gemm_bf16_pipe<EPI, C, ROLE>),
+      reinterpret_cast<const void*>(&grouped_gemm_bf16_pipe<EPI, C, ROLE, BT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (attr != hipSuccess) return attr;
   const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
   p.n_tiles = (p.N + out_cols - 1) / out_cols;
   const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
   const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
-  hipLaunchKernelGGL((grouped_gemm_bf16_pipe<EPI, C, ROLE>), dim3(grid), dim3(C::NT), C::kLds, s, p);
+  hipLaunchKernelGGL((grouped_gemm_bf16_pipe<EPI, C, ROLE, BT>), dim3(grid), dim3(C::NT), C::kLds, s, p);
   return hipGetLastError();
 }
 
@@ -743,11 +802,16 @@ typedef PipeCfg<32, 64, 128, 4, 1, 1, 4> Cfg15;
 typedef PipeCfg<32, 128, 64, 6, 1, 2, 2> Cfg16;
 typedef PipeCfg<32, 128, 128, 3, 1, 2, 4> Cfg17;  // 8 waves
 typedef PipeCfg<32, 128, 64, 3, 1, 2, 2> Cfg18;
+typedef PipeCfg<128, 256, 32, 4, 2, 2> Cfg19;
+typedef PipeCfg<256, 128, 64, 3, 4, 2> Cfg20;  // 8 waves
+typedef PipeCfg<128, 128, 64, 3> Cfg21;
+typedef PipeCfg<128, 256, 64, 2, 2, 2> Cfg22;
 
 template <int V> struct CfgOf { typedef Cfg1 type; };
 #define MOE_CFG(V) template <> struct CfgOf<V> { typedef Cfg##V type; };
 MOE_CFG(2) MOE_CFG(3) MOE_CFG(4) MOE_CFG(5) MOE_CFG(6) MOE_CFG(7) MOE_CFG(8) MOE_CFG(9) MOE_CFG(10)
 MOE_CFG(11) MOE_CFG(12) MOE_CFG(13) MOE_CFG(14) MOE_CFG(15) MOE_CFG(16) MOE_CFG(17) MOE_CFG(18)
+MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22)
 #undef MOE_CFG
 
 // Calls f(Cfg{}) for configuration number v.  The shipped build instantiates
@@ -760,12 +824,13 @@ hipError_t with_cfg(int v, F&& f) {
 #define MOE_CASE(V) case V: return f(typename CfgOf<V>::type{});
     MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8) MOE_CASE(9)
     MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
-    MOE_CASE(17) MOE_CASE(18)
+    MOE_CASE(17) MOE_CASE(18) MOE_CASE(19) MOE_CASE(20) MOE_CASE(21) MOE_CASE(22)
 #undef MOE_CASE
     default: return f(Cfg1{});
   }
 #else
   if (v == 8) return f(Cfg8{});
+  if (v == MOE_MID_FC1) return f(typename CfgOf<MOE_MID_FC1>::type{});
   if (v == MOE_DECODE_FC1) return f(typename CfgOf<MOE_DECODE_FC1>::type{});
   if (v == MOE_DECODE_FC2) return f(typename CfgOf<MOE_DECODE_FC2>::type{});
   return f(Cfg1{});
@@ -781,9 +846,10 @@ hipError_t with_cfg(int v, F&& f) {
 //  * groups of at most 32 rows (decode) take a 32-row tile whose waves split
 //    the reduction, so that many more tiles, each with several weight slices
 //    in flight, stream the expert weights;
-//  * everything else (skewed routing, many mid-sized groups) takes the
-//    128x128 tile with two workgroups per CU, which wastes fewer MFMA rows on
-//    partial tiles.
+//  * everything else (skewed routing, many mid-sized groups) takes 128-row
+//    tiles, which waste fewer MFMA rows on partial tiles: fc1 a 128x256 tile
+//    with 8 waves (half the activation re-reads of a 128-column tile), fc2 the
+//    128x128 tile with two workgroups per CU.
 int64_t rows_per_active_group(const GemmParams<bf16_t>& p) {
   const int64_t active = p.groups < p.rows ? p.groups : p.rows;  // at most one group per row
   return (int64_t)p.rows / (active > 0 ? active : 1);
@@ -794,18 +860,20 @@ constexpr int64_t kDecodeRows = 32;
 template <int EPI>
 constexpr int decode_variant() { return EPI == kSwiGLU ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
 
-int pick_pipe_variant(const GemmParams<bf16_t>& p, int decode_v) {
+template <int EPI>
+int pick_pipe_variant(const GemmParams<bf16_t>& p) {
   if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
-  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_v;
+  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
-  return rows_per_group >= 512 ? 8 : 1;
+  if (rows_per_group >= 512) return 8;
+  return EPI == kSwiGLU ? MOE_MID_FC1 : 1;
 }
 
-template <int EPI_R, int EPI_S, class C>
+template <int EPI_R, int EPI_S, class C, bool BT>
 hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
-  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, Cfg1>(pr, ps, cu_count, s);
+  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, Cfg1, BT>(pr, ps, cu_count, s);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C>),
+      reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (attr != hipSuccess) return attr;
   const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
@@ -815,7 +883,7 @@ hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_cou
   const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
   const int64_t tiles_s = (int64_t)((ps.rows + C::BM - 1) / C::BM) * ps.n_tiles;
   const int grid = persistent_grid(ub_r + tiles_s, cu_count * C::kWgsPerCu);
-  hipLaunchKernelGGL((grouped_gemm_bf16_fused<EPI_R, EPI_S, C>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
+  hipLaunchKernelGGL((grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
   return hipGetLastError();
 }
 
@@ -835,14 +903,22 @@ hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16
   else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
            ps.K % 128 == 0)
     v = decode_variant<EPI_R>();
-  return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c)>(pr, ps, cu_count, s); });
+  else if (EPI_R == kSwiGLU)
+    v = MOE_MID_FC1;
+  if (pr.bt)
+    return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), true>(pr, ps, cu_count, s); });
+  return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), false>(pr, ps, cu_count, s); });
 }
 
 template <int EPI, int ROLE>
 hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  if (p.K % 64 == 0)
-    return with_cfg(pick_pipe_variant(p, decode_variant<EPI>()),
-                    [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE>(p, cu_count, s); });
+  if (p.K % 64 == 0) {
+    if (p.bt)
+      return with_cfg(pick_pipe_variant<EPI>(p),
+                      [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, true>(p, cu_count, s); });
+    return with_cfg(pick_pipe_variant<EPI>(p),
+                    [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, false>(p, cu_count, s); });
+  }
   p.n_tiles = EPI == kSwiGLU ? (p.N + 63) / 64 : (p.N + 127) / 128;
   const int grid = persistent_grid(upper_row_tiles(p.rows, p.groups) * p.n_tiles, 2 * cu_count);
   hipLaunchKernelGGL((grouped_gemm_bf16_generic<EPI, ROLE>), dim3(grid), dim3(kThreads), 0, s, p);
@@ -854,34 +930,39 @@ hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
 
 namespace moe_launch {
 
-hipError_t grouped_swiglu_fc1(int dt, const void* a, const int32_t* offsets, int groups, int rows, const void* w1,
-                              int64_t w1_group_stride, int K, int I, void* act, int role, int cu_count,
-                              hipStream_t s) {
+// Weights of one group: bt == 0: [K, 2I] (fc1) / [K, N] (fc2), N contiguous;
+// bt == 1: [2I, K] / [N, K], K contiguous.  fc1's up half starts at column
+// (bt == 0) or row (bt == 1) I.
+hipError_t grouped_swiglu_fc1(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
+                              const void* w1, int64_t w1_group_stride, int K, int I, void* act, int role,
+                              int cu_count, hipStream_t s) {
   using namespace moe;
+  const int ldb = bt ? K : 2 * I;
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)a, offsets, groups, rows, K, I, (const bf16_t*)w1, w1_group_stride,
-                         2 * I, I, act, nullptr, 0, 0};
+                         ldb, I, act, nullptr, 0, 0, bt};
     return role ? launch_bf16<kSwiGLU, 1>(p, cu_count, s) : launch_bf16<kSwiGLU, 0>(p, cu_count, s);
   }
   GemmParams<float> p{(const float*)a, offsets, groups, rows, K, I, (const float*)w1, w1_group_stride,
-                      2 * I, I, act, nullptr, 0, 0};
+                      ldb, I, act, nullptr, 0, 0, bt};
   const int64_t n = (int64_t)rows * I;
   hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLU>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int groups, int rows, const void* w2,
-                       int64_t w2_group_stride, int K, int N, float* out, const float* row_scale, int accumulate,
-                       int plain_store, int role, int cu_count, hipStream_t s) {
+hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, int groups, int rows,
+                       const void* w2, int64_t w2_group_stride, int K, int N, float* out, const float* row_scale,
+                       int accumulate, int plain_store, int role, int cu_count, hipStream_t s) {
   using namespace moe;
+  const int ldb = bt ? K : N;
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)act, offsets, groups, rows, K, N, (const bf16_t*)w2, w2_group_stride,
-                         N, 0, out, row_scale, accumulate, 0};
+                         ldb, 0, out, row_scale, accumulate, 0, bt};
     if (plain_store) return role ? launch_bf16<kStoreF32, 1>(p, cu_count, s) : launch_bf16<kStoreF32, 0>(p, cu_count, s);
     return role ? launch_bf16<kScaleAdd, 1>(p, cu_count, s) : launch_bf16<kScaleAdd, 0>(p, cu_count, s);
   }
   GemmParams<float> p{(const float*)act, offsets, groups, rows, K, N, (const float*)w2, w2_group_stride,
-                      N, 0, out, row_scale, accumulate, 0};
+                      ldb, 0, out, row_scale, accumulate, 0, bt};
   const int64_t n = (int64_t)rows * N;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (plain_store)
@@ -900,30 +981,32 @@ hipError_t grouped_fc2(int dt, const void* act, const int32_t* offsets, int grou
 // and ~16 (DeepSeek-V3-shaped prefill) and loses from ~128 (Scout-shaped).
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T) {
   if (!(dt == 1 && H % 64 == 0 && I % 64 == 0 && I_s % 64 == 0)) return false;
+  if (MOE_FUSE_POLICY == 1) return true;
+  if (MOE_FUSE_POLICY == 2) return false;
   const double routed_bytes = (double)(E < R ? E : R) * 3.0 * H * I * 2.0;
   const double shared_flops = 6.0 * T * H * I_s;
   return shared_flops < 50.0 * routed_bytes;
 }
 
-hipError_t fused_fc1(const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
+hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
                      void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
                      hipStream_t s) {
   using namespace moe;
   GemmParams<bf16_t> pr{(const bf16_t*)xs, offsets, E, R, H, I, (const bf16_t*)w1, (int64_t)H * 2 * I,
-                        2 * I, I, act, nullptr, 0, 0};
+                        bt ? H : 2 * I, I, act, nullptr, 0, 0, bt};
   GemmParams<bf16_t> ps{(const bf16_t*)x, nullptr, 1, T, H, I_s, (const bf16_t*)ws1, 0,
-                        2 * I_s, I_s, act_s, nullptr, 0, 0};
+                        bt ? H : 2 * I_s, I_s, act_s, nullptr, 0, 0, bt};
   return launch_fused_bf16<kSwiGLU, kSwiGLU>(pr, ps, cu_count, s);
 }
 
-hipError_t fused_fc2(const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
+hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
                      float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
                      int accumulate, float* y, int cu_count, hipStream_t s) {
   using namespace moe;
   GemmParams<bf16_t> pr{(const bf16_t*)act, offsets, E, R, I, H, (const bf16_t*)w2, (int64_t)I * H,
-                        H, 0, y_rows, nullptr, 0, 0};
+                        bt ? I : H, 0, y_rows, nullptr, 0, 0, bt};
   GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2, 0,
-                        H, 0, y, gate, accumulate, 0};
+                        bt ? I_s : H, 0, y, gate, accumulate, 0, bt};
   return launch_fused_bf16<kStoreF32, kScaleAdd>(pr, ps, cu_count, s);
 }
 

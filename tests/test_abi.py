@@ -96,12 +96,21 @@ def test_scatter_validation_and_workspace(lib):
 
 
 def test_grouped_gemm_validation(lib):
-    assert lib.moe_grouped_swiglu_fc1(1, FAKE, FAKE, FAKE, 256, 256, 8, 100, FAKE, None) == 2
+    assert lib.moe_grouped_swiglu_fc1(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 100, FAKE, None) == 2
     assert "I must be a multiple of 8" in _err(lib)
-    assert lib.moe_grouped_swiglu_fc1(1, FAKE, None, FAKE, 256, 256, 8, 128, FAKE, None) == 1
+    assert lib.moe_grouped_swiglu_fc1(1, 0, FAKE, None, FAKE, 256, 256, 8, 128, FAKE, None) == 1
     assert "expert_offsets" in _err(lib)
-    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 0, 128, 8, 256, FAKE, None) == 1
-    assert lib.moe_grouped_fc2(1, FAKE, FAKE, FAKE, 256, 128, 8, 250, FAKE, None) == 2
+    assert lib.moe_grouped_fc2(1, 0, FAKE, FAKE, FAKE, 0, 128, 8, 256, FAKE, None) == 1
+    assert lib.moe_grouped_fc2(1, 0, FAKE, FAKE, FAKE, 256, 128, 8, 250, FAKE, None) == 2
+
+
+def test_weight_layout_validation(lib):
+    assert lib.moe_grouped_swiglu_fc1(1, 2, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, None) == 1
+    assert "weight layout" in _err(lib)
+    assert lib.moe_grouped_fc2(1, -1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, None) == 1
+    assert lib.moe_shared_expert(1, 5, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, 1 << 20, None) == 1
+    assert lib.moe_grouped_fc2_and_shared(1, 3, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None,
+                                          64, 128, 0, FAKE, FAKE, 1 << 20, None) == 1
 
 
 def test_combine_and_shared_validation(lib):
@@ -111,23 +120,23 @@ def test_combine_and_shared_validation(lib):
     need = lib.moe_shared_expert_workspace_bytes(1, 64, 128)
     assert need >= 64 * 128 * 2 + 64 * 4
     # half-specified shared branch: a width without its weights
-    assert lib.moe_shared_expert(1, FAKE, FAKE, None, None, 64, 256, 128, 1, FAKE, FAKE, need, None) == 1
+    assert lib.moe_shared_expert(1, 0, FAKE, FAKE, None, None, 64, 256, 128, 1, FAKE, FAKE, need, None) == 1
     assert "ws2 must not be NULL" in _err(lib)
-    assert lib.moe_shared_expert(1, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, need - 1, None) == 3
+    assert lib.moe_shared_expert(1, 0, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, need - 1, None) == 3
 
 
 def test_fused_shared_calls_validation(lib):
-    assert lib.moe_grouped_swiglu_fc1_and_shared(1, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, FAKE, None, 64, 128,
+    assert lib.moe_grouped_swiglu_fc1_and_shared(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, FAKE, None, 64, 128,
                                                  FAKE, None) == 1
     assert "ws1 must not be NULL" in _err(lib)
     need = lib.moe_shared_expert_workspace_bytes(1, 64, 128)
-    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
+    assert lib.moe_grouped_fc2_and_shared(1, 0, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
                                           128, 0, FAKE, FAKE, need - 1, None) == 3
-    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
+    assert lib.moe_grouped_fc2_and_shared(1, 0, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, FAKE, None, 64,
                                           128, 3, FAKE, FAKE, need, None) == 1
     assert "accumulate" in _err(lib)
     # a gate needs x
-    assert lib.moe_grouped_fc2_and_shared(1, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, None, FAKE, 64,
+    assert lib.moe_grouped_fc2_and_shared(1, 0, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, FAKE, None, FAKE, 64,
                                           128, 0, FAKE, FAKE, need, None) == 1
     assert "x (needed for the gate)" in _err(lib)
 

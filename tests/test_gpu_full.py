@@ -1,7 +1,7 @@
 """Full-size GPU parity for every layer workload, in the launch configuration
 the benchmark times (the same binding calls on the same buffers: routing and
 scatter through moe_route_and_scatter; routed and shared experts through the
-*_and_shared calls).
+*_and_shared calls; expert weights stored [K, N]).
 
 Checked on each workload:
   * routing: logits within the certified fp32 bound of the oracle's; top-k

@@ -61,6 +61,19 @@ def _contract(cfg):
     return cfg.dtype == "bf16"
 
 
+LAYOUTS = [B.MOE_W_KN, B.MOE_W_NK]
+LAYOUT_IDS = ["kn", "nk"]
+
+
+def _device_weights(layer, layout):
+    """W1, W2 and the shared weights stored in `layout` (the same matrices)."""
+    if layout == B.MOE_W_KN:
+        return layer["W1"], layer["W2"], layer["shared"]
+    t = lambda w: w.transpose(-1, -2).contiguous()
+    sh = layer["shared"]
+    return t(layer["W1"]), t(layer["W2"]), ((t(sh[0]), t(sh[1]), sh[2]) if sh is not None else None)
+
+
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
 def test_route_parity(cfg):
     layer = _layer(cfg)
@@ -229,10 +242,13 @@ def test_route_and_scatter_matches_the_two_calls(T, H, E, k, with_bias):
     _check_scatter(b, ids, host(x), E)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
-def test_grouped_gemms_per_call(cfg):
-    """fc1 on the oracle's scattered rows, then fc2 on the GPU's own activation."""
+def test_grouped_gemms_per_call(cfg, layout):
+    """fc1 on the oracle's scattered rows, then fc2 on the GPU's own activation,
+    with the weights stored [K, N] or [N, K]."""
     layer = _layer(cfg)
+    W1d, W2d, _ = _device_weights(layer, layout)
     x = layer["x"]
     rng = np.random.default_rng(5)
     ids = rng.integers(0, cfg.E, (cfg.T, cfg.top_k)).astype(np.int32)
@@ -246,9 +262,9 @@ def test_grouped_gemms_per_call(cfg):
     offsets = torch.from_numpy(sc["offsets"]).to(DEV)
     xs_dev = torch.from_numpy(np.nan_to_num(Xs)).to(x.dtype).to(DEV)
     act = torch.full((R, cfg.I), float("nan"), dtype=x.dtype, device=DEV)
-    B.moe_grouped_swiglu_fc1(xs_dev, offsets, layer["W1"], act)
+    B.moe_grouped_swiglu_fc1(xs_dev, offsets, W1d, act, layout=layout)
     y_rows = torch.full((R, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
-    B.moe_grouped_fc2(act, offsets, layer["W2"], y_rows)
+    B.moe_grouped_fc2(act, offsets, W2d, y_rows, layout=layout)
     torch.cuda.synchronize()
     A_ref = O.grouped_swiglu_up(Xs, sc["offsets"], W1, contract=_contract(cfg), dtype=np.float64)
     A = host(act)
@@ -264,9 +280,10 @@ def test_grouped_gemms_per_call(cfg):
     assert mx <= 1e-5, f"fc2 relative max error {mx:.3e} against the oracle on the same activation"
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("mode", ["separate", "fused", "overlap"])
 @pytest.mark.parametrize("cfg", CASES, ids=_ids)
-def test_layer_end_to_end(cfg, mode):
+def test_layer_end_to_end(cfg, mode, layout):
     """All six calls; or, fused: routing and scatter through
     moe_route_and_scatter and the routed and shared experts together through
     the *_and_shared calls; or, overlap: routing and scatter through
@@ -280,9 +297,10 @@ def test_layer_end_to_end(cfg, mode):
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.act.fill_(float("nan"))
     bufs.y_rows.fill_(float("nan"))
-    B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
+    W1d, W2d, shd = _device_weights(layer, layout)
+    B.moe_layer_forward(x, wr, bias_t, W1d, W2d, cfg.top_k, shared=shd, bufs=bufs,
                         fused_shared=mode == "fused", fused_route=mode != "separate",
-                        side_stream=torch.cuda.Stream() if mode == "overlap" else None)
+                        side_stream=torch.cuda.Stream() if mode == "overlap" else None, layout=layout)
     torch.cuda.synchronize()
     ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
     check_routing(host(bufs.logits), ids, w, host(x), host(wr), layer["bias"], cfg.top_k, O)
@@ -331,20 +349,23 @@ def test_all_duplicate_routes_every_row_computed_zero_error(cfg):
     assert_output_close(host(bufs.y), y0, cfg.dtype)
 
 
-def test_shared_expert_gate_and_accumulate():
-    cfg = wl.LayerConfig("shared", "bf16", T=333, H=264, E=1, top_k=1, I=8, I_s=200, gated=True)
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
+@pytest.mark.parametrize("T,H,I_s", [(333, 264, 200), (600, 512, 320)])
+def test_shared_expert_gate_and_accumulate(T, H, I_s, layout):
+    cfg = wl.LayerConfig("shared", "bf16", T=T, H=H, E=1, top_k=1, I=8, I_s=I_s, gated=True)
     layer = _layer(cfg)
     x = layer["x"]
-    ws1, ws2, wg = layer["shared"]
+    _, _, (ws1, ws2, wg) = _device_weights(layer, layout)
     ws = torch.empty(B.moe_shared_expert_workspace_bytes(x.dtype, cfg.T, cfg.I_s), dtype=torch.uint8, device=DEV)
     base = torch.randn((cfg.T, cfg.H), device=DEV)
     y_acc = base.clone()
     y_new = torch.full((cfg.T, cfg.H), float("nan"), device=DEV)
     y_ung = torch.empty((cfg.T, cfg.H), device=DEV)
-    B.moe_shared_expert(x, ws1, ws2, wg, y_acc, ws, accumulate=True)
-    B.moe_shared_expert(x, ws1, ws2, wg, y_new, ws, accumulate=False)
-    B.moe_shared_expert(x, ws1, ws2, None, y_ung, ws, accumulate=False)
+    B.moe_shared_expert(x, ws1, ws2, wg, y_acc, ws, accumulate=True, layout=layout)
+    B.moe_shared_expert(x, ws1, ws2, wg, y_new, ws, accumulate=False, layout=layout)
+    B.moe_shared_expert(x, ws1, ws2, None, y_ung, ws, accumulate=False, layout=layout)
     torch.cuda.synchronize()
+    ws1, ws2, wg = layer["shared"]
     xs, s1, s2, g = host(x), host(ws1), host(ws2), host(wg)
     ref_g = O.shared_expert(xs, s1, s2, g, contract=True)
     ref_u = O.shared_expert(xs, s1, s2, None, contract=True)
