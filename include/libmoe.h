@@ -272,6 +272,13 @@ moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, 
  * the routed weight bytes) or run one after the other; results are the same
  * either way.
  */
+/* Kernel launches one moe_grouped_swiglu_fc1_and_shared call makes for these
+ * sizes (R = T * top_k routed rows): 1 when the routed experts and the shared
+ * expert share one launch, 2 when they run one after the other; 0 for invalid
+ * sizes.  moe_grouped_fc2_and_shared makes the same choice (plus one small
+ * gate launch when w_gate is given).  For profiling and reporting only. */
+int32_t moe_and_shared_launches(moe_dtype dt, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T, int32_t I_s);
+
 moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
                                              const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
                                              int32_t E, int32_t I, void* act, const void* x, const void* ws1,

@@ -54,6 +54,7 @@ _SIGNATURES = {
     "moe_shared_expert_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_shared_expert": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                    _c_size, _vp]),
+    "moe_and_shared_launches": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
@@ -259,6 +260,11 @@ def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream
             int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_shared_expert(*args))
+
+
+def moe_and_shared_launches(dtype, R, H, E, I, T, I_s) -> int:
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_and_shared_launches(dt, int(R), int(H), int(E), int(I), int(T), int(I_s)))
 
 
 def moe_grouped_swiglu_fc1_and_shared(x_scattered, expert_offsets, w1, act, x, ws1, act_shared, stream=None,

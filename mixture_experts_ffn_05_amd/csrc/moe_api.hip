@@ -344,6 +344,11 @@ moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, 
       fn);
 }
 
+int32_t moe_and_shared_launches(moe_dtype dt, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T, int32_t I_s) {
+  if (R < 1 || H < 1 || E < 1 || I < 1 || T < 1 || I_s < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
+  return moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T) ? 1 : 2;
+}
+
 moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
                                              const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
                                              int32_t E, int32_t I, void* act, const void* x, const void* ws1,

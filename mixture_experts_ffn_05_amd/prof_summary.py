@@ -1,17 +1,20 @@
 """Summarise rocprofv3 CSV output into the short text kept under profiles/.
 
-    python -m mixture_experts_ffn_05_amd.prof_summary trace <kernel_stats.csv> <out.md> <command...>
+    python -m mixture_experts_ffn_05_amd.prof_summary trace <kernel_stats.csv> <kernel_substr> <out.md> <command...>
     python -m mixture_experts_ffn_05_amd.prof_summary pmc <fetch_dir> <write_dir> <copy_mib> <kernel_substr> \
         <out.md> <command...>
 
-`trace` writes per-kernel call counts and average durations.  `pmc` reads two
-counter-collection runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
-calibrates both against the device copy of <copy_mib> MiB that the profiled
-command performed first (its counters should read copy_mib*1024 KiB each),
-and writes the calibrated HBM bytes per dispatch of the kernels whose name
-contains <kernel_substr>, plus a JSON line that bench.py reads for the
-roofline object's `traffic` field.  The JSON line records a hash of the GEMM
-source, so a later change of the kernel voids the figure.
+`trace` writes per-kernel call counts and average durations, and the summed
+average duration of the kernels whose name contains <kernel_substr> (the
+launches of one fc1 call).  `pmc` reads two counter-collection runs
+(FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), calibrates both against the
+device copy of <copy_mib> MiB that the profiled command performed first (its
+counters should read copy_mib*1024 KiB each), and writes the calibrated HBM
+bytes per dispatch of every kernel, plus a JSON line, read by bench.py for the
+roofline object's `traffic` field, with the bytes of one fc1 call: the sum
+over the kernels whose name contains <kernel_substr> (each launched once per
+call).  The JSON line records a hash of the GEMM source, so a later change of
+the kernel voids the figure.
 """
 
 from __future__ import annotations
@@ -40,13 +43,20 @@ def short(name: str) -> str:
     return name if len(name) < 110 else name[:107] + "..."
 
 
-def trace(stats_csv: str, out_md: str, command: str) -> None:
+def trace(stats_csv: str, kernel_substr: str, out_md: str, command: str) -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = ["# rocprofv3 kernel trace", "", f"Command: `{command}`", "",
              "| kernel | calls | avg us | total share % |", "|---|---|---|---|"]
+    matched = 0.0
+    names = []
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
+        if kernel_substr in r["Name"]:
+            matched += float(r["AverageNs"]) / 1e3
+            names.append(short(r["Name"]))
+    lines += ["", f"fc1 call (kernels containing `{kernel_substr}`: {'; '.join(names)}): "
+                  f"summed average duration {matched:.2f} us"]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -84,11 +94,16 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
         wa = sum(wv) / len(wv) if wv else 0.0
         hbm = (fa * (f_scale or 1.0) + wa * (w_scale or 1.0)) * 1024 / 1e6
         lines.append(f"| {short(k)} | {len(fv)} | {fa:.0f} | {wa:.0f} | {hbm:.1f} |")
-        if kernel_substr in k and record is None:
-            record = {"kernel": short(k), "fetch_kib": fa, "write_kib": wa, "fetch_scale": f_scale,
-                      "write_scale": w_scale, "hbm_bytes_per_dispatch": hbm * 1e6,
-                      "gemm_source_hash": kernel_source_hash()}
-    lines += ["", "Machine-readable record for the dominant kernel (read by bench.py):", "",
+        if kernel_substr in k:
+            if record is None:
+                record = {"kernels": [], "fetch_kib": 0.0, "write_kib": 0.0, "fetch_scale": f_scale,
+                          "write_scale": w_scale, "hbm_bytes_per_call": 0.0, "gemm_source_hash": kernel_source_hash()}
+            record["kernels"].append(short(k))
+            record["fetch_kib"] += fa
+            record["write_kib"] += wa
+            record["hbm_bytes_per_call"] += hbm * 1e6
+    lines += ["", f"Machine-readable record for the fc1 call (kernels containing `{kernel_substr}`; read by "
+                  "bench.py):", "",
               "TRAFFIC_JSON " + json.dumps(record)]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
@@ -96,7 +111,7 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "trace":
-        trace(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
     elif mode == "pmc":
         pmc(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5], sys.argv[6], " ".join(sys.argv[7:]))
     else:

@@ -125,6 +125,15 @@ def test_combine_and_shared_validation(lib):
     assert lib.moe_shared_expert(1, 0, FAKE, FAKE, FAKE, None, 64, 256, 128, 1, FAKE, FAKE, need - 1, None) == 3
 
 
+def test_and_shared_launch_count_query(lib):
+    # Scout-shaped: a wide shared expert next to 16 routed experts -> two launches;
+    # DeepSeek-V3-shaped prefill: a light shared expert next to 256 experts -> one launch
+    assert lib.moe_and_shared_launches(1, 2048, 5120, 16, 8192, 2048, 8192) == 2
+    assert lib.moe_and_shared_launches(1, 32768, 7168, 256, 2048, 4096, 2048) == 1
+    assert lib.moe_and_shared_launches(0, 32768, 7168, 256, 2048, 4096, 2048) == 2   # f32: never one launch
+    assert lib.moe_and_shared_launches(1, 0, 7168, 256, 2048, 4096, 2048) == 0
+
+
 def test_fused_shared_calls_validation(lib):
     assert lib.moe_grouped_swiglu_fc1_and_shared(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, FAKE, None, 64, 128,
                                                  FAKE, None) == 1
