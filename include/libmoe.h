@@ -272,6 +272,44 @@ moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, 
  * the routed weight bytes) or run one after the other; results are the same
  * either way.
  */
+/*
+ * MXFP8 expert weights: moe_grouped_swiglu_fc1_mx8, moe_grouped_fc2_mx8,
+ * moe_shared_expert_mx8.
+ *
+ * Source: PLENA_Compiler PR #69, section "Group C -- shared experts" (the
+ * fusion-identity paragraph: expert weights are MXFP8 -- e4m3 values, one e8m0
+ * scale per block of 8 along the intermediate axis).  Encodings (the OCP
+ * microscaling definitions): e4m3 = sign, 4-bit exponent (bias 7, subnormals at
+ * 0), 3-bit mantissa, no infinities, 0x7F/0xFF NaN; e8m0 = 2^(byte - 127), 0xFF
+ * NaN.  A weight element is e4m3(code) * e8m0(scale of its block).
+ *
+ * Each call computes exactly what its bf16 counterpart computes on the
+ * dequantized weights (activations, act and the outputs keep their bf16/fp32
+ * types; dt is implicitly MOE_BF16).  Codes are stored [N, K] per matrix (K
+ * contiguous, one byte each), the layout of MOE_W_NK:
+ *   fc1:    w1q [E, 2I, H], scales w1s [E, 2I/8, H] (blocks of 8 along the
+ *           intermediate axis 2I: scale w1s[e][n/8][k] for code w1q[e][n][k]);
+ *   fc2:    w2q [E, H, I],  scales w2s [E, H, I/8]  (blocks along I:
+ *           w2s[e][n][k/8] for w2q[e][n][k]);
+ *   shared: ws1q [2I_s, H] / ws1s [2I_s/8, H] and ws2q [H, I_s] / ws2s [H, I_s/8].
+ * The weights are dequantized to bf16 inside the kernels; this is exact while
+ * every scale exponent lies in 10..246 (the products stay normal bf16 numbers).
+ * Limits: the reduction size of each product (H for fc1 and the shared fc1, I
+ * for fc2, I_s for the shared fc2) must be a multiple of 128
+ * (MOE_ERR_UNSUPPORTED otherwise).  Other arguments, ownership and errors are
+ * those of the bf16 calls.
+ */
+moe_status moe_grouped_swiglu_fc1_mx8(const void* x_scattered, const int32_t* expert_offsets, const uint8_t* w1q,
+                                      const uint8_t* w1s, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
+                                      void* stream);
+moe_status moe_grouped_fc2_mx8(const void* act, const int32_t* expert_offsets, const uint8_t* w2q,
+                               const uint8_t* w2s, int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
+                               void* stream);
+moe_status moe_shared_expert_mx8(const void* x, const uint8_t* ws1q, const uint8_t* ws1s, const uint8_t* ws2q,
+                                 const uint8_t* ws2s, const void* w_gate, int32_t T, int32_t H, int32_t I_s,
+                                 int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Kernel launches one moe_grouped_swiglu_fc1_and_shared call makes for these
  * sizes (R = T * top_k routed rows): 1 when the routed experts and the shared
  * expert share one launch, 2 when they run one after the other; 0 for invalid

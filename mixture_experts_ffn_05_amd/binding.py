@@ -54,6 +54,10 @@ _SIGNATURES = {
     "moe_shared_expert_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "moe_shared_expert": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                    _c_size, _vp]),
+    "moe_grouped_swiglu_fc1_mx8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2_mx8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "moe_shared_expert_mx8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                       _c_size, _vp]),
     "moe_and_shared_launches": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
@@ -260,6 +264,50 @@ def moe_shared_expert(x, ws1, ws2, w_gate, y, workspace, accumulate=True, stream
             int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_shared_expert(*args))
+
+
+def moe_grouped_swiglu_fc1_mx8(x_scattered, expert_offsets, w1q, w1s, act, stream=None):
+    """fc1 + SwiGLU with MXFP8 weights: w1q [E, 2I, H] e4m3 codes, w1s [E, 2I/8, H] e8m0 scales (uint8)."""
+    lib = load()
+    R, H = x_scattered.shape
+    E, I2, _ = w1q.shape
+    I = I2 // 2
+    dev = x_scattered.device
+    u8 = torch.uint8
+    args = (_ptr(x_scattered, "x_scattered", torch.bfloat16, (R, H), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1q, "w1q", u8, (E, 2 * I, H), dev), _ptr(w1s, "w1s", u8, (E, 2 * I // 8, H), dev), R, H, E, I,
+            _ptr(act, "act", torch.bfloat16, (R, I), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_mx8(*args))
+
+
+def moe_grouped_fc2_mx8(act, expert_offsets, w2q, w2s, y_rows, stream=None):
+    """fc2 with MXFP8 weights: w2q [E, H, I] e4m3 codes, w2s [E, H, I/8] e8m0 scales (uint8)."""
+    lib = load()
+    R, I = act.shape
+    E, H, _ = w2q.shape
+    dev = act.device
+    u8 = torch.uint8
+    args = (_ptr(act, "act", torch.bfloat16, (R, I), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2q, "w2q", u8, (E, H, I), dev), _ptr(w2s, "w2s", u8, (E, H, I // 8), dev), R, I, E, H,
+            _ptr(y_rows, "y_rows", torch.float32, (R, H), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_fc2_mx8(*args))
+
+
+def moe_shared_expert_mx8(x, ws1q, ws1s, ws2q, ws2s, w_gate, y, workspace, accumulate=True, stream=None):
+    """Shared expert with MXFP8 weights: ws1q [2I_s, H] / ws1s [2I_s/8, H], ws2q [H, I_s] / ws2s [H, I_s/8]."""
+    lib = load()
+    T, H = x.shape
+    I_s = ws2q.shape[1]
+    dev = x.device
+    u8 = torch.uint8
+    args = (_ptr(x, "x", torch.bfloat16, (T, H), dev), _ptr(ws1q, "ws1q", u8, (2 * I_s, H), dev),
+            _ptr(ws1s, "ws1s", u8, (2 * I_s // 8, H), dev), _ptr(ws2q, "ws2q", u8, (H, I_s), dev),
+            _ptr(ws2s, "ws2s", u8, (H, I_s // 8), dev), _ptr(w_gate, "w_gate", torch.bfloat16, (H,), dev), T, H,
+            I_s, int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
+            _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_shared_expert_mx8(*args))
 
 
 def moe_and_shared_launches(dtype, R, H, E, I, T, I_s) -> int:

@@ -177,6 +177,14 @@ hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, 
                        const float* row_scale, int accumulate, int plain_store, int role, int cu_count,
                        hipStream_t s);
 
+// MXFP8 weights (e4m3 codes [N, K] per group, e8m0 scales per 8 along the
+// intermediate axis: [2I / 8, K] for fc1, [N, K / 8] for fc2); K a multiple of 128.
+hipError_t grouped_swiglu_fc1_mx8(const void* a, const int32_t* offsets, int groups, int rows, const void* w1q,
+                                  const void* w1s, int K, int I, void* act, int role, int cu_count, hipStream_t s);
+hipError_t grouped_fc2_mx8(const void* act, const int32_t* offsets, int groups, int rows, const void* w2q,
+                           const void* w2s, int K, int N, float* out, const float* row_scale, int accumulate,
+                           int plain_store, int role, int cu_count, hipStream_t s);
+
 // Routed groups and the shared expert in one launch (bf16, reduction sizes
 // multiples of 64, and a shared expert that is light next to the routed
 // weights; fused_supported() decides from the shapes).

@@ -101,6 +101,8 @@ struct GemmParams {
   int accumulate;           // kScaleAdd: add into out instead of overwriting
   int n_tiles;              // output column tiles per group
   int bt;                   // 0: b rows are k ([K, ldb], N contiguous); 1: b rows are n ([N, ldb = K], K contiguous)
+  const uint8_t* sc;        // MXFP8: e8m0 scales of group 0 (b then holds e4m3 codes, [N, K] bytes)
+  int64_t sc_stride;        // MXFP8: bytes between the scales of consecutive groups
 };
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
@@ -522,6 +524,78 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
   }
 }
 
+// Split-K reduction (KW > 1) and epilogue of one tile whose accumulators the
+// waves hold; the ring must be idle (every wave past its last LDS read).
+template <int EPI, class C>
+__device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 (&acc)[C::kMB][C::kNB], int row0,
+                                            int row_end, int n0, unsigned char* __restrict__ smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kw = wave / C::kPos, wpos = wave % C::kPos;
+  const int wm = wpos / C::WN, wn = wpos % C::WN;
+  if constexpr (C::KW > 1) {
+    // Split-K partials through the (now idle) ring: waves kw >= 1 store theirs,
+    // wave kw == 0 of each position adds them in the order kw = 1, 2, ... and
+    // runs the epilogue.
+    float* red = (float*)smem;
+    auto slot = [&](int q, int mb, int nb, int i) {
+      return ((((q - 1) * C::kPos + wpos) * C::kMB + mb) * C::kNB + nb) * 16 * kWave + i * kWave + lane;
+    };
+    if (kw > 0) {
+#pragma unroll
+      for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[slot(kw, mb, nb, i)] = acc[mb][nb][i];
+    }
+    lds_barrier();
+    if (kw == 0) {
+      for (int q = 1; q < C::KW; ++q)
+#pragma unroll
+        for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][nb][i] += red[slot(q, mb, nb, i)];
+    }
+    lds_barrier();  // partials consumed before the next tile refills the ring
+    if (kw > 0) return;
+  }
+
+  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = row0 + wm * (C::BM / C::WM) + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (row >= row_end) continue;
+      if (EPI == kSwiGLU) {
+#pragma unroll
+        for (int j = 0; j < C::kNB / 2; ++j) {
+          const int col = n0 + wn * (C::BN / 2 / C::WN) + 32 * j + (lane & 31);
+          if (col < p.N)
+            ((bf16_t*)p.out)[(int64_t)row * p.N + col] =
+                (bf16_t)f32_to_bf16_rne(swiglu(acc[mb][j][i], acc[mb][j + C::kNB / 2][i]));
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < C::kNB; ++nb) {
+          const int col = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
+          if (col >= p.N) continue;
+          float* o = (float*)p.out + (int64_t)row * p.N + col;
+          const float v = acc[mb][nb][i];
+          if (EPI == kStoreF32) {
+            *o = v;
+          } else {
+            const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
+            *o = (p.accumulate ? *o : 0.0f) + sc * v;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem) {
@@ -597,69 +671,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
                           a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
-
-  if constexpr (C::KW > 1) {
-    // Split-K partials through the (now idle) ring: waves kw >= 1 store theirs,
-    // wave kw == 0 of each position adds them in the order kw = 1, 2, ... and
-    // runs the epilogue.
-    float* red = (float*)smem;
-    auto slot = [&](int q, int mb, int nb, int i) {
-      return ((((q - 1) * C::kPos + wpos) * C::kMB + mb) * C::kNB + nb) * 16 * kWave + i * kWave + lane;
-    };
-    if (kw > 0) {
-#pragma unroll
-      for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::kNB; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) red[slot(kw, mb, nb, i)] = acc[mb][nb][i];
-    }
-    lds_barrier();
-    if (kw == 0) {
-      for (int q = 1; q < C::KW; ++q)
-#pragma unroll
-        for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < C::kNB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[mb][nb][i] += red[slot(q, mb, nb, i)];
-    }
-    lds_barrier();  // partials consumed before the next tile refills the ring
-    if (kw > 0) return;
-  }
-
-  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
-#pragma unroll
-  for (int mb = 0; mb < C::kMB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = row0 + wm * (C::BM / C::WM) + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (row >= row_end) continue;
-      if (EPI == kSwiGLU) {
-#pragma unroll
-        for (int j = 0; j < C::kNB / 2; ++j) {
-          const int col = n0 + wn * (C::BN / 2 / C::WN) + 32 * j + (lane & 31);
-          if (col < p.N)
-            ((bf16_t*)p.out)[(int64_t)row * p.N + col] =
-                (bf16_t)f32_to_bf16_rne(swiglu(acc[mb][j][i], acc[mb][j + C::kNB / 2][i]));
-        }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < C::kNB; ++nb) {
-          const int col = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
-          if (col >= p.N) continue;
-          float* o = (float*)p.out + (int64_t)row * p.N + col;
-          const float v = acc[mb][nb][i];
-          if (EPI == kStoreF32) {
-            *o = v;
-          } else {
-            const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
-            *o = (p.accumulate ? *o : 0.0f) + sc * v;
-          }
-        }
-      }
-    }
-  }
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
 }
 
 template <int EPI, class C, int ROLE, bool BT>
@@ -708,6 +720,240 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(G
       const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
       run_tile_pipe<EPI_R, C, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// MXFP8 weights: e4m3 codes with one e8m0 scale per 8 elements along the intermediate axis
+// ------------------------------------------------------------------------------------------
+// PLENA_Compiler PR #69, section "Group C -- shared experts" (fusion-identity
+// paragraph).  Codes are stored [N, K] per group (K contiguous, one byte each).
+// Their scales run along N for fc1 (kScaleN: scale [n / 8][k]) and along K for
+// fc2 (kScaleK: scale [n][k / 8]).  Each ring stage holds the activation tile
+// (bf16, as in the pipelined path), the code tile ([BN][BK] bytes) and the
+// scale tile, all by direct loads (the scale tile with 4-byte loads, so every
+// wave issues the same number of loads).  A weight fragment is one 8-byte LDS
+// read of codes plus their scales, converted to bf16 by
+// v_cvt_scalef32_pk_bf16_fp8 right before the bf16 MFMA.  An e4m3 value times
+// a power of two has at most four significant bits, so the conversion is exact
+// whenever the result is a normal bf16 (e8m0 exponents 10..246).
+enum ScaleAxis { kScaleN = 0, kScaleK = 1 };
+
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_, int KW_>
+struct MxCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_, KW = KW_;
+  static constexpr int kPos = WM * WN;
+  static constexpr int kWaves = kPos * KW;
+  static constexpr int NT = kWaves * kWave;
+  static constexpr int kARow = BK * 2;                  // activation row bytes (bf16)
+  static constexpr int kAChunks = BK / 8;
+  static constexpr int kAStage = BM * kARow;
+  static constexpr int kBRow = BK;                      // code row bytes
+  static constexpr int kBChunks = BK / 16;
+  static constexpr int kBStage = BN * BK;
+  static constexpr int kSStage = BN * BK / 8;
+  static constexpr int kStage = kAStage + kBStage + kSStage;
+  static constexpr int kALoads = kAStage / 1024 / kWaves;
+  static constexpr int kBLoads = kBStage / 1024 / kWaves;
+  static constexpr int kSLoads = kSStage / 256 / kWaves;  // 4 bytes per lane
+  static constexpr int kLoads = kALoads + kBLoads + kSLoads;
+  static constexpr int kARowsPerLoad = 1024 / kARow;
+  static constexpr int kBRowsPerLoad = 1024 / kBRow;
+  static constexpr int kMB = BM / WM / 32;
+  static constexpr int kNB = BN / WN / 32;
+  static constexpr int kKS = BK / 16;
+  static constexpr int kKSW = kKS / KW;
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kRed = (KW - 1) * kPos * kMB * kNB * 16 * kWave * 4;
+  static constexpr int kFit = (160 * 1024) / (kLds + 9 * 1024);
+  static constexpr int kWgsPerCu = kFit < 1 ? 1 : (kFit > 4 ? 4 : kFit);
+  static_assert(kAStage % (1024 * kWaves) == 0 && kBStage % (1024 * kWaves) == 0 &&
+                    kSStage % (256 * kWaves) == 0,
+                "slices must split evenly into direct loads per wave");
+  static_assert(kMB >= 1 && kNB >= 2 && kNB % 2 == 0, "wave tile must hold whole 32x32 blocks");
+  static_assert(kKS % KW == 0 && kRed <= kLds, "split-K layout");
+  static_assert(BK == 128, "the scale tiles below assume 128-deep slices");
+};
+
+// 32-row tiles, 128 staged columns, 128-deep slices, 4-stage ring, 4 waves
+// (2 column positions x 2 split-K waves): the decode tile of the bf16 path.
+typedef MxCfg<32, 128, 128, 4, 1, 2, 2> MxCfg1;
+
+template <int ROWBYTES>
+__device__ __forceinline__ int row_swizzle(int row) {
+  return (row / (256 / ROWBYTES)) % (ROWBYTES / 16);
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : (s << 23)));
+}
+
+// Two e4m3 codes (bytes 0-1, or with HI bytes 2-3, of `codes`) times `scale`, as bf16x2.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_bf16x2(uint32_t codes, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, scale, HI));
+}
+
+// 8 consecutive-k codes of one column, one scale for all of them (kScaleK).
+__device__ __forceinline__ u32x4 mx_frag_one_scale(u32x2 c, float f) {
+  return u32x4{cvt_bf16x2<false>(c[0], f), cvt_bf16x2<true>(c[0], f), cvt_bf16x2<false>(c[1], f),
+               cvt_bf16x2<true>(c[1], f)};
+}
+
+// 8 consecutive-k codes of one column with a scale each (kScaleN): each
+// conversion scales a pair by one factor, so the pair's two halves come from
+// two conversions.
+template <bool HI>
+__device__ __forceinline__ uint32_t mx_pair_two_scales(uint32_t word, uint32_t sbytes) {
+  const uint32_t lo_val = cvt_bf16x2<HI>(word, e8m0_to_f32(sbytes & 0xffu));
+  const uint32_t hi_val = cvt_bf16x2<HI>(word, e8m0_to_f32((sbytes >> 8) & 0xffu));
+  return (lo_val & 0xffffu) | (hi_val & 0xffff0000u);
+}
+
+__device__ __forceinline__ u32x4 mx_frag_eight_scales(u32x2 c, u32x2 sw) {
+  return u32x4{mx_pair_two_scales<false>(c[0], sw[0]), mx_pair_two_scales<true>(c[0], sw[0] >> 16),
+               mx_pair_two_scales<false>(c[1], sw[1]), mx_pair_two_scales<true>(c[1], sw[1] >> 16)};
+}
+
+template <int EPI, class C, int SAX>
+__device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+                                            unsigned char* __restrict__ smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kw = wave / C::kPos, wpos = wave % C::kPos;
+  const int wm = wpos / C::WN, wn = wpos % C::WN;
+  const int K = p.K;
+  const unsigned char* __restrict__ bq = (const unsigned char*)p.b + (int64_t)g * p.b_stride;
+  const unsigned char* __restrict__ bs = p.sc + (int64_t)g * p.sc_stride;
+
+  // Weight row (an n in [0, rows of the group's weight)) of staged column r;
+  // columns past N read row 0 and only feed outputs that are never stored.
+  auto wrow = [&](int r) -> int {
+    if (EPI == kSwiGLU) {
+      const int half = C::BN / 2;
+      const int nc = n0 + r % half;
+      return (nc < p.N ? nc : 0) + (r < half ? 0 : p.up_off);
+    }
+    const int nc = n0 + r;
+    return nc < p.N ? nc : 0;
+  };
+
+  int64_t a_off[C::kALoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
+    const int chunk = (lane % C::kAChunks) ^ row_swizzle<C::kARow>(r);
+    const int row = min(row0 + r, row_end - 1);
+    a_off[i] = (int64_t)row * K + chunk * 8;
+  }
+  int b_off[C::kBLoads];
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i) {
+    const int r = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
+    const int chunk = (lane % C::kBChunks) ^ row_swizzle<C::kBRow>(r);
+    b_off[i] = wrow(r) * K + chunk * 16;
+  }
+  int s_off[C::kSLoads];
+#pragma unroll
+  for (int i = 0; i < C::kSLoads; ++i) {
+    const int j = wave * C::kSLoads + i;  // 256-byte piece of the scale tile
+    if (SAX == kScaleN) {
+      // [BN / 8][BK] bytes: piece j holds scale rows 2j and 2j + 1
+      const int srow = 2 * j + lane / 32, col = 4 * (lane % 32);
+      s_off[i] = (wrow(8 * srow) / 8) * K + col;
+    } else {
+      // [BN][BK / 8] bytes: piece j holds staged columns 16j .. 16j + 15
+      const int r = 16 * j + lane / 4, col = 4 * (lane % 4);
+      s_off[i] = wrow(r) * (K / 8) + col;
+    }
+  }
+  constexpr int kSStep = SAX == kScaleN ? C::BK : C::BK / 8;  // scale bytes per slice along k
+  const int nk = K / C::BK;
+
+  auto issue = [&](unsigned char* st, int kt) {
+    const bf16_t* a_k = p.a + (int64_t)kt * C::BK;
+    const unsigned char* b_k = bq + (int64_t)kt * C::BK;
+    const unsigned char* s_k = bs + (int64_t)kt * kSStep;
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                       MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                       MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::kSLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
+                                       MOE_LDS(void, st + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256),
+                                       4, 0, 0);
+  };
+
+  f32x16 acc[C::kMB][C::kNB];
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) issue(smem + s * C::kStage, s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    const int kn = kt + C::STAGES - 1;
+    if (kn < nk) issue(smem + (kn % C::STAGES) * C::kStage, kn);
+    const unsigned char* As = smem + (kt % C::STAGES) * C::kStage;
+    const unsigned char* Bs = As + C::kAStage;
+    const unsigned char* Ss = Bs + C::kBStage;
+#pragma unroll
+    for (int jj = 0; jj < C::kKSW; ++jj) {
+      const int ks = kw + jj * C::KW;
+      u32x4 af[C::kMB], bfr[C::kNB];
+#pragma unroll
+      for (int mb = 0; mb < C::kMB; ++mb) {
+        const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+        const int chunk = (2 * ks + (lane >> 5)) ^ row_swizzle<C::kARow>(m);
+        af[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
+      }
+#pragma unroll
+      for (int nb = 0; nb < C::kNB; ++nb) {
+        const int n = pipe_col_base<EPI, C>(nb, wn) + (lane & 31);
+        const int kg = lane >> 5;  // k = 16 ks + 8 kg .. + 7
+        const int chunk = ks ^ row_swizzle<C::kBRow>(n);
+        const u32x2 codes = *(const u32x2*)(Bs + n * C::kBRow + chunk * 16 + 8 * kg);
+        if (SAX == kScaleK) {
+          bfr[nb] = mx_frag_one_scale(codes, e8m0_to_f32(Ss[n * (C::BK / 8) + 2 * ks + kg]));
+        } else {
+          const u32x2 sw = *(const u32x2*)(Ss + (n / 8) * C::BK + 16 * ks + 8 * kg);
+          bfr[nb] = mx_frag_eight_scales(codes, sw);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[mb], bfr[nb], acc[mb][nb]);
+    }
+  }
+  lds_barrier();  // every wave is done with the ring before the next tile refills it
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+}
+
+template <int EPI, class C, int SAX, int ROLE>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8(GemmParams<bf16_t> p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int32_t sOff[kMaxExperts + 1];
+  __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sWave[C::kWaves];
+  const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave);
+  const int64_t nt = p.n_tiles;
+  const int64_t total = (int64_t)mtiles * nt;
+  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
+    run_tile_mx<EPI, C, SAX>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
   }
 }
 
@@ -778,6 +1024,21 @@ hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
   const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
   hipLaunchKernelGGL((grouped_gemm_bf16_pipe<EPI, C, ROLE, BT>), dim3(grid), dim3(C::NT), C::kLds, s, p);
+  return hipGetLastError();
+}
+
+template <int EPI, int SAX, int ROLE>
+hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
+  typedef MxCfg1 C;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&grouped_gemm_mx8<EPI, C, SAX, ROLE>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      C::kLds);
+  if (attr != hipSuccess) return attr;
+  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  p.n_tiles = (p.N + out_cols - 1) / out_cols;
+  const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
+  const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
+  hipLaunchKernelGGL((grouped_gemm_mx8<EPI, C, SAX, ROLE>), dim3(grid), dim3(C::NT), C::kLds, s, p);
   return hipGetLastError();
 }
 
@@ -1008,6 +1269,27 @@ hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int
   GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2, 0,
                         bt ? I_s : H, 0, y, gate, accumulate, 0, bt};
   return launch_fused_bf16<kStoreF32, kScaleAdd>(pr, ps, cu_count, s);
+}
+
+// MXFP8 weights (codes [N, K] bytes per group, scales as described above),
+// bf16 activations; K must be a multiple of 128.
+hipError_t grouped_swiglu_fc1_mx8(const void* a, const int32_t* offsets, int groups, int rows, const void* w1q,
+                                  const void* w1s, int K, int I, void* act, int role, int cu_count, hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> p{(const bf16_t*)a, offsets, groups, rows, K, I, (const bf16_t*)w1q, (int64_t)2 * I * K,
+                       K, I, act, nullptr, 0, 0, 1, (const uint8_t*)w1s, (int64_t)2 * I / 8 * K};
+  return role ? launch_mx8<kSwiGLU, kScaleN, 1>(p, cu_count, s) : launch_mx8<kSwiGLU, kScaleN, 0>(p, cu_count, s);
+}
+
+hipError_t grouped_fc2_mx8(const void* act, const int32_t* offsets, int groups, int rows, const void* w2q,
+                           const void* w2s, int K, int N, float* out, const float* row_scale, int accumulate,
+                           int plain_store, int role, int cu_count, hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> p{(const bf16_t*)act, offsets, groups, rows, K, N, (const bf16_t*)w2q, (int64_t)N * K,
+                       K, 0, out, row_scale, accumulate, 0, 1, (const uint8_t*)w2s, (int64_t)N * (K / 8)};
+  if (plain_store)
+    return role ? launch_mx8<kStoreF32, kScaleK, 1>(p, cu_count, s) : launch_mx8<kStoreF32, kScaleK, 0>(p, cu_count, s);
+  return role ? launch_mx8<kScaleAdd, kScaleK, 1>(p, cu_count, s) : launch_mx8<kScaleAdd, kScaleK, 0>(p, cu_count, s);
 }
 
 }  // namespace moe_launch

@@ -26,6 +26,18 @@ Recipe (all tensors row-major, contiguous):
 * Skewed routing uses a per-expert float32 logit bias stored in
   route_bias.json next to this file.  That file is written by a script in the
   oracle directory which fits the bias on these same x and W_r draws.
+* MXFP8 expert weights (e4m3 codes, one e8m0 scale per 8 consecutive elements
+  along the intermediate axis; PLENA_Compiler PR #69, section "Group C -- shared
+  experts") are made from the bf16 weights above by mx_quantize: per block, the
+  scale is the smallest power of two that brings max |w| to at most 448 (the
+  largest e4m3 value), so nothing saturates and the block maximum lands in
+  (224, 448]; each value divided by its scale is rounded to e4m3 by torch's
+  conversion.  This is input preparation only: the
+  layer consumes the codes and scales as given, and both the HIP path and the
+  oracle dequantize them.  They are stored [N, K] per weight (K contiguous):
+  W1q [E, 2I, H] with scales [E, 2I/8, H] (blocks along the output axis), W2q
+  [E, H, I] with scales [E, H, I/8] (blocks along the reduction axis), and the
+  shared Ws1q [2 I_s, H] / [2 I_s/8, H], Ws2q [H, I_s] / [H, I_s/8].
 """
 
 from __future__ import annotations
@@ -175,6 +187,38 @@ def all_duplicate_routes(cfg: LayerConfig):
     ids = np.zeros((cfg.T, cfg.top_k), np.int32)
     w = np.full((cfg.T, cfg.top_k), 1.0 / cfg.top_k, np.float32)
     return ids, w
+
+
+def mx_quantize(w: torch.Tensor, axis: int, block: int = 8):
+    """(codes uint8, scales uint8) of w with one e8m0 scale per `block`
+    consecutive elements along `axis` (see the module notes)."""
+    axis = axis % w.dim()
+    wf = w.float()
+    shape = list(wf.shape)
+    shape[axis:axis + 1] = [shape[axis] // block, block]
+    blocks = wf.reshape(shape)
+    amax = blocks.abs().amax(dim=axis + 1, keepdim=True)
+    exp = torch.ceil(torch.log2(torch.where(amax > 0, amax, torch.full_like(amax, 448.0)) / 448.0))
+    sbyte = (exp + 127).clamp(1, 254)
+    scaled = (blocks / torch.exp2(sbyte - 127)).clamp(-448.0, 448.0)
+    codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8).reshape(wf.shape)
+    return codes.contiguous(), sbyte.squeeze(axis + 1).to(torch.uint8).contiguous()
+
+
+def mx_layer_weights(layer: dict) -> dict:
+    """MXFP8 codes and scales of a layer's expert and shared weights, stored [N, K]."""
+    t = lambda w: w.transpose(-1, -2).contiguous()
+    out = {}
+    out["W1q"], out["W1s"] = mx_quantize(t(layer["W1"]), axis=-2)   # [E, 2I, H]; blocks along 2I
+    out["W2q"], out["W2s"] = mx_quantize(t(layer["W2"]), axis=-1)   # [E, H, I]; blocks along I
+    sh = layer.get("shared")
+    if sh is not None:
+        ws1q, ws1s = mx_quantize(t(sh[0]), axis=-2)                  # [2 I_s, H]
+        ws2q, ws2s = mx_quantize(t(sh[1]), axis=-1)                  # [H, I_s]
+        out["shared"] = (ws1q, ws1s, ws2q, ws2s, sh[2])
+    else:
+        out["shared"] = None
+    return out
 
 
 def make_layer(cfg: LayerConfig, device="cpu", with_experts: bool = True) -> dict:

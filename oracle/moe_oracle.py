@@ -76,6 +76,9 @@ __all__ = [
     "moe_forward",
     "dense_mask_forward",
     "token_outputs",
+    "e4m3_decode",
+    "e8m0_decode",
+    "mx_dequant",
 ]
 
 
@@ -97,6 +100,50 @@ def bf16_rne(a) -> np.ndarray:
     out = (rounded & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32)
     out = np.where(np.isnan(a32), np.float32(np.nan), out)
     return out.reshape(a32.shape)
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 expert weights
+# ----------------------------------------------------------------------------
+# [PLENA-C], section "Group C -- shared experts" (the paragraph on the fusion
+# identity): expert weights are MXFP8 -- e4m3 values with one e8m0 scale per
+# block of 8 consecutive elements along the intermediate axis.  The pages name
+# the two encodings without spelling out their bits; the reading taken here is
+# the OCP microscaling definition: e4m3 has a sign bit, a 4-bit exponent with
+# bias 7 and a 3-bit mantissa, subnormals at exponent 0, no infinities, and
+# only S.1111.111 is NaN (largest finite value 448); e8m0 is a bare exponent
+# with bias 127 whose all-ones code is NaN.  Dequantization is exact: value =
+# e4m3(code) * 2**(scale - 127), evaluated in float64.
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 value of each e4m3 byte."""
+    b = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = sign * (m / 8.0) * 2.0 ** -6
+    out = np.where(e == 0, subnormal, normal)
+    return np.where((e == 0xF) & (m == 7), np.nan, out)
+
+
+def e8m0_decode(scales) -> np.ndarray:
+    """float64 value 2**(s - 127) of each e8m0 byte (255 is NaN)."""
+    s = np.asarray(scales).astype(np.int64) & 0xFF
+    return np.where(s == 255, np.nan, np.exp2(s.astype(np.float64) - 127.0))
+
+
+def mx_dequant(codes, scales, axis: int, block: int = 8) -> np.ndarray:
+    """Exact float64 weights from e4m3 codes and their e8m0 block scales.
+
+    ``scales`` has the shape of ``codes`` with dimension ``axis`` divided by
+    ``block``: element i along that axis takes the scale of block i // block."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    if codes.shape[axis] != scales.shape[axis] * block:
+        raise ValueError(f"scales cover {scales.shape[axis] * block} elements along axis {axis}, "
+                         f"codes have {codes.shape[axis]}")
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), block, axis=axis)
 
 
 # ----------------------------------------------------------------------------

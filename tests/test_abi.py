@@ -113,6 +113,22 @@ def test_weight_layout_validation(lib):
                                           64, 128, 0, FAKE, FAKE, 1 << 20, None) == 1
 
 
+def test_mx8_validation(lib):
+    # fc1: the reduction size H must be a multiple of 128
+    assert lib.moe_grouped_swiglu_fc1_mx8(FAKE, FAKE, FAKE, FAKE, 64, 192, 4, 128, FAKE, None) == 2
+    assert "multiple of 128" in _err(lib) and "H" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_mx8(FAKE, FAKE, FAKE, None, 64, 256, 4, 128, FAKE, None) == 1
+    assert "w1s" in _err(lib)
+    # fc2: the reduction size I must be a multiple of 128
+    assert lib.moe_grouped_fc2_mx8(FAKE, FAKE, FAKE, FAKE, 64, 200, 4, 256, FAKE, None) == 2
+    assert lib.moe_grouped_fc2_mx8(FAKE, FAKE, None, FAKE, 64, 256, 4, 256, FAKE, None) == 1
+    need = lib.moe_shared_expert_workspace_bytes(1, 64, 256)
+    assert lib.moe_shared_expert_mx8(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 256, 200, 1, FAKE, FAKE, need,
+                                     None) == 2
+    assert lib.moe_shared_expert_mx8(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 256, 256, 1, FAKE, FAKE, need - 1,
+                                     None) == 3
+
+
 def test_combine_and_shared_validation(lib):
     assert lib.moe_gather_combine(FAKE, FAKE, FAKE, 4, 16, 2, 2, FAKE, None) == 1
     assert "accumulate must be 0 or 1" in _err(lib)

@@ -406,3 +406,136 @@ def test_two_runs_bit_identical(mode):
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                               b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+# ---- MXFP8 expert weights: every result against the oracle on the exactly dequantized weights
+
+def _mx_np(layer_mx):
+    """Oracle-side K x N matrices from the stored codes and scales."""
+    W1 = O.mx_dequant(host(layer_mx["W1q"]), host(layer_mx["W1s"]), axis=-2)   # [E, 2I, H]
+    W2 = O.mx_dequant(host(layer_mx["W2q"]), host(layer_mx["W2s"]), axis=-1)   # [E, H, I]
+    W1 = [np.ascontiguousarray(W1[e].T) for e in range(W1.shape[0])]
+    W2 = [np.ascontiguousarray(W2[e].T) for e in range(W2.shape[0])]
+    shared = None
+    if layer_mx["shared"] is not None:
+        q1, s1, q2, s2, wg = layer_mx["shared"]
+        shared = (np.ascontiguousarray(O.mx_dequant(host(q1), host(s1), axis=-2).T),
+                  np.ascontiguousarray(O.mx_dequant(host(q2), host(s2), axis=-1).T),
+                  host(wg) if wg is not None else None)
+    return W1, W2, shared
+
+
+MX_CASES = [
+    wl.LayerConfig("mx_small", "bf16", T=200, H=256, E=6, top_k=2, I=128, I_s=256, gated=True),
+    wl.LayerConfig("mx_decode1", "bf16", T=1, H=512, E=16, top_k=4, I=384, I_s=128),
+    wl.LayerConfig("mx_groups", "bf16", T=300, H=384, E=5, top_k=3, I=256, I_s=384),
+    wl.LayerConfig("mx_big_group", "bf16", T=700, H=256, E=2, top_k=1, I=256, I_s=128),
+]
+
+
+@pytest.mark.parametrize("cfg", MX_CASES, ids=_ids)
+def test_mx8_grouped_gemms_per_call(cfg):
+    layer = _layer(cfg)
+    mx = wl.mx_layer_weights(layer)
+    x = layer["x"]
+    rng = np.random.default_rng(6)
+    ids = rng.integers(0, cfg.E, (cfg.T, cfg.top_k)).astype(np.int32)
+    ids[: min(cfg.T, 5)] = 0
+    if cfg.E > 3:
+        ids[ids == 2] = 1                                   # an empty expert
+    sc = O.build_scatter(ids, cfg.E)
+    W1, W2, _ = _mx_np(mx)
+    Xs = O.scatter_rows(host(x), sc["row_token"])
+    offsets = torch.from_numpy(sc["offsets"]).to(DEV)
+    xs_dev = torch.from_numpy(Xs).to(x.dtype).to(DEV)
+    act = torch.full((cfg.R, cfg.I), float("nan"), dtype=x.dtype, device=DEV)
+    B.moe_grouped_swiglu_fc1_mx8(xs_dev, offsets, mx["W1q"], mx["W1s"], act)
+    y_rows = torch.full((cfg.R, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+    B.moe_grouped_fc2_mx8(act, offsets, mx["W2q"], mx["W2s"], y_rows)
+    torch.cuda.synchronize()
+    A_ref = O.grouped_swiglu_up(Xs, sc["offsets"], W1, contract=True, dtype=np.float64)
+    A = host(act)
+    assert np.isfinite(A).all()
+    assert (np.abs(A - A_ref) <= np.abs(A_ref) * 2.0 ** -7 + 1e-4).all()
+    Y_ref = O.grouped_down(A, sc["offsets"], W2, dtype=np.float64)
+    Y = host(y_rows)
+    assert np.isfinite(Y).all(), "rows left uncomputed"
+    mx_err = np.abs(Y - Y_ref).max() / max(np.abs(Y_ref).max(), 1e-30)
+    assert mx_err <= 1e-5, f"fc2 relative max error {mx_err:.3e} against the oracle on the same activation"
+
+
+@pytest.mark.parametrize("H,I,N_tail", [(256, 200, "fc1 output columns past a tile"),
+                                         (384, 256, "fc2 output columns past a tile")])
+def test_mx8_column_tails(H, I, N_tail):
+    """fc1 with I = 200 (a partial 64-column tile); fc2 with H = 200 (a partial 128-column tile)."""
+    if "fc1" in N_tail:
+        cfg = wl.LayerConfig("mx_tail1", "bf16", T=130, H=H, E=3, top_k=2, I=I)
+    else:
+        cfg = wl.LayerConfig("mx_tail2", "bf16", T=130, H=200, E=3, top_k=2, I=I)
+    layer = _layer(cfg)
+    mx = wl.mx_layer_weights(layer)
+    W1, W2, _ = _mx_np(mx)
+    ids = np.random.default_rng(2).integers(0, cfg.E, (cfg.T, cfg.top_k)).astype(np.int32)
+    sc = O.build_scatter(ids, cfg.E)
+    Xs = O.scatter_rows(host(layer["x"]), sc["row_token"])
+    offsets = torch.from_numpy(sc["offsets"]).to(DEV)
+    xs_dev = torch.from_numpy(Xs).to(torch.bfloat16).to(DEV)
+    if "fc1" in N_tail:
+        act = torch.full((cfg.R, cfg.I), float("nan"), dtype=torch.bfloat16, device=DEV)
+        B.moe_grouped_swiglu_fc1_mx8(xs_dev, offsets, mx["W1q"], mx["W1s"], act)
+        torch.cuda.synchronize()
+        A_ref = O.grouped_swiglu_up(Xs, sc["offsets"], W1, contract=True, dtype=np.float64)
+        assert (np.abs(host(act) - A_ref) <= np.abs(A_ref) * 2.0 ** -7 + 1e-4).all()
+    else:
+        A = O.bf16_rne(np.random.default_rng(3).standard_normal((cfg.R, cfg.I)))
+        y_rows = torch.full((cfg.R, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+        B.moe_grouped_fc2_mx8(torch.from_numpy(A.astype(np.float32)).to(torch.bfloat16).to(DEV), offsets,
+                              mx["W2q"], mx["W2s"], y_rows)
+        torch.cuda.synchronize()
+        Y_ref = O.grouped_down(A, sc["offsets"], W2, dtype=np.float64)
+        Y = host(y_rows)
+        assert np.isfinite(Y).all()
+        assert np.abs(Y - Y_ref).max() / np.abs(Y_ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_mx8_shared_expert(gated):
+    cfg = wl.LayerConfig("mx_shared", "bf16", T=333, H=256, E=1, top_k=1, I=8, I_s=384, gated=gated)
+    layer = _layer(cfg)
+    mx = wl.mx_layer_weights(layer)
+    _, _, shared = _mx_np(mx)
+    q1, s1, q2, s2, wg = mx["shared"]
+    x = layer["x"]
+    ws = torch.empty(B.moe_shared_expert_workspace_bytes(x.dtype, cfg.T, cfg.I_s), dtype=torch.uint8, device=DEV)
+    base = torch.randn((cfg.T, cfg.H), device=DEV)
+    y = base.clone()
+    B.moe_shared_expert_mx8(x, q1, s1, q2, s2, wg, y, ws, accumulate=True)
+    torch.cuda.synchronize()
+    ref = O.shared_expert(host(x), shared[0], shared[1], shared[2], contract=True)
+    assert_output_close(host(y) - host(base), ref, "bf16", "mx shared")
+
+
+@pytest.mark.parametrize("cfg", MX_CASES, ids=_ids)
+def test_mx8_layer_end_to_end(cfg):
+    """Routing and scatter in one call, MXFP8 routed experts, combine, MXFP8 shared expert."""
+    layer = _layer(cfg)
+    mx = wl.mx_layer_weights(layer)
+    x, wr = layer["x"], layer["w_router"]
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
+    bufs.y_rows.fill_(float("nan"))
+    B.moe_route_and_scatter(x, wr, None, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                            bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                            bufs.x_scattered, bufs.route_scatter_ws)
+    B.moe_grouped_swiglu_fc1_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"], bufs.act)
+    B.moe_grouped_fc2_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows)
+    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
+    q1, s1, q2, s2, wg = mx["shared"]
+    B.moe_shared_expert_mx8(x, q1, s1, q2, s2, wg, bufs.y, bufs.shared_ws, accumulate=True)
+    torch.cuda.synchronize()
+    ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
+    check_routing(host(bufs.logits), ids, w, host(x), host(wr), None, cfg.top_k, O)
+    W1, W2, shared = _mx_np(mx)
+    ref = O.moe_forward(host(x), None, W1, W2, cfg.top_k, routes=(ids, w), shared=shared, contract=True,
+                        dtype=np.float64)
+    assert np.array_equal(host(bufs.scatter_index), ref["scatter_index"])
+    assert_output_close(host(bufs.y), ref["y"], "bf16", "mx layer")

@@ -353,3 +353,56 @@ def test_token_outputs_matches_forward():
     for n, t in enumerate(sel):
         for j in range(2):
             assert np.allclose(tok["per_slot"][n, j], out["Ys"][out["scatter_index"][t, j]], rtol=1e-12, atol=1e-12)
+
+
+# ---- MXFP8 expert weights ([PLENA-C] "Group C -- shared experts", fusion-identity paragraph:
+# e4m3 values, one e8m0 scale per block of 8 along the intermediate axis; OCP encodings)
+
+def test_e4m3_decode_matches_torch_float8_on_every_code():
+    import torch
+    v = O.e4m3_decode(np.arange(256))
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    assert np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    assert np.isnan(v).sum() == 2                     # only S.1111.111
+
+
+def test_e4m3_and_e8m0_known_values():
+    known = {0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6,
+             0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x00: 0.0}
+    for code, val in known.items():
+        assert O.e4m3_decode(code) == val, hex(code)
+    neg0 = O.e4m3_decode(0x80)
+    assert neg0 == 0.0 and np.signbit(neg0)
+    assert np.isnan(O.e4m3_decode(0x7F)) and np.isnan(O.e4m3_decode(0xFF))
+    assert O.e8m0_decode(127) == 1.0 and O.e8m0_decode(120) == 2.0 ** -7
+    assert O.e8m0_decode(0) == 2.0 ** -127 and O.e8m0_decode(254) == 2.0 ** 127
+    assert np.isnan(O.e8m0_decode(255))
+
+
+def test_mx_dequant_blocks_run_along_the_given_axis():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 0x7F, (24, 40))           # no NaN codes
+    codes[rng.random(codes.shape) < 0.5] |= 0x80      # both signs
+    for axis in (0, 1):
+        sshape = (24 // 8, 40) if axis == 0 else (24, 40 // 8)
+        scales = rng.integers(110, 140, sshape)
+        W = O.mx_dequant(codes, scales, axis)
+        # one element by hand
+        r, c = 13, 29
+        s = scales[r // 8, c] if axis == 0 else scales[r, c // 8]
+        assert W[r, c] == O.e4m3_decode(codes[r, c]) * 2.0 ** (int(s) - 127)
+        # raising one scale by 1 doubles exactly its block of 8 along `axis`
+        bumped = scales.copy()
+        bumped[1, 2] += 1
+        W2 = O.mx_dequant(codes, bumped, axis)
+        changed = W2 != W
+        block = np.zeros_like(changed)
+        if axis == 0:
+            block[8:16, 2] = True
+        else:
+            block[1, 16:24] = True
+        assert np.array_equal(changed, block & (W != 0))
+        assert np.array_equal(W2[block], 2 * W[block])
+    with pytest.raises(ValueError):
+        O.mx_dequant(codes, np.ones((3, 41), np.int64), 0)

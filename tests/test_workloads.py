@@ -74,3 +74,31 @@ def test_bias_file_is_well_formed():
     path = os.path.join(os.path.dirname(wl.__file__), "route_bias.json")
     data = json.load(open(path))
     assert len(data["scout_zipf"]["bias"]) == 16 and len(data["v3_top4"]["bias"]) == 256
+
+
+def test_mx_quantize_codes_scales_and_precision():
+    """The MXFP8 input preparation: blocks of 8 along the requested axis, the
+    smallest power-of-two scale that keeps the block maximum within 448 (so it
+    lands in (224, 448]), values within e4m3 rounding of the bf16 weights
+    (checked with the oracle's decoder)."""
+    from oracle import moe_oracle as O
+    cfg = wl.LayerConfig("mxq", "bf16", T=4, H=64, E=2, top_k=1, I=32, I_s=16)
+    layer = wl.make_layer(cfg)
+    mx = wl.mx_layer_weights(layer)
+    assert mx["W1q"].shape == (2, 64, 64) and mx["W1s"].shape == (2, 8, 64)
+    assert mx["W2q"].shape == (2, 64, 32) and mx["W2s"].shape == (2, 64, 4)
+    assert mx["W1q"].dtype == torch.uint8 and mx["W1s"].dtype == torch.uint8
+    W1 = layer["W1"].float().numpy().transpose(0, 2, 1)          # [E, 2I, H]
+    D1 = O.mx_dequant(mx["W1q"].numpy(), mx["W1s"].numpy(), axis=-2)
+    # each element within half an e4m3 step (2**-3 relative to its binade) plus the block's subnormal step
+    blocks = np.abs(W1).reshape(2, 8, 8, 64).max(axis=2, keepdims=True)
+    step = np.repeat(blocks, 8, axis=2).reshape(W1.shape) * 2.0 ** -9
+    assert (np.abs(D1 - W1) <= np.abs(W1) * 2.0 ** -4 + step).all()
+    # the block maximum lands in (224, 448] after scaling (before rounding: the exact weight)
+    scale = np.repeat(O.e8m0_decode(mx["W1s"].numpy()), 8, axis=-2)
+    top = (np.abs(W1) / scale).reshape(2, 8, 8, 64).max(axis=2)
+    assert ((top > 224.0) & (top <= 448.0)).all()
+    # the fc2 blocks run along the reduction axis (last axis of the stored [E, H, I])
+    W2 = layer["W2"].float().numpy().transpose(0, 2, 1)          # [E, H, I]
+    D2 = O.mx_dequant(mx["W2q"].numpy(), mx["W2s"].numpy(), axis=-1)
+    assert np.abs(D2 - W2).max() <= np.abs(W2).max() * 2.0 ** -4
