@@ -47,24 +47,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_work(cfg, counts, shared_in_gemms=True):
+def algorithmic_work(cfg, counts, shared_in_gemms=True, weight_bytes=None):
     """FLOPs and bytes the layer must do for the realized routes (counts per expert).
     fc1/fc2 figures cover what the timed fc1/fc2 launches carry: the routed
-    groups and, with shared_in_gemms and a shared expert, the shared expert."""
+    groups and, with shared_in_gemms and a shared expert, the shared expert.
+    weight_bytes: bytes per expert-weight element (MXFP8: 1 + 1/8); activations
+    keep the workload's element size."""
     T, H, E, k, I, I_s = cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s
     R = int(counts.sum())
     active = int((counts > 0).sum())
     el = 2 if cfg.dtype == "bf16" else 4
+    wel = weight_bytes if weight_bytes is not None else el
     S = I_s if shared_in_gemms else 0
     fc1_flops = 4.0 * R * H * I + 4.0 * T * H * S
     fc2_flops = 2.0 * R * I * H + 2.0 * T * S * H
-    fc1_bytes = (active * H * 2 * I * el + R * H * el + R * I * el          # routed weights + X_s read + A write
-                 + (H * 2 * S * el + T * H * el + T * S * el if S else 0))
-    fc2_bytes = (active * I * H * el + R * I * el + R * H * 4               # routed weights + A read + Y_s write
-                 + (S * H * el + T * S * el + T * H * 4 if S else 0))
+    fc1_bytes = (active * H * 2 * I * wel + R * H * el + R * I * el         # routed weights + X_s read + A write
+                 + (H * 2 * S * wel + T * H * el + T * S * el if S else 0))
+    fc2_bytes = (active * I * H * wel + R * I * el + R * H * 4              # routed weights + A read + Y_s write
+                 + (S * H * wel + T * S * el + T * H * 4 if S else 0))
     shared_flops = 6.0 * T * H * I_s + (2.0 * T * H if cfg.gated else 0.0)
     layer_flops = 2.0 * T * H * E + 4.0 * R * H * I + 2.0 * R * I * H + shared_flops
-    layer_bytes = (active * 3 * H * I * el + 3 * H * I_s * el + H * E * el + T * H * el + T * H * 4)
+    layer_bytes = (active * 3 * H * I * wel + 3 * H * I_s * wel + H * E * el + T * H * el + T * H * 4)
     return {"R": R, "active_experts": active, "fc1_flops": fc1_flops, "fc2_flops": fc2_flops,
             "fc1_bytes": fc1_bytes, "fc2_bytes": fc2_bytes, "shared_flops": shared_flops,
             "layer_flops": layer_flops, "layer_bytes": layer_bytes}
@@ -108,6 +111,30 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
     x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     shared = layer["shared"]
+    mx = layer.get("mx")
+    if mx is not None:  # MXFP8 expert weights: routed and shared experts together, then the combine
+        rec(0)
+        B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                                bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                                bufs.x_scattered, bufs.route_scatter_ws)
+        rec(1)
+        if mx["shared"] is not None:
+            q1, s1, q2, s2, wg = mx["shared"]
+            B.moe_grouped_swiglu_fc1_and_shared_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"],
+                                                    bufs.act, x, q1, s1, bufs.act_shared)
+            rec(2)
+            B.moe_grouped_fc2_and_shared_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows,
+                                             bufs.act_shared, q2, s2, x, wg, bufs.y, bufs.shared_ws,
+                                             accumulate=False)
+        else:
+            B.moe_grouped_swiglu_fc1_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"], bufs.act)
+            rec(2)
+            B.moe_grouped_fc2_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows)
+        rec(3)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y,
+                             mx["shared"] is not None)
+        rec(4)
+        return
     if side is not None and shared is not None:
         main = torch.cuda.current_stream()
         side.wait_stream(main)
@@ -161,12 +188,38 @@ def cpu_baseline(layer, cfg, bufs, sample_tokens):
     log(f"cpu baseline: copying inputs for {S} tokens to the host")
     x = f(layer["x"][:S])
     wr = f(layer["w_router"])
-    W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
-    W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
-    shared = None
-    if layer["shared"] is not None:
-        ws1, ws2, wg = layer["shared"]
-        shared = (fw(ws1), fw(ws2), f(wg) if wg is not None else None)
+    mx = layer.get("mx")
+    if mx is not None:  # the oracle dequantizes the MXFP8 codes exactly, one expert when it is first used
+        u = lambda t: t.cpu().numpy()
+
+        class _Lazy:
+            def __init__(self, q, sc, axis):
+                self.q, self.sc, self.axis, self.cache = q, sc, axis, {}
+
+            def __len__(self):
+                return self.q.shape[0]
+
+            def __getitem__(self, e):
+                if e not in self.cache:
+                    d = O.mx_dequant(u(self.q[e]), u(self.sc[e]), axis=self.axis)
+                    self.cache[e] = np.ascontiguousarray(d.T.astype(np.float32))
+                return self.cache[e]
+
+        W1 = _Lazy(mx["W1q"], mx["W1s"], 0)
+        W2 = _Lazy(mx["W2q"], mx["W2s"], 1)
+        shared = None
+        if mx["shared"] is not None:
+            q1, s1, q2, s2, wg = mx["shared"]
+            shared = (np.ascontiguousarray(O.mx_dequant(u(q1), u(s1), axis=0).T.astype(np.float32)),
+                      np.ascontiguousarray(O.mx_dequant(u(q2), u(s2), axis=1).T.astype(np.float32)),
+                      f(wg) if wg is not None else None)
+    else:
+        W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
+        W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
+        shared = None
+        if layer["shared"] is not None:
+            ws1, ws2, wg = layer["shared"]
+            shared = (fw(ws1), fw(ws2), f(wg) if wg is not None else None)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     log(f"cpu baseline: oracle over {S} tokens with {threads} BLAS threads")
@@ -215,6 +268,9 @@ def main():
     ap.add_argument("--shared", choices=("fused", "overlap"), default="fused",
                     help="shared expert inside the routed fc1/fc2 launches (fused, the default: measured faster "
                          "on every workload) or on a second stream concurrent with routing (overlap)")
+    ap.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert weight format: bf16, or MXFP8 (e4m3 codes, one e8m0 scale per 8 along the "
+                         "intermediate axis, dequantized exactly in the kernels; activations stay bf16)")
     ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
                     help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default: measured "
                          "as fast or faster on every workload), nk = [N, K] (torch.nn.Linear layout)")
@@ -234,7 +290,14 @@ def main():
     log(f"workload {cfg}")
     layer = wl.make_layer(cfg, dev)
     layer["layout"] = B.MOE_W_NK if args.layout == "nk" else B.MOE_W_KN
-    if args.layout == "nk":  # the same matrices, stored [N, K]
+    if args.weights == "mxfp8":
+        if cfg.dtype != "bf16":
+            print("--weights mxfp8 needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        layer["mx"] = wl.mx_layer_weights(layer)
+        layer["W1"] = layer["W2"] = layer["shared"] = None   # only the MXFP8 copies stay on the device
+        torch.cuda.empty_cache()
+    elif args.layout == "nk":  # the same matrices, stored [N, K]
         t = lambda w: w.transpose(-1, -2).contiguous()
         for key in ("W1", "W2"):
             layer[key] = t(layer[key])
@@ -257,6 +320,8 @@ def main():
     mode = args.shared
     if not cfg.I_s:
         mode = "none"
+    if args.weights == "mxfp8":
+        mode = "mx"
     side = torch.cuda.Stream() if mode == "overlap" else None
     for _ in range(args.warmup):
         run_step(layer, bufs, cfg, bias_t, side=side)
@@ -299,11 +364,12 @@ def main():
                 for i, c in enumerate(CALLS)}
     log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
 
-    work = algorithmic_work(cfg, counts, shared_in_gemms=(mode == "fused"))
+    work = algorithmic_work(cfg, counts, shared_in_gemms=(mode in ("fused", "mx")),
+                            weight_bytes=1.125 if args.weights == "mxfp8" else None)
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
-    tr = committed_traffic(cfg.name)
+    tr = committed_traffic(cfg.name) if mode != "mx" else None
     roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per fc1 call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = work["fc1_bytes"]
@@ -315,6 +381,9 @@ def main():
     elif mode == "fused":
         roof["kernel"] = ("fc1 call = two launches of grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1_and_shared:"
                           " routed experts, then the shared expert)")
+    elif mode == "mx":
+        roof["kernel"] = ("fc1 call = one launch of grouped_gemm_mx8_fused<SwiGLU> (moe_grouped_swiglu_fc1_and_shared_mx8:"
+                          " routed and shared experts, MXFP8 weights)")
     else:
         roof["kernel"] = "fc1 call = grouped_gemm_bf16_pipe<SwiGLU> (moe_grouped_swiglu_fc1: routed experts)"
     gg_s = fc1_s + fc2_s
@@ -349,9 +418,14 @@ def main():
                   "frac_roofline": round(t_roof / layer_s, 4), "roofline_ms": round(t_roof * 1e3, 4),
                   "active_experts": work["active_experts"]},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "per_call_note": ("fc1/fc2 carry the shared expert too (see shared_expert)" if mode in ("fused", "mx")
+                          else "fc1/fc2 are the routed experts only"),
         "timing": "hip graph replay" if args.graph else "eager launches",
         "weight_layout": "[N, K] per expert (torch.nn.Linear)" if args.layout == "nk" else "[K, N] per expert",
-        "shared_expert": {"fused": "inside the routed fc1/fc2 launches",
+        "weights": ("MXFP8 (e4m3 + e8m0 per 8 along the intermediate axis), dequantized to bf16 in the kernels"
+                    if args.weights == "mxfp8" else "bf16"),
+        "shared_expert": {"mx": "inside the routed fc1/fc2 launches (MXFP8 *_and_shared_mx8 calls)",
+                          "fused": "inside the routed fc1/fc2 launches",
                           "overlap": "moe_shared_expert on a second stream, concurrent with routing and the "
                                      "routed experts; the combine waits for it",
                           "none": "layer has no shared expert"}[mode],

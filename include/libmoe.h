@@ -310,6 +310,23 @@ moe_status moe_shared_expert_mx8(const void* x, const uint8_t* ws1q, const uint8
                                  int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* MXFP8 counterparts of moe_grouped_swiglu_fc1_and_shared and
+ * moe_grouped_fc2_and_shared: the routed groups and the shared expert in one
+ * launch per half (always), weights and scales as for the *_mx8 calls above,
+ * other arguments as for the bf16 calls.  Limits: H, I and I_s multiples of
+ * 128. */
+moe_status moe_grouped_swiglu_fc1_and_shared_mx8(const void* x_scattered, const int32_t* expert_offsets,
+                                                 const uint8_t* w1q, const uint8_t* w1s, int32_t R, int32_t H,
+                                                 int32_t E, int32_t I, void* act, const void* x, const uint8_t* ws1q,
+                                                 const uint8_t* ws1s, int32_t T, int32_t I_s, void* act_shared,
+                                                 void* stream);
+moe_status moe_grouped_fc2_and_shared_mx8(const void* act, const int32_t* expert_offsets, const uint8_t* w2q,
+                                          const uint8_t* w2s, int32_t R, int32_t I, int32_t E, int32_t H,
+                                          float* y_rows, const void* act_shared, const uint8_t* ws2q,
+                                          const uint8_t* ws2s, const void* x, const void* w_gate, int32_t T,
+                                          int32_t I_s, int32_t accumulate, float* y, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Kernel launches one moe_grouped_swiglu_fc1_and_shared call makes for these
  * sizes (R = T * top_k routed rows): 1 when the routed experts and the shared
  * expert share one launch, 2 when they run one after the other; 0 for invalid

@@ -58,6 +58,11 @@ _SIGNATURES = {
     "moe_grouped_fc2_mx8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
     "moe_shared_expert_mx8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                        _c_size, _vp]),
+    "moe_grouped_swiglu_fc1_and_shared_mx8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                                       _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
+    "moe_grouped_fc2_and_shared_mx8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                                _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
+                                                _vp]),
     "moe_and_shared_launches": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
@@ -308,6 +313,43 @@ def moe_shared_expert_mx8(x, ws1q, ws1s, ws2q, ws2s, w_gate, y, workspace, accum
             I_s, int(bool(accumulate)), _ptr(y, "y", torch.float32, (T, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_shared_expert_mx8(*args))
+
+
+def moe_grouped_swiglu_fc1_and_shared_mx8(x_scattered, expert_offsets, w1q, w1s, act, x, ws1q, ws1s, act_shared,
+                                          stream=None):
+    lib = load()
+    R, H = x_scattered.shape
+    E, I2, _ = w1q.shape
+    I = I2 // 2
+    T = x.shape[0]
+    I_s = ws1q.shape[0] // 2
+    dev = x.device
+    u8, b16 = torch.uint8, torch.bfloat16
+    args = (_ptr(x_scattered, "x_scattered", b16, (R, H), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1q, "w1q", u8, (E, 2 * I, H), dev), _ptr(w1s, "w1s", u8, (E, 2 * I // 8, H), dev), R, H, E, I,
+            _ptr(act, "act", b16, (R, I), dev), _ptr(x, "x", b16, (T, H), dev),
+            _ptr(ws1q, "ws1q", u8, (2 * I_s, H), dev), _ptr(ws1s, "ws1s", u8, (2 * I_s // 8, H), dev), T, I_s,
+            _ptr(act_shared, "act_shared", b16, (T, I_s), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_and_shared_mx8(*args))
+
+
+def moe_grouped_fc2_and_shared_mx8(act, expert_offsets, w2q, w2s, y_rows, act_shared, ws2q, ws2s, x, w_gate, y,
+                                   workspace, accumulate=False, stream=None):
+    lib = load()
+    R, I = act.shape
+    E, H, _ = w2q.shape
+    T, I_s = act_shared.shape
+    dev = act.device
+    u8, b16 = torch.uint8, torch.bfloat16
+    args = (_ptr(act, "act", b16, (R, I), dev), _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2q, "w2q", u8, (E, H, I), dev), _ptr(w2s, "w2s", u8, (E, H, I // 8), dev), R, I, E, H,
+            _ptr(y_rows, "y_rows", torch.float32, (R, H), dev), _ptr(act_shared, "act_shared", b16, (T, I_s), dev),
+            _ptr(ws2q, "ws2q", u8, (H, I_s), dev), _ptr(ws2s, "ws2s", u8, (H, I_s // 8), dev),
+            _ptr(x, "x", b16, (T, H), dev), _ptr(w_gate, "w_gate", b16, (H,), dev), T, I_s, int(bool(accumulate)),
+            _ptr(y, "y", torch.float32, (T, H), dev), _ptr(workspace, "workspace", torch.uint8, None, dev),
+            workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_grouped_fc2_and_shared_mx8(*args))
 
 
 def moe_and_shared_launches(dtype, R, H, E, I, T, I_s) -> int:

@@ -426,6 +426,78 @@ moe_status moe_shared_expert_mx8(const void* x, const uint8_t* ws1q, const uint8
                     fn);
 }
 
+moe_status moe_grouped_swiglu_fc1_and_shared_mx8(const void* x_scattered, const int32_t* expert_offsets,
+                                                 const uint8_t* w1q, const uint8_t* w1s, int32_t R, int32_t H,
+                                                 int32_t E, int32_t I, void* act, const void* x, const uint8_t* ws1q,
+                                                 const uint8_t* ws1s, int32_t T, int32_t I_s, void* act_shared,
+                                                 void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1_and_shared_mx8";
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1q, fn, "w1q"));
+  MOE_CHECK(need_ptr(w1s, fn, "w1s"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(ws1q, fn, "ws1q"));
+  MOE_CHECK(need_ptr(ws1s, fn, "ws1s"));
+  MOE_CHECK(need_ptr(act_shared, fn, "act_shared"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult128(H, fn, "H"));
+  MOE_CHECK(need_mult128(I, fn, "I"));
+  MOE_CHECK(need_mult128(I_s, fn, "I_s"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  return hip_result(moe_launch::fused_fc1_mx8(x_scattered, expert_offsets, E, R, w1q, w1s, H, I, act, x, T, ws1q,
+                                              ws1s, I_s, act_shared, cu_count(), (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_grouped_fc2_and_shared_mx8(const void* act, const int32_t* expert_offsets, const uint8_t* w2q,
+                                          const uint8_t* w2s, int32_t R, int32_t I, int32_t E, int32_t H,
+                                          float* y_rows, const void* act_shared, const uint8_t* ws2q,
+                                          const uint8_t* ws2s, const void* x, const void* w_gate, int32_t T,
+                                          int32_t I_s, int32_t accumulate, float* y, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_grouped_fc2_and_shared_mx8";
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w2q, fn, "w2q"));
+  MOE_CHECK(need_ptr(w2s, fn, "w2s"));
+  MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
+  MOE_CHECK(need_ptr(act_shared, fn, "act_shared"));
+  MOE_CHECK(need_ptr(ws2q, fn, "ws2q"));
+  MOE_CHECK(need_ptr(ws2s, fn, "ws2s"));
+  MOE_CHECK(need_ptr(y, fn, "y"));
+  if (w_gate) MOE_CHECK(need_ptr(x, fn, "x (needed for the gate)"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult128(I, fn, "I"));
+  MOE_CHECK(need_mult128(I_s, fn, "I_s"));
+  MOE_CHECK(need_flag(accumulate, fn, "accumulate"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  const size_t need = moe_shared_expert_workspace_bytes(MOE_BF16, T, I_s);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  float* gate = w_gate ? (float*)((char*)workspace + align256((size_t)T * I_s * elem_size(MOE_BF16))) : nullptr;
+  if (gate) MOE_CHECK(hip_result(moe_launch::shared_gate(1, x, w_gate, T, H, gate, s), fn));
+  return hip_result(moe_launch::fused_fc2_mx8(act, expert_offsets, E, R, w2q, w2s, I, H, y_rows, act_shared, T, ws2q,
+                                              ws2s, I_s, gate, accumulate, y, cu_count(), s),
+                    fn);
+}
+
 int32_t moe_and_shared_launches(moe_dtype dt, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T, int32_t I_s) {
   if (R < 1 || H < 1 || E < 1 || I < 1 || T < 1 || I_s < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
   return moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T) ? 1 : 2;

@@ -185,6 +185,13 @@ hipError_t grouped_fc2_mx8(const void* act, const int32_t* offsets, int groups, 
                            const void* w2s, int K, int N, float* out, const float* row_scale, int accumulate,
                            int plain_store, int role, int cu_count, hipStream_t s);
 
+hipError_t fused_fc1_mx8(const void* xs, const int32_t* offsets, int E, int R, const void* w1q, const void* w1s,
+                         int H, int I, void* act, const void* x, int T, const void* ws1q, const void* ws1s, int I_s,
+                         void* act_s, int cu_count, hipStream_t s);
+hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, const void* w2q, const void* w2s,
+                         int I, int H, float* y_rows, const void* act_s, int T, const void* ws2q, const void* ws2s,
+                         int I_s, const float* gate, int accumulate, float* y, int cu_count, hipStream_t s);
+
 // Routed groups and the shared expert in one launch (bf16, reduction sizes
 // multiples of 64, and a shared expert that is light next to the routed
 // weights; fused_supported() decides from the shapes).

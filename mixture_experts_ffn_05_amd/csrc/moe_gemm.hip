@@ -51,6 +51,8 @@
 // f32 path: one thread per output element (used by the float32 workload).
 #include "moe_common.h"
 
+#include <type_traits>
+
 // Build-time switches used when tuning (the defaults are the shipped
 // configuration; MOE_TUNING makes every numbered configuration reachable).
 #ifndef MOE_FRAG_PREFETCH
@@ -778,15 +780,22 @@ struct MxCfg {
 // 32-row tiles, 128 staged columns, 128-deep slices, 4-stage ring, 4 waves
 // (2 column positions x 2 split-K waves): the decode tile of the bf16 path.
 typedef MxCfg<32, 128, 128, 4, 1, 2, 2> MxCfg1;
+typedef MxCfg<32, 128, 128, 2, 1, 2, 2> MxCfg2;   // two workgroups per CU
+typedef MxCfg<32, 64, 128, 4, 1, 1, 4> MxCfg3;    // 64 columns, 4 split-K waves, two workgroups per CU
+#ifndef MOE_MX_VARIANT
+#define MOE_MX_VARIANT 2
+#endif
+typedef typename std::conditional<MOE_MX_VARIANT == 2, MxCfg2,
+                                  typename std::conditional<MOE_MX_VARIANT == 3, MxCfg3, MxCfg1>::type>::type MxCfgUsed;
 
 template <int ROWBYTES>
 __device__ __forceinline__ int row_swizzle(int row) {
   return (row / (256 / ROWBYTES)) % (ROWBYTES / 16);
 }
 
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return __uint_as_float(s == 0 ? 0x00400000u : (s == 255 ? 0x7fc00000u : (s << 23)));
-}
+// 2^(s - 127) for e8m0 byte s in 1..254 (the kernels require exponents 10..246
+// anyway; 0 and the NaN code 255 are not decoded).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) { return __uint_as_float(s << 23); }
 
 // Two e4m3 codes (bytes 0-1, or with HI bytes 2-3, of `codes`) times `scale`, as bf16x2.
 template <bool HI>
@@ -813,6 +822,87 @@ __device__ __forceinline__ uint32_t mx_pair_two_scales(uint32_t word, uint32_t s
 __device__ __forceinline__ u32x4 mx_frag_eight_scales(u32x2 c, u32x2 sw) {
   return u32x4{mx_pair_two_scales<false>(c[0], sw[0]), mx_pair_two_scales<true>(c[0], sw[0] >> 16),
                mx_pair_two_scales<false>(c[1], sw[1]), mx_pair_two_scales<true>(c[1], sw[1] >> 16)};
+}
+
+// Raw fragments of one MX substep: the activation blocks, and per weight
+// block 8 codes plus their scale bytes (8 for kScaleN, 1 for kScaleK).
+template <class C>
+struct MxFrags {
+  u32x4 a[C::kMB];
+  u32x2 codes[C::kNB];
+  u32x2 scales[C::kNB];
+};
+
+template <int EPI, class C, int SAX>
+__device__ __forceinline__ void mx_read(const unsigned char* __restrict__ As, const unsigned char* __restrict__ Bs,
+                                        const unsigned char* __restrict__ Ss, int ks, int wm, int wn,
+                                        MxFrags<C>& f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb) {
+    const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+    const int chunk = (2 * ks + (lane >> 5)) ^ row_swizzle<C::kARow>(m);
+    f.a[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
+  }
+#pragma unroll
+  for (int nb = 0; nb < C::kNB; ++nb) {
+    const int n = pipe_col_base<EPI, C>(nb, wn) + (lane & 31);
+    const int kg = lane >> 5;  // k = 16 ks + 8 kg .. + 7
+    const int chunk = ks ^ row_swizzle<C::kBRow>(n);
+    f.codes[nb] = *(const u32x2*)(Bs + n * C::kBRow + chunk * 16 + 8 * kg);
+    if (SAX == kScaleK)
+      f.scales[nb] = u32x2{(uint32_t)Ss[n * (C::BK / 8) + 2 * ks + kg], 0u};
+    else
+      f.scales[nb] = *(const u32x2*)(Ss + (n / 8) * C::BK + 16 * ks + 8 * kg);
+  }
+}
+
+// One MX pipeline step: start the direct loads of a future slice into `wst`,
+// then run this wave's substeps of the slice held in `rst`, reading the
+// fragments of the next substep while the current one is converted and
+// multiplied.  The __restrict__ stage pointers let the compiler skip waiting
+// for the in-flight direct loads before the LDS reads.
+template <int EPI, class C, int SAX>
+__device__ __forceinline__ void mx_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
+                                        bool issue, const bf16_t* a_k, const unsigned char* b_k,
+                                        const unsigned char* s_k, const int64_t* a_off, const int* b_off,
+                                        const int* s_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw) {
+  const int wave = threadIdx.x >> 6;
+  if (issue) {
+#pragma unroll
+    for (int i = 0; i < C::kALoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                       MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                       MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < C::kSLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
+                                       MOE_LDS(void, wst + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256),
+                                       4, 0, 0);
+  }
+  const unsigned char* As = rst;
+  const unsigned char* Bs = rst + C::kAStage;
+  const unsigned char* Ss = rst + C::kAStage + C::kBStage;
+  MxFrags<C> fr[2];
+  mx_read<EPI, C, SAX>(As, Bs, Ss, kw, wm, wn, fr[0]);
+#pragma unroll
+  for (int j = 0; j < C::kKSW; ++j) {
+    if (j + 1 < C::kKSW) mx_read<EPI, C, SAX>(As, Bs, Ss, kw + (j + 1) * C::KW, wm, wn, fr[(j + 1) & 1]);
+    const MxFrags<C>& f = fr[j & 1];
+    u32x4 bfr[C::kNB];
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+      bfr[nb] = SAX == kScaleK ? mx_frag_one_scale(f.codes[nb], e8m0_to_f32(f.scales[nb][0]))
+                               : mx_frag_eight_scales(f.codes[nb], f.scales[nb]);
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(f.a[mb], bfr[nb], acc[mb][nb]);
+  }
 }
 
 template <int EPI, class C, int SAX>
@@ -869,25 +959,6 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
   constexpr int kSStep = SAX == kScaleN ? C::BK : C::BK / 8;  // scale bytes per slice along k
   const int nk = K / C::BK;
 
-  auto issue = [&](unsigned char* st, int kt) {
-    const bf16_t* a_k = p.a + (int64_t)kt * C::BK;
-    const unsigned char* b_k = bq + (int64_t)kt * C::BK;
-    const unsigned char* s_k = bs + (int64_t)kt * kSStep;
-#pragma unroll
-    for (int i = 0; i < C::kALoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                       MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                       MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kSLoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
-                                       MOE_LDS(void, st + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256),
-                                       4, 0, 0);
-  };
-
   f32x16 acc[C::kMB][C::kNB];
 #pragma unroll
   for (int mb = 0; mb < C::kMB; ++mb)
@@ -896,46 +967,40 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
+  // Prologue: the first STAGES - 1 slices (the second stage pointer of each
+  // call is unused because nothing is computed yet).
 #pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) issue(smem + s * C::kStage, s);
+  for (int s = 0; s < C::STAGES - 1; ++s) {
+    if (s < nk) {
+      unsigned char* st = smem + s * C::kStage;
+      const int wave_ = wave;
+      const bf16_t* a_k = p.a + (int64_t)s * C::BK;
+      const unsigned char* b_k = bq + (int64_t)s * C::BK;
+      const unsigned char* s_k = bs + (int64_t)s * kSStep;
+#pragma unroll
+      for (int i = 0; i < C::kALoads; ++i)
+        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                         MOE_LDS(void, st + (wave_ * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < C::kBLoads; ++i)
+        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                         MOE_LDS(void, st + C::kAStage + (wave_ * C::kBLoads + i) * 1024), 16, 0,
+                                         0);
+#pragma unroll
+      for (int i = 0; i < C::kSLoads; ++i)
+        __builtin_amdgcn_global_load_lds(
+            MOE_GLOBAL(void, s_k + s_off[i]),
+            MOE_LDS(void, st + C::kAStage + C::kBStage + (wave_ * C::kSLoads + i) * 256), 4, 0, 0);
+    }
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
     if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
     lds_barrier();
     const int kn = kt + C::STAGES - 1;
-    if (kn < nk) issue(smem + (kn % C::STAGES) * C::kStage, kn);
-    const unsigned char* As = smem + (kt % C::STAGES) * C::kStage;
-    const unsigned char* Bs = As + C::kAStage;
-    const unsigned char* Ss = Bs + C::kBStage;
-#pragma unroll
-    for (int jj = 0; jj < C::kKSW; ++jj) {
-      const int ks = kw + jj * C::KW;
-      u32x4 af[C::kMB], bfr[C::kNB];
-#pragma unroll
-      for (int mb = 0; mb < C::kMB; ++mb) {
-        const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
-        const int chunk = (2 * ks + (lane >> 5)) ^ row_swizzle<C::kARow>(m);
-        af[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
-      }
-#pragma unroll
-      for (int nb = 0; nb < C::kNB; ++nb) {
-        const int n = pipe_col_base<EPI, C>(nb, wn) + (lane & 31);
-        const int kg = lane >> 5;  // k = 16 ks + 8 kg .. + 7
-        const int chunk = ks ^ row_swizzle<C::kBRow>(n);
-        const u32x2 codes = *(const u32x2*)(Bs + n * C::kBRow + chunk * 16 + 8 * kg);
-        if (SAX == kScaleK) {
-          bfr[nb] = mx_frag_one_scale(codes, e8m0_to_f32(Ss[n * (C::BK / 8) + 2 * ks + kg]));
-        } else {
-          const u32x2 sw = *(const u32x2*)(Ss + (n / 8) * C::BK + 16 * ks + 8 * kg);
-          bfr[nb] = mx_frag_eight_scales(codes, sw);
-        }
-      }
-#pragma unroll
-      for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[mb], bfr[nb], acc[mb][nb]);
-    }
+    mx_step<EPI, C, SAX>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
+                         p.a + (int64_t)kn * C::BK, bq + (int64_t)kn * C::BK, bs + (int64_t)kn * kSStep, a_off,
+                         b_off, s_off, acc, wn, wm, kw);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
   finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
@@ -954,6 +1019,35 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8(GemmPara
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
     run_tile_mx<EPI, C, SAX>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
+  }
+}
+
+// MXFP8 routed groups and the MXFP8 shared expert in one persistent launch
+// (tiles interleaved as in grouped_gemm_bf16_fused).
+template <int EPI_R, int EPI_S, class C, int SAX>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8_fused(GemmParams<bf16_t> pr,
+                                                                               GemmParams<bf16_t> ps) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int32_t sOff[kMaxExperts + 1];
+  __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sWave[C::kWaves];
+  const int mtiles = build_tile_prefix<C::BM, C::NT>(pr, sOff, sPre, sWave);
+  const int64_t ntr = pr.n_tiles;
+  const int64_t tiles_r = (int64_t)mtiles * ntr;
+  const int64_t mts = (ps.rows + C::BM - 1) / C::BM;
+  const int64_t tiles_s = mts * ps.n_tiles;
+  const int64_t total = tiles_r + tiles_s;
+  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const int64_t s_before = id * tiles_s / total;
+    if ((id + 1) * tiles_s / total != s_before) {
+      const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
+      run_tile_mx<EPI_S, C, SAX>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
+    } else {
+      const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
+      run_tile_mx<EPI_R, C, SAX>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
+    }
   }
 }
 
@@ -1029,7 +1123,7 @@ hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
 
 template <int EPI, int SAX, int ROLE>
 hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  typedef MxCfg1 C;
+  typedef MxCfgUsed C;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_mx8<EPI, C, SAX, ROLE>), hipFuncAttributeMaxDynamicSharedMemorySize,
       C::kLds);
@@ -1039,6 +1133,24 @@ hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
   const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
   hipLaunchKernelGGL((grouped_gemm_mx8<EPI, C, SAX, ROLE>), dim3(grid), dim3(C::NT), C::kLds, s, p);
+  return hipGetLastError();
+}
+
+template <int EPI_R, int EPI_S, int SAX>
+hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
+  typedef MxCfgUsed C;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&grouped_gemm_mx8_fused<EPI_R, EPI_S, C, SAX>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (attr != hipSuccess) return attr;
+  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  pr.n_tiles = (pr.N + out_r - 1) / out_r;
+  ps.n_tiles = (ps.N + out_s - 1) / out_s;
+  const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
+  const int64_t tiles_s = (int64_t)((ps.rows + C::BM - 1) / C::BM) * ps.n_tiles;
+  const int grid = persistent_grid(ub_r + tiles_s, cu_count * C::kWgsPerCu);
+  hipLaunchKernelGGL((grouped_gemm_mx8_fused<EPI_R, EPI_S, C, SAX>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
   return hipGetLastError();
 }
 
@@ -1290,6 +1402,28 @@ hipError_t grouped_fc2_mx8(const void* act, const int32_t* offsets, int groups, 
   if (plain_store)
     return role ? launch_mx8<kStoreF32, kScaleK, 1>(p, cu_count, s) : launch_mx8<kStoreF32, kScaleK, 0>(p, cu_count, s);
   return role ? launch_mx8<kScaleAdd, kScaleK, 1>(p, cu_count, s) : launch_mx8<kScaleAdd, kScaleK, 0>(p, cu_count, s);
+}
+
+hipError_t fused_fc1_mx8(const void* xs, const int32_t* offsets, int E, int R, const void* w1q, const void* w1s,
+                         int H, int I, void* act, const void* x, int T, const void* ws1q, const void* ws1s, int I_s,
+                         void* act_s, int cu_count, hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> pr{(const bf16_t*)xs, offsets, E, R, H, I, (const bf16_t*)w1q, (int64_t)2 * I * H,
+                        H, I, act, nullptr, 0, 0, 1, (const uint8_t*)w1s, (int64_t)2 * I / 8 * H};
+  GemmParams<bf16_t> ps{(const bf16_t*)x, nullptr, 1, T, H, I_s, (const bf16_t*)ws1q, 0,
+                        H, I_s, act_s, nullptr, 0, 0, 1, (const uint8_t*)ws1s, 0};
+  return launch_mx8_fused<kSwiGLU, kSwiGLU, kScaleN>(pr, ps, cu_count, s);
+}
+
+hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, const void* w2q, const void* w2s,
+                         int I, int H, float* y_rows, const void* act_s, int T, const void* ws2q, const void* ws2s,
+                         int I_s, const float* gate, int accumulate, float* y, int cu_count, hipStream_t s) {
+  using namespace moe;
+  GemmParams<bf16_t> pr{(const bf16_t*)act, offsets, E, R, I, H, (const bf16_t*)w2q, (int64_t)H * I,
+                        I, 0, y_rows, nullptr, 0, 0, 1, (const uint8_t*)w2s, (int64_t)H * (I / 8)};
+  GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2q, 0,
+                        I_s, 0, y, gate, accumulate, 0, 1, (const uint8_t*)ws2s, 0};
+  return launch_mx8_fused<kStoreF32, kScaleAdd, kScaleK>(pr, ps, cu_count, s);
 }
 
 }  // namespace moe_launch

@@ -125,6 +125,12 @@ def test_mx8_validation(lib):
     need = lib.moe_shared_expert_workspace_bytes(1, 64, 256)
     assert lib.moe_shared_expert_mx8(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 256, 200, 1, FAKE, FAKE, need,
                                      None) == 2
+    # fused routed + shared: all three reduction sizes must be multiples of 128
+    assert lib.moe_grouped_swiglu_fc1_and_shared_mx8(FAKE, FAKE, FAKE, FAKE, 64, 256, 4, 128, FAKE, FAKE, FAKE,
+                                                     FAKE, 64, 200, FAKE, None) == 2
+    assert "I_s" in _err(lib)
+    assert lib.moe_grouped_fc2_and_shared_mx8(FAKE, FAKE, FAKE, FAKE, 64, 256, 4, 256, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, None, 64, 256, 0, FAKE, FAKE, need - 1, None) == 3
     assert lib.moe_shared_expert_mx8(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 256, 256, 1, FAKE, FAKE, need - 1,
                                      None) == 3
 

@@ -89,3 +89,54 @@ def test_full_size_layer(name):
     per_slot = np.stack([Ys[sc["scatter_index"][t]] for t in toks])
     assert_output_close(per_slot.reshape(-1, cfg.H), ref["per_slot"].reshape(-1, cfg.H), "bf16", f"{name} Y_s")
     print(f"[full] {name}: y max|err| {mx:.3e} rel_fro {rel:.3e} over {len(toks)} tokens", flush=True)
+
+
+MX_FULL = ["v2l_decode1", "v2l_decode64", "v3_decode64"]
+
+
+@pytest.mark.parametrize("name", MX_FULL)
+def test_full_size_layer_mxfp8(name):
+    """The benchmark's MXFP8 step (moe_route_and_scatter, the routed and shared experts through
+    the *_and_shared_mx8 calls, combine) at full size; sampled tokens against the oracle on the
+    dequantized weights."""
+    cfg = wl.WORKLOADS[name]
+    print(f"[full-mx] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k} I={cfg.I} I_s={cfg.I_s}", flush=True)
+    layer = wl.make_layer(cfg, DEV)
+    mx = wl.mx_layer_weights(layer)
+    del layer["W1"], layer["W2"]
+    torch.cuda.empty_cache()
+    x, wr = layer["x"], layer["w_router"]
+    bias = layer["bias"]
+    bias_t = torch.from_numpy(bias).to(DEV) if bias is not None else None
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
+    bufs.y_rows.fill_(float("nan"))
+    B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                            bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                            bufs.x_scattered, bufs.route_scatter_ws)
+    q1, s1, q2, s2, wg = mx["shared"]
+    B.moe_grouped_swiglu_fc1_and_shared_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"], bufs.act,
+                                            x, q1, s1, bufs.act_shared)
+    B.moe_grouped_fc2_and_shared_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows,
+                                     bufs.act_shared, q2, s2, x, wg, bufs.y, bufs.shared_ws, accumulate=False)
+    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
+    torch.cuda.synchronize()
+
+    xh = host(x)
+    ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
+    check_routing(host(bufs.logits), ids, w, xh, host(wr), bias, cfg.top_k, O)
+    sc = O.build_scatter(ids, cfg.E)
+    assert np.array_equal(host(bufs.scatter_index), sc["scatter_index"])
+    assert np.array_equal(host(bufs.expert_offsets), sc["offsets"])
+
+    def expert(e):   # K x N matrices, dequantized exactly by the oracle
+        w1 = O.mx_dequant(host(mx["W1q"][e]), host(mx["W1s"][e]), axis=0).T.astype(np.float32)
+        w2 = O.mx_dequant(host(mx["W2q"][e]), host(mx["W2s"][e]), axis=1).T.astype(np.float32)
+        return np.ascontiguousarray(w1), np.ascontiguousarray(w2)
+
+    shared = (np.ascontiguousarray(O.mx_dequant(host(q1), host(s1), axis=0).T.astype(np.float32)),
+              np.ascontiguousarray(O.mx_dequant(host(q2), host(s2), axis=1).T.astype(np.float32)),
+              host(wg) if wg is not None else None)
+    toks = _sample_tokens(cfg.T, 4 if cfg.E >= 256 else 12, seed=cfg.T + 1)
+    ref = O.token_outputs(xh[toks], ids[toks], w[toks], expert, shared=shared, contract=True, dtype=np.float32)
+    mxe, rel = assert_output_close(host(bufs.y)[toks], ref["y"], "bf16", f"{name} mx y")
+    print(f"[full-mx] {name}: y max|err| {mxe:.3e} rel_fro {rel:.3e} over {len(toks)} tokens", flush=True)

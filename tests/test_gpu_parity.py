@@ -515,9 +515,11 @@ def test_mx8_shared_expert(gated):
     assert_output_close(host(y) - host(base), ref, "bf16", "mx shared")
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("cfg", MX_CASES, ids=_ids)
-def test_mx8_layer_end_to_end(cfg):
-    """Routing and scatter in one call, MXFP8 routed experts, combine, MXFP8 shared expert."""
+def test_mx8_layer_end_to_end(cfg, fused):
+    """Routing and scatter in one call, MXFP8 routed experts, combine, MXFP8 shared expert
+    (separate calls, or the routed and shared experts together through the *_and_shared_mx8 calls)."""
     layer = _layer(cfg)
     mx = wl.mx_layer_weights(layer)
     x, wr = layer["x"], layer["w_router"]
@@ -526,11 +528,18 @@ def test_mx8_layer_end_to_end(cfg):
     B.moe_route_and_scatter(x, wr, None, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                             bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
                             bufs.x_scattered, bufs.route_scatter_ws)
-    B.moe_grouped_swiglu_fc1_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"], bufs.act)
-    B.moe_grouped_fc2_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows)
-    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
     q1, s1, q2, s2, wg = mx["shared"]
-    B.moe_shared_expert_mx8(x, q1, s1, q2, s2, wg, bufs.y, bufs.shared_ws, accumulate=True)
+    if fused:
+        B.moe_grouped_swiglu_fc1_and_shared_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"],
+                                                bufs.act, x, q1, s1, bufs.act_shared)
+        B.moe_grouped_fc2_and_shared_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows,
+                                         bufs.act_shared, q2, s2, x, wg, bufs.y, bufs.shared_ws, accumulate=False)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
+    else:
+        B.moe_grouped_swiglu_fc1_mx8(bufs.x_scattered, bufs.expert_offsets, mx["W1q"], mx["W1s"], bufs.act)
+        B.moe_grouped_fc2_mx8(bufs.act, bufs.expert_offsets, mx["W2q"], mx["W2s"], bufs.y_rows)
+        B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
+        B.moe_shared_expert_mx8(x, q1, s1, q2, s2, wg, bufs.y, bufs.shared_ws, accumulate=True)
     torch.cuda.synchronize()
     ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
     check_routing(host(bufs.logits), ids, w, host(x), host(wr), None, cfg.top_k, O)
