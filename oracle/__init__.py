@@ -1,4 +1,4 @@
-"""CPU oracle for the forward pass of one MoE FFN layer.
+"""CPU oracle for one MoE FFN layer: the forward pass and the routed experts' backward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library, its
 Python binding, the timed part of the benchmark) may import or call this

@@ -1,4 +1,5 @@
-"""Plain CPU oracle for the forward pass of one MoE FFN layer (NumPy).
+"""Plain CPU oracle for the forward pass of one MoE FFN layer, and for the
+backward of its routed experts (NumPy).
 
 TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the CPU-baseline
 leg of the benchmark.  It shares no code with the HIP library and never imports it.
@@ -46,7 +47,9 @@ Readings taken where the pages are silent (each is also listed in the design not
   receive scatter_index -1 and contribute nothing;
 * the combine adds routed slots in ascending j, in the working precision;
 * the shared gate is sigmoid(x . w_gate), one scalar per token, scaling only the
-  shared branch.
+  shared branch;
+* the backward (section "Backward of the routed experts" below) holds the routes
+  fixed and follows the chain rule of the forward steps.
 
 Parity status: every function below is pinned by a CPU test against something
 other than itself (closed forms, hand-derived examples, brute force, invariants,
@@ -79,6 +82,12 @@ __all__ = [
     "e4m3_decode",
     "e8m0_decode",
     "mx_dequant",
+    "swiglu_grad",
+    "grouped_fc1_saved",
+    "scatter_grad",
+    "grouped_experts_backward",
+    "gather_sum",
+    "moe_backward",
 ]
 
 
@@ -510,4 +519,187 @@ def token_outputs(x_rows, ids_rows, w_rows, get_expert, *, shared=None,
         out["y_shared"] = ys
         y = y + ys
     out["y"] = y
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Backward of the routed experts (routes held fixed)
+# ----------------------------------------------------------------------------
+# [VEOMNI], sections "Backward grouped-GEMM launch bound", "Duplicate top-k
+# routes" and "Regression test pattern": the backward scatters the output
+# gradient into the expert-grouped rows (grad_fc2_output is moe_scatter of
+# grad_output through scatter_index), runs same-N/K grouped GEMMs for the input
+# gradients (every row of the largest group covered, not only the first
+# `tokens` rows) and same-M/N grouped GEMMs for the weight gradients (the
+# reduction runs over a group's rows), and its results must stay finite when
+# every slot of every token names the same expert.  The page gives no
+# formulas; the ones below are the chain rule applied to the forward above:
+#
+# * row r = scatter_index[t, j] receives dYs[r] = w[t, j] * dy[t], because the
+#   combine weights that row by w[t, j];
+# * the route weight's gradient is dw[t, j] = dy[t] . Ys[r]; the routes
+#   themselves are constants (no gradient flows through the top-k choice, and
+#   the softmax's own backward to the router logits is not part of this step);
+# * d[silu(g) u]/dg = u s (1 + g (1 - s)) with s = sigmoid(g), d/du = silu(g);
+# * dA = dYs W2[e]^T, dH = [dG | dU], dXs = dH W1[e]^T, dW2[e] = A^T dYs and
+#   dW1[e] = Xs^T dH over the rows of group e;
+# * x's gradient through the routed experts is the unweighted sum of the dXs
+#   rows of its k slots (the weights were applied to dYs already).
+#
+# Precision with ``contract``: values are rounded to bfloat16 where a bf16
+# implementation stores them before they feed a later product -- the fc1
+# pre-activation H_pre and the SwiGLU output A (each from the unrounded
+# fc1 result), the scattered gradient dYs (formed in float32, then rounded) and
+# the fc1 gradient dH.  Everything else is left in the working precision.
+def swiglu_grad(g, u, dA):
+    """Gradient of silu(g) * u: returns (dG, dU) = (dA u s (1 + g (1 - s)), dA silu(g)), s = sigmoid(g)."""
+    g = np.asarray(g)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-g))
+    dG = dA * u * s * (1.0 + g * (1.0 - s))
+    dU = dA * g * s
+    return dG, dU
+
+
+def grouped_fc1_saved(Xs, offsets, W1, *, contract: bool = False, dtype=np.float64,
+                      _stale_row_bound: int | None = None):
+    """fc1 of every group, keeping what the backward needs: (H_pre [R, 2I], A [R, I]).
+
+    H_pre[r] = X_s[r] W1[e] (gate columns [0, I), up columns [I, 2I)) and
+    A[r] = silu(gate) * up, both from the unrounded product; with ``contract``
+    each is then rounded to bfloat16.  Rows outside every group stay NaN.
+    """
+    Xs = np.asarray(Xs)
+    I = np.asarray(W1[0]).shape[1] // 2
+    Hp = np.full((Xs.shape[0], 2 * I), np.nan, dtype)
+    A = np.full((Xs.shape[0], I), np.nan, dtype)
+    for e, lo, hi in _group_bounds(offsets, _stale_row_bound):
+        if hi > lo:
+            h = np.asarray(Xs[lo:hi], dtype) @ np.asarray(W1[e], dtype)
+            a = silu(h[:, :I]) * h[:, I:]
+            if contract:
+                h = bf16_rne(h.astype(np.float32)).astype(dtype)
+                a = bf16_rne(a.astype(np.float32)).astype(dtype)
+            Hp[lo:hi] = h
+            A[lo:hi] = a
+    return Hp, A
+
+
+def scatter_grad(dy, Ys, scatter_index, weights, *, contract: bool = False, dtype=np.float64):
+    """Output gradient into the expert-grouped rows, and the route weights' gradient.
+
+    For every pair (t, j) with r = scatter_index[t, j] >= 0:
+    dYs[r] = w[t, j] * dy[t] and dw[t, j] = dy[t] . Ys[r].  Rows that no pair
+    names stay NaN; pairs with index -1 get dw = 0.  With ``contract`` the
+    product w * dy is formed in float32 and rounded to bfloat16.
+    """
+    dy = np.asarray(dy, dtype)
+    Ys = np.asarray(Ys, dtype)
+    si = np.asarray(scatter_index, np.int64)
+    w = np.asarray(weights)
+    T, k = si.shape
+    dYs = np.full((Ys.shape[0], dy.shape[1]), np.nan, dtype)
+    dw = np.zeros((T, k), dtype)
+    for t in range(T):
+        for j in range(k):
+            r = si[t, j]
+            if r < 0:
+                continue
+            if contract:
+                prod = np.float32(w[t, j]) * dy[t].astype(np.float32)
+                dYs[r] = bf16_rne(prod).astype(dtype)
+            else:
+                dYs[r] = np.asarray(w[t, j], dtype) * dy[t]
+            dw[t, j] = dy[t] @ Ys[r]
+    return dYs, dw
+
+
+def grouped_experts_backward(Xs, offsets, W1, W2, H_pre, A, dYs, *, contract: bool = False,
+                             dtype=np.float64, split_fc1: bool = False,
+                             _stale_row_bound: int | None = None) -> dict:
+    """Input and weight gradients of every expert over its group.
+
+    For group e (rows [offsets[e], offsets[e+1])): dA = dYs W2[e]^T, then
+    (dG, dU) = swiglu_grad(gate, up, dA) on H_pre, dH = [dG | dU],
+    dXs = dH W1[e]^T, dW2[e] = A^T dYs and dW1[e] = Xs^T dH.
+
+    ``split_fc1`` treats fc1 as two separate projections (gate weights
+    W1[e][:, :I], up weights W1[e][:, I:]): dXs = dG Wg^T + dU Wu^T and the two
+    weight gradients are computed apart and placed side by side -- the split
+    formulation that the merged one must match.  An empty group gets zero
+    weight gradients.  Rows outside every group stay NaN in dH and dXs.
+    Returns {"dA", "dH", "dXs", "dW1" [E, H, 2I], "dW2" [E, I, H]}.
+    """
+    Xs = np.asarray(Xs)
+    E = len(W1)
+    Hd = np.asarray(W1[0]).shape[0]
+    I = np.asarray(W2[0]).shape[0]
+    R = Xs.shape[0]
+    dA_all = np.full((R, I), np.nan, dtype)
+    dH_all = np.full((R, 2 * I), np.nan, dtype)
+    dXs = np.full((R, Hd), np.nan, dtype)
+    dW1 = np.zeros((E, Hd, 2 * I), dtype)
+    dW2 = np.zeros((E, I, np.asarray(W2[0]).shape[1]), dtype)
+    for e, lo, hi in _group_bounds(offsets, _stale_row_bound):
+        if hi <= lo:
+            continue
+        w1 = np.asarray(W1[e], dtype)
+        w2 = np.asarray(W2[e], dtype)
+        x = np.asarray(Xs[lo:hi], dtype)
+        dy = np.asarray(dYs[lo:hi], dtype)
+        dA = dy @ w2.T
+        hp = np.asarray(H_pre[lo:hi], dtype)
+        dG, dU = swiglu_grad(hp[:, :I], hp[:, I:], dA)
+        if contract:
+            dG = bf16_rne(dG.astype(np.float32)).astype(dtype)
+            dU = bf16_rne(dU.astype(np.float32)).astype(dtype)
+        dA_all[lo:hi] = dA
+        dH_all[lo:hi, :I] = dG
+        dH_all[lo:hi, I:] = dU
+        dW2[e] = np.asarray(A[lo:hi], dtype).T @ dy
+        if split_fc1:
+            wg, wu = w1[:, :I], w1[:, I:]
+            dXs[lo:hi] = dG @ wg.T + dU @ wu.T
+            dW1[e, :, :I] = x.T @ dG
+            dW1[e, :, I:] = x.T @ dU
+        else:
+            dH = np.concatenate([dG, dU], axis=1)
+            dXs[lo:hi] = dH @ w1.T
+            dW1[e] = x.T @ dH
+    return {"dA": dA_all, "dH": dH_all, "dXs": dXs, "dW1": dW1, "dW2": dW2}
+
+
+def gather_sum(dXs, scatter_index, *, dtype=np.float64) -> np.ndarray:
+    """dx[t] = sum over j ascending of dXs[scatter_index[t, j]] (pairs with index -1 add nothing)."""
+    si = np.asarray(scatter_index, np.int64)
+    return gather_combine(dXs, si, np.ones(si.shape, dtype), dtype=dtype)
+
+
+def moe_backward(x, W1, W2, routes, dy, *, contract: bool = False, dtype=np.float64,
+                 split_fc1: bool = False, _stale_row_bound: int | None = None) -> dict:
+    """Gradients of the routed part of the layer for fixed routes.
+
+    ``routes`` = (ids [T, k], weights [T, k]); ``dy`` [T, H] is the gradient of
+    the loss with respect to the layer output y.  Runs the forward steps
+    (scatter, fc1 keeping H_pre and A, fc2) and then the backward steps above.
+    Returns every intermediate plus dx [T, H], dW1 [E, H, 2I], dW2 [E, I, H]
+    and dweights [T, k].  ``_stale_row_bound`` exists only for the mutation
+    test: it limits every group to that many rows, as a launch bound of
+    `tokens` rows would.
+    """
+    ids = np.asarray(routes[0], np.int64)
+    w = np.asarray(routes[1])
+    E = len(W1)
+    sc = build_scatter(ids, E)
+    Xs = scatter_rows(x, sc["row_token"])
+    Hp, A = grouped_fc1_saved(Xs, sc["offsets"], W1, contract=contract, dtype=dtype,
+                              _stale_row_bound=_stale_row_bound)
+    Ys = grouped_down(A, sc["offsets"], W2, dtype=dtype, _stale_row_bound=_stale_row_bound)
+    dYs, dw = scatter_grad(dy, Ys, sc["scatter_index"], w, contract=contract, dtype=dtype)
+    g = grouped_experts_backward(Xs, sc["offsets"], W1, W2, Hp, A, dYs, contract=contract, dtype=dtype,
+                                 split_fc1=split_fc1, _stale_row_bound=_stale_row_bound)
+    out = dict(sc)
+    out.update({"Xs": Xs, "H_pre": Hp, "A": A, "Ys": Ys, "dYs": dYs, "dweights": dw})
+    out.update(g)
+    out["dx"] = gather_sum(g["dXs"], sc["scatter_index"], dtype=dtype)
     return out
