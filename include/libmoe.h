@@ -1,6 +1,7 @@
 /*
  * libmoe -- forward pass of one Mixture-of-Experts FFN layer on an AMD MI355X
- * (gfx950), as hand-written HIP kernels behind a plain C ABI.
+ * (gfx950), and the backward of its routed experts, as hand-written HIP
+ * kernels behind a plain C ABI.
  *
  * The layer (PLENA_Compiler PR #69 and PLENA_Simulator PR #97, sections
  * "Group C -- shared experts" / "Part 2 -- Shared experts"):
@@ -344,6 +345,92 @@ moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const 
                                       int32_t H, float* y_rows, const void* act_shared, const void* ws2,
                                       const void* x, const void* w_gate, int32_t T, int32_t I_s, int32_t accumulate,
                                       float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the routed experts, routes held fixed:
+ *
+ *   forward (training):  moe_build_scatter -> moe_grouped_swiglu_fc1_save -> moe_grouped_fc2
+ *                        -> moe_gather_combine
+ *   backward:            moe_scatter_grad -> moe_grouped_fc2_backward -> moe_grouped_fc1_backward
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", sections "Backward grouped-GEMM
+ * launch bound" (the fc2 output gradient is moe_scatter of the output gradient
+ * through scatter_index; the input-gradient GEMMs are same-N/K grouped GEMMs
+ * that must cover the largest group, and the weight-gradient GEMMs are
+ * same-M/N grouped GEMMs whose reduction runs over a group's rows), "Duplicate
+ * top-k routes" and "Regression test pattern" (every gradient finite when all
+ * slots of every token name one expert).  The formulas are the chain rule of
+ * the forward calls above.  Every bound comes from the realized
+ * expert_offsets, so a group of any size up to R rows is covered.  Precision:
+ * fp32 accumulation; h_pre, act, d_rows, d_h, d_w1 and d_w2 are stored as dt
+ * (bf16 round-to-nearest-even); d_x and d_topk_weights are fp32.
+ */
+
+/* moe_grouped_swiglu_fc1_save -- moe_grouped_swiglu_fc1 that also stores the
+ * pre-activation for the backward: h_pre[r] = [g | u] (gate columns [0, I),
+ * up columns [I, 2I)), h_pre [R, 2I] (dt) out.  act is computed from the
+ * unrounded g and u exactly as in moe_grouped_swiglu_fc1.  Other arguments as
+ * for moe_grouped_swiglu_fc1. */
+moe_status moe_grouped_swiglu_fc1_save(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                       const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
+                                       int32_t E, int32_t I, void* act, void* h_pre, void* stream);
+
+/*
+ * moe_scatter_grad -- output gradient into the expert-grouped rows, and the
+ * route weights' gradient (the adjoint of moe_gather_combine).
+ *
+ * For every pair (t, j) with r = scatter_index[t, j] in [0, R):
+ *   d_rows[r]         = topk_weights[t, j] * dy[t]   (product in fp32, stored as dt)
+ *   d_topk_weights[t, j] = dy[t] . y_rows[r]          (fp32, fixed summation order)
+ * Pairs with any other index get d_topk_weights 0 and write no row; rows that
+ * no pair names are not written.
+ *
+ * dy [T, H] fp32 (gradient of the layer output y), y_rows [R, H] fp32 (the
+ * moe_grouped_fc2 output of the forward), topk_weights and scatter_index
+ * [T, top_k], d_rows [R, H] (dt) out, d_topk_weights [T, top_k] fp32 out.
+ */
+moe_status moe_scatter_grad(moe_dtype dt, const float* dy, const float* y_rows, const float* topk_weights,
+                            const int32_t* scatter_index, int32_t T, int32_t H, int32_t top_k, int32_t R,
+                            void* d_rows, float* d_topk_weights, void* stream);
+
+/*
+ * moe_grouped_fc2_backward -- gradients through the down projection and SwiGLU.
+ *
+ * For every expert e and row r of its group, with da = d_rows[r] @ w2[e]^T:
+ *   d_h[r][i]     = da[i] * u * s * (1 + g * (1 - s))   (gate half; g = h_pre[r][i],
+ *   d_h[r][I + i] = da[i] * g * s                        u = h_pre[r][I + i], s = sigmoid(g))
+ *   d_w2[e]       = act[group e]^T @ d_rows[group e]     (zero for an empty expert)
+ * d_rows [R, H] (dt), act [R, I] (dt) and h_pre [R, 2I] (dt) from the forward,
+ * expert_offsets [E+1], w2 (dt) in layout wl, d_h [R, 2I] (dt) out, d_w2 (dt)
+ * out in the layout of w2 ([E, I, H] for MOE_W_KN, [E, H, I] for MOE_W_NK).
+ * Two launches: the input gradient (a same-N/K grouped GEMM, SwiGLU'
+ * in its epilogue) and the weight gradient (same-M/N).
+ */
+moe_status moe_grouped_fc2_backward(moe_dtype dt, moe_weight_layout wl, const void* d_rows, const void* act,
+                                    const void* h_pre, const int32_t* expert_offsets, const void* w2, int32_t R,
+                                    int32_t I, int32_t E, int32_t H, void* d_h, void* d_w2, void* stream);
+
+/* Workspace bytes moe_grouped_fc1_backward needs (the fp32 [R, H] input
+ * gradient of the scattered rows); 0 for invalid sizes. */
+size_t moe_grouped_fc1_backward_workspace_bytes(int32_t R, int32_t H);
+
+/*
+ * moe_grouped_fc1_backward -- gradients through the gate/up projection, and
+ * the input gradient gathered back to tokens.
+ *
+ *   d_xs[r]  = d_h[r] @ w1[e]^T                    (fp32, in the workspace)
+ *   d_x[t]   = (accumulate ? d_x[t] : 0) + sum_{j ascending} d_xs[scatter_index[t, j]]
+ *   d_w1[e]  = x_scattered[group e]^T @ d_h[group e]   (zero for an empty expert)
+ * d_h [R, 2I] (dt), x_scattered [R, H] (dt), expert_offsets [E+1], w1 (dt) in
+ * layout wl, scatter_index [T, top_k], d_x [T, H] fp32 in/out, d_w1 (dt) out in
+ * the layout of w1 ([E, H, 2I] for MOE_W_KN, [E, 2I, H] for MOE_W_NK),
+ * workspace of at least moe_grouped_fc1_backward_workspace_bytes(R, H) bytes.
+ */
+moe_status moe_grouped_fc1_backward(moe_dtype dt, moe_weight_layout wl, const void* d_h, const void* x_scattered,
+                                    const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H, int32_t E,
+                                    int32_t I, const int32_t* scatter_index, int32_t T, int32_t top_k,
+                                    int32_t accumulate, float* d_x, void* d_w1, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,6 +68,14 @@ _SIGNATURES = {
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                             _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "moe_grouped_swiglu_fc1_save": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                             _vp, _vp]),
+    "moe_scatter_grad": (_c_int, [_c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_grouped_fc2_backward": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                          _vp, _vp, _vp]),
+    "moe_grouped_fc1_backward_workspace_bytes": (_c_size, [_c_int, _c_int]),
+    "moe_grouped_fc1_backward": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
+                                          _c_int, _c_int, _c_int, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -485,3 +493,117 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         ws1, ws2, wg = shared
         moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, True, stream, layout=layout)
     return bufs
+
+
+# ------------------------------------------------------------------------------------------
+# Backward of the routed experts
+# ------------------------------------------------------------------------------------------
+def _w1_shape(E, H, I, layout):
+    return (E, 2 * I, H) if layout == MOE_W_NK else (E, H, 2 * I)
+
+
+def _w2_shape(E, H, I, layout):
+    return (E, H, I) if layout == MOE_W_NK else (E, I, H)
+
+
+def moe_grouped_swiglu_fc1_save(x_scattered, expert_offsets, w1, act, h_pre, stream=None, layout=MOE_W_KN):
+    lib = load()
+    R, H = x_scattered.shape
+    E, _, I = _fc1_sizes(w1, layout)
+    dev = x_scattered.device
+    dt = x_scattered.dtype
+    args = (_dt(x_scattered), int(layout), _ptr(x_scattered, "x_scattered"),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", dt, _w1_shape(E, H, I, layout), dev), R, H, E, I,
+            _ptr(act, "act", dt, (R, I), dev), _ptr(h_pre, "h_pre", dt, (R, 2 * I), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_save(*args))
+
+
+def moe_scatter_grad(dy, y_rows, topk_weights, scatter_index, d_rows, d_topk_weights, stream=None):
+    lib = load()
+    T, H = dy.shape
+    k = scatter_index.shape[1]
+    R = y_rows.shape[0]
+    dev = dy.device
+    args = (_dt(d_rows), _ptr(dy, "dy", torch.float32, (T, H), dev),
+            _ptr(y_rows, "y_rows", torch.float32, (R, H), dev),
+            _ptr(topk_weights, "topk_weights", torch.float32, (T, k), dev),
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev), T, H, k, R,
+            _ptr(d_rows, "d_rows", None, (R, H), dev),
+            _ptr(d_topk_weights, "d_topk_weights", torch.float32, (T, k), dev), _stream(stream, dev))
+    _check(lib.moe_scatter_grad(*args))
+
+
+def moe_grouped_fc2_backward(d_rows, act, h_pre, expert_offsets, w2, d_h, d_w2, stream=None, layout=MOE_W_KN):
+    lib = load()
+    R, I = act.shape
+    H = d_rows.shape[1]
+    E = w2.shape[0]
+    dev = act.device
+    dt = act.dtype
+    args = (_dt(act), int(layout), _ptr(d_rows, "d_rows", dt, (R, H), dev), _ptr(act, "act"),
+            _ptr(h_pre, "h_pre", dt, (R, 2 * I), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w2, "w2", dt, _w2_shape(E, H, I, layout), dev), R, I, E, H,
+            _ptr(d_h, "d_h", dt, (R, 2 * I), dev), _ptr(d_w2, "d_w2", dt, _w2_shape(E, H, I, layout), dev),
+            _stream(stream, dev))
+    _check(lib.moe_grouped_fc2_backward(*args))
+
+
+def moe_grouped_fc1_backward_workspace_bytes(R, H) -> int:
+    return int(load().moe_grouped_fc1_backward_workspace_bytes(int(R), int(H)))
+
+
+def moe_grouped_fc1_backward(d_h, x_scattered, expert_offsets, w1, scatter_index, d_x, d_w1, workspace,
+                             accumulate=False, stream=None, layout=MOE_W_KN):
+    lib = load()
+    R, H = x_scattered.shape
+    E, _, I = _fc1_sizes(w1, layout)
+    T, k = scatter_index.shape
+    dev = x_scattered.device
+    dt = x_scattered.dtype
+    args = (_dt(x_scattered), int(layout), _ptr(d_h, "d_h", dt, (R, 2 * I), dev), _ptr(x_scattered, "x_scattered"),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", dt, _w1_shape(E, H, I, layout), dev), R, H, E, I,
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev), T, k, int(bool(accumulate)),
+            _ptr(d_x, "d_x", torch.float32, (T, H), dev), _ptr(d_w1, "d_w1", dt, _w1_shape(E, H, I, layout), dev),
+            _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
+    _check(lib.moe_grouped_fc1_backward(*args))
+
+
+class MoEBackwardBuffers:
+    """Device buffers of the routed experts' training forward and backward for T tokens."""
+
+    def __init__(self, T, H, E, top_k, I, dtype, device, layout=MOE_W_KN):
+        R = T * top_k
+        f32 = torch.float32
+        self.h_pre = torch.empty((R, 2 * I), dtype=dtype, device=device)
+        self.d_rows = torch.empty((R, H), dtype=dtype, device=device)
+        self.d_topk_weights = torch.empty((T, top_k), dtype=f32, device=device)
+        self.d_h = torch.empty((R, 2 * I), dtype=dtype, device=device)
+        self.d_x = torch.empty((T, H), dtype=f32, device=device)
+        self.d_w1 = torch.empty(_w1_shape(E, H, I, layout), dtype=dtype, device=device)
+        self.d_w2 = torch.empty(_w2_shape(E, H, I, layout), dtype=dtype, device=device)
+        self.ws = torch.empty((moe_grouped_fc1_backward_workspace_bytes(R, H),), dtype=torch.uint8, device=device)
+
+
+def moe_routed_train_forward(x, W1, W2, routes, bufs, bwd, stream=None, layout=MOE_W_KN):
+    """Routed part of the layer for fed-in routes (ids, weights), keeping what
+    the backward needs: scatter -> fc1 (saving h_pre) -> fc2 -> combine into bufs.y."""
+    E = W1.shape[0]
+    ids, w = routes
+    moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                      bufs.x_scattered, bufs.scatter_ws, stream)
+    moe_grouped_swiglu_fc1_save(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, bwd.h_pre, stream, layout=layout)
+    moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream, layout=layout)
+    moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, False, stream)
+
+
+def moe_routed_backward(dy, W1, W2, topk_weights, bufs, bwd, stream=None, layout=MOE_W_KN):
+    """The three backward calls after moe_routed_train_forward: gradients into
+    bwd.d_x, bwd.d_w1, bwd.d_w2 and bwd.d_topk_weights."""
+    moe_scatter_grad(dy, bufs.y_rows, topk_weights, bufs.scatter_index, bwd.d_rows, bwd.d_topk_weights, stream)
+    moe_grouped_fc2_backward(bwd.d_rows, bufs.act, bwd.h_pre, bufs.expert_offsets, W2, bwd.d_h, bwd.d_w2, stream,
+                             layout=layout)
+    moe_grouped_fc1_backward(bwd.d_h, bufs.x_scattered, bufs.expert_offsets, W1, bufs.scatter_index, bwd.d_x,
+                             bwd.d_w1, bwd.ws, False, stream, layout=layout)

@@ -589,4 +589,134 @@ moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const 
                     fn);
 }
 
+// ------------------------------------------------------------------------------------------
+// Backward of the routed experts
+// ------------------------------------------------------------------------------------------
+moe_status moe_grouped_swiglu_fc1_save(moe_dtype dt, moe_weight_layout wl, const void* x_scattered,
+                                       const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
+                                       int32_t E, int32_t I, void* act, void* h_pre, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1_save";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(h_pre, fn, "h_pre"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  return hip_result(moe_launch::grouped_swiglu_fc1_save((int)dt, (int)wl, x_scattered, expert_offsets, E, R, w1,
+                                                        (int64_t)H * 2 * I, H, I, act, h_pre, cu_count(),
+                                                        (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_scatter_grad(moe_dtype dt, const float* dy, const float* y_rows, const float* topk_weights,
+                            const int32_t* scatter_index, int32_t T, int32_t H, int32_t top_k, int32_t R,
+                            void* d_rows, float* d_topk_weights, void* stream) {
+  const char* fn = "moe_scatter_grad";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_ptr(dy, fn, "dy"));
+  MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
+  MOE_CHECK(need_ptr(topk_weights, fn, "topk_weights"));
+  MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
+  MOE_CHECK(need_ptr(d_rows, fn, "d_rows"));
+  MOE_CHECK(need_ptr(d_topk_weights, fn, "d_topk_weights"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_topk(top_k, fn));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  return hip_result(moe_launch::scatter_grad((int)dt, dy, y_rows, topk_weights, scatter_index, T, H, top_k, R, d_rows,
+                                             d_topk_weights, (hipStream_t)stream),
+                    fn);
+}
+
+moe_status moe_grouped_fc2_backward(moe_dtype dt, moe_weight_layout wl, const void* d_rows, const void* act,
+                                    const void* h_pre, const int32_t* expert_offsets, const void* w2, int32_t R,
+                                    int32_t I, int32_t E, int32_t H, void* d_h, void* d_w2, void* stream) {
+  const char* fn = "moe_grouped_fc2_backward";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
+  MOE_CHECK(need_ptr(d_rows, fn, "d_rows"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(h_pre, fn, "h_pre"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w2, fn, "w2"));
+  MOE_CHECK(need_ptr(d_h, fn, "d_h"));
+  MOE_CHECK(need_ptr(d_w2, fn, "d_w2"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  const hipStream_t s = (hipStream_t)stream;
+  const int cus = cu_count();
+  hipError_t err = moe_launch::grouped_fc2_dgrad_swiglu((int)dt, (int)wl, d_rows, expert_offsets, E, R, w2, I, H,
+                                                        h_pre, d_h, cus, s);
+  // d_w2 in the layout of w2: [I, H] = act^T d_rows, or [H, I] = d_rows^T act.
+  if (err == hipSuccess)
+    err = wl == MOE_W_KN ? moe_launch::grouped_wgrad((int)dt, act, d_rows, expert_offsets, E, R, I, H, d_w2, cus, s)
+                         : moe_launch::grouped_wgrad((int)dt, d_rows, act, expert_offsets, E, R, H, I, d_w2, cus, s);
+  return hip_result(err, fn);
+}
+
+size_t moe_grouped_fc1_backward_workspace_bytes(int32_t R, int32_t H) {
+  if (R < 1 || H < 1) return 0;
+  return align256((size_t)R * H * sizeof(float));
+}
+
+moe_status moe_grouped_fc1_backward(moe_dtype dt, moe_weight_layout wl, const void* d_h, const void* x_scattered,
+                                    const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H, int32_t E,
+                                    int32_t I, const int32_t* scatter_index, int32_t T, int32_t top_k,
+                                    int32_t accumulate, float* d_x, void* d_w1, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_grouped_fc1_backward";
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
+  MOE_CHECK(need_ptr(d_h, fn, "d_h"));
+  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
+  MOE_CHECK(need_ptr(d_x, fn, "d_x"));
+  MOE_CHECK(need_ptr(d_w1, fn, "d_w1"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_topk(top_k, fn));
+  MOE_CHECK(need_flag(accumulate, fn, "accumulate"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
+  const size_t need = moe_grouped_fc1_backward_workspace_bytes(R, H);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  const hipStream_t s = (hipStream_t)stream;
+  const int cus = cu_count();
+  float* d_xs = (float*)workspace;
+  hipError_t err = moe_launch::grouped_fc1_dgrad((int)dt, (int)wl, d_h, expert_offsets, E, R, w1, H, I, d_xs, cus, s);
+  if (err == hipSuccess)
+    err = moe_launch::gather_combine(d_xs, scatter_index, nullptr, T, H, top_k, accumulate, d_x, s);
+  // d_w1 in the layout of w1: [H, 2I] = x_scattered^T d_h, or [2I, H] = d_h^T x_scattered.
+  if (err == hipSuccess)
+    err = wl == MOE_W_KN
+              ? moe_launch::grouped_wgrad((int)dt, x_scattered, d_h, expert_offsets, E, R, H, 2 * I, d_w1, cus, s)
+              : moe_launch::grouped_wgrad((int)dt, d_h, x_scattered, expert_offsets, E, R, 2 * I, H, d_w1, cus, s);
+  return hip_result(err, fn);
+}
+
 }  // extern "C"

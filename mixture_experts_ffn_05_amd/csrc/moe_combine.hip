@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void gather_combine_k(const f32x4* __restrict_
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
     s_idx[threadIdx.x] = scatter_index[(int64_t)t * k + threadIdx.x];
-    s_w[threadIdx.x] = weights[(int64_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = weights ? weights[(int64_t)t * k + threadIdx.x] : 1.0f;
   }
   __syncthreads();
   const int hv = H / 4;

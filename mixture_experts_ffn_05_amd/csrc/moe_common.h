@@ -203,8 +203,26 @@ hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int
                      float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
                      int accumulate, float* y, int cu_count, hipStream_t s);
 
+// weights may be null: every slot then counts with weight 1 (the backward's gather of input gradients).
 hipError_t gather_combine(const float* y_rows, const int32_t* scatter_index, const float* weights,
                           int T, int H, int top_k, int accumulate, float* y, hipStream_t s);
+
+// Backward of the routed experts (routes fixed).  wt_nk: 0 = weights stored
+// [K, N] per group as in the forward (x @ W), 1 = [N, K].
+hipError_t grouped_swiglu_fc1_save(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
+                                   const void* w1, int64_t w1_group_stride, int K, int I, void* act, void* h_pre,
+                                   int cu_count, hipStream_t s);
+hipError_t scatter_grad(int dt, const float* dy, const float* y_rows, const float* weights,
+                        const int32_t* scatter_index, int T, int H, int top_k, int R, void* d_rows, float* d_weights,
+                        hipStream_t s);
+hipError_t grouped_fc2_dgrad_swiglu(int dt, int wt_nk, const void* d_rows, const int32_t* offsets, int groups,
+                                    int rows, const void* w2, int I, int H, const void* h_pre, void* d_h,
+                                    int cu_count, hipStream_t s);
+hipError_t grouped_fc1_dgrad(int dt, int wt_nk, const void* d_h, const int32_t* offsets, int groups, int rows,
+                             const void* w1, int H, int I, float* d_xs, int cu_count, hipStream_t s);
+// out[g] = P[rows of g]^T Q[rows of g]: P [rows, M], Q [rows, N], out [groups, M, N] (element type of dt).
+hipError_t grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets, int groups, int rows, int M,
+                         int N, void* out, int cu_count, hipStream_t s);
 hipError_t shared_gate(int dt, const void* x, const void* w_gate, int T, int H, float* gate,
                        hipStream_t s);
 

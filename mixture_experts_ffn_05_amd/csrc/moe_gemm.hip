@@ -84,7 +84,13 @@ constexpr int kLds = 72;   // padded LDS row in bf16 elements (144 bytes)
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-enum Epilogue { kSwiGLU = 0, kStoreF32 = 1, kScaleAdd = 2 };
+// kSwiGLUSave: the SwiGLU epilogue that also stores the fc1 pre-activation
+// (training forward); kSwiGLUBwd: the gradient of SwiGLU applied to the
+// accumulated gradient of its output (backward through fc2).
+enum Epilogue { kSwiGLU = 0, kStoreF32 = 1, kScaleAdd = 2, kSwiGLUSave = 3, kSwiGLUBwd = 4 };
+
+// Epilogues whose staged weight columns are gate/up pairs of the same outputs.
+constexpr bool paired(int epi) { return epi == kSwiGLU || epi == kSwiGLUSave; }
 
 template <typename T>
 struct GemmParams {
@@ -105,7 +111,34 @@ struct GemmParams {
   int bt;                   // 0: b rows are k ([K, ldb], N contiguous); 1: b rows are n ([N, ldb = K], K contiguous)
   const uint8_t* sc;        // MXFP8: e8m0 scales of group 0 (b then holds e4m3 codes, [N, K] bytes)
   int64_t sc_stride;        // MXFP8: bytes between the scales of consecutive groups
+  const void* aux;          // kSwiGLUBwd: fc1 pre-activation T [rows, 2N] (gate columns, then up columns)
+  void* out2;               // kSwiGLUSave: fc1 pre-activation out, T [rows, 2N]
 };
+
+// SwiGLU output at (row, col) from the gate and up accumulators; with
+// kSwiGLUSave the two pre-activations are stored as well.
+template <int EPI, typename T>
+__device__ __forceinline__ void epi_swiglu(const GemmParams<T>& p, int64_t row, int col, float g, float u) {
+  store_from_f32((T*)p.out, row * p.N + col, swiglu(g, u));
+  if (EPI == kSwiGLUSave) {
+    T* h = (T*)p.out2 + row * 2 * p.N;
+    store_from_f32(h, col, g);
+    store_from_f32(h, p.N + col, u);
+  }
+}
+
+// Backward through SwiGLU at (row, col): `da` is the gradient of silu(g) * u.
+// dg = da * u * s * (1 + g * (1 - s)) with s = sigmoid(g), du = da * g * s;
+// they land in columns col and N + col of the output row, like g and u.
+template <typename T>
+__device__ __forceinline__ void epi_swiglu_bwd(const GemmParams<T>& p, int64_t row, int col, float da) {
+  const T* h = (const T*)p.aux + row * 2 * p.N;
+  const float g = load_as_f32(h, col), u = load_as_f32(h, p.N + col);
+  const float s = sigmoidf_(g);
+  T* d = (T*)p.out + row * 2 * p.N;
+  store_from_f32(d, col, da * u * s * (1.0f + g * (1.0f - s)));
+  store_from_f32(d, p.N + col, da * g * s);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -114,7 +147,7 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 template <int EPI>
 __device__ __forceinline__ int wave_col_base(int nb, int wn) {
-  return EPI == kSwiGLU ? (64 * nb + 32 * wn) : (64 * wn + 32 * nb);
+  return paired(EPI) ? (64 * nb + 32 * wn) : (64 * wn + 32 * nb);
 }
 
 template <int EPI>
@@ -128,7 +161,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
   const int co = tid & 15, kq = tid >> 4;
   int bcol;
   bool bcol_ok;
-  if (EPI == kSwiGLU) {
+  if (paired(EPI)) {
     const int c = co * 8;
     const int nc = n0 + (c & 63);
     bcol = (c < 64 ? 0 : p.up_off) + nc;
@@ -165,7 +198,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
         const int k = k0 + ko * 8;
         int nrow;
         bool ok;
-        if (EPI == kSwiGLU) {
+        if (paired(EPI)) {
           const int nc = n0 + (c & 63);
           nrow = (c < 64 ? 0 : p.up_off) + nc;
           ok = nc < p.N;
@@ -243,15 +276,18 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
     for (int i = 0; i < 16; ++i) {
       const int row = row0 + wm * 64 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (row >= row_end) continue;
-      if (EPI == kSwiGLU) {
+      if (paired(EPI)) {
         const int col = n0 + 32 * wn + (lane & 31);
-        if (col < p.N)
-          ((bf16_t*)p.out)[(int64_t)row * p.N + col] = (bf16_t)f32_to_bf16_rne(swiglu(acc[mb][0][i], acc[mb][1][i]));
+        if (col < p.N) epi_swiglu<EPI>(p, row, col, acc[mb][0][i], acc[mb][1][i]);
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int col = n0 + 64 * wn + 32 * nb + (lane & 31);
           if (col >= p.N) continue;
+          if (EPI == kSwiGLUBwd) {
+            epi_swiglu_bwd(p, row, col, acc[mb][nb][i]);
+            continue;
+          }
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
@@ -350,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_generic(GemmPar
   const int64_t total = (int64_t)mtiles * nt;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<kBM>(id, p.groups, nt, sOff, sPre);
-    run_tile_bf16<EPI>(p, c.g, c.row0, c.row_end, c.ntile * (EPI == kSwiGLU ? 64 : 128), sA, sB);
+    run_tile_bf16<EPI>(p, c.g, c.row0, c.row_end, c.ntile * (paired(EPI) ? 64 : 128), sA, sB);
   }
 }
 
@@ -437,7 +473,7 @@ __device__ __forceinline__ int b_swizzle(int k) { return C::kBChunks >= 16 ? 4 *
 template <int EPI, class C>
 __device__ __forceinline__ int pipe_col_base(int nb, int wn) {
   // SwiGLU: blocks [0, kNB/2) are gate columns, [kNB/2, kNB) the matching up columns.
-  return EPI == kSwiGLU
+  return paired(EPI)
              ? ((nb < C::kNB / 2 ? 0 : C::BN / 2) + wn * (C::BN / 2 / C::WN) + 32 * (nb % (C::kNB / 2)))
              : (wn * (C::BN / C::WN) + 32 * nb);
 }
@@ -571,19 +607,21 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
     for (int i = 0; i < 16; ++i) {
       const int row = row0 + wm * (C::BM / C::WM) + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (row >= row_end) continue;
-      if (EPI == kSwiGLU) {
+      if (paired(EPI)) {
 #pragma unroll
         for (int j = 0; j < C::kNB / 2; ++j) {
           const int col = n0 + wn * (C::BN / 2 / C::WN) + 32 * j + (lane & 31);
-          if (col < p.N)
-            ((bf16_t*)p.out)[(int64_t)row * p.N + col] =
-                (bf16_t)f32_to_bf16_rne(swiglu(acc[mb][j][i], acc[mb][j + C::kNB / 2][i]));
+          if (col < p.N) epi_swiglu<EPI>(p, row, col, acc[mb][j][i], acc[mb][j + C::kNB / 2][i]);
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < C::kNB; ++nb) {
           const int col = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
           if (col >= p.N) continue;
+          if (EPI == kSwiGLUBwd) {
+            epi_swiglu_bwd(p, row, col, acc[mb][nb][i]);
+            continue;
+          }
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
@@ -624,7 +662,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
       const int r = (wave * C::kBLoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
       const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
       int nrow;
-      if (EPI == kSwiGLU) {
+      if (paired(EPI)) {
         const int half = C::BN / 2;
         const int nc = n0 + r % half;
         nrow = (nc < p.N ? nc : 0) + (r < half ? 0 : p.up_off);
@@ -638,7 +676,7 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
     const int kr = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
     const int chunk = (lane % C::kBChunks) ^ b_swizzle<C>(kr);
     int col;
-    if (EPI == kSwiGLU) {
+    if (paired(EPI)) {
       const int half = C::kBChunks / 2;
       const int nc = n0 + 8 * (chunk % half);
       col = (nc < p.N ? nc : 0) + (chunk < half ? 0 : p.up_off);
@@ -685,7 +723,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
   const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave);
   const int64_t nt = p.n_tiles;
   const int64_t total = (int64_t)mtiles * nt;
-  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
     run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
@@ -711,8 +749,8 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(G
   const int64_t mts = (ps.rows + C::BM - 1) / C::BM;
   const int64_t tiles_s = mts * ps.n_tiles;
   const int64_t total = tiles_r + tiles_s;
-  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
-  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
+  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const int64_t s_before = id * tiles_s / total;
     if ((id + 1) * tiles_s / total != s_before) {
@@ -918,7 +956,7 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
   // Weight row (an n in [0, rows of the group's weight)) of staged column r;
   // columns past N read row 0 and only feed outputs that are never stored.
   auto wrow = [&](int r) -> int {
-    if (EPI == kSwiGLU) {
+    if (paired(EPI)) {
       const int half = C::BN / 2;
       const int nc = n0 + r % half;
       return (nc < p.N ? nc : 0) + (r < half ? 0 : p.up_off);
@@ -1015,7 +1053,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8(GemmPara
   const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave);
   const int64_t nt = p.n_tiles;
   const int64_t total = (int64_t)mtiles * nt;
-  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
     run_tile_mx<EPI, C, SAX>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
@@ -1037,8 +1075,8 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8_fused(Ge
   const int64_t mts = (ps.rows + C::BM - 1) / C::BM;
   const int64_t tiles_s = mts * ps.n_tiles;
   const int64_t total = tiles_r + tiles_s;
-  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
-  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
+  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const int64_t s_before = id * tiles_s / total;
     if ((id + 1) * tiles_s / total != s_before) {
@@ -1049,6 +1087,236 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8_fused(Ge
       run_tile_mx<EPI_R, C, SAX>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// Weight gradients: out[g] = P[rows of g]^T Q[rows of g] (same-M/N grouped GEMM)
+// ------------------------------------------------------------------------------------------
+// VeOmni docs "Fused MoE Kernel Notes", section "Backward grouped-GEMM launch
+// bound": the weight gradients are a grouped GEMM whose groups share the output
+// shape [M, N] and differ in reduction length -- the group's row count, which
+// comes from the realized expert_offsets like every other bound here.
+//
+// P [rows, M] and Q [rows, N] are row-major, so both operands sit in LDS like
+// the [K, N] weight tile of the forward path: a group row (the reduction index
+// k) per LDS row, M or N across it, 16-byte chunks XOR-swizzled by the row.
+// Both MFMA fragments come from two ds_read_b64_tr_b16 transpose reads each:
+// an A fragment (8 consecutive k of one output row) and a B fragment (8
+// consecutive k of one output column) have the same register layout.  A
+// group's last slice is partial unless its row count is a multiple of BK: its
+// rows past the group end are fetched from the group's last row and then
+// overwritten with zeros in LDS, so no other group's rows contribute.  A group
+// with no rows stores a zero tile.
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_>
+struct WgCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int NT = kWaves * kWave;
+  static constexpr int kPChunks = BM / 8, kQChunks = BN / 8;   // 16-byte chunks per LDS row
+  static constexpr int kPRow = BM * 2, kQRow = BN * 2;           // LDS row bytes
+  static constexpr int kPStage = BK * kPRow, kQStage = BK * kQRow;
+  static constexpr int kStage = kPStage + kQStage;
+  static constexpr int kPLoads = kPStage / 1024 / kWaves, kQLoads = kQStage / 1024 / kWaves;
+  static constexpr int kLoads = kPLoads + kQLoads;
+  static constexpr int kPRowsPerLoad = 64 / kPChunks, kQRowsPerLoad = 64 / kQChunks;
+  static constexpr int kMB = BM / WM / 32, kNB = BN / WN / 32;
+  static constexpr int kKS = BK / 16;
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kFit = (160 * 1024) / (kLds + 1024);
+  static constexpr int kWgsPerCu = kFit < 1 ? 1 : (kFit > 4 ? 4 : kFit);
+  static_assert(kPChunks >= 8 && kQChunks >= 8 && kPChunks <= 64 && kQChunks <= 64, "tile widths 64..512");
+  static_assert(kPStage % (1024 * kWaves) == 0 && kQStage % (1024 * kWaves) == 0,
+                "slices must split into 1 KiB loads per wave");
+  static_assert(kMB >= 1 && kNB >= 1, "wave tile must hold whole 32x32 blocks");
+};
+
+typedef WgCfg<128, 128, 64, 2, 2, 2> WgCfg1;
+typedef WgCfg<256, 256, 64, 2, 4, 2> WgCfg2;   // 8 waves
+#ifndef MOE_WGRAD_VARIANT
+#define MOE_WGRAD_VARIANT 1
+#endif
+typedef typename std::conditional<MOE_WGRAD_VARIANT == 2, WgCfg2, WgCfg1>::type WgCfgUsed;
+
+struct WgParams {
+  const bf16_t* p;          // [rows, M]
+  const bf16_t* q;          // [rows, N]
+  const int32_t* offsets;   // [groups + 1]
+  int groups, rows, M, N;
+  bf16_t* out;              // [groups, M, N]
+  int m_tiles, n_tiles;
+};
+
+// Swizzle of a k-major tile with CHUNKS 16-byte chunks per row (see a_swizzle/b_swizzle).
+template <int CHUNKS>
+__device__ __forceinline__ int kn_swizzle(int k) { return CHUNKS >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+
+// MFMA fragment of the 32 columns [c_blk, c_blk + 32) of a k-major LDS tile,
+// k rows [16 ks, 16 ks + 16): lane L gets column c_blk + L % 32, k = 8 (L / 32) .. + 7.
+template <int CHUNKS>
+__device__ __forceinline__ u32x4 kn_frag(const unsigned char* __restrict__ tile, int c_blk, int ks) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, s16 = lane & 15;
+  const int row = 16 * ks + 8 * (grp >> 1) + (s16 >> 2);
+  const int c0 = c_blk + 16 * (grp & 1);
+  const int chunk = (c0 / 8 + ((s16 & 3) >> 1)) ^ kn_swizzle<CHUNKS>(s16 >> 2);
+  const unsigned char* ptr = tile + row * (16 * CHUNKS) + chunk * 16 + (s16 & 1) * 8;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * 16 * CHUNKS));
+  return u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+}
+
+// Direct loads of one slice (rows row0 .. row0 + BK - 1 of the group, clamped
+// to its last row) of the P and Q tiles into ring stage `st`.
+template <class C>
+__device__ __forceinline__ void wg_issue(unsigned char* __restrict__ st, const WgParams& p, int row0, int last_row,
+                                         const int* p_kr, const int* p_col, const int* q_kr, const int* q_col) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < C::kPLoads; ++i) {
+    const int row = min(row0 + p_kr[i], last_row);
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.p + (int64_t)row * p.M + p_col[i]),
+                                     MOE_LDS(void, st + (wave * C::kPLoads + i) * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < C::kQLoads; ++i) {
+    const int row = min(row0 + q_kr[i], last_row);
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.q + (int64_t)row * p.N + q_col[i]),
+                                     MOE_LDS(void, st + C::kPStage + (wave * C::kQLoads + i) * 1024), 16, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void wg_compute(const unsigned char* __restrict__ st, f32x16 (&acc)[C::kMB][C::kNB],
+                                           int wm, int wn) {
+  const unsigned char* Ps = st;
+  const unsigned char* Qs = st + C::kPStage;
+  u32x4 af[2][C::kMB], bf[2][C::kNB];
+  auto read = [&](int ks, u32x4 (&a)[C::kMB], u32x4 (&b)[C::kNB]) {
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb) a[mb] = kn_frag<C::kPChunks>(Ps, wm * (C::BM / C::WM) + 32 * mb, ks);
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb) b[nb] = kn_frag<C::kQChunks>(Qs, wn * (C::BN / C::WN) + 32 * nb, ks);
+  };
+  read(0, af[0], bf[0]);
+#pragma unroll
+  for (int ks = 0; ks < C::kKS; ++ks) {
+    if (ks + 1 < C::kKS) read(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+#pragma unroll
+    for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb]);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void run_tile_wgrad(const WgParams& p, int g, int lo, int hi, int m0, int n0,
+                                               unsigned char* __restrict__ smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int cnt = hi - lo;
+  const int nk = (cnt + C::BK - 1) / C::BK;
+
+  // Per-lane slice row and source column of each direct load (columns past
+  // M or N read column 0; they only feed outputs that are never stored).
+  int p_kr[C::kPLoads], p_col[C::kPLoads], q_kr[C::kQLoads], q_col[C::kQLoads];
+#pragma unroll
+  for (int i = 0; i < C::kPLoads; ++i) {
+    const int kr = (wave * C::kPLoads + i) * C::kPRowsPerLoad + lane / C::kPChunks;
+    const int chunk = (lane % C::kPChunks) ^ kn_swizzle<C::kPChunks>(kr);
+    const int col = m0 + 8 * chunk;
+    p_kr[i] = kr;
+    p_col[i] = col < p.M ? col : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < C::kQLoads; ++i) {
+    const int kr = (wave * C::kQLoads + i) * C::kQRowsPerLoad + lane / C::kQChunks;
+    const int chunk = (lane % C::kQChunks) ^ kn_swizzle<C::kQChunks>(kr);
+    const int col = n0 + 8 * chunk;
+    q_kr[i] = kr;
+    q_col[i] = col < p.N ? col : 0;
+  }
+
+  f32x16 acc[C::kMB][C::kNB];
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+  const int last_row = hi - 1;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) wg_issue<C>(smem + s * C::kStage, p, lo + s * C::BK, last_row, p_kr, p_col, q_kr, q_col);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    unsigned char* st = smem + (kt % C::STAGES) * C::kStage;
+    const int valid = cnt - kt * C::BK;
+    if (valid < C::BK) {
+      // Last, partial slice (nothing else in flight): zero its rows past the group end.
+      const int p0 = valid * C::kPRow, q0 = valid * C::kQRow;
+      for (int b = p0 + tid * 16; b < C::kPStage; b += C::NT * 16) *(u32x4*)(st + b) = u32x4{0u, 0u, 0u, 0u};
+      for (int b = q0 + tid * 16; b < C::kQStage; b += C::NT * 16)
+        *(u32x4*)(st + C::kPStage + b) = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier();
+    }
+    const int kn = kt + C::STAGES - 1;
+    if (kn < nk)
+      wg_issue<C>(smem + (kn % C::STAGES) * C::kStage, p, lo + kn * C::BK, last_row, p_kr, p_col, q_kr, q_col);
+    wg_compute<C>(st, acc, wm, wn);
+  }
+  lds_barrier();  // every wave is done with the ring before the next tile refills it
+
+  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
+  bf16_t* out = p.out + (int64_t)g * p.M * p.N;
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb) {
+      const int n = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * (C::BM / C::WM) + 32 * mb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (m < p.M) out[(int64_t)m * p.N + n] = (bf16_t)f32_to_bf16_rne(acc[mb][nb][i]);
+      }
+    }
+}
+
+// Tile ids run group-major, then M tile, then N tile; consecutive ids share a
+// group's rows and land on one XCD.
+template <class C>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_wgrad_bf16(WgParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int64_t per_group = (int64_t)p.m_tiles * p.n_tiles;
+  const int64_t total = per_group * p.groups;
+  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
+    const int g = (int)(id / per_group);
+    const int rem = (int)(id % per_group);
+    const int lo = min(max(p.offsets[g], 0), p.rows);
+    const int hi = max(min(max(p.offsets[g + 1], 0), p.rows), lo);
+    run_tile_wgrad<C>(p, g, lo, hi, (rem / p.n_tiles) * C::BM, (rem % p.n_tiles) * C::BN, smem);
+  }
+}
+
+// float32 weight gradients: one thread per output element, rows of its group in order.
+__global__ __launch_bounds__(256) void grouped_wgrad_f32(const float* __restrict__ P, const float* __restrict__ Q,
+                                                        const int32_t* __restrict__ offsets, int groups, int rows,
+                                                        int M, int N, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)groups * M * N) return;
+  const int g = (int)(i / ((int64_t)M * N));
+  const int64_t mn = i % ((int64_t)M * N);
+  const int m = (int)(mn / N), n = (int)(mn % N);
+  const int lo = min(max(offsets[g], 0), rows);
+  const int hi = max(min(max(offsets[g + 1], 0), rows), lo);
+  float v = 0.f;
+  for (int r = lo; r < hi; ++r) v = fmaf(P[(int64_t)r * M + m], Q[(int64_t)r * N + n], v);
+  out[i] = v;
 }
 
 // float32 path: one thread per output element.
@@ -1073,17 +1341,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmParams<float> p) {
   const float* ar = p.a + (int64_t)row * p.K;
   // element (k, n) of the group's weight
   auto w = [&](int k, int n) { return p.bt ? bg[(int64_t)n * p.ldb + k] : bg[(int64_t)k * p.ldb + n]; };
-  if (EPI == kSwiGLU) {
+  if (paired(EPI)) {
     float gs = 0.f, us = 0.f;
     for (int k = 0; k < p.K; ++k) {
       const float av = ar[k];
       gs = fmaf(av, w(k, col), gs);
       us = fmaf(av, w(k, p.up_off + col), us);
     }
-    ((float*)p.out)[(int64_t)row * p.N + col] = swiglu(gs, us);
+    epi_swiglu<EPI>(p, row, col, gs, us);
   } else {
     float v = 0.f;
     for (int k = 0; k < p.K; ++k) v = fmaf(ar[k], w(k, col), v);
+    if (EPI == kSwiGLUBwd) {
+      epi_swiglu_bwd(p, row, col, v);
+      return;
+    }
     float* o = (float*)p.out + (int64_t)row * p.N + col;
     if (EPI == kStoreF32) {
       *o = v;
@@ -1113,7 +1385,7 @@ hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
       reinterpret_cast<const void*>(&grouped_gemm_bf16_pipe<EPI, C, ROLE, BT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (attr != hipSuccess) return attr;
-  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   p.n_tiles = (p.N + out_cols - 1) / out_cols;
   const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
   const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
@@ -1128,7 +1400,7 @@ hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
       reinterpret_cast<const void*>(&grouped_gemm_mx8<EPI, C, SAX, ROLE>), hipFuncAttributeMaxDynamicSharedMemorySize,
       C::kLds);
   if (attr != hipSuccess) return attr;
-  const int out_cols = EPI == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   p.n_tiles = (p.N + out_cols - 1) / out_cols;
   const int64_t ub_m = (int64_t)p.rows / C::BM + (p.groups < p.rows ? p.groups : p.rows);
   const int grid = persistent_grid(ub_m * p.n_tiles, cu_count * C::kWgsPerCu);
@@ -1143,8 +1415,8 @@ hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu
       reinterpret_cast<const void*>(&grouped_gemm_mx8_fused<EPI_R, EPI_S, C, SAX>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (attr != hipSuccess) return attr;
-  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
-  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
+  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
   pr.n_tiles = (pr.N + out_r - 1) / out_r;
   ps.n_tiles = (ps.N + out_s - 1) / out_s;
   const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
@@ -1231,7 +1503,7 @@ int64_t rows_per_active_group(const GemmParams<bf16_t>& p) {
 constexpr int64_t kDecodeRows = 32;
 
 template <int EPI>
-constexpr int decode_variant() { return EPI == kSwiGLU ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
+constexpr int decode_variant() { return paired(EPI) ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
 
 template <int EPI>
 int pick_pipe_variant(const GemmParams<bf16_t>& p) {
@@ -1239,7 +1511,7 @@ int pick_pipe_variant(const GemmParams<bf16_t>& p) {
   if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   if (rows_per_group >= 512) return 8;
-  return EPI == kSwiGLU ? MOE_MID_FC1 : 1;
+  return paired(EPI) ? MOE_MID_FC1 : 1;
 }
 
 template <int EPI_R, int EPI_S, class C, bool BT>
@@ -1249,8 +1521,8 @@ hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_cou
       reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (attr != hipSuccess) return attr;
-  const int out_r = EPI_R == kSwiGLU ? C::BN / 2 : C::BN;
-  const int out_s = EPI_S == kSwiGLU ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
+  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
   pr.n_tiles = (pr.N + out_r - 1) / out_r;
   ps.n_tiles = (ps.N + out_s - 1) / out_s;
   const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
@@ -1276,7 +1548,7 @@ hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16
   else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
            ps.K % 128 == 0)
     v = decode_variant<EPI_R>();
-  else if (EPI_R == kSwiGLU)
+  else if (paired(EPI_R))
     v = MOE_MID_FC1;
   if (pr.bt)
     return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), true>(pr, ps, cu_count, s); });
@@ -1292,7 +1564,7 @@ hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
     return with_cfg(pick_pipe_variant<EPI>(p),
                     [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, false>(p, cu_count, s); });
   }
-  p.n_tiles = EPI == kSwiGLU ? (p.N + 63) / 64 : (p.N + 127) / 128;
+  p.n_tiles = paired(EPI) ? (p.N + 63) / 64 : (p.N + 127) / 128;
   const int grid = persistent_grid(upper_row_tiles(p.rows, p.groups) * p.n_tiles, 2 * cu_count);
   hipLaunchKernelGGL((grouped_gemm_bf16_generic<EPI, ROLE>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
@@ -1424,6 +1696,91 @@ hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, 
   GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2q, 0,
                         I_s, 0, y, gate, accumulate, 0, 1, (const uint8_t*)ws2s, 0};
   return launch_mx8_fused<kStoreF32, kScaleAdd, kScaleK>(pr, ps, cu_count, s);
+}
+
+// Training forward of fc1: the SwiGLU output plus the pre-activation
+// h_pre [rows, 2I] (gate columns, then up columns) in the element type.
+hipError_t grouped_swiglu_fc1_save(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
+                                   const void* w1, int64_t w1_group_stride, int K, int I, void* act, void* h_pre,
+                                   int cu_count, hipStream_t s) {
+  using namespace moe;
+  const int ldb = bt ? K : 2 * I;
+  if (dt == 1) {
+    GemmParams<bf16_t> p{(const bf16_t*)a, offsets, groups, rows, K, I, (const bf16_t*)w1, w1_group_stride,
+                         ldb, I, act, nullptr, 0, 0, bt};
+    p.out2 = h_pre;
+    return launch_bf16<kSwiGLUSave, 0>(p, cu_count, s);
+  }
+  GemmParams<float> p{(const float*)a, offsets, groups, rows, K, I, (const float*)w1, w1_group_stride,
+                      ldb, I, act, nullptr, 0, 0, bt};
+  p.out2 = h_pre;
+  const int64_t n = (int64_t)rows * I;
+  hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLUSave>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// Input gradient through fc2 and SwiGLU: d_h = SwiGLU'(h_pre) * (d_rows W2^T),
+// d_rows [rows, H], W2 per group [I, H] (wt_nk == 0) or [H, I] (wt_nk == 1).
+hipError_t grouped_fc2_dgrad_swiglu(int dt, int wt_nk, const void* d_rows, const int32_t* offsets, int groups,
+                                    int rows, const void* w2, int I, int H, const void* h_pre, void* d_h,
+                                    int cu_count, hipStream_t s) {
+  using namespace moe;
+  // As a GEMM with reduction H and I output columns, W2 [I, H] is the [N, K]
+  // layout and W2 [H, I] the [K, N] layout.
+  const int bt = wt_nk ? 0 : 1;
+  const int ldb = bt ? H : I;
+  if (dt == 1) {
+    GemmParams<bf16_t> p{(const bf16_t*)d_rows, offsets, groups, rows, H, I, (const bf16_t*)w2, (int64_t)I * H,
+                         ldb, 0, d_h, nullptr, 0, 0, bt};
+    p.aux = h_pre;
+    return launch_bf16<kSwiGLUBwd, 2>(p, cu_count, s);
+  }
+  GemmParams<float> p{(const float*)d_rows, offsets, groups, rows, H, I, (const float*)w2, (int64_t)I * H,
+                      ldb, 0, d_h, nullptr, 0, 0, bt};
+  p.aux = h_pre;
+  const int64_t n = (int64_t)rows * I;
+  hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLUBwd>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// Input gradient through fc1: d_xs [rows, H] (float32) = d_h W1^T, d_h
+// [rows, 2I], W1 per group [H, 2I] (wt_nk == 0) or [2I, H] (wt_nk == 1).
+hipError_t grouped_fc1_dgrad(int dt, int wt_nk, const void* d_h, const int32_t* offsets, int groups, int rows,
+                             const void* w1, int H, int I, float* d_xs, int cu_count, hipStream_t s) {
+  using namespace moe;
+  const int bt = wt_nk ? 0 : 1;
+  const int ldb = bt ? 2 * I : H;
+  if (dt == 1) {
+    GemmParams<bf16_t> p{(const bf16_t*)d_h, offsets, groups, rows, 2 * I, H, (const bf16_t*)w1,
+                         (int64_t)2 * I * H, ldb, 0, d_xs, nullptr, 0, 0, bt};
+    return launch_bf16<kStoreF32, 2>(p, cu_count, s);
+  }
+  GemmParams<float> p{(const float*)d_h, offsets, groups, rows, 2 * I, H, (const float*)w1, (int64_t)2 * I * H,
+                      ldb, 0, d_xs, nullptr, 0, 0, bt};
+  const int64_t n = (int64_t)rows * H;
+  hipLaunchKernelGGL(grouped_gemm_f32<kStoreF32>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets, int groups, int rows, int M,
+                         int N, void* out, int cu_count, hipStream_t s) {
+  using namespace moe;
+  if (dt == 1) {
+    typedef WgCfgUsed C;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16<C>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (attr != hipSuccess) return attr;
+    WgParams p{(const bf16_t*)P, (const bf16_t*)Q, offsets, groups, rows, M, N, (bf16_t*)out,
+               (M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN};
+    const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles * groups;
+    const int grid = persistent_grid(tiles, cu_count * C::kWgsPerCu);
+    hipLaunchKernelGGL(grouped_wgrad_bf16<C>, dim3(grid), dim3(C::NT), C::kLds, s, p);
+    return hipGetLastError();
+  }
+  const int64_t n = (int64_t)groups * M * N;
+  hipLaunchKernelGGL(grouped_wgrad_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (const float*)P,
+                     (const float*)Q, offsets, groups, rows, M, N, (float*)out);
+  return hipGetLastError();
 }
 
 }  // namespace moe_launch

@@ -172,6 +172,40 @@ def test_fused_shared_calls_validation(lib):
     assert "x (needed for the gate)" in _err(lib)
 
 
+def test_backward_validation(lib):
+    assert lib.moe_grouped_swiglu_fc1_save(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, None, None) == 1
+    assert "h_pre must not be NULL" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_save(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 100, FAKE, FAKE, None) == 2
+    assert lib.moe_scatter_grad(1, FAKE, FAKE, FAKE, FAKE, 4, 16, 0, 8, FAKE, FAKE, None) == 1
+    assert "top_k must be positive" in _err(lib)
+    assert lib.moe_scatter_grad(1, FAKE, None, FAKE, FAKE, 4, 16, 2, 8, FAKE, FAKE, None) == 1
+    assert "y_rows" in _err(lib)
+    assert lib.moe_scatter_grad(1, FAKE, FAKE, FAKE, FAKE, 4, 12, 2, 8, FAKE, FAKE, None) == 2
+    assert lib.moe_scatter_grad(1, FAKE, FAKE, FAKE, FAKE, 4, 16, 2, 0, FAKE, FAKE, None) == 1
+    assert lib.moe_grouped_fc2_backward(1, 0, FAKE, FAKE, None, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, None) == 1
+    assert "h_pre" in _err(lib)
+    assert lib.moe_grouped_fc2_backward(1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, FAKE, None) == 1
+    assert "weight layout" in _err(lib)
+    assert lib.moe_grouped_fc2_backward(1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 128, 8, 256, FAKE, None, None) == 1
+    assert "d_w2" in _err(lib)
+    need = lib.moe_grouped_fc1_backward_workspace_bytes(256, 64)
+    assert need >= 256 * 64 * 4
+    assert lib.moe_grouped_fc1_backward_workspace_bytes(0, 64) == 0
+
+    def fc1(**kw):
+        a = dict(wl=0, H=64, I=128, k=2, acc=0, ws=FAKE, wsb=need, dx=FAKE)
+        a.update(kw)
+        return lib.moe_grouped_fc1_backward(1, a["wl"], FAKE, FAKE, FAKE, FAKE, 256, a["H"], 8, a["I"], FAKE, 128,
+                                            a["k"], a["acc"], a["dx"], FAKE, a["ws"], a["wsb"], None)
+
+    assert fc1(wsb=need - 1) == 3 and "workspace needs" in _err(lib)
+    assert fc1(ws=None) == 3
+    assert fc1(acc=2) == 1 and "accumulate" in _err(lib)
+    assert fc1(dx=None) == 1 and "d_x" in _err(lib)
+    assert fc1(I=100) == 2
+    assert fc1(k=33) == 2
+
+
 def test_build_compiles_all_kernels_for_gfx950():
     import __graft_entry__ as ge
     ge.build()
