@@ -17,6 +17,11 @@ The CPU baseline runs the NumPy oracle (float32, bf16 contract mode) over the
 first --cpu-sample tokens of the same workload on the host cores, after the
 GPU timing, and compares the GPU's output on those tokens with it; a parity
 failure makes the run exit non-zero.
+
+With --backward, one step is instead the backward of the routed experts for the
+routes a forward pass realized (moe_scatter_grad, moe_grouped_fc2_backward,
+moe_grouped_fc1_backward), with the forward's saved tensors resident; the
+roofline object covers the moe_grouped_fc1_backward call.
 """
 
 from __future__ import annotations
@@ -84,19 +89,19 @@ def roofline(flops, nbytes, seconds):
             "frac": round(a / PEAK_HBM_GBPS, 4)}
 
 
-def committed_traffic(workload):
-    """Calibrated HBM bytes per dispatch of the dominant kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on a different kernel source."""
-    import glob
+def committed_traffic(workload, backward=False):
+    """Calibrated HBM bytes of one timed call from the committed rocprofv3 counter
+    summary (profiles/hbm_counters_<workload>[_backward]_pmc.md), or None if
+    absent or taken on a different kernel source."""
     import re
     from mixture_experts_ffn_05_amd import prof_summary
-    for path in glob.glob(os.path.join(ROOT, "profiles", f"*{workload}*pmc*.md")):
-        m = re.search(r"^TRAFFIC_JSON (.*)$", open(path).read(), re.M)
-        if not m:
-            continue
-        rec = json.loads(m.group(1))
-        if rec and rec.get("gemm_source_hash") == prof_summary.kernel_source_hash():
-            return rec
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}{'_backward' if backward else ''}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^TRAFFIC_JSON (.*)$", open(path).read(), re.M)
+    rec = json.loads(m.group(1)) if m else None
+    if rec and rec.get("gemm_source_hash") == prof_summary.kernel_source_hash():
+        return rec
     return None
 
 
@@ -255,6 +260,167 @@ def cpu_baseline(layer, cfg, bufs, sample_tokens):
     return base, parity
 
 
+BWD_CALLS = ("scatter_grad", "fc2_backward", "fc1_backward")
+
+
+def backward_work(cfg, counts):
+    """FLOPs and algorithmic bytes of the three backward calls for the realized routes."""
+    T, H, E, I = cfg.T, cfg.H, cfg.E, cfg.I
+    R = int(counts.sum())
+    active = int((counts > 0).sum())
+    el = 2 if cfg.dtype == "bf16" else 4
+    k = cfg.top_k
+    scat_bytes = T * H * 4 + R * H * 4 + R * H * el + 3 * T * k * 4            # dy, y_rows, d_rows, index/weights
+    fc2_flops = 4.0 * R * H * I                                                 # dgrad + wgrad
+    fc2_bytes = (active * I * H * el + R * H * el + 2 * R * 2 * I * el          # W2, d_rows, h_pre, d_h (dgrad)
+                 + R * I * el + R * H * el + E * I * H * el)                    # act, d_rows, d_w2 (wgrad)
+    fc1_flops = 8.0 * R * H * I                                                 # dgrad + wgrad
+    fc1_bytes = (active * H * 2 * I * el + R * 2 * I * el + R * H * 4           # W1, d_h, d_xs (dgrad)
+                 + R * H * 4 + T * H * 4                                        # gather
+                 + R * H * el + R * 2 * I * el + E * H * 2 * I * el)            # x_s, d_h, d_w1 (wgrad)
+    return {"R": R, "active_experts": active, "scatter_bytes": scat_bytes, "fc2_flops": fc2_flops,
+            "fc2_bytes": fc2_bytes, "fc1_flops": fc1_flops, "fc1_bytes": fc1_bytes,
+            "flops": fc1_flops + fc2_flops, "bytes": scat_bytes + fc1_bytes + fc2_bytes}
+
+
+def run_backward_step(layer, bufs, bwd, dy, events=None):
+    lay = layer["layout"]
+    rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+    rec(0)
+    B.moe_scatter_grad(dy, bufs.y_rows, bufs.topk_weights, bufs.scatter_index, bwd.d_rows, bwd.d_topk_weights)
+    rec(1)
+    B.moe_grouped_fc2_backward(bwd.d_rows, bufs.act, bwd.h_pre, bufs.expert_offsets, layer["W2"], bwd.d_h, bwd.d_w2,
+                               layout=lay)
+    rec(2)
+    B.moe_grouped_fc1_backward(bwd.d_h, bufs.x_scattered, bufs.expert_offsets, layer["W1"], bufs.scatter_index,
+                               bwd.d_x, bwd.d_w1, bwd.ws, False, layout=lay)
+    rec(3)
+
+
+def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens):
+    """Time the oracle's backward on the first `sample_tokens` tokens (their GPU
+    routes) and check the GPU's d_x and route-weight gradients on them: both
+    depend on a token's own rows only, so they are exact on a sample."""
+    import threadpoolctl
+    from oracle import moe_oracle as O
+
+    S = min(sample_tokens, cfg.T)
+    f = lambda t: t.detach().float().cpu().numpy()
+    fw = (lambda t: np.ascontiguousarray(f(t).T)) if layer["layout"] == B.MOE_W_NK else f
+    log(f"cpu baseline (backward): copying inputs for {S} tokens to the host")
+    x = f(layer["x"][:S])
+    W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
+    W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
+    ids = bufs.topk_ids[:S].cpu().numpy()
+    w = bufs.topk_weights[:S].cpu().numpy()
+    dys = f(dy[:S])
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    log(f"cpu baseline (backward): oracle over {S} tokens with {threads} BLAS threads")
+    runs = []
+    while True:
+        t0 = time.perf_counter()
+        ref = O.moe_backward(x, W1, W2, (ids, w), dys, contract=True, dtype=np.float32)
+        runs.append(time.perf_counter() - t0)
+        if len(runs) >= 5 or sum(runs) >= 10.0:
+            break
+    dt = float(np.median(runs))
+    log(f"cpu baseline (backward): {len(runs)} runs, median {dt:.2f} s")
+    parity = {}
+    ok = True
+    for name, gpu, r in (("d_x", f(bwd.d_x[:S]), ref["dx"]), ("d_topk_weights", f(bwd.d_topk_weights[:S]),
+                                                               ref["dweights"])):
+        d = gpu.astype(np.float64) - r
+        mx = float(np.abs(d).max() / max(np.abs(r).max(), 1e-30))
+        rel = float(np.linalg.norm(d) / max(np.linalg.norm(r), 1e-30))
+        parity[name] = {"max_err_over_max_ref": mx, "rel_fro_err": rel}
+        ok = ok and np.isfinite(gpu).all() and mx <= 2e-2 and rel <= 1e-2
+    parity["tokens_compared"] = S
+    parity["pass"] = bool(ok)
+    base = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload with their GPU routes: routed "
+                      f"experts' training forward and backward (moe_backward, NumPy float32, bf16 storage "
+                      f"rounding); median of {len(runs)} runs ({', '.join(f'{r:.2f}' for r in runs)} s)"}
+    return base, parity
+
+
+def bench_backward(args, cfg, layer, bias_t, dev):
+    lay = layer["layout"]
+    x = layer["x"]
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, 0, x.dtype, dev)
+    bwd = B.MoEBackwardBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, x.dtype, dev, lay)
+    # training forward of the routed experts, routes from the router
+    B.moe_route_and_scatter(x, layer["w_router"], bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
+                            bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
+                            bufs.x_scattered, bufs.route_scatter_ws)
+    B.moe_grouped_swiglu_fc1_save(bufs.x_scattered, bufs.expert_offsets, layer["W1"], bufs.act, bwd.h_pre,
+                                  layout=lay)
+    B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, layer["W2"], bufs.y_rows, layout=lay)
+    B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    dy = (torch.randn((cfg.T, cfg.H), generator=g, dtype=torch.float32) / np.sqrt(cfg.H)).to(dev)
+    torch.cuda.synchronize()
+    counts = np.diff(bufs.expert_offsets.cpu().numpy())
+    for _ in range(args.warmup):
+        run_backward_step(layer, bufs, bwd, dy)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_CALLS) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_backward_step(layer, bufs, bwd, dy, ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, c in enumerate(BWD_CALLS)}
+    log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
+    work = backward_work(cfg, counts)
+    roof = roofline(work["fc1_flops"], work["fc1_bytes"], per_call["fc1_backward"] / 1e3)
+    tr = committed_traffic(cfg.name, backward=True) if lay == B.MOE_W_KN else None
+    roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
+    roof["traffic_unit"] = "GB per fc1_backward call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    roof["kernel"] = ("fc1_backward call = grouped_gemm_bf16_pipe<StoreF32, ROLE 2> (input gradient) + "
+                      "gather_combine_k + grouped_wgrad_bf16<ROLE 1> (weight gradient)")
+    step_s = ms_per_step / 1e3
+    t_roof = max(work["flops"] / (PEAK_BF16_TFLOPS * 1e12), work["bytes"] / (PEAK_HBM_GBPS * 1e9))
+    result = {
+        "metric": "MoE-layer backward (routed experts) tokens/s",
+        "value": round(cfg.T / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normals; random-init weights of the layer shape; dy seeded normal / sqrt(H))",
+        "config": {"workload": cfg.name, "pass": "backward of the routed experts (routes fixed)", "T": cfg.T,
+                   "H": cfg.H, "E": cfg.E, "top_k": cfg.top_k, "I": cfg.I, "routing": cfg.skew or "natural",
+                   "shared_expert": "not included", "realized_rows_per_expert": counts.tolist()},
+        "roofline": roof,
+        "step": {"flops": work["flops"], "bytes_alg": work["bytes"],
+                 "tflops": round(work["flops"] / step_s / 1e12, 2),
+                 "gbps_alg": round(work["bytes"] / step_s / 1e9, 1),
+                 "frac_roofline": round(t_roof / step_s, 4), "roofline_ms": round(t_roof * 1e3, 4)},
+        "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
+        "weight_layout": "[N, K] per expert (torch.nn.Linear)" if args.layout == "nk" else "[K, N] per expert",
+        "cpu_baseline": None,
+    }
+    rc = 0
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline_backward(layer, cfg, bufs, bwd, dy, args.cpu_sample or 512)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+        if not parity["pass"]:
+            log(f"PARITY FAILURE: {parity}")
+            rc = 1
+    print(json.dumps(result), flush=True)
+    sys.exit(rc)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +428,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="scout", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens in the CPU-baseline sample (default 2048 for the forward, 512 for --backward)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step into a HIP graph and time graph replays (launch-bound decode shapes)")
     ap.add_argument("--shared", choices=("fused", "overlap"), default="fused",
@@ -274,6 +441,9 @@ def main():
     ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
                     help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default: measured "
                          "as fast or faster on every workload), nk = [N, K] (torch.nn.Linear layout)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the routed experts (for the routes a forward realized) instead of "
+                         "the forward")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -316,6 +486,12 @@ def main():
         torch.cuda.synchronize()
         log(f"copy reference: {n} bytes read and {n} bytes written by one device copy")
         del src, dst
+
+    if args.backward:
+        if args.weights != "bf16" or args.graph:
+            print("--backward runs with bf16 weights and eager launches", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, cfg, layer, bias_t, dev)
 
     mode = args.shared
     if not cfg.I_s:
@@ -369,7 +545,7 @@ def main():
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
-    tr = committed_traffic(cfg.name) if mode != "mx" else None
+    tr = committed_traffic(cfg.name) if mode != "mx" and args.layout == "kn" else None
     roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per fc1 call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = work["fc1_bytes"]
@@ -433,7 +609,7 @@ def main():
     }
     rc = 0
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline(layer, cfg, bufs, args.cpu_sample)
+        base, parity = cpu_baseline(layer, cfg, bufs, args.cpu_sample or 2048)
         result["cpu_baseline"] = base
         result["parity"] = parity
         if not parity["pass"]:

@@ -665,8 +665,8 @@ moe_status moe_grouped_fc2_backward(moe_dtype dt, moe_weight_layout wl, const vo
                                                         h_pre, d_h, cus, s);
   // d_w2 in the layout of w2: [I, H] = act^T d_rows, or [H, I] = d_rows^T act.
   if (err == hipSuccess)
-    err = wl == MOE_W_KN ? moe_launch::grouped_wgrad((int)dt, act, d_rows, expert_offsets, E, R, I, H, d_w2, cus, s)
-                         : moe_launch::grouped_wgrad((int)dt, d_rows, act, expert_offsets, E, R, H, I, d_w2, cus, s);
+    err = wl == MOE_W_KN ? moe_launch::grouped_wgrad((int)dt, act, d_rows, expert_offsets, E, R, I, H, d_w2, 2, cus, s)
+                         : moe_launch::grouped_wgrad((int)dt, d_rows, act, expert_offsets, E, R, H, I, d_w2, 2, cus, s);
   return hip_result(err, fn);
 }
 
@@ -714,8 +714,8 @@ moe_status moe_grouped_fc1_backward(moe_dtype dt, moe_weight_layout wl, const vo
   // d_w1 in the layout of w1: [H, 2I] = x_scattered^T d_h, or [2I, H] = d_h^T x_scattered.
   if (err == hipSuccess)
     err = wl == MOE_W_KN
-              ? moe_launch::grouped_wgrad((int)dt, x_scattered, d_h, expert_offsets, E, R, H, 2 * I, d_w1, cus, s)
-              : moe_launch::grouped_wgrad((int)dt, d_h, x_scattered, expert_offsets, E, R, 2 * I, H, d_w1, cus, s);
+              ? moe_launch::grouped_wgrad((int)dt, x_scattered, d_h, expert_offsets, E, R, H, 2 * I, d_w1, 1, cus, s)
+              : moe_launch::grouped_wgrad((int)dt, d_h, x_scattered, expert_offsets, E, R, 2 * I, H, d_w1, 1, cus, s);
   return hip_result(err, fn);
 }
 

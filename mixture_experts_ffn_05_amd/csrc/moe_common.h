@@ -221,8 +221,9 @@ hipError_t grouped_fc2_dgrad_swiglu(int dt, int wt_nk, const void* d_rows, const
 hipError_t grouped_fc1_dgrad(int dt, int wt_nk, const void* d_h, const int32_t* offsets, int groups, int rows,
                              const void* w1, int H, int I, float* d_xs, int cu_count, hipStream_t s);
 // out[g] = P[rows of g]^T Q[rows of g]: P [rows, M], Q [rows, N], out [groups, M, N] (element type of dt).
+// role (1: fc1's weight gradient, 2: fc2's) only selects a separately named kernel for profiles.
 hipError_t grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets, int groups, int rows, int M,
-                         int N, void* out, int cu_count, hipStream_t s);
+                         int N, void* out, int role, int cu_count, hipStream_t s);
 hipError_t shared_gate(int dt, const void* x, const void* w_gate, int T, int H, float* gate,
                        hipStream_t s);
 

@@ -73,6 +73,9 @@
 #ifndef MOE_DECODE_FC2
 #define MOE_DECODE_FC2 13
 #endif
+#ifndef MOE_MID_DGRAD
+#define MOE_MID_DGRAD 1   // input-gradient GEMMs of the backward, mid-sized groups
+#endif
 
 namespace moe {
 namespace {
@@ -1130,12 +1133,23 @@ struct WgCfg {
   static_assert(kMB >= 1 && kNB >= 1, "wave tile must hold whole 32x32 blocks");
 };
 
-typedef WgCfg<128, 128, 64, 2, 2, 2> WgCfg1;
-typedef WgCfg<256, 256, 64, 2, 4, 2> WgCfg2;   // 8 waves
+// 128x128 tiles, 32-deep slices, a 32 KiB two-stage ring: four workgroups per
+// CU.  Measured on MI355X against 64-deep slices, 3- to 6-stage rings,
+// 128x256 / 256x128 / 64x256 tiles, 8-byte stores of a swapped product,
+// non-temporal stores and an M-fastest tile order: all within a few percent or
+// slower.
+typedef WgCfg<128, 128, 32, 2, 2, 2> WgCfg1;
+typedef WgCfg<128, 128, 64, 2, 2, 2> WgCfg2;
+typedef WgCfg<128, 256, 64, 2, 2, 4> WgCfg3;   // 8 waves
 #ifndef MOE_WGRAD_VARIANT
 #define MOE_WGRAD_VARIANT 1
 #endif
-typedef typename std::conditional<MOE_WGRAD_VARIANT == 2, WgCfg2, WgCfg1>::type WgCfgUsed;
+#ifndef MOE_WG_LDS_EPI
+#define MOE_WG_LDS_EPI 1   // output tiles through LDS (1) or straight from the accumulators (0)
+#endif
+typedef typename std::conditional<
+    MOE_WGRAD_VARIANT == 2, WgCfg2,
+    typename std::conditional<MOE_WGRAD_VARIANT == 3, WgCfg3, WgCfg1>::type>::type WgCfgUsed;
 
 struct WgParams {
   const bf16_t* p;          // [rows, M]
@@ -1167,26 +1181,6 @@ __device__ __forceinline__ u32x4 kn_frag(const unsigned char* __restrict__ tile,
                (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
 }
 
-// Direct loads of one slice (rows row0 .. row0 + BK - 1 of the group, clamped
-// to its last row) of the P and Q tiles into ring stage `st`.
-template <class C>
-__device__ __forceinline__ void wg_issue(unsigned char* __restrict__ st, const WgParams& p, int row0, int last_row,
-                                         const int* p_kr, const int* p_col, const int* q_kr, const int* q_col) {
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = 0; i < C::kPLoads; ++i) {
-    const int row = min(row0 + p_kr[i], last_row);
-    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.p + (int64_t)row * p.M + p_col[i]),
-                                     MOE_LDS(void, st + (wave * C::kPLoads + i) * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < C::kQLoads; ++i) {
-    const int row = min(row0 + q_kr[i], last_row);
-    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.q + (int64_t)row * p.N + q_col[i]),
-                                     MOE_LDS(void, st + C::kPStage + (wave * C::kQLoads + i) * 1024), 16, 0, 0);
-  }
-}
-
 template <class C>
 __device__ __forceinline__ void wg_compute(const unsigned char* __restrict__ st, f32x16 (&acc)[C::kMB][C::kNB],
                                            int wm, int wn) {
@@ -1203,40 +1197,203 @@ __device__ __forceinline__ void wg_compute(const unsigned char* __restrict__ st,
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
     if (ks + 1 < C::kKS) read(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+    // With the staged epilogue the product is taken swapped (the Q fragment as
+    // the MFMA's A operand), so that a lane holds four consecutive output
+    // columns of one output row.
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb]);
+      for (int nb = 0; nb < C::kNB; ++nb)
+        acc[mb][nb] = MOE_WG_LDS_EPI ? mfma32(bf[ks & 1][nb], af[ks & 1][mb], acc[mb][nb])
+                                     : mfma32(af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb]);
   }
 }
 
-template <class C>
-__device__ __forceinline__ void run_tile_wgrad(const WgParams& p, int g, int lo, int hi, int m0, int n0,
-                                               unsigned char* __restrict__ smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int cnt = hi - lo;
-  const int nk = (cnt + C::BK - 1) / C::BK;
+#ifndef MOE_WG_BAND_M
+#define MOE_WG_BAND_M 8
+#endif
+#ifndef MOE_WG_BAND_N
+#define MOE_WG_BAND_N 16
+#endif
+constexpr int kBandM = MOE_WG_BAND_M, kBandN = MOE_WG_BAND_N;
 
-  // Per-lane slice row and source column of each direct load (columns past
-  // M or N read column 0; they only feed outputs that are never stored).
-  int p_kr[C::kPLoads], p_col[C::kPLoads], q_kr[C::kQLoads], q_col[C::kQLoads];
+// Position of a workgroup in its stream of slices: tile id (>= total when the
+// stream is exhausted), the tile's group, row range and output corner, and the
+// slice kt of nk.
+struct WgCursor {
+  int64_t id;
+  int g, lo, hi, m0, n0, kt, nk;
+};
+
+template <class C>
+__device__ __forceinline__ void wg_locate(const WgParams& p, int64_t per_group, WgCursor& c) {
+  c.g = (int)(c.id / per_group);
+  const int rem = (int)(c.id % per_group);
+  c.lo = min(max(p.offsets[c.g], 0), p.rows);
+  c.hi = max(min(max(p.offsets[c.g + 1], 0), p.rows), c.lo);
+  // Blocks of up to kBandM x kBandN tiles (a band of M tiles, then blocks of N
+  // tiles along it; N fastest inside a block): the 128 consecutive ids an XCD
+  // runs at once read kBandM + kBandN operand tiles, which stay in its L2.
+  const int band = rem / (kBandM * p.n_tiles);
+  const int r1 = rem % (kBandM * p.n_tiles);
+  const int sm = min(kBandM, p.m_tiles - band * kBandM);
+  const int blk = r1 / (sm * kBandN);
+  const int r2 = r1 % (sm * kBandN);
+  const int sn = min(kBandN, p.n_tiles - blk * kBandN);
+  c.m0 = (band * kBandM + r2 / sn) * C::BM;
+  c.n0 = (blk * kBandN + r2 % sn) * C::BN;
+  c.kt = 0;
+  c.nk = (c.hi - c.lo + C::BK - 1) / C::BK;
+}
+
+// Zero tile of a group without rows (16-byte stores; N is a multiple of 8).
+template <class C>
+__device__ __forceinline__ void wg_store_zero(const WgParams& p, const WgCursor& c) {
+  constexpr int kChunks = C::BN / 8;
+  bf16_t* out = p.out + (int64_t)c.g * p.M * p.N;
+  for (int v = threadIdx.x; v < C::BM * kChunks; v += C::NT) {
+    const int m = c.m0 + v / kChunks, n = c.n0 + 8 * (v % kChunks);
+    if (m < p.M && n < p.N) *(u32x4*)(out + (int64_t)m * p.N + n) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Moves c to the first tile at or after c.id whose group has rows; with ZERO,
+// stores the zero tiles of the empty groups it passes.
+template <class C, bool ZERO>
+__device__ __forceinline__ void wg_seek(const WgParams& p, int64_t per_group, int64_t total, WgCursor& c) {
+  while (c.id < total) {
+    wg_locate<C>(p, per_group, c);
+    if (c.nk > 0) return;
+    if (ZERO) wg_store_zero<C>(p, c);
+    c.id += gridDim.x;
+  }
+}
+
+// Direct loads of slice c.kt of tile c into ring stage `st`: rows
+// lo + kt*BK .. + BK - 1, clamped to the group's last row; columns past M or N
+// read column 0 (they only feed outputs that are never stored).
+template <class C>
+__device__ __forceinline__ void wg_issue(unsigned char* __restrict__ st, const WgParams& p, const WgCursor& c) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = c.lo + c.kt * C::BK, last = c.hi - 1;
 #pragma unroll
   for (int i = 0; i < C::kPLoads; ++i) {
     const int kr = (wave * C::kPLoads + i) * C::kPRowsPerLoad + lane / C::kPChunks;
-    const int chunk = (lane % C::kPChunks) ^ kn_swizzle<C::kPChunks>(kr);
-    const int col = m0 + 8 * chunk;
-    p_kr[i] = kr;
-    p_col[i] = col < p.M ? col : 0;
+    const int col = c.m0 + 8 * ((lane % C::kPChunks) ^ kn_swizzle<C::kPChunks>(kr));
+    const int row = min(row0 + kr, last);
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.p + (int64_t)row * p.M + (col < p.M ? col : 0)),
+                                     MOE_LDS(void, st + (wave * C::kPLoads + i) * 1024), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::kQLoads; ++i) {
     const int kr = (wave * C::kQLoads + i) * C::kQRowsPerLoad + lane / C::kQChunks;
-    const int chunk = (lane % C::kQChunks) ^ kn_swizzle<C::kQChunks>(kr);
-    const int col = n0 + 8 * chunk;
-    q_kr[i] = kr;
-    q_col[i] = col < p.N ? col : 0;
+    const int col = c.n0 + 8 * ((lane % C::kQChunks) ^ kn_swizzle<C::kQChunks>(kr));
+    const int row = min(row0 + kr, last);
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, p.q + (int64_t)row * p.N + (col < p.N ? col : 0)),
+                                     MOE_LDS(void, st + C::kPStage + (wave * C::kQLoads + i) * 1024), 16, 0, 0);
   }
+}
+
+template <class C>
+__device__ __forceinline__ void wg_store_tile(const WgParams& p, const WgCursor& c, f32x16 (&acc)[C::kMB][C::kNB],
+                                              int wm, int wn) {
+  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
+  const int lane = threadIdx.x & 63;
+  bf16_t* out = p.out + (int64_t)c.g * p.M * p.N;
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb) {
+      const int n = c.n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = c.m0 + wm * (C::BM / C::WM) + 32 * mb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (m < p.M && n < p.N) out[(int64_t)m * p.N + n] = (bf16_t)f32_to_bf16_rne(acc[mb][nb][i]);
+        acc[mb][nb][i] = 0.f;
+      }
+    }
+}
+
+// Output tile through LDS (the ring stage just consumed, which every wave has
+// finished reading): each wave owns a 64x64 sub-tile and moves it in two
+// halves of 32 rows x 64 columns (4 KiB per wave).  The swapped product gives
+// a lane four consecutive columns of one row, written as 8 bytes; the 16-byte
+// chunks of a row are XOR-swizzled by (row / 2) % 8 so that both the writes and
+// the row reads are conflict-free; each lane then stores 16 bytes, 8 lanes per
+// 128-byte row.  Two-byte stores straight from the accumulators keep the
+// texture-address unit busy several times longer than the tile's loads do.
+template <class C>
+__device__ __forceinline__ void wg_store_tile_staged(const WgParams& p, const WgCursor& c,
+                                                     f32x16 (&acc)[C::kMB][C::kNB], int wm, int wn,
+                                                     unsigned char* __restrict__ stage) {
+  static_assert(C::BM / C::WM == 64 && C::BN / C::WN == 64, "staged epilogue: 64x64 per wave");
+  static_assert(C::NT / kWave * 4096 <= C::kStage, "staged epilogue: 4 KiB per wave in one stage");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned char* buf = stage + wave * 4096;
+  bf16_t* out = p.out + (int64_t)c.g * p.M * p.N;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int r = lane & 31;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& a = acc[mb][nb];
+        const u32x2 v{f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16),
+                      f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16)};
+        const int chunk = (4 * nb + q) ^ ((r >> 1) & 7);
+        *(u32x2*)(buf + r * 128 + chunk * 16 + 8 * (lane >> 5)) = v;
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * j + (lane >> 3), ch = lane & 7;
+      const u32x4 v = *(const u32x4*)(buf + row * 128 + ((ch ^ ((row >> 1) & 7)) * 16));
+      const int m = c.m0 + wm * 64 + 32 * mb + row, n = c.n0 + wn * 64 + 8 * ch;
+      if (m < p.M && n < p.N) *(u32x4*)(out + (int64_t)m * p.N + n) = v;
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+}
+
+// A workgroup's tiles (ids slot, slot + grid, ... group-major, then in the
+// blocks described at wg_locate, so consecutive ids share a group's rows and
+// an XCD's L2, and neighbouring output tiles of one row band are written together)
+// form one stream of reduction slices.  The LDS ring keeps STAGES - 1 slices
+// in flight across tile boundaries, so the next tile's loads overlap the
+// current tile's last MFMAs and its stores; groups are short (a few hundred
+// rows), so a ring restarted per tile would expose the load latency on every
+// tile.  Tiles of groups without rows take no slices: the issue cursor stores
+// their zero tiles as it passes them.
+// ROLE (1: fc1's weights, 2: fc2's) only names the two launches apart in profiles.
+template <class C, int ROLE>
+__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_wgrad_bf16(WgParams p) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int64_t per_group = (int64_t)p.m_tiles * p.n_tiles;
+  const int64_t total = per_group * p.groups;
+
+  WgCursor ic;
+  ic.id = xcd_slot();
+  wg_seek<C, true>(p, per_group, total, ic);
+  WgCursor cc = ic;
+  int outstanding = 0;  // slices issued and not yet consumed
+  auto issue_next = [&](int stage) {
+    wg_issue<C>(smem + stage * C::kStage, p, ic);
+    ++outstanding;
+    if (++ic.kt == ic.nk) {
+      ic.id += gridDim.x;
+      wg_seek<C, true>(p, per_group, total, ic);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (ic.id < total) issue_next(s);
 
   f32x16 acc[C::kMB][C::kNB];
 #pragma unroll
@@ -1246,60 +1403,36 @@ __device__ __forceinline__ void run_tile_wgrad(const WgParams& p, int g, int lo,
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-  const int last_row = hi - 1;
-#pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) wg_issue<C>(smem + s * C::kStage, p, lo + s * C::BK, last_row, p_kr, p_col, q_kr, q_col);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+  int stage = 0;
+  while (cc.id < total) {
+    // The slice in `stage` has landed once at most `outstanding - 1` newer slices' loads are pending.
+    if (outstanding - 1 >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
     lds_barrier();
-    unsigned char* st = smem + (kt % C::STAGES) * C::kStage;
-    const int valid = cnt - kt * C::BK;
+    unsigned char* st = smem + stage * C::kStage;
+    const int valid = (cc.hi - cc.lo) - cc.kt * C::BK;
     if (valid < C::BK) {
-      // Last, partial slice (nothing else in flight): zero its rows past the group end.
-      const int p0 = valid * C::kPRow, q0 = valid * C::kQRow;
-      for (int b = p0 + tid * 16; b < C::kPStage; b += C::NT * 16) *(u32x4*)(st + b) = u32x4{0u, 0u, 0u, 0u};
-      for (int b = q0 + tid * 16; b < C::kQStage; b += C::NT * 16)
+      // A group's partial last slice: zero its rows past the group end.
+      for (int b = valid * C::kPRow + tid * 16; b < C::kPStage; b += C::NT * 16)
+        *(u32x4*)(st + b) = u32x4{0u, 0u, 0u, 0u};
+      for (int b = valid * C::kQRow + tid * 16; b < C::kQStage; b += C::NT * 16)
         *(u32x4*)(st + C::kPStage + b) = u32x4{0u, 0u, 0u, 0u};
       lds_barrier();
     }
-    const int kn = kt + C::STAGES - 1;
-    if (kn < nk)
-      wg_issue<C>(smem + (kn % C::STAGES) * C::kStage, p, lo + kn * C::BK, last_row, p_kr, p_col, q_kr, q_col);
+    // The stage consumed in the previous iteration is free (every wave passed the barrier).
+    if (ic.id < total) issue_next((stage + C::STAGES - 1) % C::STAGES);
     wg_compute<C>(st, acc, wm, wn);
-  }
-  lds_barrier();  // every wave is done with the ring before the next tile refills it
-
-  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
-  bf16_t* out = p.out + (int64_t)g * p.M * p.N;
-#pragma unroll
-  for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::kNB; ++nb) {
-      const int n = n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * (C::BM / C::WM) + 32 * mb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (m < p.M) out[(int64_t)m * p.N + n] = (bf16_t)f32_to_bf16_rne(acc[mb][nb][i]);
+    --outstanding;
+    if (++cc.kt == cc.nk) {
+      if (MOE_WG_LDS_EPI) {
+        lds_barrier();  // every wave is done reading `st`; the next iteration's barrier frees it again
+        wg_store_tile_staged<C>(p, cc, acc, wm, wn, st);
+      } else {
+        wg_store_tile<C>(p, cc, acc, wm, wn);
       }
+      cc.id += gridDim.x;
+      wg_seek<C, false>(p, per_group, total, cc);
     }
-}
-
-// Tile ids run group-major, then M tile, then N tile; consecutive ids share a
-// group's rows and land on one XCD.
-template <class C>
-__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_wgrad_bf16(WgParams p) {
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const int64_t per_group = (int64_t)p.m_tiles * p.n_tiles;
-  const int64_t total = per_group * p.groups;
-  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
-    const int g = (int)(id / per_group);
-    const int rem = (int)(id % per_group);
-    const int lo = min(max(p.offsets[g], 0), p.rows);
-    const int hi = max(min(max(p.offsets[g + 1], 0), p.rows), lo);
-    run_tile_wgrad<C>(p, g, lo, hi, (rem / p.n_tiles) * C::BM, (rem % p.n_tiles) * C::BN, smem);
+    stage = (stage + 1) % C::STAGES;
   }
 }
 
@@ -1505,12 +1638,13 @@ constexpr int64_t kDecodeRows = 32;
 template <int EPI>
 constexpr int decode_variant() { return paired(EPI) ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
 
-template <int EPI>
+template <int EPI, int ROLE>
 int pick_pipe_variant(const GemmParams<bf16_t>& p) {
   if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
   if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   if (rows_per_group >= 512) return 8;
+  if (ROLE == 2) return MOE_MID_DGRAD;
   return paired(EPI) ? MOE_MID_FC1 : 1;
 }
 
@@ -1559,9 +1693,9 @@ template <int EPI, int ROLE>
 hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   if (p.K % 64 == 0) {
     if (p.bt)
-      return with_cfg(pick_pipe_variant<EPI>(p),
+      return with_cfg(pick_pipe_variant<EPI, ROLE>(p),
                       [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, true>(p, cu_count, s); });
-    return with_cfg(pick_pipe_variant<EPI>(p),
+    return with_cfg(pick_pipe_variant<EPI, ROLE>(p),
                     [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, false>(p, cu_count, s); });
   }
   p.n_tiles = paired(EPI) ? (p.N + 63) / 64 : (p.N + 127) / 128;
@@ -1763,18 +1897,22 @@ hipError_t grouped_fc1_dgrad(int dt, int wt_nk, const void* d_h, const int32_t* 
 }
 
 hipError_t grouped_wgrad(int dt, const void* P, const void* Q, const int32_t* offsets, int groups, int rows, int M,
-                         int N, void* out, int cu_count, hipStream_t s) {
+                         int N, void* out, int role, int cu_count, hipStream_t s) {
   using namespace moe;
   if (dt == 1) {
     typedef WgCfgUsed C;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16<C>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (attr != hipSuccess) return attr;
+    auto kern = role == 1 ? &grouped_wgrad_bf16<C, 1> : &grouped_wgrad_bf16<C, 2>;
+    static const hipError_t attr1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16<C, 1>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    static const hipError_t attr2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_wgrad_bf16<C, 2>),
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (attr1 != hipSuccess) return attr1;
+    if (attr2 != hipSuccess) return attr2;
     WgParams p{(const bf16_t*)P, (const bf16_t*)Q, offsets, groups, rows, M, N, (bf16_t*)out,
                (M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN};
     const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles * groups;
     const int grid = persistent_grid(tiles, cu_count * C::kWgsPerCu);
-    hipLaunchKernelGGL(grouped_wgrad_bf16<C>, dim3(grid), dim3(C::NT), C::kLds, s, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::kLds, s, p);
     return hipGetLastError();
   }
   const int64_t n = (int64_t)groups * M * N;

@@ -6,15 +6,15 @@
 
 `trace` writes per-kernel call counts and average durations, and the summed
 average duration of the kernels whose name contains <kernel_substr> (the
-launches of one fc1 call).  `pmc` reads two counter-collection runs
+launches of one timed call; '|' separates alternatives).  `pmc` reads two counter-collection runs
 (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), calibrates both against the
 device copy of <copy_mib> MiB that the profiled command performed first (its
 counters should read copy_mib*1024 KiB each), and writes the calibrated HBM
 bytes per dispatch of every kernel, plus a JSON line, read by bench.py for the
-roofline object's `traffic` field, with the bytes of one fc1 call: the sum
+roofline object's `traffic` field, with the bytes of one timed call: the sum
 over the kernels whose name contains <kernel_substr> (each launched once per
-call).  The JSON line records a hash of the GEMM source, so a later change of
-the kernel voids the figure.
+call).  The JSON line records a hash of the kernel sources, so a later change
+of a kernel voids the figure.
 """
 
 from __future__ import annotations
@@ -31,11 +31,18 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 
 def kernel_source_hash() -> str:
+    """Hash of every kernel source: a change to any of them voids a recorded figure."""
     h = hashlib.sha256()
-    for name in ("moe_gemm.hip", "moe_common.h"):
-        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h"))):
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def matches(name: str, kernel_substr: str) -> bool:
+    """True if any '|'-separated alternative of kernel_substr occurs in name."""
+    name = name.replace("moe::(anonymous namespace)::", "")
+    return any(alt and alt in name for alt in kernel_substr.split("|"))
 
 
 def short(name: str) -> str:
@@ -52,10 +59,10 @@ def trace(stats_csv: str, kernel_substr: str, out_md: str, command: str) -> None
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
-        if kernel_substr in r["Name"]:
+        if matches(r["Name"], kernel_substr):
             matched += float(r["AverageNs"]) / 1e3
             names.append(short(r["Name"]))
-    lines += ["", f"fc1 call (kernels containing `{kernel_substr}`: {'; '.join(names)}): "
+    lines += ["", f"Timed call (kernels containing `{kernel_substr}`: {'; '.join(names)}): "
                   f"summed average duration {matched:.2f} us"]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
@@ -94,7 +101,7 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
         wa = sum(wv) / len(wv) if wv else 0.0
         hbm = (fa * (f_scale or 1.0) + wa * (w_scale or 1.0)) * 1024 / 1e6
         lines.append(f"| {short(k)} | {len(fv)} | {fa:.0f} | {wa:.0f} | {hbm:.1f} |")
-        if kernel_substr in k:
+        if matches(k, kernel_substr):
             if record is None:
                 record = {"kernels": [], "fetch_kib": 0.0, "write_kib": 0.0, "fetch_scale": f_scale,
                           "write_scale": w_scale, "hbm_bytes_per_call": 0.0, "gemm_source_hash": kernel_source_hash()}
@@ -102,7 +109,7 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
             record["fetch_kib"] += fa
             record["write_kib"] += wa
             record["hbm_bytes_per_call"] += hbm * 1e6
-    lines += ["", f"Machine-readable record for the fc1 call (kernels containing `{kernel_substr}`; read by "
+    lines += ["", f"Machine-readable record for the timed call (kernels containing `{kernel_substr}`; read by "
                   "bench.py):", "",
               "TRAFFIC_JSON " + json.dumps(record)]
     open(out_md, "w").write("\n".join(lines) + "\n")
