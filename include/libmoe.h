@@ -55,6 +55,18 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Stage of a call, in the stage vocabulary of the PLENA pages (PLENA_Compiler
+ * PR #69, sections "Group B" and "Group E": router_topk, expert_route_weight,
+ * accumulator_init, residual_setup, gather, scatter_combine, expert_projection,
+ * expert_bias, shared_expert_projection / _activation / _gate, other).  Every
+ * call below opens a roctx range with this name for the duration of the call
+ * (seen by `rocprofv3 --marker-trace`); '+' joins the stages of a call that
+ * serves several, and backward calls carry the prefix "backward:".  `call` is
+ * the function name; `gated` selects the label of the calls whose stages
+ * depend on w_gate being given.  Returns "other" for unknown names; the string
+ * is static. */
+const char* moe_call_stage(const char* call, int32_t gated);
+
 /* Storage of an expert weight W that maps K inputs to N outputs (the layer
  * computes x @ W with W a K x N matrix in the pages' notation):
  *   MOE_W_KN: row-major [K, N], N contiguous (the pages' x @ W form);

@@ -27,6 +27,11 @@ MOE_OK = 0
 _lib = None
 
 
+def moe_call_stage(call: str, gated: bool = False) -> str:
+    """Stage label of a libmoe call (the name of the roctx range it opens)."""
+    return load().moe_call_stage(call.encode(), int(bool(gated))).decode()
+
+
 class MoEError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} [{status}]")
@@ -39,6 +44,7 @@ _SIGNATURES = {
     "moe_status_name": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_int, []),
+    "moe_call_stage": (ctypes.c_char_p, [ctypes.c_char_p, _c_int]),
     "moe_route": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size,
                            _vp]),
     "moe_route_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),

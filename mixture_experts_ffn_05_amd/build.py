@@ -61,7 +61,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # roctx (the stage ranges every call opens) from ROCm's profiler SDK
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-L/opt/rocm/lib",
+           "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -4,9 +4,12 @@
 #include "libmoe.h"
 #include "moe_common.h"
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 #include <string>
 
 namespace {
@@ -105,6 +108,57 @@ moe_status need_flag(int32_t v, const char* fn, const char* name) {
                             : fail(MOE_ERR_INVALID_ARGUMENT, "%s: %s must be 0 or 1 (got %d)", fn, name, (int)v);
 }
 
+
+// Stage of every call, in the stage vocabulary of the PLENA pages
+// (PLENA_Compiler PR #69, sections "Group B" and "Group E"; PLENA_Simulator
+// PR #97, section "Stage attribution"); '+' joins the stages of a call that
+// serves several.  The routed SwiGLU runs in the fc1 epilogue, so it bills to
+// expert_projection; the combine overwrites its output, so no separate
+// accumulator_init launch exists.  Backward calls carry a "backward:" prefix.
+struct CallStage {
+  const char* call;
+  const char* stage;
+};
+constexpr CallStage kCallStages[] = {
+    {"moe_route", "router_topk"},
+    {"moe_route_and_scatter", "router_topk+gather"},
+    {"moe_build_scatter", "gather"},
+    {"moe_grouped_swiglu_fc1", "expert_projection"},
+    {"moe_grouped_fc2", "expert_projection"},
+    {"moe_gather_combine", "scatter_combine"},
+    {"moe_shared_expert", "shared_expert_projection"},
+    {"moe_shared_expert:gated", "shared_expert_gate+shared_expert_projection"},
+    {"moe_grouped_swiglu_fc1_mx8", "expert_projection"},
+    {"moe_grouped_fc2_mx8", "expert_projection"},
+    {"moe_shared_expert_mx8", "shared_expert_projection"},
+    {"moe_shared_expert_mx8:gated", "shared_expert_gate+shared_expert_projection"},
+    {"moe_grouped_swiglu_fc1_and_shared_mx8", "expert_projection+shared_expert_projection"},
+    {"moe_grouped_fc2_and_shared_mx8", "expert_projection+shared_expert_projection"},
+    {"moe_grouped_fc2_and_shared_mx8:gated", "expert_projection+shared_expert_gate+shared_expert_projection"},
+    {"moe_grouped_swiglu_fc1_and_shared", "expert_projection+shared_expert_projection"},
+    {"moe_grouped_fc2_and_shared", "expert_projection+shared_expert_projection"},
+    {"moe_grouped_fc2_and_shared:gated", "expert_projection+shared_expert_gate+shared_expert_projection"},
+    {"moe_grouped_swiglu_fc1_save", "expert_projection"},
+    {"moe_scatter_grad", "backward:scatter_combine"},
+    {"moe_grouped_fc2_backward", "backward:expert_projection"},
+    {"moe_grouped_fc1_backward", "backward:expert_projection+backward:gather"},
+};
+
+const char* stage_of(const char* call) {
+  for (const CallStage& c : kCallStages)
+    if (strcmp(c.call, call) == 0) return c.stage;
+  return "other";
+}
+
+// roctx range around one call, named with its stage: a rocprofv3 marker
+// trace then attributes every launch to a stage.
+struct StageRange {
+  explicit StageRange(const char* stage) { roctxRangePushA(stage); }
+  ~StageRange() { roctxRangePop(); }
+  StageRange(const StageRange&) = delete;
+  StageRange& operator=(const StageRange&) = delete;
+};
+
 }  // namespace
 
 extern "C" {
@@ -124,6 +178,16 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int moe_version(void) { return kVersion; }
 
+const char* moe_call_stage(const char* call, int32_t gated) {
+  if (!call) return "other";
+  if (gated) {
+    const std::string g = std::string(call) + ":gated";
+    for (const CallStage& c : kCallStages)
+      if (g == c.call) return c.stage;
+  }
+  return stage_of(call);
+}
+
 size_t moe_route_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E) {
   if (T < 1 || H < 1 || E < 1 || (dt != MOE_F32 && dt != MOE_BF16)) return 0;
   return moe_launch::route_workspace_bytes((int)dt, T, H, E);
@@ -133,6 +197,7 @@ moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const fl
                      int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights, float* logits, void* workspace,
                      size_t workspace_bytes, void* stream) {
   const char* fn = "moe_route";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(w_router, fn, "w_router"));
@@ -169,6 +234,7 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
                                  int32_t* expert_offsets, int32_t* status_words, void* x_scattered, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   const char* fn = "moe_route_and_scatter";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(w_router, fn, "w_router"));
@@ -220,6 +286,7 @@ moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_id
                              int32_t* status_words, void* x_scattered, void* workspace, size_t workspace_bytes,
                              void* stream) {
   const char* fn = "moe_build_scatter";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(topk_ids, fn, "topk_ids"));
@@ -248,6 +315,7 @@ moe_status moe_grouped_swiglu_fc1(moe_dtype dt, moe_weight_layout wl, const void
                                   const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H, int32_t E,
                                   int32_t I, void* act, void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
@@ -269,6 +337,7 @@ moe_status moe_grouped_swiglu_fc1(moe_dtype dt, moe_weight_layout wl, const void
 moe_status moe_grouped_fc2(moe_dtype dt, moe_weight_layout wl, const void* act, const int32_t* expert_offsets,
                            const void* w2, int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows, void* stream) {
   const char* fn = "moe_grouped_fc2";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
@@ -290,6 +359,7 @@ moe_status moe_grouped_fc2(moe_dtype dt, moe_weight_layout wl, const void* act, 
 moe_status moe_gather_combine(const float* y_rows, const int32_t* scatter_index, const float* topk_weights, int32_t T,
                               int32_t H, int32_t top_k, int32_t accumulate, float* y, void* stream) {
   const char* fn = "moe_gather_combine";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
   MOE_CHECK(need_ptr(scatter_index, fn, "scatter_index"));
   MOE_CHECK(need_ptr(topk_weights, fn, "topk_weights"));
@@ -314,6 +384,7 @@ moe_status moe_shared_expert(moe_dtype dt, moe_weight_layout wl, const void* x, 
                              const void* w_gate, int32_t T, int32_t H, int32_t I_s, int32_t accumulate, float* y,
                              void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "moe_shared_expert";
+  StageRange stage_range(stage_of(w_gate ? "moe_shared_expert:gated" : fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
@@ -354,6 +425,7 @@ moe_status moe_grouped_swiglu_fc1_mx8(const void* x_scattered, const int32_t* ex
                                       const uint8_t* w1s, int32_t R, int32_t H, int32_t E, int32_t I, void* act,
                                       void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1_mx8";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w1q, fn, "w1q"));
@@ -375,6 +447,7 @@ moe_status moe_grouped_fc2_mx8(const void* act, const int32_t* expert_offsets, c
                                const uint8_t* w2s, int32_t R, int32_t I, int32_t E, int32_t H, float* y_rows,
                                void* stream) {
   const char* fn = "moe_grouped_fc2_mx8";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w2q, fn, "w2q"));
@@ -397,6 +470,7 @@ moe_status moe_shared_expert_mx8(const void* x, const uint8_t* ws1q, const uint8
                                  int32_t accumulate, float* y, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   const char* fn = "moe_shared_expert_mx8";
+  StageRange stage_range(stage_of(w_gate ? "moe_shared_expert_mx8:gated" : fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(ws1q, fn, "ws1q"));
   MOE_CHECK(need_ptr(ws1s, fn, "ws1s"));
@@ -432,6 +506,7 @@ moe_status moe_grouped_swiglu_fc1_and_shared_mx8(const void* x_scattered, const 
                                                  const uint8_t* ws1s, int32_t T, int32_t I_s, void* act_shared,
                                                  void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1_and_shared_mx8";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w1q, fn, "w1q"));
@@ -464,6 +539,7 @@ moe_status moe_grouped_fc2_and_shared_mx8(const void* act, const int32_t* expert
                                           int32_t I_s, int32_t accumulate, float* y, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   const char* fn = "moe_grouped_fc2_and_shared_mx8";
+  StageRange stage_range(stage_of(w_gate ? "moe_grouped_fc2_and_shared_mx8:gated" : fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(w2q, fn, "w2q"));
@@ -508,6 +584,7 @@ moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl,
                                              int32_t E, int32_t I, void* act, const void* x, const void* ws1,
                                              int32_t T, int32_t I_s, void* act_shared, void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1_and_shared";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
@@ -547,6 +624,7 @@ moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const 
                                       const void* x, const void* w_gate, int32_t T, int32_t I_s, int32_t accumulate,
                                       float* y, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "moe_grouped_fc2_and_shared";
+  StageRange stage_range(stage_of(w_gate ? "moe_grouped_fc2_and_shared:gated" : fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(act, fn, "act"));
@@ -596,6 +674,7 @@ moe_status moe_grouped_swiglu_fc1_save(moe_dtype dt, moe_weight_layout wl, const
                                        const int32_t* expert_offsets, const void* w1, int32_t R, int32_t H,
                                        int32_t E, int32_t I, void* act, void* h_pre, void* stream) {
   const char* fn = "moe_grouped_swiglu_fc1_save";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
@@ -620,6 +699,7 @@ moe_status moe_scatter_grad(moe_dtype dt, const float* dy, const float* y_rows, 
                             const int32_t* scatter_index, int32_t T, int32_t H, int32_t top_k, int32_t R,
                             void* d_rows, float* d_topk_weights, void* stream) {
   const char* fn = "moe_scatter_grad";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(dy, fn, "dy"));
   MOE_CHECK(need_ptr(y_rows, fn, "y_rows"));
@@ -643,6 +723,7 @@ moe_status moe_grouped_fc2_backward(moe_dtype dt, moe_weight_layout wl, const vo
                                     const void* h_pre, const int32_t* expert_offsets, const void* w2, int32_t R,
                                     int32_t I, int32_t E, int32_t H, void* d_h, void* d_w2, void* stream) {
   const char* fn = "moe_grouped_fc2_backward";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(d_rows, fn, "d_rows"));
@@ -681,6 +762,7 @@ moe_status moe_grouped_fc1_backward(moe_dtype dt, moe_weight_layout wl, const vo
                                     int32_t accumulate, float* d_x, void* d_w1, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   const char* fn = "moe_grouped_fc1_backward";
+  StageRange stage_range(stage_of(fn));
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_layout(wl, fn));
   MOE_CHECK(need_ptr(d_h, fn, "d_h"));

@@ -1,0 +1,425 @@
+"""Route traces: one layer's routing as a JSON document, its validator, a seeded
+sample generator, a replay through libmoe with per-stage GPU times, and the
+stage summary with the shared-vs-routed split.
+
+    python -m mixture_experts_ffn_05_amd.route_trace sample --preset v3 --tokens 64 --out t.json
+    python -m mixture_experts_ffn_05_amd.route_trace validate t.json
+    python -m mixture_experts_ffn_05_amd.route_trace replay t.json [--repeats 20] [--out r.json]
+
+Sources: PLENA_Simulator PR #97, "Part 1 -- Timing-replay harnesses" (a
+dependency-free route-trace schema and validator, a sample-trace generator, a
+replay runner, timing gates and result export) and "Route-trace schema v2"
+(the model gains shared_experts / shared_intermediate_size / shared_gate; a
+v1 trace is a v2 trace without a shared branch; half-specified shared
+settings are rejected; the summary splits time into shared and routed terms
+that both leave out gather, scatter_combine and accumulator_init, and sums
+exact times, rounding once); PLENA_Compiler PR #69, sections "Group B" and
+"Group E" (the stage vocabulary).
+
+Trace document (the pages name the v2 fields only; the rest is this module's
+layout):
+
+    {"schema_version": 1 | 2,
+     "model": {"name": str, "hidden_size": H, "num_experts": E, "top_k": k,
+               "moe_intermediate_size": I,
+               "shared_experts": n, "shared_intermediate_size": I_s,   # v2, all three
+               "shared_gate": bool},                                    # or none
+     "dtype": "bf16" | "f32",
+     "tokens": T,
+     "routes": {"expert_ids": [[k ints in [0, E)] x T],
+                "weights": [[k finite floats >= 0] x T]},
+     "source": str}                                                     # optional
+
+shared_intermediate_size is the fused width of the n shared experts (n times
+one expert's width), so it must be a multiple of n.  A shared branch is
+specified completely or not at all: shared_experts >= 1 with a width and an
+explicit gate flag, or none of the three fields (shared_experts = 0 alone is
+the same as none).  Unknown keys are errors, like unknown stage names.
+
+The replay feeds a trace's routes to libmoe on seeded synthetic x and weights
+of the traced shapes.  Each call runs under the roctx range of its stage (the
+library opens it); the replay brackets every call with HIP events on the launch
+stream, so per-stage times are GPU times.  Its gates: every stage name belongs
+to the vocabulary, times are non-negative, the output is finite and bitwise
+identical across repeats, and the scatter saw no out-of-range expert id.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+
+import numpy as np
+
+SCHEMA_VERSIONS = (1, 2)
+
+# The stage vocabulary of the pages (PLENA_Compiler PR #69, "Group B" / "Group E").
+MOE_STAGES = ("residual_setup", "router_topk", "expert_route_weight", "accumulator_init", "gather",
+              "expert_projection", "expert_bias", "scatter_combine", "shared_expert_projection",
+              "shared_expert_activation", "shared_expert_gate", "other")
+SHARED_STAGES = frozenset({"shared_expert_projection", "shared_expert_activation", "shared_expert_gate"})
+ROUTED_STAGES = frozenset({"router_topk", "expert_route_weight", "expert_projection", "expert_bias"})
+PLUMBING_STAGES = frozenset({"gather", "scatter_combine", "accumulator_init"})   # in neither term
+
+_MODEL_KEYS = {"name", "hidden_size", "num_experts", "top_k", "moe_intermediate_size"}
+_SHARED_KEYS = ("shared_experts", "shared_intermediate_size", "shared_gate")
+_TOP_KEYS = {"schema_version", "model", "dtype", "tokens", "routes", "source"}
+
+# Layer shapes of the pages' routing and shared-expert tables (PLENA_Compiler
+# PR #69, "Group A" and "Group C"): routed experts / top-k, shared experts
+# stored fused.
+MODEL_PRESETS = {
+    "tiny": {"name": "tiny", "hidden_size": 256, "num_experts": 8, "top_k": 2, "moe_intermediate_size": 128},
+    "scout": {"name": "llama4-scout-shaped", "hidden_size": 5120, "num_experts": 16, "top_k": 1,
+              "moe_intermediate_size": 8192, "shared_experts": 1, "shared_intermediate_size": 8192,
+              "shared_gate": False},
+    "qwen2": {"name": "qwen2-moe-shaped", "hidden_size": 2048, "num_experts": 60, "top_k": 4,
+              "moe_intermediate_size": 1408, "shared_experts": 1, "shared_intermediate_size": 5632,
+              "shared_gate": True},
+    "v2l": {"name": "deepseek-v2-lite-shaped", "hidden_size": 2048, "num_experts": 64, "top_k": 6,
+            "moe_intermediate_size": 1408, "shared_experts": 2, "shared_intermediate_size": 2816,
+            "shared_gate": False},
+    "v3": {"name": "deepseek-v3-shaped", "hidden_size": 7168, "num_experts": 256, "top_k": 8,
+           "moe_intermediate_size": 2048, "shared_experts": 1, "shared_intermediate_size": 2048,
+           "shared_gate": False},
+}
+
+
+class TraceError(ValueError):
+    """A route trace that does not satisfy the schema; the message names the field."""
+
+
+def _pos_int(v, what):
+    if isinstance(v, bool) or not isinstance(v, int) or v < 1:
+        raise TraceError(f"{what} must be a positive integer (got {v!r})")
+    return v
+
+
+def shared_branch(model: dict):
+    """(n_shared, fused width, gated) of a validated model, or None without a shared branch."""
+    n = model.get("shared_experts", 0)
+    if not n:
+        return None
+    return n, model["shared_intermediate_size"], model["shared_gate"]
+
+
+def validate_trace(doc: dict) -> dict:
+    """Check a trace document against the schema; returns it unchanged or raises TraceError."""
+    if not isinstance(doc, dict):
+        raise TraceError("a trace is a JSON object")
+    unknown = set(doc) - _TOP_KEYS
+    if unknown:
+        raise TraceError(f"unknown top-level keys {sorted(unknown)}")
+    ver = doc.get("schema_version")
+    if ver not in SCHEMA_VERSIONS:
+        raise TraceError(f"schema_version must be one of {SCHEMA_VERSIONS} (got {ver!r})")
+    model = doc.get("model")
+    if not isinstance(model, dict):
+        raise TraceError("model must be an object")
+    unknown = set(model) - _MODEL_KEYS - set(_SHARED_KEYS)
+    if unknown:
+        raise TraceError(f"unknown model keys {sorted(unknown)}")
+    missing = _MODEL_KEYS - set(model)
+    if missing:
+        raise TraceError(f"model is missing {sorted(missing)}")
+    if not isinstance(model["name"], str):
+        raise TraceError("model.name must be a string")
+    H = _pos_int(model["hidden_size"], "model.hidden_size")
+    E = _pos_int(model["num_experts"], "model.num_experts")
+    k = _pos_int(model["top_k"], "model.top_k")
+    _pos_int(model["moe_intermediate_size"], "model.moe_intermediate_size")
+    if k > E:
+        raise TraceError(f"model.top_k ({k}) exceeds model.num_experts ({E})")
+    present = [key for key in _SHARED_KEYS if key in model]
+    if present and ver == 1:
+        raise TraceError(f"schema_version 1 has no shared branch; {present} need schema_version 2")
+    if present:
+        n = model.get("shared_experts")
+        if n is None:
+            raise TraceError(f"half-specified shared branch: {present} without shared_experts")
+        if isinstance(n, bool) or not isinstance(n, int) or n < 0:
+            raise TraceError(f"model.shared_experts must be a non-negative integer (got {n!r})")
+        if n == 0:
+            if len(present) > 1:
+                raise TraceError("half-specified shared branch: shared_experts is 0 but "
+                                 f"{[p for p in present if p != 'shared_experts']} are given")
+        else:
+            if "shared_intermediate_size" not in model:
+                raise TraceError("half-specified shared branch: shared_experts without shared_intermediate_size "
+                                 "(it would replay as routed-only while labelled shared)")
+            if "shared_gate" not in model:
+                raise TraceError("half-specified shared branch: shared_experts without shared_gate")
+            w = _pos_int(model["shared_intermediate_size"], "model.shared_intermediate_size")
+            if w % n:
+                raise TraceError(f"model.shared_intermediate_size ({w}) is the fused width of "
+                                 f"{n} shared experts and must be a multiple of it")
+            if not isinstance(model["shared_gate"], bool):
+                raise TraceError("model.shared_gate must be true or false")
+    if doc.get("dtype") not in ("bf16", "f32"):
+        raise TraceError(f"dtype must be 'bf16' or 'f32' (got {doc.get('dtype')!r})")
+    T = _pos_int(doc.get("tokens"), "tokens")
+    routes = doc.get("routes")
+    if not isinstance(routes, dict) or set(routes) != {"expert_ids", "weights"}:
+        raise TraceError("routes must be an object with exactly expert_ids and weights")
+    ids, wts = routes["expert_ids"], routes["weights"]
+    if not isinstance(ids, list) or len(ids) != T:
+        raise TraceError(f"routes.expert_ids must hold {T} rows (one per token)")
+    if not isinstance(wts, list) or len(wts) != T:
+        raise TraceError(f"routes.weights must hold {T} rows (one per token)")
+    for t in range(T):
+        ri, rw = ids[t], wts[t]
+        if not isinstance(ri, list) or len(ri) != k:
+            raise TraceError(f"routes.expert_ids[{t}] must hold top_k = {k} ids")
+        if not isinstance(rw, list) or len(rw) != k:
+            raise TraceError(f"routes.weights[{t}] must hold top_k = {k} weights")
+        for j in range(k):
+            e = ri[j]
+            if isinstance(e, bool) or not isinstance(e, int) or not 0 <= e < E:
+                raise TraceError(f"routes.expert_ids[{t}][{j}] = {e!r} is not an expert id in [0, {E})")
+            v = rw[j]
+            if isinstance(v, bool) or not isinstance(v, (int, float)) or not math.isfinite(v) or v < 0:
+                raise TraceError(f"routes.weights[{t}][{j}] = {v!r} is not a finite non-negative number")
+    if "source" in doc and not isinstance(doc["source"], str):
+        raise TraceError("source must be a string")
+    if H % 8:
+        raise TraceError(f"model.hidden_size ({H}) must be a multiple of 8")
+    return doc
+
+
+def load_trace(path: str) -> dict:
+    with open(path) as f:
+        return validate_trace(json.load(f))
+
+
+def sample_trace(model: dict, tokens: int, seed: int = 0, routing: str = "natural", version: int = 2,
+                 dtype: str = "bf16") -> dict:
+    """A synthetic trace with seeded routes.
+
+    routing: "uniform" (k distinct experts, uniformly), "zipf:<s>" (k distinct
+    experts drawn by popularity 1/rank^s over a seeded ranking of the experts,
+    by Gumbel top-k), "natural" (= "zipf:0.8"), or "all_dup" (every slot of
+    every token on expert 0, the duplicate-route pattern).  Weights are the
+    softmax of seeded normal scores over a token's k slots, stored as float32
+    values.  version 1 drops the shared-branch fields.
+    """
+    model = dict(model)
+    if version == 1:
+        for key in _SHARED_KEYS:
+            model.pop(key, None)
+    E, k = model["num_experts"], model["top_k"]
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(0x7E,)))
+    if routing == "all_dup":
+        ids = np.zeros((tokens, k), np.int64)
+    else:
+        s = 0.8 if routing == "natural" else (0.0 if routing == "uniform" else None)
+        if s is None:
+            if not routing.startswith("zipf:"):
+                raise ValueError(f"unknown routing {routing!r}")
+            s = float(routing.split(":", 1)[1])
+        rank = rng.permutation(E) + 1
+        logp = -s * np.log(rank.astype(np.float64))
+        g = rng.gumbel(size=(tokens, E))
+        ids = np.argsort(-(logp[None, :] + g), axis=1, kind="stable")[:, :k]
+    z = rng.standard_normal((tokens, k))
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    doc = {"schema_version": version, "model": model, "dtype": dtype, "tokens": int(tokens),
+           "routes": {"expert_ids": ids.astype(int).tolist(), "weights": [[float(v) for v in row] for row in w]},
+           "source": f"synthetic: seed {seed}, routing {routing}"}
+    return validate_trace(doc)
+
+
+def stage_category(label: str) -> str:
+    """shared / routed / excluded (combine plumbing) / mixed / other for a stage label ('+' joins stages)."""
+    parts = set(label.split("+"))
+    if parts <= SHARED_STAGES:
+        return "shared"
+    if parts <= ROUTED_STAGES:
+        return "routed"
+    if parts <= PLUMBING_STAGES:
+        return "excluded"
+    if parts <= set(MOE_STAGES):
+        return "mixed"
+    return "other"
+
+
+def summarize(stage_ns: dict) -> dict:
+    """Per-stage times and the shared-vs-routed split from exact per-stage times (ns, floats).
+
+    Sums are taken over the exact values and rounded once (to whole
+    nanoseconds); time_fraction uses the exact values.  shared and routed
+    leave out gather / scatter_combine / accumulator_init; labels that join
+    stages of different kinds are reported as mixed, in neither term.
+    """
+    total = math.fsum(stage_ns.values())
+    stages = {lab: {"wall_ns": round(v), "time_fraction": (v / total if total > 0 else 0.0),
+                    "category": stage_category(lab)} for lab, v in stage_ns.items()}
+    terms = {}
+    for cat in ("shared", "routed", "excluded", "mixed", "other"):
+        terms[cat] = math.fsum(v for lab, v in stage_ns.items() if stage_category(lab) == cat)
+    sr = terms["shared"] + terms["routed"]
+    split = {f"{cat}_ns": round(v) for cat, v in terms.items()}
+    split["shared_fraction"] = terms["shared"] / sr if sr > 0 else 0.0
+    split["excluded_stages"] = sorted(PLUMBING_STAGES)
+    return {"total_profiled_ns": round(total), "stages": stages, "shared_vs_routed": split}
+
+
+def _layer_config(doc: dict, seed: int):
+    from . import workloads as wl
+    m = doc["model"]
+    sb = shared_branch(m)
+    f32 = doc["dtype"] == "f32"
+    return wl.LayerConfig(f"trace_{m['name']}", doc["dtype"], T=doc["tokens"], H=m["hidden_size"],
+                          E=m["num_experts"], top_k=m["top_k"], I=m["moe_intermediate_size"],
+                          I_s=sb[1] if sb else 0, gated=bool(sb and sb[2]), fan_in_init=f32, seed=seed)
+
+
+def replay(doc: dict, repeats: int = 10, warmup: int = 3, include_router: bool = True, seed: int = 0,
+           device: str = "cuda:0", return_output: bool = False):
+    """Replay a validated trace through libmoe and time each stage.
+
+    One step: [moe_route on the synthetic x, for its cost only: the trace's
+    routes are used] -> moe_build_scatter -> moe_grouped_swiglu_fc1 ->
+    moe_grouped_fc2 -> moe_gather_combine -> [moe_shared_expert, accumulating].
+    Returns the summary dict; with return_output, also the host copy of y and
+    the layer (x, weights) that was replayed.
+    """
+    import torch
+
+    from . import binding as B
+    from . import workloads as wl
+
+    validate_trace(doc)
+    cfg = _layer_config(doc, seed)
+    dev = torch.device(device)
+    layer = wl.make_layer(cfg, dev)
+    x, W1, W2 = layer["x"], layer["W1"], layer["W2"]
+    T, k, E = cfg.T, cfg.top_k, cfg.E
+    ids = torch.tensor(doc["routes"]["expert_ids"], dtype=torch.int32, device=dev)
+    wts = torch.tensor(doc["routes"]["weights"], dtype=torch.float32, device=dev)
+    bufs = B.MoELayerBuffers(T, cfg.H, E, k, cfg.I, cfg.I_s, x.dtype, dev)
+    r_ids = torch.empty_like(ids)
+    r_w = torch.empty_like(wts)
+    sh = layer["shared"]
+    gated = bool(cfg.gated)
+
+    steps = []
+    if include_router:
+        steps.append(("moe_route", lambda: B.moe_route(x, layer["w_router"], None, k, r_ids, r_w, bufs.logits,
+                                                        bufs.route_ws)))
+    steps += [
+        ("moe_build_scatter", lambda: B.moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token,
+                                                          bufs.expert_offsets, bufs.status_words, bufs.x_scattered,
+                                                          bufs.scatter_ws)),
+        ("moe_grouped_swiglu_fc1", lambda: B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1,
+                                                                    bufs.act)),
+        ("moe_grouped_fc2", lambda: B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)),
+        ("moe_gather_combine", lambda: B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, wts, bufs.y, False)),
+    ]
+    if sh is not None:
+        steps.append(("moe_shared_expert", lambda: B.moe_shared_expert(x, sh[0], sh[1], sh[2], bufs.y,
+                                                                        bufs.shared_ws, True)))
+    labels = [B.moe_call_stage(name, gated and name == "moe_shared_expert") for name, _ in steps]
+
+    def run(events=None):
+        for i, (_, fn) in enumerate(steps):
+            if events is not None:
+                events[i].record()
+            fn()
+        if events is not None:
+            events[len(steps)].record()
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize(dev)
+    ys, per_rep = [], []
+    for _ in range(repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+        run(ev)
+        torch.cuda.synchronize(dev)
+        per_rep.append([ev[i].elapsed_time(ev[i + 1]) * 1e6 for i in range(len(steps))])   # ns
+        ys.append(bufs.y.detach().cpu().numpy().copy())
+    status = bufs.status_words.cpu().tolist()          # [largest group, out-of-range ids]
+    rows = int(bufs.expert_offsets[E].item())
+
+    stage_ns = {}
+    for i, lab in enumerate(labels):   # mean over repeats, summed per stage label
+        stage_ns[lab] = stage_ns.get(lab, 0.0) + math.fsum(r[i] for r in per_rep) / repeats
+    summary = summarize(stage_ns)
+    parts = {p for lab in labels for p in lab.split("+")}
+    gates = {
+        "stages_in_vocabulary": parts <= set(MOE_STAGES),
+        "times_non_negative": all(v >= 0 for r in per_rep for v in r),
+        "output_finite": bool(np.isfinite(ys[-1]).all()),
+        "output_identical_across_repeats": all(np.array_equal(ys[0], y) for y in ys[1:]),
+        "no_out_of_range_ids": status[1] == 0 and rows == T * k,
+    }
+    m = doc["model"]
+    result = {
+        "trace": {"schema_version": doc["schema_version"], "model": m, "dtype": doc["dtype"], "tokens": T,
+                  "source": doc.get("source", ""), "largest_group_rows": status[0],
+                  "active_experts": int((torch.diff(bufs.expert_offsets) > 0).sum().item())},
+        "replay": {"repeats": repeats, "warmup": warmup, "router_included": include_router,
+                   "calls": [{"call": name, "stage": lab} for (name, _), lab in zip(steps, labels)],
+                   "timing": "HIP events on the launch stream around every call (GPU time); every call runs "
+                             "under the roctx range of its stage"},
+        **summary,
+        "gates": gates,
+        "gates_pass": all(gates.values()),
+        "notes": ["routed SwiGLU runs in the fc1 epilogue and bills to expert_projection",
+                  "the combine overwrites y, so there is no separate accumulator_init launch",
+                  "the shared expert's gate runs inside moe_shared_expert (one label for both stages)"],
+    }
+    if return_output:
+        return result, ys[-1], layer
+    return result
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="route_trace", description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("sample", help="write a synthetic trace")
+    s.add_argument("--preset", choices=sorted(MODEL_PRESETS), default="tiny")
+    s.add_argument("--tokens", type=int, default=64)
+    s.add_argument("--seed", type=int, default=0)
+    s.add_argument("--routing", default="natural")
+    s.add_argument("--version", type=int, choices=SCHEMA_VERSIONS, default=2)
+    s.add_argument("--dtype", choices=("bf16", "f32"), default=None)
+    s.add_argument("--out", required=True)
+    v = sub.add_parser("validate", help="check a trace against the schema")
+    v.add_argument("trace")
+    r = sub.add_parser("replay", help="replay a trace through libmoe and print the stage summary")
+    r.add_argument("trace")
+    r.add_argument("--repeats", type=int, default=10)
+    r.add_argument("--warmup", type=int, default=3)
+    r.add_argument("--no-router", action="store_true")
+    r.add_argument("--out")
+    args = ap.parse_args(argv)
+    if args.cmd == "sample":
+        dtype = args.dtype or ("f32" if args.preset == "tiny" else "bf16")
+        doc = sample_trace(MODEL_PRESETS[args.preset], args.tokens, args.seed, args.routing, args.version, dtype)
+        with open(args.out, "w") as f:
+            json.dump(doc, f)
+        print(f"wrote {args.out}: {args.tokens} tokens, schema v{args.version}")
+        return 0
+    if args.cmd == "validate":
+        try:
+            load_trace(args.trace)
+        except TraceError as e:
+            print(f"invalid: {e}")
+            return 1
+        print("valid")
+        return 0
+    res = replay(load_trace(args.trace), args.repeats, args.warmup, not args.no_router)
+    text = json.dumps(res, indent=1)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+    return 0 if res["gates_pass"] else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())
