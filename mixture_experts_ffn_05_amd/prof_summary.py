@@ -6,7 +6,11 @@
 
 `trace` writes per-kernel call counts and average durations, and the summed
 average duration of the kernels whose name contains <kernel_substr> (the
-launches of one timed call; '|' separates alternatives).  `pmc` reads two counter-collection runs
+launches of one timed call; '|' separates alternatives).  `replay` tabulates route-trace replay results (per-stage GPU times and the
+shared-vs-routed split); `marker` counts the roctx stage ranges of a
+rocprofv3 marker trace.
+
+`pmc` reads two counter-collection runs
 (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), calibrates both against the
 device copy of <copy_mib> MiB that the profiled command performed first (its
 counters should read copy_mib*1024 KiB each), and writes the calibrated HBM
@@ -115,8 +119,48 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def replay(out_md: str, command: str, results: list) -> None:
+    lines = ["# Route-trace replay: per-stage GPU time", "", f"Command (per trace): `{command}`", "",
+             "Times are means over the repeats of HIP-event intervals around each libmoe call, in microseconds; "
+             "shared and routed leave out gather / scatter_combine / accumulator_init.", "",
+             "| trace | T | total us | router_topk | gather | expert_projection | scatter_combine | shared expert "
+             "| shared us | routed us | excluded us | shared fraction | gates |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for path in results:
+        r = json.load(open(path))
+        st = {k: v["wall_ns"] / 1e3 for k, v in r["stages"].items()}
+        shared = sum(v for k, v in st.items() if k.startswith("shared_expert"))
+        sp = r["shared_vs_routed"]
+        tr = r["trace"]
+        lines.append(f"| {tr['model']['name']} ({tr['source']}) | {tr['tokens']} | {r['total_profiled_ns'] / 1e3:.1f} "
+                     f"| {st.get('router_topk', 0):.1f} | {st.get('gather', 0):.1f} "
+                     f"| {st.get('expert_projection', 0):.1f} | {st.get('scatter_combine', 0):.1f} | {shared:.1f} "
+                     f"| {sp['shared_ns'] / 1e3:.1f} | {sp['routed_ns'] / 1e3:.1f} | {sp['excluded_ns'] / 1e3:.1f} "
+                     f"| {sp['shared_fraction']:.3f} | {'pass' if r['gates_pass'] else 'FAIL'} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def marker(marker_csv: str, kernel_csv: str, out_md: str, command: str) -> None:
+    """Counts of the roctx ranges (stage names) and of the kernels in one marker + kernel trace."""
+    ranges = collections.Counter(r.get("Function") or r.get("Message") for r in csv.DictReader(open(marker_csv))
+                                 if "RANGE" in r.get("Domain", ""))
+    kernels = collections.Counter(short(r["Kernel_Name"]) for r in csv.DictReader(open(kernel_csv)))
+    lines = ["# rocprofv3 marker trace of a route-trace replay", "", f"Command: `{command}`", "",
+             "| roctx range (stage) | count |", "|---|---|"]
+    lines += [f"| {k} | {v} |" for k, v in sorted(ranges.items())]
+    lines += ["", "| kernel | dispatches |", "|---|---|"]
+    lines += [f"| {k} | {v} |" for k, v in sorted(kernels.items()) if "at::" not in k]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
+    if mode == "replay":
+        replay(sys.argv[2], sys.argv[3], sys.argv[4:])
+        sys.exit(0)
+    if mode == "marker":
+        marker(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        sys.exit(0)
     if mode == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
     elif mode == "pmc":
