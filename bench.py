@@ -344,12 +344,14 @@ def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens):
     return base, parity
 
 
-def bench_backward(args, cfg, layer, bias_t, dev):
+def backward_setup(cfg, layer, bias_t, dev):
+    """State the timed backward steps start from: routes from the router, the
+    routed experts' training forward (fc1 keeping h_pre), and a seeded output
+    gradient dy = N(0, 1) / sqrt(H).  Returns (bufs, bwd, dy)."""
     lay = layer["layout"]
     x = layer["x"]
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, 0, x.dtype, dev)
     bwd = B.MoEBackwardBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, x.dtype, dev, lay)
-    # training forward of the routed experts, routes from the router
     B.moe_route_and_scatter(x, layer["w_router"], bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                             bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
                             bufs.x_scattered, bufs.route_scatter_ws)
@@ -359,6 +361,12 @@ def bench_backward(args, cfg, layer, bias_t, dev):
     B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, False)
     g = torch.Generator(device="cpu").manual_seed(1234)
     dy = (torch.randn((cfg.T, cfg.H), generator=g, dtype=torch.float32) / np.sqrt(cfg.H)).to(dev)
+    return bufs, bwd, dy
+
+
+def bench_backward(args, cfg, layer, bias_t, dev):
+    lay = layer["layout"]
+    bufs, bwd, dy = backward_setup(cfg, layer, bias_t, dev)
     torch.cuda.synchronize()
     counts = np.diff(bufs.expert_offsets.cpu().numpy())
     for _ in range(args.warmup):

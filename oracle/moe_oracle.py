@@ -615,7 +615,7 @@ def scatter_grad(dy, Ys, scatter_index, weights, *, contract: bool = False, dtyp
 
 
 def grouped_experts_backward(Xs, offsets, W1, W2, H_pre, A, dYs, *, contract: bool = False,
-                             dtype=np.float64, split_fc1: bool = False,
+                             dtype=np.float64, split_fc1: bool = False, weight_grads: bool = True,
                              _stale_row_bound: int | None = None) -> dict:
     """Input and weight gradients of every expert over its group.
 
@@ -628,6 +628,8 @@ def grouped_experts_backward(Xs, offsets, W1, W2, H_pre, A, dYs, *, contract: bo
     weight gradients are computed apart and placed side by side -- the split
     formulation that the merged one must match.  An empty group gets zero
     weight gradients.  Rows outside every group stay NaN in dH and dXs.
+    With ``weight_grads`` False the weight gradients are not formed (dW1 and
+    dW2 are None; nothing else changes).
     Returns {"dA", "dH", "dXs", "dW1" [E, H, 2I], "dW2" [E, I, H]}.
     """
     Xs = np.asarray(Xs)
@@ -638,8 +640,8 @@ def grouped_experts_backward(Xs, offsets, W1, W2, H_pre, A, dYs, *, contract: bo
     dA_all = np.full((R, I), np.nan, dtype)
     dH_all = np.full((R, 2 * I), np.nan, dtype)
     dXs = np.full((R, Hd), np.nan, dtype)
-    dW1 = np.zeros((E, Hd, 2 * I), dtype)
-    dW2 = np.zeros((E, I, np.asarray(W2[0]).shape[1]), dtype)
+    dW1 = np.zeros((E, Hd, 2 * I), dtype) if weight_grads else None
+    dW2 = np.zeros((E, I, np.asarray(W2[0]).shape[1]), dtype) if weight_grads else None
     for e, lo, hi in _group_bounds(offsets, _stale_row_bound):
         if hi <= lo:
             continue
@@ -656,16 +658,19 @@ def grouped_experts_backward(Xs, offsets, W1, W2, H_pre, A, dYs, *, contract: bo
         dA_all[lo:hi] = dA
         dH_all[lo:hi, :I] = dG
         dH_all[lo:hi, I:] = dU
-        dW2[e] = np.asarray(A[lo:hi], dtype).T @ dy
+        if weight_grads:
+            dW2[e] = np.asarray(A[lo:hi], dtype).T @ dy
         if split_fc1:
             wg, wu = w1[:, :I], w1[:, I:]
             dXs[lo:hi] = dG @ wg.T + dU @ wu.T
-            dW1[e, :, :I] = x.T @ dG
-            dW1[e, :, I:] = x.T @ dU
+            if weight_grads:
+                dW1[e, :, :I] = x.T @ dG
+                dW1[e, :, I:] = x.T @ dU
         else:
             dH = np.concatenate([dG, dU], axis=1)
             dXs[lo:hi] = dH @ w1.T
-            dW1[e] = x.T @ dH
+            if weight_grads:
+                dW1[e] = x.T @ dH
     return {"dA": dA_all, "dH": dH_all, "dXs": dXs, "dW1": dW1, "dW2": dW2}
 
 
@@ -676,7 +681,8 @@ def gather_sum(dXs, scatter_index, *, dtype=np.float64) -> np.ndarray:
 
 
 def moe_backward(x, W1, W2, routes, dy, *, contract: bool = False, dtype=np.float64,
-                 split_fc1: bool = False, _stale_row_bound: int | None = None) -> dict:
+                 split_fc1: bool = False, weight_grads: bool = True,
+                 _stale_row_bound: int | None = None) -> dict:
     """Gradients of the routed part of the layer for fixed routes.
 
     ``routes`` = (ids [T, k], weights [T, k]); ``dy`` [T, H] is the gradient of
@@ -685,7 +691,8 @@ def moe_backward(x, W1, W2, routes, dy, *, contract: bool = False, dtype=np.floa
     Returns every intermediate plus dx [T, H], dW1 [E, H, 2I], dW2 [E, I, H]
     and dweights [T, k].  ``_stale_row_bound`` exists only for the mutation
     test: it limits every group to that many rows, as a launch bound of
-    `tokens` rows would.
+    `tokens` rows would.  ``weight_grads`` False skips dW1 / dW2 (for checks
+    of dx and dweights on a sample of tokens of a large layer).
     """
     ids = np.asarray(routes[0], np.int64)
     w = np.asarray(routes[1])
@@ -697,7 +704,8 @@ def moe_backward(x, W1, W2, routes, dy, *, contract: bool = False, dtype=np.floa
     Ys = grouped_down(A, sc["offsets"], W2, dtype=dtype, _stale_row_bound=_stale_row_bound)
     dYs, dw = scatter_grad(dy, Ys, sc["scatter_index"], w, contract=contract, dtype=dtype)
     g = grouped_experts_backward(Xs, sc["offsets"], W1, W2, Hp, A, dYs, contract=contract, dtype=dtype,
-                                 split_fc1=split_fc1, _stale_row_bound=_stale_row_bound)
+                                 split_fc1=split_fc1, weight_grads=weight_grads,
+                                 _stale_row_bound=_stale_row_bound)
     out = dict(sc)
     out.update({"Xs": Xs, "H_pre": Hp, "A": A, "Ys": Ys, "dYs": dYs, "dweights": dw})
     out.update(g)

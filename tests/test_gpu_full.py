@@ -23,7 +23,7 @@ import torch
 from mixture_experts_ffn_05_amd import binding as B
 from mixture_experts_ffn_05_amd import workloads as wl
 from oracle import moe_oracle as O
-from tests.gpu_helpers import assert_output_close, check_routing, host
+from tests.gpu_helpers import assert_grad_close, assert_output_close, check_routing, host
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +140,71 @@ def test_full_size_layer_mxfp8(name):
     ref = O.token_outputs(xh[toks], ids[toks], w[toks], expert, shared=shared, contract=True, dtype=np.float32)
     mxe, rel = assert_output_close(host(bufs.y)[toks], ref["y"], "bf16", f"{name} mx y")
     print(f"[full-mx] {name}: y max|err| {mxe:.3e} rel_fro {rel:.3e} over {len(toks)} tokens", flush=True)
+
+
+BWD_FULL = ["scout", "qwen2", "v2l_decode64", "v3_decode64", "v3"]
+
+
+class _LazyExperts:
+    """Expert weights as K x N host matrices, copied from the device on first use."""
+
+    def __init__(self, w):
+        self.w, self.cache = w, {}
+
+    def __len__(self):
+        return self.w.shape[0]
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            self.cache[e] = host(self.w[e])
+        return self.cache[e]
+
+
+@pytest.mark.parametrize("name", BWD_FULL)
+def test_full_size_backward(name):
+    """The benchmark's backward step (bench.backward_setup, then bench.run_backward_step) at
+    full size.  d_x and the route-weight gradients of sampled tokens depend on those tokens'
+    rows only, so the oracle's backward over the sampled tokens gives them exactly; the weight
+    gradients of the smallest non-empty expert group are recomputed from that group's rows."""
+    import bench
+
+    cfg = wl.WORKLOADS[name]
+    print(f"[full-bwd] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k} I={cfg.I}", flush=True)
+    layer = wl.make_layer(cfg, DEV)
+    layer["shared"] = None
+    layer["layout"] = B.MOE_W_KN
+    torch.cuda.empty_cache()
+    bias_t = torch.from_numpy(layer["bias"]).to(DEV) if layer["bias"] is not None else None
+    bufs, bwd, dy = bench.backward_setup(cfg, layer, bias_t, DEV)
+    for t in (bwd.d_rows, bwd.d_h, bwd.d_x, bwd.d_w1, bwd.d_w2, bwd.d_topk_weights):
+        t.fill_(float("nan"))
+    bench.run_backward_step(layer, bufs, bwd, dy)
+    torch.cuda.synchronize()
+
+    xh = host(layer["x"])
+    ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
+    check_routing(host(bufs.logits), ids, w, xh, host(layer["w_router"]), layer["bias"], cfg.top_k, O)
+    sc = O.build_scatter(ids, cfg.E)
+    assert np.array_equal(host(bufs.scatter_index), sc["scatter_index"])
+    dyh = host(dy)
+    W1, W2 = _LazyExperts(layer["W1"]), _LazyExperts(layer["W2"])
+
+    toks = _sample_tokens(cfg.T, 8 if cfg.E >= 256 else 16, seed=cfg.T + 2)
+    ref = O.moe_backward(xh[toks], W1, W2, (ids[toks], w[toks]), dyh[toks], contract=True, dtype=np.float32,
+                         weight_grads=False)
+    assert_grad_close(host(bwd.d_x)[toks], ref["dx"], "bf16", f"{name} d_x")
+    assert_grad_close(host(bwd.d_topk_weights)[toks], ref["dweights"], "bf16", f"{name} d_topk_weights")
+
+    counts = sc["counts"]
+    e = int(np.flatnonzero(counts)[np.argmin(counts[counts > 0])])
+    sub = np.flatnonzero((ids == e).any(axis=1))
+    ids_e = np.where(ids[sub] == e, 0, -1)            # expert e as the only expert; other slots dropped
+    ref_e = O.moe_backward(xh[sub], [W1[e]], [W2[e]], (ids_e, w[sub]), dyh[sub], contract=True, dtype=np.float32)
+    assert_grad_close(host(bwd.d_w1[e]), ref_e["dW1"][0], "bf16", f"{name} d_w1[{e}] ({counts[e]} rows)")
+    assert_grad_close(host(bwd.d_w2[e]), ref_e["dW2"][0], "bf16", f"{name} d_w2[{e}] ({counts[e]} rows)")
+    empty = np.flatnonzero(counts == 0)
+    if empty.size:
+        assert not host(bwd.d_w1[int(empty[0])]).any() and not host(bwd.d_w2[int(empty[0])]).any()
+    assert torch.isfinite(bwd.d_x).all() and torch.isfinite(bwd.d_w1.float()).all()
+    print(f"[full-bwd] {name}: sampled {len(toks)} tokens, expert {e} with {counts[e]} rows; "
+          f"{empty.size} empty experts", flush=True)

@@ -163,3 +163,12 @@ def test_contract_mode_rounds_stored_intermediates_only():
     for name in ("dx", "dW1", "dW2", "dweights"):
         rel = np.linalg.norm(c[name] - e[name]) / np.linalg.norm(e[name])
         assert rel < 1e-2, (name, rel)
+
+
+def test_skipping_weight_gradients_changes_nothing_else():
+    x, W1, W2, ids, w, dy = _problem(seed=8)
+    full = O.moe_backward(x, list(W1), list(W2), (ids, w), dy, contract=True)
+    part = O.moe_backward(x, list(W1), list(W2), (ids, w), dy, contract=True, weight_grads=False)
+    assert part["dW1"] is None and part["dW2"] is None
+    for name in ("dx", "dweights", "dH", "dXs", "dYs"):
+        np.testing.assert_array_equal(part[name], full[name], err_msg=name)
