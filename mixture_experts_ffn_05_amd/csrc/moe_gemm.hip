@@ -65,7 +65,7 @@
 #define MOE_DECODE_FC1 13
 #endif
 #ifndef MOE_MID_FC1
-#define MOE_MID_FC1 10
+#define MOE_MID_FC1 23
 #endif
 #ifndef MOE_FUSE_POLICY
 #define MOE_FUSE_POLICY 0  // tuning: 0 by shape, 1 always, 2 never
@@ -1584,12 +1584,13 @@ typedef PipeCfg<128, 256, 32, 4, 2, 2> Cfg19;
 typedef PipeCfg<256, 128, 64, 3, 4, 2> Cfg20;  // 8 waves
 typedef PipeCfg<128, 128, 64, 3> Cfg21;
 typedef PipeCfg<128, 256, 64, 2, 2, 2> Cfg22;
+typedef PipeCfg<128, 256, 32, 2, 2, 4> Cfg23;  // 8 waves, 48 KiB ring: two workgroups per CU
 
 template <int V> struct CfgOf { typedef Cfg1 type; };
 #define MOE_CFG(V) template <> struct CfgOf<V> { typedef Cfg##V type; };
 MOE_CFG(2) MOE_CFG(3) MOE_CFG(4) MOE_CFG(5) MOE_CFG(6) MOE_CFG(7) MOE_CFG(8) MOE_CFG(9) MOE_CFG(10)
 MOE_CFG(11) MOE_CFG(12) MOE_CFG(13) MOE_CFG(14) MOE_CFG(15) MOE_CFG(16) MOE_CFG(17) MOE_CFG(18)
-MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22)
+MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22) MOE_CFG(23)
 #undef MOE_CFG
 
 // Calls f(Cfg{}) for configuration number v.  The shipped build instantiates
@@ -1602,7 +1603,7 @@ hipError_t with_cfg(int v, F&& f) {
 #define MOE_CASE(V) case V: return f(typename CfgOf<V>::type{});
     MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8) MOE_CASE(9)
     MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
-    MOE_CASE(17) MOE_CASE(18) MOE_CASE(19) MOE_CASE(20) MOE_CASE(21) MOE_CASE(22)
+    MOE_CASE(17) MOE_CASE(18) MOE_CASE(19) MOE_CASE(20) MOE_CASE(21) MOE_CASE(22) MOE_CASE(23)
 #undef MOE_CASE
     default: return f(Cfg1{});
   }
@@ -1626,8 +1627,10 @@ hipError_t with_cfg(int v, F&& f) {
 //    in flight, stream the expert weights;
 //  * everything else (skewed routing, many mid-sized groups) takes 128-row
 //    tiles, which waste fewer MFMA rows on partial tiles: fc1 a 128x256 tile
-//    with 8 waves (half the activation re-reads of a 128-column tile), fc2 the
-//    128x128 tile with two workgroups per CU.
+//    with 8 waves and 32-deep slices (half the activation re-reads of a
+//    128-column tile; its 48 KiB ring leaves room for two workgroups per CU,
+//    5-9% faster than 64-deep slices at one per CU), fc2 the 128x128 tile
+//    with two workgroups per CU.
 int64_t rows_per_active_group(const GemmParams<bf16_t>& p) {
   const int64_t active = p.groups < p.rows ? p.groups : p.rows;  // at most one group per row
   return (int64_t)p.rows / (active > 0 ? active : 1);
