@@ -488,8 +488,9 @@ __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const
   const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i)
-    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                     MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+    if (C::STAGES != 2 || a_off[i] >= 0)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                       MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i)
     __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
@@ -509,8 +510,9 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                       MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+      if (C::STAGES != 2 || a_off[i] >= 0)
+        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                         MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
@@ -649,13 +651,17 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
   const int K = p.K, ldb = p.ldb;
 
   // Per-lane source offsets (elements) of this wave's direct loads, slice 0.
+  // Rows past the group end only feed output rows that are never stored: with
+  // a 2-stage ring (whose waits drain every load) they are not fetched at all
+  // (offset -1) and their LDS rows keep stale data; deeper rings, whose waits
+  // count loads per slice, fetch the group's last row instead.
   int64_t a_off[C::kALoads];
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i) {
     const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
     const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
     const int row = min(row0 + r, row_end - 1);
-    a_off[i] = (int64_t)row * K + chunk * 8;
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
   }
   int b_off[C::kBLoads];
 #pragma unroll
