@@ -832,6 +832,12 @@ typedef MxCfg<32, 64, 128, 4, 1, 1, 4> MxCfg3;    // 64 columns, 4 split-K waves
 #ifndef MOE_MX_VARIANT
 #define MOE_MX_VARIANT 2
 #endif
+typedef MxCfg<128, 128, 128, 2, 2, 2, 1> MxCfgP1;   // prefill: 128-row tiles, 4 waves
+typedef MxCfg<128, 256, 128, 2, 2, 4, 1> MxCfgP2;   // prefill: 128 x 256, 8 waves
+#ifndef MOE_MX_PREFILL
+#define MOE_MX_PREFILL 2
+#endif
+typedef typename std::conditional<MOE_MX_PREFILL == 2, MxCfgP2, MxCfgP1>::type MxCfgPrefill;
 typedef typename std::conditional<MOE_MX_VARIANT == 2, MxCfg2,
                                   typename std::conditional<MOE_MX_VARIANT == 3, MxCfg3, MxCfg1>::type>::type MxCfgUsed;
 
@@ -1532,9 +1538,8 @@ hipError_t launch_pipe(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, int SAX, int ROLE>
-hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  typedef MxCfgUsed C;
+template <int EPI, int SAX, int ROLE, class C>
+hipError_t launch_mx8_cfg(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_mx8<EPI, C, SAX, ROLE>), hipFuncAttributeMaxDynamicSharedMemorySize,
       C::kLds);
@@ -1547,9 +1552,21 @@ hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI_R, int EPI_S, int SAX>
-hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
-  typedef MxCfgUsed C;
+// Groups of at most 32 rows on average (decode) take the 32-row tile; larger
+// ones a 128-row tile, which converts each weight fragment once per 128 rows.
+inline bool mx_decode_shape(const GemmParams<bf16_t>& p) {
+  const int64_t active = p.groups < p.rows ? p.groups : p.rows;
+  return (int64_t)p.rows / (active > 0 ? active : 1) <= 32;
+}
+
+template <int EPI, int SAX, int ROLE>
+hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
+  if (MOE_MX_PREFILL != 0 && !mx_decode_shape(p)) return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgPrefill>(p, cu_count, s);
+  return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgUsed>(p, cu_count, s);
+}
+
+template <int EPI_R, int EPI_S, int SAX, class C>
+hipError_t launch_mx8_fused_cfg(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_mx8_fused<EPI_R, EPI_S, C, SAX>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -1563,6 +1580,13 @@ hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu
   const int grid = persistent_grid(ub_r + tiles_s, cu_count * C::kWgsPerCu);
   hipLaunchKernelGGL((grouped_gemm_mx8_fused<EPI_R, EPI_S, C, SAX>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
   return hipGetLastError();
+}
+
+template <int EPI_R, int EPI_S, int SAX>
+hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
+  if (MOE_MX_PREFILL != 0 && !(mx_decode_shape(pr) && ps.rows <= 64))
+    return launch_mx8_fused_cfg<EPI_R, EPI_S, SAX, MxCfgPrefill>(pr, ps, cu_count, s);
+  return launch_mx8_fused_cfg<EPI_R, EPI_S, SAX, MxCfgUsed>(pr, ps, cu_count, s);
 }
 
 // Pipelined configurations (BM, BN, BK, STAGES, WM, WN, KW), numbered for
