@@ -924,8 +924,9 @@ __device__ __forceinline__ void mx_step(unsigned char* __restrict__ wst, const u
   if (issue) {
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                       MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+      if (C::STAGES != 2 || a_off[i] >= 0)
+        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                         MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
@@ -980,13 +981,14 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
     return nc < p.N ? nc : 0;
   };
 
+  // Rows past the group end: not fetched in 2-stage rings, as in run_tile_pipe.
   int64_t a_off[C::kALoads];
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i) {
     const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
     const int chunk = (lane % C::kAChunks) ^ row_swizzle<C::kARow>(r);
     const int row = min(row0 + r, row_end - 1);
-    a_off[i] = (int64_t)row * K + chunk * 8;
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
   }
   int b_off[C::kBLoads];
 #pragma unroll
@@ -1032,8 +1034,9 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
       const unsigned char* s_k = bs + (int64_t)s * kSStep;
 #pragma unroll
       for (int i = 0; i < C::kALoads; ++i)
-        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                         MOE_LDS(void, st + (wave_ * C::kALoads + i) * 1024), 16, 0, 0);
+        if (C::STAGES != 2 || a_off[i] >= 0)
+          __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                           MOE_LDS(void, st + (wave_ * C::kALoads + i) * 1024), 16, 0, 0);
 #pragma unroll
       for (int i = 0; i < C::kBLoads; ++i)
         __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
