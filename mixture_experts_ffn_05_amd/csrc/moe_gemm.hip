@@ -67,6 +67,9 @@
 #ifndef MOE_MID_FC1
 #define MOE_MID_FC1 23
 #endif
+#ifndef MOE_MID_FC2
+#define MOE_MID_FC2 23
+#endif
 #ifndef MOE_FUSE_POLICY
 #define MOE_FUSE_POLICY 0  // tuning: 0 by shape, 1 always, 2 never
 #endif
@@ -1643,6 +1646,7 @@ hipError_t with_cfg(int v, F&& f) {
 #else
   if (v == 8) return f(Cfg8{});
   if (v == MOE_MID_FC1) return f(typename CfgOf<MOE_MID_FC1>::type{});
+  if (v == MOE_MID_FC2) return f(typename CfgOf<MOE_MID_FC2>::type{});
   if (v == MOE_DECODE_FC1) return f(typename CfgOf<MOE_DECODE_FC1>::type{});
   if (v == MOE_DECODE_FC2) return f(typename CfgOf<MOE_DECODE_FC2>::type{});
   return f(Cfg1{});
@@ -1654,19 +1658,39 @@ hipError_t with_cfg(int v, F&& f) {
 // layers):
 //  * groups that average 512 rows or more (the shared expert, dense prefill)
 //    take the 256x256 tile with 8 waves, which halves the L2->LDS traffic per
-//    MFMA and keeps two waves per SIMD;
+//    MFMA and keeps two waves per SIMD.
+//    That tile gives way to the 128x128 one when its tiles would fill the
+//    CUs' workgroup slots much less evenly (a narrow output with few row
+//    tiles: 128 tiles of 256x256 leave half the CUs idle, where 512 tiles of
+//    128x128 fill both slots of every CU; 158 us against 118 us for the
+//    Qwen2-shaped shared fc2);
 //  * groups of at most 32 rows (decode) take a 32-row tile whose waves split
 //    the reduction, so that many more tiles, each with several weight slices
 //    in flight, stream the expert weights;
 //  * everything else (skewed routing, many mid-sized groups) takes 128-row
-//    tiles, which waste fewer MFMA rows on partial tiles: fc1 a 128x256 tile
-//    with 8 waves and 32-deep slices (half the activation re-reads of a
+//    tiles, which waste fewer MFMA rows on partial tiles: a 128x256 tile with
+//    8 waves and 32-deep slices (half the activation or weight re-reads of a
 //    128-column tile; its 48 KiB ring leaves room for two workgroups per CU,
-//    5-9% faster than 64-deep slices at one per CU), fc2 the 128x128 tile
-//    with two workgroups per CU.
+//    5-9% faster than 64-deep slices at one per CU for fc1, 4-11% faster than
+//    the 128x128 tile for fc2).  Deeper rings (3-8 slices in flight at one
+//    workgroup per CU) measured 3-15% slower on every prefill shape.
 int64_t rows_per_active_group(const GemmParams<bf16_t>& p) {
   const int64_t active = p.groups < p.rows ? p.groups : p.rows;  // at most one group per row
   return (int64_t)p.rows / (active > 0 ? active : 1);
+}
+
+// Share of the workgroup slots (slots = CUs x workgroups per CU) that the
+// tiles of a configuration keep busy over all its waves of tiles, for groups
+// of equal size.
+template <int EPI, class C>
+double slot_fill(const GemmParams<bf16_t>& p, int cu_count) {
+  const int64_t groups = p.groups > 0 ? p.groups : 1;
+  const int64_t per_group = (p.rows + groups - 1) / groups;
+  const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
+  const int64_t tiles = groups * ((per_group + C::BM - 1) / C::BM) * ((p.N + out_cols - 1) / out_cols);
+  const int64_t slots = (int64_t)cu_count * C::kWgsPerCu;
+  const int64_t waves = (tiles + slots - 1) / slots;
+  return waves > 0 ? (double)tiles / (double)(waves * slots) : 1.0;
 }
 
 constexpr int64_t kDecodeRows = 32;
@@ -1675,13 +1699,14 @@ template <int EPI>
 constexpr int decode_variant() { return paired(EPI) ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
 
 template <int EPI, int ROLE>
-int pick_pipe_variant(const GemmParams<bf16_t>& p) {
+int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
   if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
   if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
-  if (rows_per_group >= 512) return 8;
+  if (rows_per_group >= 512)
+    return slot_fill<EPI, Cfg8>(p, cu_count) + 0.25 < slot_fill<EPI, Cfg1>(p, cu_count) ? 1 : 8;
   if (ROLE == 2) return MOE_MID_DGRAD;
-  return paired(EPI) ? MOE_MID_FC1 : 1;
+  return paired(EPI) ? MOE_MID_FC1 : MOE_MID_FC2;
 }
 
 template <int EPI_R, int EPI_S, class C, bool BT>
@@ -1718,8 +1743,8 @@ hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16
   else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
            ps.K % 128 == 0)
     v = decode_variant<EPI_R>();
-  else if (paired(EPI_R))
-    v = MOE_MID_FC1;
+  else
+    v = paired(EPI_R) ? MOE_MID_FC1 : MOE_MID_FC2;
   if (pr.bt)
     return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), true>(pr, ps, cu_count, s); });
   return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), false>(pr, ps, cu_count, s); });
@@ -1729,9 +1754,9 @@ template <int EPI, int ROLE>
 hipError_t launch_bf16(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
   if (p.K % 64 == 0) {
     if (p.bt)
-      return with_cfg(pick_pipe_variant<EPI, ROLE>(p),
+      return with_cfg(pick_pipe_variant<EPI, ROLE>(p, cu_count),
                       [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, true>(p, cu_count, s); });
-    return with_cfg(pick_pipe_variant<EPI, ROLE>(p),
+    return with_cfg(pick_pipe_variant<EPI, ROLE>(p, cu_count),
                     [&](auto c) { return launch_pipe<EPI, decltype(c), ROLE, false>(p, cu_count, s); });
   }
   p.n_tiles = paired(EPI) ? (p.N + 63) / 64 : (p.N + 127) / 128;
