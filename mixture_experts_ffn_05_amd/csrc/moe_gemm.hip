@@ -73,6 +73,9 @@
 #ifndef MOE_FUSE_POLICY
 #define MOE_FUSE_POLICY 0  // tuning: 0 by shape, 1 always, 2 never
 #endif
+#ifndef MOE_DENSE
+#define MOE_DENSE 8       // groups averaging >= 512 rows
+#endif
 #ifndef MOE_DECODE_FC2
 #define MOE_DECODE_FC2 13
 #endif
@@ -645,7 +648,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
 }
 
 template <int EPI, class C, bool BT>
-__device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+__device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
@@ -724,6 +727,215 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
   finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+}
+
+
+// MFMA fragments of one 16-deep substep of a wave: its activation blocks and
+// its weight blocks.
+template <class C>
+struct PipeFrags {
+  u32x4 a[C::kMB];
+  u32x4 b[C::kNB];
+};
+
+// Reads the fragments of substep `ks` of the slice held in ring stage `rst`.
+template <int EPI, class C, bool BT>
+__device__ __forceinline__ void pipe_read(const unsigned char* __restrict__ rst, int ks, int wm, int wn,
+                                          PipeFrags<C>& f) {
+  const int lane = threadIdx.x & 63;
+  const unsigned char* As = rst;
+  const unsigned char* Bs = rst + C::kAStage;
+  const int grp = lane >> 4, s16 = lane & 15;
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb) {
+    const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+    const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(m);
+    f.a[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
+  }
+#pragma unroll
+  for (int nb = 0; nb < C::kNB; ++nb) {
+    if constexpr (BT) {  // [n][k] tile: one 16-byte read of 8 consecutive k, as for the activations
+      const int n = pipe_col_base<EPI, C>(nb, wn) + (lane & 31);
+      const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(n);
+      f.b[nb] = *(const u32x4*)(Bs + n * C::kARow + chunk * 16);
+    } else {
+      const int b_row_in = 8 * (grp >> 1) + (s16 >> 2);  // k row inside a 16-k substep; row & 3 == s16 >> 2
+      const int c0 = pipe_col_base<EPI, C>(nb, wn) + 16 * (grp & 1);
+      const int row = 16 * ks + b_row_in;
+      const int chunk = (c0 / 8 + ((s16 & 3) >> 1)) ^ b_swizzle<C>(s16 >> 2);
+      const unsigned char* ptr = Bs + row * (2 * C::BN) + chunk * 16 + (s16 & 1) * 8;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * (2 * C::BN)));
+      f.b[nb] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void pipe_mfmas(const PipeFrags<C>& f, f32x16 (&acc)[C::kMB][C::kNB]) {
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb) acc[mb][nb] = mfma32(f.a[mb], f.b[nb], acc[mb][nb]);
+}
+
+// Scheduling pattern of one substep: each MFMA is followed by up to PER LDS
+// reads of the next substep's fragments (R reads in all), so that the reads
+// run under the MFMAs and the last MFMAs leave the reads time to land.
+template <int I, int M, int R, int PER>
+__device__ __forceinline__ void sched_mfma_reads() {
+  if constexpr (I < M) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int r = R < PER ? R : PER;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
+    sched_mfma_reads<I + 1, M, R - r, PER>();
+  }
+}
+
+template <class C, bool BT>
+__device__ __forceinline__ void sched_substep() {
+  constexpr int M = C::kMB * C::kNB;
+  constexpr int R = C::kMB + C::kNB * (BT ? 1 : 2);
+  constexpr int slots = M > 2 ? M - 2 : 1;
+  sched_mfma_reads<0, M, R, (R + slots - 1) / slots>();
+}
+
+// Main loop with the fragments of the next substep read while the MFMAs of
+// the current one run, across slice boundaries too: a slice's last substep
+// first waits for the next slice (its own loads, then the workgroup barrier,
+// after which no wave reads the current stage any more), refills the current
+// stage with the slice STAGES ahead, and reads the next slice's first
+// fragments; only then do its MFMAs run.  A wave's substeps alternate between
+// two fragment sets, so the number of substeps per slice must be even.
+template <int EPI, class C, bool BT>
+__device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+                                                 unsigned char* __restrict__ smem) {
+  static_assert(C::kKSW % 2 == 0, "substeps per slice alternate between two fragment sets");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kw = wave / C::kPos, wpos = wave % C::kPos;
+  const int wm = wpos / C::WN, wn = wpos % C::WN;
+  const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
+  const int K = p.K, ldb = p.ldb;
+
+  int64_t a_off[C::kALoads];
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i) {
+    const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
+    const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
+    const int row = min(row0 + r, row_end - 1);
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
+  }
+  int b_off[C::kBLoads];
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i) {
+    if constexpr (BT) {
+      const int r = (wave * C::kBLoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
+      const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
+      int nrow;
+      if (paired(EPI)) {
+        const int half = C::BN / 2;
+        const int nc = n0 + r % half;
+        nrow = (nc < p.N ? nc : 0) + (r < half ? 0 : p.up_off);
+      } else {
+        const int nc = n0 + r;
+        nrow = nc < p.N ? nc : 0;
+      }
+      b_off[i] = nrow * ldb + chunk * 8;
+    } else {
+      const int kr = (wave * C::kBLoads + i) * C::kBRowsPerLoad + lane / C::kBChunks;
+      const int chunk = (lane % C::kBChunks) ^ b_swizzle<C>(kr);
+      int col;
+      if (paired(EPI)) {
+        const int half = C::kBChunks / 2;
+        const int nc = n0 + 8 * (chunk % half);
+        col = (nc < p.N ? nc : 0) + (chunk < half ? 0 : p.up_off);
+      } else {
+        const int nc = n0 + 8 * chunk;
+        col = nc < p.N ? nc : 0;
+      }
+      b_off[i] = kr * ldb + col;
+    }
+  }
+  const int64_t b_step = BT ? (int64_t)C::BK : (int64_t)C::BK * ldb;
+  const int nk = K / C::BK;
+
+  f32x16 acc[C::kMB][C::kNB];
+#pragma unroll
+  for (int mb = 0; mb < C::kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::kNB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+  const bf16_t* a_base = p.a;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off);
+  // slice 0 has landed in every wave (newer slices may still be in flight)
+  if (nk - 1 >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+  lds_barrier();
+  // the last stage is free: slice STAGES-1 goes there (later slices are issued
+  // at the slice boundaries below, STAGES slices ahead)
+  if (C::STAGES - 1 < nk)
+    pipe_issue<C>(smem + (C::STAGES - 1) * C::kStage, a_base + (C::STAGES - 1) * C::BK,
+                  bg + (C::STAGES - 1) * b_step, a_off, b_off);
+
+  PipeFrags<C> f0, f1;
+  pipe_read<EPI, C, BT>(smem, kw, wm, wn, f0);
+  // One slice; the last one (LAST) has no boundary.  The last slice is peeled
+  // off the loop so that no branch separates a boundary's reads from the
+  // MFMAs that hide them.
+  auto slice = [&](int kt, auto last) {
+    const unsigned char* rst = smem + (kt % C::STAGES) * C::kStage;
+#pragma unroll
+    for (int j = 0; j < C::kKSW; ++j) {
+      PipeFrags<C>& cur = (j & 1) ? f1 : f0;
+      PipeFrags<C>& nxt = (j & 1) ? f0 : f1;
+      if (j + 1 < C::kKSW) {
+        pipe_read<EPI, C, BT>(rst, kw + (j + 1) * C::KW, wm, wn, nxt);
+      } else if constexpr (!decltype(last)::value) {
+        // the previous substep's MFMAs all issue before this wave waits at the barrier
+        __builtin_amdgcn_sched_barrier(0);
+        if (nk - 2 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
+        lds_barrier();
+        const int kn = kt + C::STAGES;
+        if (kn < nk)
+          pipe_issue<C>(smem + (kt % C::STAGES) * C::kStage, a_base + kn * C::BK, bg + kn * b_step, a_off, b_off);
+        pipe_read<EPI, C, BT>(smem + ((kt + 1) % C::STAGES) * C::kStage, kw, wm, wn, nxt);
+      }
+      pipe_mfmas<C>(cur, acc);
+      sched_substep<C, BT>();
+    }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::false_type{});
+  slice(nk - 1, std::true_type{});
+  lds_barrier();  // every wave is done with the ring before the next tile refills it
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+}
+
+#ifndef MOE_PIPE_LOOP
+#define MOE_PIPE_LOOP 1
+#endif
+
+// The loop with two fragment sets holds about 24-48 more VGPRs per lane; it is
+// used where each SIMD runs at most two waves of the kernel (256 VGPRs each).
+// With four waves per SIMD the extra registers would cost a workgroup per CU
+// (128x256x32 with 8 waves: 117 -> 140 VGPRs, 12-24% slower measured).
+template <class C>
+constexpr bool pipe_loop_v1() {
+  return MOE_PIPE_LOOP == 1 && C::kKSW % 2 == 0 && C::kWgsPerCu * C::kWaves <= 8;
+}
+
+template <int EPI, class C, bool BT>
+__device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+                                              unsigned char* __restrict__ smem) {
+  if constexpr (pipe_loop_v1<C>())
+    run_tile_pipe_v1<EPI, C, BT>(p, g, row0, row_end, n0, smem);
+  else
+    run_tile_pipe_v0<EPI, C, BT>(p, g, row0, row_end, n0, smem);
 }
 
 template <int EPI, class C, int ROLE, bool BT>
@@ -1621,12 +1833,14 @@ typedef PipeCfg<256, 128, 64, 3, 4, 2> Cfg20;  // 8 waves
 typedef PipeCfg<128, 128, 64, 3> Cfg21;
 typedef PipeCfg<128, 256, 64, 2, 2, 2> Cfg22;
 typedef PipeCfg<128, 256, 32, 2, 2, 4> Cfg23;  // 8 waves, 48 KiB ring: two workgroups per CU
+typedef PipeCfg<128, 256, 32, 2, 2, 2> Cfg24;  // 4 waves of 64x128, 48 KiB ring: two workgroups per CU
+typedef PipeCfg<128, 256, 32, 2, 1, 2> Cfg25;  // 2 waves of 128x128, 48 KiB ring: two workgroups per CU
 
 template <int V> struct CfgOf { typedef Cfg1 type; };
 #define MOE_CFG(V) template <> struct CfgOf<V> { typedef Cfg##V type; };
 MOE_CFG(2) MOE_CFG(3) MOE_CFG(4) MOE_CFG(5) MOE_CFG(6) MOE_CFG(7) MOE_CFG(8) MOE_CFG(9) MOE_CFG(10)
 MOE_CFG(11) MOE_CFG(12) MOE_CFG(13) MOE_CFG(14) MOE_CFG(15) MOE_CFG(16) MOE_CFG(17) MOE_CFG(18)
-MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22) MOE_CFG(23)
+MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22) MOE_CFG(23) MOE_CFG(24) MOE_CFG(25)
 #undef MOE_CFG
 
 // Calls f(Cfg{}) for configuration number v.  The shipped build instantiates
@@ -1640,11 +1854,12 @@ hipError_t with_cfg(int v, F&& f) {
     MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8) MOE_CASE(9)
     MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
     MOE_CASE(17) MOE_CASE(18) MOE_CASE(19) MOE_CASE(20) MOE_CASE(21) MOE_CASE(22) MOE_CASE(23)
+    MOE_CASE(24) MOE_CASE(25)
 #undef MOE_CASE
     default: return f(Cfg1{});
   }
 #else
-  if (v == 8) return f(Cfg8{});
+  if (v == MOE_DENSE) return f(typename CfgOf<MOE_DENSE>::type{});
   if (v == MOE_MID_FC1) return f(typename CfgOf<MOE_MID_FC1>::type{});
   if (v == MOE_MID_FC2) return f(typename CfgOf<MOE_MID_FC2>::type{});
   if (v == MOE_DECODE_FC1) return f(typename CfgOf<MOE_DECODE_FC1>::type{});
@@ -1704,7 +1919,9 @@ int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
   if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   if (rows_per_group >= 512)
-    return slot_fill<EPI, Cfg8>(p, cu_count) + 0.25 < slot_fill<EPI, Cfg1>(p, cu_count) ? 1 : 8;
+    return slot_fill<EPI, typename CfgOf<MOE_DENSE>::type>(p, cu_count) + 0.25 < slot_fill<EPI, Cfg1>(p, cu_count)
+               ? 1
+               : MOE_DENSE;
   if (ROLE == 2) return MOE_MID_DGRAD;
   return paired(EPI) ? MOE_MID_FC1 : MOE_MID_FC2;
 }
@@ -1739,7 +1956,7 @@ hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16
   if (MOE_PIPE_VARIANT != 0)
     v = MOE_PIPE_VARIANT;
   else if (per_group >= 512 && ps.rows >= 512)
-    v = 8;
+    v = MOE_DENSE;
   else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
            ps.K % 128 == 0)
     v = decode_variant<EPI_R>();
