@@ -10,6 +10,9 @@ launches of one timed call; '|' separates alternatives).  `replay` tabulates rou
 shared-vs-routed split); `marker` counts the roctx stage ranges of a
 rocprofv3 marker trace.
 
+`sq` tabulates SQ/TA/TD counter runs per kernel (MFMA busy share, waiting
+shares, texture-data unit busy and stalled shares, implied clock).
+
 `pmc` reads two counter-collection runs
 (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), calibrates both against the
 device copy of <copy_mib> MiB that the profiled command performed first (its
@@ -119,6 +122,49 @@ def pmc(fetch_dir: str, write_dir: str, copy_mib: float, kernel_substr: str, out
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def sq(out_md: str, command: str, dirs: list, cus: int = 256, xcds: int = 8) -> None:
+    """Per-kernel averages of the SQ/TA/TD counters of several counter runs (one
+    directory each), with ratios that need no unit assumptions (waiting shares of
+    the wave cycles) and ratios that take GRBM_GUI_ACTIVE as the sum over the XCDs
+    of the kernel's clock cycles (MFMA busy per SIMD cycle, TD busy per CU cycle,
+    and the clock implied by the dispatch duration)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(path)):
+                k = r["Kernel_Name"]
+                if "moe::" not in k:
+                    continue
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    avg = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    lines = ["# rocprofv3 SQ / TA / TD counters per kernel", "",
+             f"Command (one run per counter set): `{command}`", "",
+             "Ratios: *wait* = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of resident wave time spent in s_waitcnt); "
+             "*LDS wait* = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; *MFMA busy* = SQ_VALU_MFMA_BUSY_CYCLES / "
+             f"({cus * 4} SIMDs x cycles); *TD busy*, *TD stalled on TC* = TD_TD_BUSY, TD_TC_STALL / ({cus} CUs x "
+             f"cycles); cycles = GRBM_GUI_ACTIVE / {xcds} (taken as summed over the XCDs); *clock* = cycles / the "
+             "dispatch's duration under counter collection. For short kernels the counter window outlasts the dispatch "
+             "(implied clocks above the 2.4 GHz maximum); the clock and the cycle-based shares are meaningful only for "
+             "the long GEMM launches.", "",
+             "| kernel | dispatches | MFMA insts | MFMA busy | wait | LDS wait | LDS bank conflicts | TD busy | "
+             "TD stalled on TC | clock GHz |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(vals):
+        v = {c: avg(x) for c, x in vals[k].items()}
+        cyc = v.get("GRBM_GUI_ACTIVE", float("nan")) / xcds
+        wc = v.get("SQ_WAVE_CYCLES", float("nan"))
+        pct = lambda a, b: f"{100.0 * a / b:.0f}%" if b == b and b > 0 and a == a else "n/a"
+        lines.append(
+            f"| {short(k)} | {len(vals[k].get('SQ_WAVES', []))} | {v.get('SQ_INSTS_MFMA', float('nan')):.4g} | "
+            f"{pct(v.get('SQ_VALU_MFMA_BUSY_CYCLES', float('nan')), cus * 4 * cyc)} | "
+            f"{pct(v.get('SQ_WAIT_ANY', float('nan')), wc)} | {pct(v.get('SQ_WAIT_INST_LDS', float('nan')), wc)} | "
+            f"{v.get('SQ_LDS_BANK_CONFLICT', float('nan')):.4g} | {pct(v.get('TD_TD_BUSY', float('nan')), cus * cyc)} | "
+            f"{pct(v.get('TD_TC_STALL', float('nan')), cus * cyc)} | {cyc / avg(dur[k]) / 1e9:.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def replay(out_md: str, command: str, results: list) -> None:
     lines = ["# Route-trace replay: per-stage GPU time", "", f"Command (per trace): `{command}`", "",
              "Times are means over the repeats of HIP-event intervals around each libmoe call, in microseconds; "
@@ -160,6 +206,10 @@ if __name__ == "__main__":
         sys.exit(0)
     if mode == "marker":
         marker(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        sys.exit(0)
+    if mode == "sq":  # sq <out.md> <dir> [<dir> ...] -- <command...>
+        cut = sys.argv.index("--")
+        sq(sys.argv[2], " ".join(sys.argv[cut + 1:]), sys.argv[3:cut])
         sys.exit(0)
     if mode == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
