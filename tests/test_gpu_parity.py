@@ -27,6 +27,9 @@ CASES = [
     wl.LayerConfig("big_groups_bf16", "bf16", T=1100, H=512, E=2, top_k=1, I=320, I_s=192, gated=True),
     # a light shared expert next to >= 512-row routed groups: one launch with the 256x256 tile
     wl.LayerConfig("fused_big_bf16", "bf16", T=1024, H=512, E=2, top_k=1, I=2048, I_s=64, gated=True),
+    # the 256x256 tile with one 64-deep slice (fc1, shared fc2) and two (fc2): the main loop's
+    # shortest reductions, with no slice boundary and with one boundary that refills nothing
+    wl.LayerConfig("big_groups_short_k_bf16", "bf16", T=1030, H=64, E=2, top_k=1, I=128, I_s=64),
 ]
 
 
