@@ -4,7 +4,8 @@
                     [--no-cpu-baseline] [--cpu-sample TOKENS]
 
 One step = the whole layer through libmoe (routing and scatter build in one
-call, grouped fc1 + SwiGLU with the shared expert's fc1 in the same launch,
+call, with no copy of the routed rows: fc1 gathers them from x on load;
+grouped fc1 + SwiGLU with the shared expert's fc1 in the same launch,
 grouped fc2 with the shared expert's fc2 and gate in the same launch,
 gather/combine) over one batch of synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
 between two stream synchronisations.  Prints ONE JSON line.
@@ -158,22 +159,30 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
         rec(4)
         return
+    gather = layer.get("gather", False)   # fc1 reads the routed rows from x through row_token
     rec(0)
     B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                             bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                            bufs.x_scattered, bufs.route_scatter_ws)
+                            None if gather else bufs.x_scattered, bufs.route_scatter_ws)
     rec(1)
     if shared is not None:
         ws1, ws2, wg = shared
-        B.moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
-                                            bufs.act_shared, layout=lay)
+        if gather:
+            B.moe_grouped_swiglu_fc1_and_shared_gather(x, bufs.row_token, bufs.expert_offsets, W1, bufs.act, ws1,
+                                                       bufs.act_shared, layout=lay)
+        else:
+            B.moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
+                                                bufs.act_shared, layout=lay)
         rec(2)
         B.moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
                                      bufs.y, bufs.shared_ws, False, layout=lay)
         rec(3)
         B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, bufs.topk_weights, bufs.y, True)
     else:
-        B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, layout=lay)
+        if gather:
+            B.moe_grouped_swiglu_fc1_gather(x, bufs.row_token, bufs.expert_offsets, W1, bufs.act, layout=lay)
+        else:
+            B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, layout=lay)
         rec(2)
         B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, layout=lay)
         rec(3)
@@ -449,6 +458,9 @@ def main():
     ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
                     help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default: measured "
                          "as fast or faster on every workload), nk = [N, K] (torch.nn.Linear layout)")
+    ap.add_argument("--rows", choices=("gather", "copy"), default="gather",
+                    help="routed rows for fc1: gathered from x through row_token on load (default), or copied to "
+                         "x_scattered by the scatter build (the MXFP8 and overlap paths always copy)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the routed experts (for the routes a forward realized) instead of "
                          "the forward")
@@ -507,6 +519,7 @@ def main():
     if args.weights == "mxfp8":
         mode = "mx"
     side = torch.cuda.Stream() if mode == "overlap" else None
+    layer["gather"] = args.rows == "gather" and mode in ("fused", "none")
     for _ in range(args.warmup):
         run_step(layer, bufs, cfg, bias_t, side=side)
     torch.cuda.synchronize()
@@ -553,7 +566,8 @@ def main():
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
-    tr = committed_traffic(cfg.name) if mode != "mx" and args.layout == "kn" else None
+    # the committed counters were taken in the default configuration (fused shared expert, [K, N], gathered rows)
+    tr = committed_traffic(cfg.name) if mode == "fused" and args.layout == "kn" and layer["gather"] else None
     roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per fc1 call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     roof["algorithmic_bytes"] = work["fc1_bytes"]
@@ -606,6 +620,8 @@ def main():
                           else "fc1/fc2 are the routed experts only"),
         "timing": "hip graph replay" if args.graph else "eager launches",
         "weight_layout": "[N, K] per expert (torch.nn.Linear)" if args.layout == "nk" else "[K, N] per expert",
+        "routed_rows": ("gathered from x through row_token by fc1" if layer["gather"]
+                        else "copied to x_scattered by the scatter build"),
         "weights": ("MXFP8 (e4m3 + e8m0 per 8 along the intermediate axis), dequantized to bf16 in the kernels"
                     if args.weights == "mxfp8" else "bf16"),
         "shared_expert": {"mx": "inside the routed fc1/fc2 launches (MXFP8 *_and_shared_mx8 calls)",

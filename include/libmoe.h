@@ -138,7 +138,10 @@ size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  * out-of-range expert ids} -- a non-zero second word means the routes were
  * invalid and those pairs were dropped; x_scattered [R, H] (dt):
  * x_scattered[r] = x[row_token[r]] for r < expert_offsets[E], other rows
- * untouched.  workspace: device scratch of at least
+ * untouched.  x_scattered may be NULL: the rows are then not copied, and the
+ * *_gather fc1 calls below read them from x through row_token on load (the
+ * same values, without writing and re-reading R*H elements).  The same holds
+ * for moe_route_and_scatter.  workspace: device scratch of at least
  * moe_build_scatter_workspace_bytes(T, top_k, E) bytes, contents undefined
  * on entry and exit.
  */
@@ -357,6 +360,31 @@ moe_status moe_grouped_fc2_and_shared(moe_dtype dt, moe_weight_layout wl, const 
                                       int32_t H, float* y_rows, const void* act_shared, const void* ws2,
                                       const void* x, const void* w_gate, int32_t T, int32_t I_s, int32_t accumulate,
                                       float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu_fc1_gather / moe_grouped_swiglu_fc1_and_shared_gather --
+ * moe_grouped_swiglu_fc1 / moe_grouped_swiglu_fc1_and_shared with the routed
+ * rows gathered from x on load instead of read from x_scattered.
+ *
+ * Source: as for moe_grouped_swiglu_fc1 (VeOmni docs "Fused MoE Kernel Notes",
+ * section "Scatter/gather layout": row r of the expert-grouped layout is token
+ * row_token[r]).  Row r of the product is x[row_token[r]] -- exactly the row
+ * moe_build_scatter would have copied to x_scattered[r] -- so act (and
+ * act_shared) are bit-identical to the non-gather calls.  x [T, H] (dt) in;
+ * row_token [R] int32 in, from moe_build_scatter or moe_route_and_scatter for
+ * the same routes (values are clamped to [0, T) on the device; only rows
+ * r < expert_offsets[E] are read).  Every other argument, the layouts, the
+ * ownership and the errors are those of the non-gather calls; additionally T
+ * must be >= 1.  bf16 and fp32; MXFP8 weights have no gather variant.
+ */
+moe_status moe_grouped_swiglu_fc1_gather(moe_dtype dt, moe_weight_layout wl, const void* x, const int32_t* row_token,
+                                         const int32_t* expert_offsets, const void* w1, int32_t T, int32_t R,
+                                         int32_t H, int32_t E, int32_t I, void* act, void* stream);
+moe_status moe_grouped_swiglu_fc1_and_shared_gather(moe_dtype dt, moe_weight_layout wl, const void* x,
+                                                    const int32_t* row_token, const int32_t* expert_offsets,
+                                                    const void* w1, int32_t R, int32_t H, int32_t E, int32_t I,
+                                                    void* act, const void* ws1, int32_t T, int32_t I_s,
+                                                    void* act_shared, void* stream);
 
 /*
  * Backward of the routed experts, routes held fixed:

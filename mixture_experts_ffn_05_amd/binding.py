@@ -74,6 +74,10 @@ _SIGNATURES = {
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                             _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "moe_grouped_swiglu_fc1_gather": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                               _c_int, _vp, _vp]),
+    "moe_grouped_swiglu_fc1_and_shared_gather": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                                          _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_grouped_swiglu_fc1_save": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                                              _vp, _vp]),
     "moe_scatter_grad": (_c_int, [_c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
@@ -237,6 +241,21 @@ def moe_grouped_swiglu_fc1(x_scattered, expert_offsets, w1, act, stream=None, la
     _check(lib.moe_grouped_swiglu_fc1(*args))
 
 
+def moe_grouped_swiglu_fc1_gather(x, row_token, expert_offsets, w1, act, stream=None, layout=MOE_W_KN):
+    """moe_grouped_swiglu_fc1 reading routed row r as x[row_token[r]] (no x_scattered)."""
+    lib = load()
+    T, H = x.shape
+    R = row_token.shape[0]
+    E, _, I = _fc1_sizes(w1, layout)
+    dev = x.device
+    wshape = (E, 2 * I, H) if layout == MOE_W_NK else (E, H, 2 * I)
+    args = (_dt(x), int(layout), _ptr(x, "x"), _ptr(row_token, "row_token", torch.int32, (R,), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", x.dtype, wshape, dev), T, R, H, E, I,
+            _ptr(act, "act", x.dtype, (R, I), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_gather(*args))
+
+
 def moe_grouped_fc2(act, expert_offsets, w2, y_rows, stream=None, layout=MOE_W_KN):
     lib = load()
     R, I = act.shape
@@ -390,6 +409,26 @@ def moe_grouped_swiglu_fc1_and_shared(x_scattered, expert_offsets, w1, act, x, w
     _check(lib.moe_grouped_swiglu_fc1_and_shared(*args))
 
 
+def moe_grouped_swiglu_fc1_and_shared_gather(x, row_token, expert_offsets, w1, act, ws1, act_shared, stream=None,
+                                             layout=MOE_W_KN):
+    """moe_grouped_swiglu_fc1_and_shared reading routed row r as x[row_token[r]] (no x_scattered)."""
+    lib = load()
+    T, H = x.shape
+    R = row_token.shape[0]
+    E, _, I = _fc1_sizes(w1, layout)
+    nk = layout == MOE_W_NK
+    I_s = (ws1.shape[0] if nk else ws1.shape[1]) // 2
+    dev = x.device
+    dt = x.dtype
+    args = (_dt(x), int(layout), _ptr(x, "x", dt, (T, H), dev), _ptr(row_token, "row_token", torch.int32, (R,), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(w1, "w1", dt, (E, 2 * I, H) if nk else (E, H, 2 * I), dev), R, H, E, I,
+            _ptr(act, "act", dt, (R, I), dev),
+            _ptr(ws1, "ws1", dt, (2 * I_s, H) if nk else (H, 2 * I_s), dev), T, I_s,
+            _ptr(act_shared, "act_shared", dt, (T, I_s), dev), _stream(stream, dev))
+    _check(lib.moe_grouped_swiglu_fc1_and_shared_gather(*args))
+
+
 def moe_grouped_fc2_and_shared(act, expert_offsets, w2, y_rows, act_shared, ws2, x, w_gate, y, workspace,
                                accumulate=False, stream=None, layout=MOE_W_KN):
     lib = load()
@@ -442,7 +481,8 @@ class MoELayerBuffers:
 
 
 def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=None, routes=None,
-                      stream=None, fused_shared=False, fused_route=False, side_stream=None, layout=MOE_W_KN):
+                      stream=None, fused_shared=False, fused_route=False, side_stream=None, layout=MOE_W_KN,
+                      gather=False):
     """The six calls in order.  ``routes`` = (topk_ids int32, topk_weights fp32)
     device tensors skips moe_route.  ``shared`` = (ws1, ws2, w_gate or None).
     With ``fused_shared`` and a shared expert, the routed experts and the shared
@@ -453,7 +493,9 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
     torch.cuda.Stream; not with ``fused_shared``) and a shared expert, the shared
     expert runs there first (y = shared(x)), concurrently with routing and the
     routed experts, and the combine waits for it and adds onto y.  ``layout``
-    (MOE_W_KN or MOE_W_NK) is the storage of W1, W2 and the shared weights."""
+    (MOE_W_KN or MOE_W_NK) is the storage of W1, W2 and the shared weights.  With
+    ``gather`` the scatter build copies no rows (x_scattered NULL) and fc1 reads
+    the routed rows from x through row_token (the *_gather calls)."""
     T, H = x.shape
     E, _, I = _fc1_sizes(W1, layout)
     I_s = (shared[1].shape[1] if layout == MOE_W_NK else shared[1].shape[0]) if shared is not None else 0
@@ -462,7 +504,7 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
     if routes is None and fused_route:
         moe_route_and_scatter(x, w_router, logit_bias, top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
                               bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                              bufs.x_scattered, bufs.route_scatter_ws, stream)
+                              None if gather else bufs.x_scattered, bufs.route_scatter_ws, stream)
         w = bufs.topk_weights
     else:
         if routes is None:
@@ -472,7 +514,7 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         else:
             ids, w = routes
         moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                          bufs.x_scattered, bufs.scatter_ws, stream)
+                          None if gather else bufs.x_scattered, bufs.scatter_ws, stream)
     if side_stream is not None and shared is not None and not fused_shared:
         if stream is not None and not isinstance(stream, torch.cuda.Stream):
             raise ValueError("side_stream needs stream to be None or a torch.cuda.Stream")
@@ -482,13 +524,20 @@ def moe_layer_forward(x, w_router, logit_bias, W1, W2, top_k, shared=None, bufs=
         moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, side_stream, layout=layout)
     if fused_shared and shared is not None:
         ws1, ws2, wg = shared
-        moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
-                                          bufs.act_shared, stream, layout=layout)
+        if gather:
+            moe_grouped_swiglu_fc1_and_shared_gather(x, bufs.row_token, bufs.expert_offsets, W1, bufs.act, ws1,
+                                                     bufs.act_shared, stream, layout=layout)
+        else:
+            moe_grouped_swiglu_fc1_and_shared(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, x, ws1,
+                                              bufs.act_shared, stream, layout=layout)
         moe_grouped_fc2_and_shared(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, bufs.act_shared, ws2, x, wg,
                                    bufs.y, bufs.shared_ws, False, stream, layout=layout)
         moe_gather_combine(bufs.y_rows, bufs.scatter_index, w, bufs.y, True, stream)
         return bufs
-    moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream, layout=layout)
+    if gather:
+        moe_grouped_swiglu_fc1_gather(x, bufs.row_token, bufs.expert_offsets, W1, bufs.act, stream, layout=layout)
+    else:
+        moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, stream, layout=layout)
     moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows, stream, layout=layout)
     if side_stream is not None and shared is not None:
         main.wait_stream(side_stream)

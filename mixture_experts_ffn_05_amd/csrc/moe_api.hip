@@ -136,6 +136,8 @@ constexpr CallStage kCallStages[] = {
     {"moe_grouped_fc2_and_shared_mx8", "expert_projection+shared_expert_projection"},
     {"moe_grouped_fc2_and_shared_mx8:gated", "expert_projection+shared_expert_gate+shared_expert_projection"},
     {"moe_grouped_swiglu_fc1_and_shared", "expert_projection+shared_expert_projection"},
+    {"moe_grouped_swiglu_fc1_gather", "expert_projection"},
+    {"moe_grouped_swiglu_fc1_and_shared_gather", "expert_projection+shared_expert_projection"},
     {"moe_grouped_fc2_and_shared", "expert_projection+shared_expert_projection"},
     {"moe_grouped_fc2_and_shared:gated", "expert_projection+shared_expert_gate+shared_expert_projection"},
     {"moe_grouped_swiglu_fc1_save", "expert_projection"},
@@ -245,7 +247,7 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
   MOE_CHECK(need_ptr(row_token, fn, "row_token"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(status_words, fn, "status_words"));
-  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  // x_scattered may be NULL: the rows are then not copied (the *_gather fc1 calls read x instead)
   MOE_CHECK(need_pos(T, fn, "T"));
   MOE_CHECK(need_pos(H, fn, "H"));
   MOE_CHECK(need_experts(E, fn));
@@ -294,7 +296,7 @@ moe_status moe_build_scatter(moe_dtype dt, const void* x, const int32_t* topk_id
   MOE_CHECK(need_ptr(row_token, fn, "row_token"));
   MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
   MOE_CHECK(need_ptr(status_words, fn, "status_words"));
-  MOE_CHECK(need_ptr(x_scattered, fn, "x_scattered"));
+  // x_scattered may be NULL: the rows are then not copied (the *_gather fc1 calls read x instead)
   MOE_CHECK(need_pos(T, fn, "T"));
   MOE_CHECK(need_pos(H, fn, "H"));
   MOE_CHECK(need_experts(E, fn));
@@ -613,6 +615,72 @@ moe_status moe_grouped_swiglu_fc1_and_shared(moe_dtype dt, moe_weight_layout wl,
                       fn);
   MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x_scattered, expert_offsets, E, R, w1,
                                                       (int64_t)H * 2 * I, H, I, act, 0, cus, s),
+                       fn));
+  return hip_result(
+      moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, nullptr, 1, T, ws1, 0, H, I_s, act_shared, 1, cus, s), fn);
+}
+
+moe_status moe_grouped_swiglu_fc1_gather(moe_dtype dt, moe_weight_layout wl, const void* x, const int32_t* row_token,
+                                         const int32_t* expert_offsets, const void* w1, int32_t T, int32_t R,
+                                         int32_t H, int32_t E, int32_t I, void* act, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1_gather";
+  StageRange stage_range(stage_of(fn));
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(row_token, fn, "row_token"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  return hip_result(moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, expert_offsets, E, R, w1, (int64_t)H * 2 * I,
+                                                   H, I, act, 0, cu_count(), (hipStream_t)stream, row_token, T),
+                    fn);
+}
+
+moe_status moe_grouped_swiglu_fc1_and_shared_gather(moe_dtype dt, moe_weight_layout wl, const void* x,
+                                                    const int32_t* row_token, const int32_t* expert_offsets,
+                                                    const void* w1, int32_t R, int32_t H, int32_t E, int32_t I,
+                                                    void* act, const void* ws1, int32_t T, int32_t I_s,
+                                                    void* act_shared, void* stream) {
+  const char* fn = "moe_grouped_swiglu_fc1_and_shared_gather";
+  StageRange stage_range(stage_of(fn));
+  MOE_CHECK(need_dtype(dt, fn));
+  MOE_CHECK(need_layout(wl, fn));
+  MOE_CHECK(need_ptr(x, fn, "x"));
+  MOE_CHECK(need_ptr(row_token, fn, "row_token"));
+  MOE_CHECK(need_ptr(expert_offsets, fn, "expert_offsets"));
+  MOE_CHECK(need_ptr(w1, fn, "w1"));
+  MOE_CHECK(need_ptr(act, fn, "act"));
+  MOE_CHECK(need_ptr(ws1, fn, "ws1"));
+  MOE_CHECK(need_ptr(act_shared, fn, "act_shared"));
+  MOE_CHECK(need_pos(R, fn, "R"));
+  MOE_CHECK(need_pos(H, fn, "H"));
+  MOE_CHECK(need_experts(E, fn));
+  MOE_CHECK(need_pos(I, fn, "I"));
+  MOE_CHECK(need_pos(T, fn, "T"));
+  MOE_CHECK(need_pos(I_s, fn, "I_s"));
+  MOE_CHECK(need_mult8(H, fn, "H"));
+  MOE_CHECK(need_mult8(I, fn, "I"));
+  MOE_CHECK(need_mult8(I_s, fn, "I_s"));
+  MOE_CHECK(need_rows(R, fn, "R"));
+  MOE_CHECK(need_rows(T, fn, "T"));
+  hipStream_t s = (hipStream_t)stream;
+  const int cus = cu_count();
+  if (moe_launch::fused_supported((int)dt, H, I, I_s, E, R, T))
+    return hip_result(moe_launch::fused_fc1((int)wl, x, expert_offsets, E, R, w1, H, I, act, x, T, ws1, I_s,
+                                            act_shared, cus, s, row_token),
+                      fn);
+  MOE_CHECK(hip_result(moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, expert_offsets, E, R, w1,
+                                                      (int64_t)H * 2 * I, H, I, act, 0, cus, s, row_token, T),
                        fn));
   return hip_result(
       moe_launch::grouped_swiglu_fc1((int)dt, (int)wl, x, nullptr, 1, T, ws1, 0, H, I_s, act_shared, 1, cus, s), fn);

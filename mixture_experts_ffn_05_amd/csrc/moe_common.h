@@ -169,9 +169,12 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
 // `role` (0 routed experts, 1 shared expert) only selects a separately named
 // kernel instantiation so that profiles tell the two apart.
 // bt: weight layout, 0 = [K, N] per group (N contiguous), 1 = [N, K] (K contiguous).
+// a_rows (optional): routed row r of the product is row a_rows[r] of `a`, which has a_src_rows rows
+// (gather-on-load: `a` is then the layer input x and a_rows the scatter's row_token).
 hipError_t grouped_swiglu_fc1(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
                               const void* w1, int64_t w1_group_stride, int K, int I, void* act,
-                              int role, int cu_count, hipStream_t s);
+                              int role, int cu_count, hipStream_t s, const int32_t* a_rows = nullptr,
+                              int a_src_rows = 0);
 hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, int groups, int rows,
                        const void* w2, int64_t w2_group_stride, int K, int N, float* out,
                        const float* row_scale, int accumulate, int plain_store, int role, int cu_count,
@@ -198,7 +201,7 @@ hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, 
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T);
 hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
                      void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
-                     hipStream_t s);
+                     hipStream_t s, const int32_t* a_rows = nullptr);
 hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int R, const void* w2, int I, int H,
                      float* y_rows, const void* act_s, int T, const void* ws2, int I_s, const float* gate,
                      int accumulate, float* y, int cu_count, hipStream_t s);

@@ -122,7 +122,15 @@ struct GemmParams {
   int64_t sc_stride;        // MXFP8: bytes between the scales of consecutive groups
   const void* aux;          // kSwiGLUBwd: fc1 pre-activation T [rows, 2N] (gate columns, then up columns)
   void* out2;               // kSwiGLUSave: fc1 pre-activation out, T [rows, 2N]
+  const int32_t* a_rows;    // optional: row r of A is row a_rows[r] of `a` ([a_src_rows, K]), else row r
+  int a_src_rows;           // rows of `a` when a_rows is set (indices are clamped to [0, a_src_rows))
 };
+
+// Source row of A for row r (gather-on-load when a_rows is set).
+template <typename T>
+__device__ __forceinline__ int64_t a_src_row(const GemmParams<T>& p, int r) {
+  return p.a_rows ? (int64_t)min(max(p.a_rows[r], 0), p.a_src_rows - 1) : (int64_t)r;
+}
 
 // SwiGLU output at (row, col) from the gate and up accumulators; with
 // kSwiGLUSave the two pre-activations are stored as well.
@@ -198,7 +206,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
     for (int i = 0; i < 4; ++i) {
       const int v = tid + kThreads * i, r = v >> 3, ko = v & 7;
       const int row = row0 + r, k = k0 + ko * 8;
-      ra[i] = (row < row_end && k < p.K) ? *(const u32x4*)(p.a + (int64_t)row * p.K + k) : u32x4{0u, 0u, 0u, 0u};
+      ra[i] = (row < row_end && k < p.K) ? *(const u32x4*)(p.a + a_src_row(p, row) * p.K + k) : u32x4{0u, 0u, 0u, 0u};
     }
     if (p.bt) {  // [N, K] weights: 8 consecutive k of one staged column, like the activations
 #pragma unroll
@@ -667,7 +675,7 @@ __device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, in
     const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
     const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
     const int row = min(row0 + r, row_end - 1);
-    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : a_src_row(p, row) * K + chunk * 8;
   }
   int b_off[C::kBLoads];
 #pragma unroll
@@ -826,7 +834,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
     const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
     const int chunk = (lane % C::kAChunks) ^ a_swizzle<C>(r);
     const int row = min(row0 + r, row_end - 1);
-    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : a_src_row(p, row) * K + chunk * 8;
   }
   int b_off[C::kBLoads];
 #pragma unroll
@@ -1203,7 +1211,7 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
     const int r = (wave * C::kALoads + i) * C::kARowsPerLoad + lane / C::kAChunks;
     const int chunk = (lane % C::kAChunks) ^ row_swizzle<C::kARow>(r);
     const int row = min(row0 + r, row_end - 1);
-    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : (int64_t)row * K + chunk * 8;
+    a_off[i] = (C::STAGES == 2 && row0 + r >= row_end) ? -1 : a_src_row(p, row) * K + chunk * 8;
   }
   int b_off[C::kBLoads];
 #pragma unroll
@@ -1701,7 +1709,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmParams<float> p) {
     g = lo;
   }
   const float* bg = p.b + (int64_t)g * p.b_stride;
-  const float* ar = p.a + (int64_t)row * p.K;
+  const float* ar = p.a + a_src_row(p, row) * p.K;
   // element (k, n) of the group's weight
   auto w = [&](int k, int n) { return p.bt ? bg[(int64_t)n * p.ldb + k] : bg[(int64_t)k * p.ldb + n]; };
   if (paired(EPI)) {
@@ -1992,16 +2000,20 @@ namespace moe_launch {
 // (bt == 0) or row (bt == 1) I.
 hipError_t grouped_swiglu_fc1(int dt, int bt, const void* a, const int32_t* offsets, int groups, int rows,
                               const void* w1, int64_t w1_group_stride, int K, int I, void* act, int role,
-                              int cu_count, hipStream_t s) {
+                              int cu_count, hipStream_t s, const int32_t* a_rows, int a_src_rows) {
   using namespace moe;
   const int ldb = bt ? K : 2 * I;
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)a, offsets, groups, rows, K, I, (const bf16_t*)w1, w1_group_stride,
                          ldb, I, act, nullptr, 0, 0, bt};
+    p.a_rows = a_rows;
+    p.a_src_rows = a_src_rows;
     return role ? launch_bf16<kSwiGLU, 1>(p, cu_count, s) : launch_bf16<kSwiGLU, 0>(p, cu_count, s);
   }
   GemmParams<float> p{(const float*)a, offsets, groups, rows, K, I, (const float*)w1, w1_group_stride,
                       ldb, I, act, nullptr, 0, 0, bt};
+  p.a_rows = a_rows;
+  p.a_src_rows = a_src_rows;
   const int64_t n = (int64_t)rows * I;
   hipLaunchKernelGGL(grouped_gemm_f32<kSwiGLU>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -2047,10 +2059,12 @@ bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T) {
 
 hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
                      void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* a_rows) {
   using namespace moe;
   GemmParams<bf16_t> pr{(const bf16_t*)xs, offsets, E, R, H, I, (const bf16_t*)w1, (int64_t)H * 2 * I,
                         bt ? H : 2 * I, I, act, nullptr, 0, 0, bt};
+  pr.a_rows = a_rows;  // with a_rows set, xs is x and routed row r is x[a_rows[r]]
+  pr.a_src_rows = T;
   GemmParams<bf16_t> ps{(const bf16_t*)x, nullptr, 1, T, H, I_s, (const bf16_t*)ws1, 0,
                         bt ? H : 2 * I_s, I_s, act_s, nullptr, 0, 0, bt};
   return launch_fused_bf16<kSwiGLU, kSwiGLU>(pr, ps, cu_count, s);

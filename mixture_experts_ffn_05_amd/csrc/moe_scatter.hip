@@ -19,7 +19,8 @@
 //   scatter_rank   each wave replays its chunk; a pair's row is its chunk base
 //                  plus offsets[e] plus the number of lower lanes with the same
 //                  expert; a running per-expert cursor lives in LDS.
-//   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies.
+//   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies (skipped when
+//                  x_scattered is NULL: the fc1 call then gathers the rows on load).
 // Up to 16 chunks (decode, and prefill up to 16384 pairs) take scatter_small,
 // which runs count, scan and rank in one workgroup of 16 waves, and for at
 // most 256 rows of at most 256 KiB in all also the row copy.
@@ -381,7 +382,7 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
   const int elem = dt == 1 ? 2 : 4;
   const int row_vecs = (int)((int64_t)H * elem / 16);
   if (nchunks <= kSmallWaves && nchunks * E <= kSmallHist) {
-    const int fold = R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
+    const int fold = x_scattered && R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
     const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
     if (nchunks <= 4)
       hipLaunchKernelGGL(scatter_small<4>, dim3(1), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
@@ -406,6 +407,7 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
                        (const int32_t*)cnt, (const int32_t*)offsets, scatter_index, row_token);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if (!x_scattered) return hipSuccess;  // rows gathered on load by the fc1 call instead
   hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,
                      (const int32_t*)row_token, (const int32_t*)offsets, E, R, row_vecs, (u32x4*)x_scattered);
   return hipGetLastError();
@@ -429,7 +431,7 @@ hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const f
   while ((1 << nbits) < E) ++nbits;
   const int elem = dt == 1 ? 2 : 4;
   const int row_vecs = (int)((int64_t)H * elem / 16);
-  const int fold = R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
+  const int fold = x_scattered && R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
   const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
   if (T <= 4)  // one token per wave
     hipLaunchKernelGGL(route_scatter_small<4>, dim3(1), dim3(256), lds, s, partial, nsplit, bias, logits, T, E,
@@ -440,7 +442,7 @@ hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const f
                        bias, logits, T, E, top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets,
                        status_words, fold, (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || fold) return err;
+  if (err != hipSuccess || fold || !x_scattered) return err;  // rows copied, or not wanted
   hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,
                      (const int32_t*)row_token, (const int32_t*)offsets, E, R, row_vecs, (u32x4*)x_scattered);
   return hipGetLastError();

@@ -172,6 +172,31 @@ def test_fused_shared_calls_validation(lib):
     assert "x (needed for the gate)" in _err(lib)
 
 
+def test_gather_fc1_calls_validation(lib):
+    # moe_grouped_swiglu_fc1_gather(dt, wl, x, row_token, offsets, w1, T, R, H, E, I, act, stream)
+    assert lib.moe_grouped_swiglu_fc1_gather(1, 0, FAKE, None, FAKE, FAKE, 64, 128, 256, 8, 128, FAKE, None) == 1
+    assert "row_token must not be NULL" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_gather(1, 0, FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 8, 128, FAKE, None) == 1
+    assert "T must be >= 1" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_gather(1, 0, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 128, FAKE, None) == 1
+    assert "x must not be NULL" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_gather(1, 0, FAKE, FAKE, FAKE, FAKE, 64, 128, 256, 8, 100, FAKE, None) == 2
+    assert "I must be a multiple of 8" in _err(lib)
+    # (dt, wl, x, row_token, offsets, w1, R, H, E, I, act, ws1, T, I_s, act_shared, stream)
+    assert lib.moe_grouped_swiglu_fc1_and_shared_gather(1, 0, FAKE, None, FAKE, FAKE, 128, 256, 8, 128, FAKE, FAKE,
+                                                        64, 128, FAKE, None) == 1
+    assert "row_token must not be NULL" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_and_shared_gather(1, 0, FAKE, FAKE, FAKE, FAKE, 128, 256, 8, 128, FAKE, None,
+                                                        64, 128, FAKE, None) == 1
+    assert "ws1 must not be NULL" in _err(lib)
+    assert lib.moe_grouped_swiglu_fc1_and_shared_gather(1, 1, FAKE, FAKE, FAKE, FAKE, 128, 256, 8, 128, FAKE, FAKE,
+                                                        64, 100, FAKE, None) == 2
+    assert "I_s must be a multiple of 8" in _err(lib)
+    assert lib.moe_call_stage(b"moe_grouped_swiglu_fc1_gather", 0) == b"expert_projection"
+    assert lib.moe_call_stage(b"moe_grouped_swiglu_fc1_and_shared_gather", 0) == \
+        b"expert_projection+shared_expert_projection"
+
+
 def test_backward_validation(lib):
     assert lib.moe_grouped_swiglu_fc1_save(1, 0, FAKE, FAKE, FAKE, 256, 256, 8, 128, FAKE, None, None) == 1
     assert "h_pre must not be NULL" in _err(lib)

@@ -44,10 +44,14 @@ def _sample_tokens(T, n, seed):
     return np.array(sorted(picks))
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_layer(name):
+# every workload in the benchmark's configuration (routed rows gathered by fc1), two with the row copy
+FULL_ROWS = [(n, "gather") for n in FULL] + [("v2l", "copy"), ("v3_decode64", "copy")]
+
+
+@pytest.mark.parametrize("name,rows", FULL_ROWS, ids=[f"{n}-{r}" for n, r in FULL_ROWS])
+def test_full_size_layer(name, rows):
     cfg = wl.WORKLOADS[name]
-    print(f"[full] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k} I={cfg.I} I_s={cfg.I_s}", flush=True)
+    print(f"[full] {name} ({rows}) T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k} I={cfg.I} I_s={cfg.I_s}", flush=True)
     layer = wl.make_layer(cfg, DEV)
     x, wr = layer["x"], layer["w_router"]
     bias = layer["bias"]
@@ -55,7 +59,7 @@ def test_full_size_layer(name):
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.y_rows.fill_(float("nan"))
     B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
-                        fused_shared=True, fused_route=True)
+                        fused_shared=True, fused_route=True, gather=rows == "gather")
     torch.cuda.synchronize()
 
     # routing
@@ -70,9 +74,10 @@ def test_full_size_layer(name):
     assert np.array_equal(host(bufs.row_token), sc["row_token"])
     assert np.array_equal(host(bufs.expert_offsets), sc["offsets"])
     assert host(bufs.status_words).tolist() == [sc["max_group"], 0]
-    rows = np.unique(np.concatenate([[0, cfg.R - 1], np.random.default_rng(1).integers(0, cfg.R, 256)]))
-    xs = host(bufs.x_scattered[torch.from_numpy(rows).to(DEV)])
-    assert np.array_equal(xs.view(np.uint32), xh[sc["row_token"][rows]].view(np.uint32))
+    if rows == "copy":
+        pick = np.unique(np.concatenate([[0, cfg.R - 1], np.random.default_rng(1).integers(0, cfg.R, 256)]))
+        xs = host(bufs.x_scattered[torch.from_numpy(pick).to(DEV)])
+        assert np.array_equal(xs.view(np.uint32), xh[sc["row_token"][pick]].view(np.uint32))
 
     # outputs on sampled tokens
     toks = _sample_tokens(cfg.T, 10 if cfg.E >= 256 else 24, seed=cfg.T)

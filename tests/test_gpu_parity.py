@@ -411,6 +411,43 @@ def test_two_runs_bit_identical(mode):
                               b.view(np.uint32) if b.dtype == np.float32 else b)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
+@pytest.mark.parametrize("mode", ["separate", "fused"])
+@pytest.mark.parametrize("cfg", CASES, ids=_ids)
+def test_gather_on_load_matches_scattered_rows(cfg, mode, layout):
+    """fc1 reading the routed rows from x through row_token (scatter with no row copy, the *_gather
+    calls) gives the bit-identical activation and output of the path through x_scattered, which
+    the scatter then leaves untouched; and y matches the oracle fed the same routes."""
+    layer = _layer(cfg)
+    x, wr = layer["x"], layer["w_router"]
+    bias_t = torch.from_numpy(layer["bias"]).to(DEV) if layer["bias"] is not None else None
+    W1d, W2d, shd = _device_weights(layer, layout)
+    runs = []
+    for gather in (False, True):
+        bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
+        bufs.x_scattered.fill_(float("nan"))
+        bufs.act.fill_(float("nan"))
+        B.moe_layer_forward(x, wr, bias_t, W1d, W2d, cfg.top_k, shared=shd, bufs=bufs,
+                            fused_shared=mode == "fused", fused_route=mode == "fused", layout=layout, gather=gather)
+        torch.cuda.synchronize()
+        runs.append(bufs)
+    a, b = runs
+    assert torch.isnan(b.x_scattered).all(), "the scatter copied rows although x_scattered was NULL"
+    R = int(host(a.expert_offsets)[-1])
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    for name in ("topk_ids", "scatter_index", "row_token", "expert_offsets"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    assert torch.equal(bits(a.act[:R]), bits(b.act[:R])), "act"
+    if a.act_shared is not None and mode == "fused":   # written only by the *_and_shared calls
+        assert torch.equal(bits(a.act_shared), bits(b.act_shared)), "act_shared"
+    assert torch.equal(bits(a.y), bits(b.y)), "y"
+    ids, w = host(b.topk_ids), host(b.topk_weights)
+    W1, W2 = _np_weights(layer)
+    ref = O.moe_forward(host(x), None, W1, W2, cfg.top_k, routes=(ids, w), shared=_np_shared(layer),
+                        contract=_contract(cfg), dtype=np.float64)
+    assert_output_close(host(b.y), ref["y"], cfg.dtype)
+
+
 # ---- MXFP8 expert weights: every result against the oracle on the exactly dequantized weights
 
 def _mx_np(layer_mx):
