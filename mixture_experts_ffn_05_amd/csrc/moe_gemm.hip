@@ -10,18 +10,25 @@
 // persistent grid from the worst case floor(R/128) + min(E, R) row tiles.
 //
 // bf16 pipelined path (reduction size a multiple of 64; every configuration):
-//   * workgroup tile 128 rows x BN staged weight columns (BN = 128 or 256),
-//     reduction slice 64, 4 waves in a 2x2 arrangement, each owning 64 rows x
-//     BN/2 columns as 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, fp32
-//     accumulate).
+//   * workgroup tile BM x BN staged weight columns, reduction slice BK, WM x WN
+//     wave positions (times KW split-K waves), each owning (BM/WM) x (BN/WN)
+//     as 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, fp32 accumulate); the
+//     shapes are listed with PipeCfg below (32 to 256 rows, 128 or 256
+//     columns, 4 or 8 waves).
 //   * operands travel HBM -> LDS with global_load_lds_dwordx4 (no register
 //     round trip) through a STAGES-deep ring of LDS buffers, so several
 //     reduction slices are in flight while the MFMAs consume an older one.
 //     Each lane's 16 bytes land at LDS base + 16*lane, so the XOR swizzles
 //     below are applied by choosing which 16-byte chunk each lane fetches.
+//   * where a SIMD runs at most two waves, each wave alternates between two
+//     fragment sets: the next substep's LDS reads are interleaved with the
+//     current substep's MFMAs, across slice boundaries too (run_tile_pipe_v1).
 //   * activations ([rows, K], K-contiguous) sit in LDS as 128-byte rows with
 //     the 16-byte chunk index XORed by (row >> 1) & 7; an MFMA A fragment is
-//     one conflict-free ds_read_b128.
+//     one conflict-free ds_read_b128.  With a_rows set (gather-on-load), row r
+//     is fetched from row a_rows[r] of the layer input instead of from a
+//     scattered copy; the offsets are fixed per tile, so this costs one index
+//     load per lane and tile.
 //   * weights ([K, N] per expert, N-contiguous) sit in LDS in that natural
 //     layout (chunk index XORed by 4*(k & 3)); the B fragment (8 consecutive
 //     k of one column) is assembled from two ds_read_b64_tr_b16 transpose

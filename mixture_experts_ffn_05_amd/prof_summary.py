@@ -37,12 +37,22 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (string literals
+    are kept as they are; none of the kernel sources puts comment markers in one)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every kernel source: a change to any of them voids a recorded figure."""
+    """Hash of the code of every kernel source (comments and layout ignored): a
+    change to any kernel voids a recorded figure, an edited comment does not."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h"))):
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
