@@ -11,7 +11,7 @@
 //   router_transpose_bf16  W_r [H,E] -> [E_pad,H] in the caller's workspace, so that
 //                          both operands of the router product are K-contiguous.
 //   router_logits_mfma     x[T,H] @ W_r on MFMA (16x16x32 bf16, fp32 accumulate),
-//                          16 tokens x 64 experts per workgroup, H split across
+//                          16 (or 64 for T >= 256) tokens x 64 experts per workgroup, H split across
 //                          workgroups (grid.z) and across each workgroup's 4 waves;
 //                          partial sums land in the workspace.
 //   route_logits_f32       the same product for float32 inputs, one thread per logit.
@@ -27,7 +27,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRtTok = 16;   // tokens per workgroup
+constexpr int kRtTok = 16;   // tokens per MFMA row block
 constexpr int kRtExp = 64;   // experts per workgroup (4 MFMA column blocks of 16)
 
 int padded_experts(int E) { return (E + 15) / 16 * 16; }
@@ -50,38 +50,51 @@ __global__ __launch_bounds__(256) void router_transpose_bf16(const bf16_t* __res
   }
 }
 
-// Partial logits over one slice of H for 16 tokens x 64 experts per
+// Partial logits over one slice of H for 16*MB tokens x 64 experts per
 // workgroup.  Both MFMA operands are K-contiguous (x rows and the transposed
 // router rows), so each lane loads its 16x16x32 fragments straight from global
-// memory, four k-substeps (128 k) at a time so that many loads are in flight.
-// The 4 waves split the workgroup's slice; their sums are added in a fixed
-// order through LDS.  grid.z splits H into `ksplit` slices; partial[z][t][e]
-// is summed over z in a fixed order by topk_softmax, so the result does not
-// depend on scheduling.
+// memory, four k-substeps (128 k) at a time so that many loads are in flight;
+// each router fragment feeds the MB 16-token row blocks (MB = 4 for many tokens
+// cuts the router-row traffic per MFMA by 2.5x; the product is bound by those
+// loads).  The 4 waves split the workgroup's slice; their sums are added in a
+// fixed order through LDS.  grid.z splits H into `ksplit` slices;
+// partial[z][t][e] is summed over z in a fixed order by topk_softmax, so the
+// result does not depend on scheduling.
+template <int MB>
 __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wt, int T, int H, int E_pad,
                                                           int kslice, float* __restrict__ partial) {
-  __shared__ float red[4][kRtTok][kRtExp + 1];
+  constexpr int kTok = 16 * MB;
+  __shared__ float red[4][kTok][kRtExp + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
+  const int t0 = blockIdx.x * kTok, e0 = blockIdx.y * kRtExp;
   const int nblk = min(4, (E_pad - e0) / 16);
   const int zbeg = blockIdx.z * kslice, zend = min(H, zbeg + kslice);
   const int kq = ((kslice + 127) / 128) * 32;   // per-wave share of the slice, a multiple of 32
   const int kbeg = zbeg + wave * kq, kend = min(zend, kbeg + kq);
-  const int row = t0 + (lane & 15);
   const int koff = (lane >> 4) * 8;
-  const bool row_ok = row < T;
-  const bf16_t* xr = x + (int64_t)(row_ok ? row : 0) * H;
-  f32x4 acc[4];
+  const bf16_t* xr[MB];
+  bool row_ok[MB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = t0 + 16 * mb + (lane & 15);
+    row_ok[mb] = row < T;
+    xr[mb] = x + (int64_t)(row_ok[mb] ? row : 0) * H;
+  }
+  f32x4 acc[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = kbeg; k < kend; k += 128) {
-    u32x4 a[4], b[4][4];
+    u32x4 a[MB][4], b[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = k + 32 * u + koff;
       const bool k_ok = kk < kend;
-      a[u] = (row_ok && k_ok) ? *(const u32x4*)(xr + kk) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        a[mb][u] = (row_ok[mb] && k_ok) ? *(const u32x4*)(xr[mb] + kk) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int e = e0 + nb * 16 + (lane & 15);
@@ -91,18 +104,23 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restri
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                          __builtin_bit_cast(bf16x8, b[u][nb]), acc[nb], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][u]),
+                                                                __builtin_bit_cast(bf16x8, b[u][nb]), acc[mb][nb],
+                                                                0, 0, 0);
   }
   // 16x16 accumulator layout: row = 4*(lane/16) + r, column = lane%16.
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][nb * 16 + (lane & 15)] = acc[nb][r];
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][16 * mb + 4 * (lane >> 4) + r][nb * 16 + (lane & 15)] = acc[mb][nb][r];
   __syncthreads();
   float* out = partial + (int64_t)blockIdx.z * T * E_pad;
-  for (int i = tid; i < kRtTok * kRtExp; i += 256) {
+  for (int i = tid; i < kTok * kRtExp; i += 256) {
     const int tt = i / kRtExp, ee = i % kRtExp;
     const int t = t0 + tt, e = e0 + ee;
     if (t < T && e < E_pad)
@@ -245,11 +263,16 @@ Split router_valu_split(int T, int H) {
   return Split{(H + kslice - 1) / kslice, kslice};
 }
 
+// Tokens per workgroup of the MFMA router: 64 (four 16-token row blocks per
+// router fragment) once there are enough tokens to fill the grid, else 16.
+int router_mfma_tokens(int T) { return T >= 256 ? 4 * moe::kRtTok : moe::kRtTok; }
+
 // MFMA router: slices of H (multiples of 128) so that the grid covers about
 // 512 workgroups.
 Split router_mfma_split(int T, int H, int E) {
   using namespace moe;
-  const int tiles = ((T + kRtTok - 1) / kRtTok) * ((padded_experts(E) + kRtExp - 1) / kRtExp);
+  const int tok = router_mfma_tokens(T);
+  const int tiles = ((T + tok - 1) / tok) * ((padded_experts(E) + kRtExp - 1) / kRtExp);
   int ks = (512 + tiles - 1) / tiles;
   const int max_ks = (H + 127) / 128;
   if (ks > max_ks) ks = max_ks;
@@ -298,9 +321,14 @@ hipError_t route(int dt, const void* x, const void* w_router, const float* bias,
     hipLaunchKernelGGL(router_transpose_bf16, dim3((H + 63) / 64, (E_pad + 63) / 64), dim3(256), 0, s,
                        (const bf16_t*)w_router, H, E, E_pad, wt);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    dim3 grid((T + kRtTok - 1) / kRtTok, (E_pad + kRtExp - 1) / kRtExp, sp.nz);
-    hipLaunchKernelGGL(router_logits_mfma, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
-                       E_pad, sp.kslice, partial);
+    const int tok = router_mfma_tokens(T);
+    dim3 grid((T + tok - 1) / tok, (E_pad + kRtExp - 1) / kRtExp, sp.nz);
+    if (tok == 4 * kRtTok)
+      hipLaunchKernelGGL(router_logits_mfma<4>, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
+                         E_pad, sp.kslice, partial);
+    else
+      hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
+                         E_pad, sp.kslice, partial);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, sp.nz, E_pad, bias,
                        logits, T, E, top_k, ids, weights);

@@ -46,12 +46,18 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
+# Sources of every kernel a counter record can name (the grouped GEMMs, the
+# combine, the backward kernels) and the header they share.
+RECORDED_SOURCES = ("moe_gemm.hip", "moe_combine.hip", "moe_backward.hip", "moe_common.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the code of every kernel source (comments and layout ignored): a
-    change to any kernel voids a recorded figure, an edited comment does not."""
+    """Hash of the code of the recorded kernels' sources (comments and layout
+    ignored): a change to any of those kernels voids a recorded figure; an
+    edited comment, or a change to the routing and scatter kernels, does not."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h"))):
-        with open(path, encoding="utf-8") as f:
+    for name in sorted(RECORDED_SOURCES):
+        with open(os.path.join(PKG, "csrc", name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
