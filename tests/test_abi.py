@@ -235,3 +235,16 @@ def test_build_compiles_all_kernels_for_gfx950():
     import __graft_entry__ as ge
     ge.build()
     assert B.load() is not None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more exits with a message, before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr
+    assert res.stdout == ""
