@@ -118,22 +118,34 @@ __global__ __launch_bounds__(1024) void scatter_scan(int32_t* __restrict__ cnt, 
                                                      int32_t* __restrict__ status, int32_t* __restrict__ row_token) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t wmax[16];
+  __shared__ int32_t wbad[16];
   __shared__ int32_t s_total;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int total_e = 0;
-  if (tid < E) {  // chunk bases of expert tid (each thread owns one column)
+  if (tid < E) {  // chunk bases of expert tid (each thread owns one column), 16 chunks' loads in flight at once
+    constexpr int kBatch = 16;
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t i = (int64_t)c * E + tid;
-      const int v = cnt[i];
-      cnt[i] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = c0 + u < nchunks ? cnt[(int64_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c0 + u < nchunks) cnt[(int64_t)(c0 + u) * E + tid] = run;
+        run += v[u];
+      }
     }
     total_e = run;
   }
+  int my_bad = 0;  // out-of-range ids, summed over the chunks by the whole workgroup
+  for (int c = tid; c < nchunks; c += 1024) my_bad += bad[c];
   const int incl = wave_inclusive_scan(total_e);
   const int mx = wave_max(total_e);
-  if (lane == 63) wsum[w] = incl;
+  const int bad_w = wave_inclusive_scan(my_bad);
+  if (lane == 63) {
+    wsum[w] = incl;
+    wbad[w] = bad_w;
+  }
   if (lane == 0) wmax[w] = mx;
   __syncthreads();
   int base = 0;
@@ -144,8 +156,8 @@ __global__ __launch_bounds__(1024) void scatter_scan(int32_t* __restrict__ cnt, 
     for (int i = 0; i < 16; ++i) {
       total += wsum[i];
       maxg = max(maxg, wmax[i]);
+      nbad += wbad[i];
     }
-    for (int c = 0; c < nchunks; ++c) nbad += bad[c];
     offsets[E] = total;
     status[0] = maxg;
     status[1] = nbad;

@@ -196,13 +196,20 @@ def test_scatter_bit_exact(T, E, k, dup):
         assert host(b.status_words)[0] == 2 * T
 
 
-def test_scatter_out_of_range_ids_are_counted():
-    ids = np.array([[0, 5], [-1, 1], [2, 2], [9, 0]], np.int32)
-    x = torch.randn((4, 16), device=DEV)
-    b = _scatter(x, torch.from_numpy(ids).to(DEV), 3)
-    _check_scatter(b, ids, host(x), 3)
-    assert host(b.status_words)[1] == 3
-    assert (host(b.scatter_index)[ids >= 3] == -1).all()
+@pytest.mark.parametrize("T", [4, 9000])
+def test_scatter_out_of_range_ids_are_counted(T):
+    """Bad fed-in ids are counted and dropped: 4 tokens (one workgroup) and 9000 tokens x 2 slots
+    (18 chunks of 1024 pairs: the count / scan / rank kernels)."""
+    E = 3
+    if T == 4:
+        ids = np.array([[0, 5], [-1, 1], [2, 2], [9, 0]], np.int32)
+    else:
+        ids = np.random.default_rng(5).integers(-2, E + 2, (T, 2)).astype(np.int32)
+    x = torch.randn((T, 16), device=DEV)
+    b = _scatter(x, torch.from_numpy(ids).to(DEV), E)
+    _check_scatter(b, ids, host(x), E)
+    assert host(b.status_words)[1] == int(((ids < 0) | (ids >= E)).sum())
+    assert (host(b.scatter_index)[(ids < 0) | (ids >= E)] == -1).all()
 
 
 @pytest.mark.parametrize("T,H,E,k,with_bias", [
