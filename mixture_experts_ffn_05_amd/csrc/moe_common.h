@@ -72,61 +72,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Router order of two experts: higher logit first, lower index on ties.
-__device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
-}
-
-constexpr int kTopkPer = kMaxExperts / kWave;  // logits per lane of one token
-
-// Top-k of one token whose logits a wave holds: lane l holds raw[q], the
-// logit of expert l + 64q, for l + 64q < E.  k rounds of a wave arg-max under
-// the key (logit descending, index ascending, NaN lowest), then a softmax over
-// the k selected logits.  Lane j < k returns the j-th selection in slot order
-// (id, weight); the other lanes return id -1.
-__device__ __forceinline__ void topk_wave(const float (&raw)[kTopkPer], int E, int k, int& my_id, float& my_w) {
-  const int lane = lane_id();
-  float key[kTopkPer];
-#pragma unroll
-  for (int q = 0; q < kTopkPer; ++q) key[q] = (raw[q] != raw[q]) ? -INFINITY : raw[q];
-  uint32_t taken = 0;
-  float my_sel = 0.f;
-  my_id = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY, br = 0.f;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < kTopkPer; ++q) {
-      const int e = lane + kWave * q;
-      if (e < E && !((taken >> q) & 1u) && ranks_before(key[q], e, bv, be)) {
-        bv = key[q];
-        be = e;
-        br = raw[q];
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oe = __shfl_xor(be, d, kWave);
-      const float orw = __shfl_xor(br, d, kWave);
-      if (ranks_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-        br = orw;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_id = be;
-      my_sel = br;
-    }
-  }
-  const float m = __shfl(my_sel, 0, kWave);
-  const float ex = lane < k ? expf(my_sel - m) : 0.f;
-  const float s = wave_sum(ex);
-  my_w = ex / s;
-}
-
 // Fixed-order sum over z of p[z * stride], z = 0 .. n-1, eight loads in flight.
 __device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t stride, int n) {
   float v = 0.f;

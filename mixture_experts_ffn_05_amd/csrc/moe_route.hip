@@ -21,6 +21,7 @@
 //                          ascending, NaN lowest) and a softmax over the k selected
 //                          logits.
 #include "moe_common.h"
+#include "moe_topk.h"
 
 #include <math.h>
 

@@ -25,6 +25,7 @@
 // which runs count, scan and rank in one workgroup of 16 waves, and for at
 // most 256 rows of at most 256 KiB in all also the row copy.
 #include "moe_common.h"
+#include "moe_topk.h"
 
 namespace moe {
 namespace {
