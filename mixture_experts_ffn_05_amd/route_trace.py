@@ -277,12 +277,14 @@ def _layer_config(doc: dict, seed: int):
 
 
 def replay(doc: dict, repeats: int = 10, warmup: int = 3, include_router: bool = True, seed: int = 0,
-           device: str = "cuda:0", return_output: bool = False):
+           device: str = "cuda:0", return_output: bool = False, gather: bool = False):
     """Replay a validated trace through libmoe and time each stage.
 
     One step: [moe_route on the synthetic x, for its cost only: the trace's
     routes are used] -> moe_build_scatter -> moe_grouped_swiglu_fc1 ->
     moe_grouped_fc2 -> moe_gather_combine -> [moe_shared_expert, accumulating].
+    With gather, the scatter build copies no rows and fc1 is
+    moe_grouped_swiglu_fc1_gather, reading the routed rows from x.
     Returns the summary dict; with return_output, also the host copy of y and
     the layer (x, weights) that was replayed.
     """
@@ -309,12 +311,17 @@ def replay(doc: dict, repeats: int = 10, warmup: int = 3, include_router: bool =
     if include_router:
         steps.append(("moe_route", lambda: B.moe_route(x, layer["w_router"], None, k, r_ids, r_w, bufs.logits,
                                                         bufs.route_ws)))
+    xs = None if gather else bufs.x_scattered
     steps += [
         ("moe_build_scatter", lambda: B.moe_build_scatter(x, ids, E, bufs.scatter_index, bufs.row_token,
-                                                          bufs.expert_offsets, bufs.status_words, bufs.x_scattered,
+                                                          bufs.expert_offsets, bufs.status_words, xs,
                                                           bufs.scatter_ws)),
-        ("moe_grouped_swiglu_fc1", lambda: B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1,
-                                                                    bufs.act)),
+        (("moe_grouped_swiglu_fc1_gather", lambda: B.moe_grouped_swiglu_fc1_gather(x, bufs.row_token,
+                                                                                   bufs.expert_offsets, W1,
+                                                                                   bufs.act))
+         if gather else
+         ("moe_grouped_swiglu_fc1", lambda: B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1,
+                                                                     bufs.act))),
         ("moe_grouped_fc2", lambda: B.moe_grouped_fc2(bufs.act, bufs.expert_offsets, W2, bufs.y_rows)),
         ("moe_gather_combine", lambda: B.moe_gather_combine(bufs.y_rows, bufs.scatter_index, wts, bufs.y, False)),
     ]
@@ -396,6 +403,8 @@ def main(argv=None):
     r.add_argument("--warmup", type=int, default=3)
     r.add_argument("--no-router", action="store_true")
     r.add_argument("--out")
+    r.add_argument("--gather", action="store_true",
+                   help="no scattered-row copy: fc1 reads the routed rows from x through row_token")
     args = ap.parse_args(argv)
     if args.cmd == "sample":
         dtype = args.dtype or ("f32" if args.preset == "tiny" else "bf16")
@@ -412,7 +421,7 @@ def main(argv=None):
             return 1
         print("valid")
         return 0
-    res = replay(load_trace(args.trace), args.repeats, args.warmup, not args.no_router)
+    res = replay(load_trace(args.trace), args.repeats, args.warmup, not args.no_router, gather=args.gather)
     text = json.dumps(res, indent=1)
     if args.out:
         with open(args.out, "w") as f:

@@ -36,10 +36,11 @@ def _traces():
     ]
 
 
+@pytest.mark.parametrize("gather", [False, True], ids=["copy", "gather"])
 @pytest.mark.parametrize("name, doc", _traces(), ids=[n for n, _ in _traces()])
-def test_replay_gates_and_output(name, doc):
-    print(f"[case] {name}", flush=True)
-    res, y, layer = RT.replay(doc, repeats=3, warmup=1, return_output=True)
+def test_replay_gates_and_output(name, doc, gather):
+    print(f"[case] {name} gather={gather}", flush=True)
+    res, y, layer = RT.replay(doc, repeats=3, warmup=1, return_output=True, gather=gather)
     assert res["gates_pass"], res["gates"]
     labels = [c["stage"] for c in res["replay"]["calls"]]
     assert labels[:5] == ["router_topk", "gather", "expert_projection", "expert_projection", "scatter_combine"]
