@@ -1,23 +1,36 @@
 """Benchmark: forward pass of one MoE FFN layer through libmoe on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload scout]
-                    [--no-cpu-baseline] [--cpu-sample TOKENS]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3]
+                    [--launch auto|eager|graph] [--no-evict] [--no-cpu-baseline]
+                    [--cpu-sample TOKENS]
 
 One step = the whole layer through libmoe (routing and scatter build in one
 call, with no copy of the routed rows: fc1 gathers them from x on load;
 grouped fc1 + SwiGLU with the shared expert's fc1 in the same launch,
 grouped fc2 with the shared expert's fc2 and gate in the same launch,
-gather/combine) over one batch of synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K steps timed
-between two stream synchronisations.  Prints ONE JSON line.
+gather/combine) over one batch of synthetic input already resident in HBM.
+The default workload is the DeepSeek-V3-shaped prefill (T=4096, H=7168,
+E=256, top-8, I=2048, one shared expert), the largest layer that fits one GPU.
 
-Inside the timed steps, HIP events on the launch stream (torch's current
-stream, where every libmoe call is enqueued) bracket each call, giving the
-average duration of the dominant kernel (the fc1 launch) for the roofline object.
+Timing: W untimed warm-up steps, then exactly K steps (default 50 for prefill,
+200 for decode shapes) between two stream synchronisations.  Before every
+timed step, outside its events, an ordinary fill kernel writes 1 GiB so the
+256 MiB last-level cache holds none of the step's inputs (--no-evict skips
+this).  HIP events on the launch stream bracket each step and each call; the
+line reports the median step time (value = T / median) with p10/p90, and the
+mean duration of the dominant call (the fc1 launch) for the roofline object.
+Decode shapes (T <= 64) replay a HIP graph of the step by default (--launch
+auto); their per-call times come from an eager pass with the same eviction.
+A warm-cache figure (the same steps back to back, nothing evicted) is
+reported separately and labelled.
 
-The CPU baseline runs the NumPy oracle (float32, bf16 contract mode) over the
-first --cpu-sample tokens of the same workload on the host cores, after the
-GPU timing, and compares the GPU's output on those tokens with it; a parity
-failure makes the run exit non-zero.
+The CPU baseline runs the NumPy oracle (float32, bf16 contract mode) on a
+bounded sample of the same workload (the first --cpu-sample tokens) on the
+host cores, after the GPU timing.  Parity, checked in the same run: routing
+of all T tokens certified against the oracle's logits; the GPU layer run
+again with the oracle's routes fed in and compared with the oracle on the
+sample; the timed run's own output compared on the sampled tokens whose
+routes agree.  A parity failure makes the run exit non-zero.
 
 With --backward, one step is instead the backward of the routed experts for the
 routes a forward pass realized (moe_scatter_grad, moe_grouped_fc2_backward,
@@ -106,23 +119,109 @@ def committed_traffic(workload, backward=False):
     return None
 
 
-def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
-    lay = layer["layout"]
+def committed_trace(workload, backward=False):
+    """Average duration (us) of the timed call's kernels from the committed rocprofv3
+    kernel-trace summary (profiles/kernel_trace_<workload>[_backward].md), or None if
+    absent or taken on a different kernel source."""
+    import re
+    from mixture_experts_ffn_05_amd import prof_summary
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}{'_backward' if backward else ''}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"^TRACE_JSON (.*)$", open(path).read(), re.M)
+    rec = json.loads(m.group(1)) if m else None
+    if rec and rec.get("gemm_source_hash") == prof_summary.kernel_source_hash():
+        return rec
+    return None
+
+
+def add_profile_fraction(roof, rec):
+    """The roofline fraction recomputed from the committed kernel trace's average
+    duration of the same call, next to the live event-based one."""
+    if rec is None:
+        roof["profile_avg_us"] = roof["frac_profile"] = None
+        return
+    us = rec["avg_us_per_call"]
+    roof["profile_avg_us"] = round(us, 2)
+    work = roof["algorithmic_bytes"] if roof["bound"] == "hbm" else roof["algorithmic_flops"]
+    scale = 1e9 if roof["bound"] == "hbm" else 1e12
+    roof["frac_profile"] = round(work / (us * 1e-6) / scale / roof["peak"], 4)
+
+
+class Evictor:
+    """Writes 1 GiB with an ordinary elementwise kernel (torch's add_), so the
+    256 MiB last-level cache (and every L2) holds none of the next step's
+    inputs.  Enqueued outside the timed events and outside any captured graph."""
+
+    def __init__(self, dev, enabled=True):
+        self.buf = torch.zeros((1 << 28,), dtype=torch.int32, device=dev) if enabled else None
+
+    def __call__(self):
+        if self.buf is not None:
+            self.buf.add_(1)
+
+
+def step_stats(ms):
+    ms = np.asarray(ms, np.float64)
+    return {"median_ms": round(float(np.median(ms)), 5), "p10_ms": round(float(np.percentile(ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(ms, 90)), 5), "mean_ms": round(float(ms.mean()), 5),
+            "min_ms": round(float(ms.min()), 5), "max_ms": round(float(ms.max()), 5), "n": int(ms.size)}
+
+
+def host_info():
+    """CPU model, CPUs this process may run on, BLAS library, and the thread count
+    the CPU baseline uses (the CPUs in the affinity mask, capped by OMP_NUM_THREADS
+    when the environment sets it)."""
+    import threadpoolctl
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else affinity
+    blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+            if i.get("user_api") == "blas"]
+    return {"cpu_model": model, "affinity_cpus": affinity, "threads": threads,
+            "blas": ", ".join(blas) or "unknown"}
+
+
+def route_and_scatter(layer, bufs, cfg, bias_t, routes=None, copy_rows=False):
+    """Step 1-2: routing and the scatter build, or, with `routes` = (ids, weights)
+    device tensors, the scatter build of those fed-in routes."""
+    x = layer["x"]
+    if routes is None:
+        B.moe_route_and_scatter(x, layer["w_router"], bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights,
+                                bufs.logits, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
+                                bufs.status_words, bufs.x_scattered if copy_rows else None, bufs.route_scatter_ws)
+    else:
+        bufs.topk_ids.copy_(routes[0])
+        bufs.topk_weights.copy_(routes[1])
+        B.moe_build_scatter(x, bufs.topk_ids, cfg.E, bufs.scatter_index, bufs.row_token, bufs.expert_offsets,
+                            bufs.status_words, bufs.x_scattered if copy_rows else None, bufs.scatter_ws)
+
+
+def run_step(layer, bufs, cfg, bias_t, events=None, side=None, routes=None):
     """One layer forward: route + scatter, fc1 (+ shared fc1), fc2 (+ shared fc2, gate), combine.
+    With `routes` ((ids, weights) device tensors) the routes are fed in and only
+    the scatter build runs in the first call.
     With `side` (a second stream) and a shared expert, the shared expert runs on
     `side` (y = shared(x)) while routing and the routed experts run on the
     current stream, which waits for it before the combine adds onto y.
     With `events`, records one HIP event before each call on the current stream
     and one after the last."""
-    x, wr, W1, W2 = layer["x"], layer["w_router"], layer["W1"], layer["W2"]
+    lay = layer["layout"]
+    x, W1, W2 = layer["x"], layer["W1"], layer["W2"]
     rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
     shared = layer["shared"]
     mx = layer.get("mx")
     if mx is not None:  # MXFP8 expert weights: routed and shared experts together, then the combine
         rec(0)
-        B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
-                                bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                                bufs.x_scattered, bufs.route_scatter_ws)
+        route_and_scatter(layer, bufs, cfg, bias_t, routes, copy_rows=True)
         rec(1)
         if mx["shared"] is not None:
             q1, s1, q2, s2, wg = mx["shared"]
@@ -147,9 +246,7 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
         ws1, ws2, wg = shared
         B.moe_shared_expert(x, ws1, ws2, wg, bufs.y, bufs.shared_ws, False, stream=side, layout=lay)
         rec(0)
-        B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
-                                bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                                bufs.x_scattered, bufs.route_scatter_ws)
+        route_and_scatter(layer, bufs, cfg, bias_t, routes, copy_rows=True)
         rec(1)
         B.moe_grouped_swiglu_fc1(bufs.x_scattered, bufs.expert_offsets, W1, bufs.act, layout=lay)
         rec(2)
@@ -161,9 +258,7 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
         return
     gather = layer.get("gather", False)   # fc1 reads the routed rows from x through row_token
     rec(0)
-    B.moe_route_and_scatter(x, wr, bias_t, cfg.top_k, bufs.topk_ids, bufs.topk_weights, bufs.logits,
-                            bufs.scatter_index, bufs.row_token, bufs.expert_offsets, bufs.status_words,
-                            None if gather else bufs.x_scattered, bufs.route_scatter_ws)
+    route_and_scatter(layer, bufs, cfg, bias_t, routes, copy_rows=not gather)
     rec(1)
     if shared is not None:
         ws1, ws2, wg = shared
@@ -190,83 +285,164 @@ def run_step(layer, bufs, cfg, bias_t, events=None, side=None):
     rec(4)
 
 
-def cpu_baseline(layer, cfg, bufs, sample_tokens):
-    """Time the oracle on the first `sample_tokens` tokens and check the GPU output against it."""
+class HostExperts:
+    """Expert weights as the K x N float32 host matrices the oracle takes (x @ W),
+    copied from the device one expert at a time when the oracle first asks for it.
+    Nothing is cached, so host memory holds about one expert; the time spent
+    moving and upcasting weights is kept in `copy_s`, apart from the oracle's own
+    time.  With MXFP8 codes the oracle's exact dequantization runs on access (its
+    own arithmetic, so it is not counted in `copy_s`)."""
+
+    def __init__(self, w=None, layout=None, q=None, sc=None, axis=None):
+        self.w, self.layout, self.q, self.sc, self.axis = w, layout, q, sc, axis
+        self.copy_s = 0.0
+
+    def __len__(self):
+        return (self.w if self.w is not None else self.q).shape[0]
+
+    def __getitem__(self, e):
+        from oracle import moe_oracle as O
+        t0 = time.perf_counter()
+        if self.q is not None:
+            q, sc = self.q[e].cpu().numpy(), self.sc[e].cpu().numpy()
+            self.copy_s += time.perf_counter() - t0
+            return np.ascontiguousarray(O.mx_dequant(q, sc, axis=self.axis).T.astype(np.float32))
+        a = self.w[e].cpu().float().numpy()
+        if self.layout == B.MOE_W_NK:
+            a = np.ascontiguousarray(a.T)
+        self.copy_s += time.perf_counter() - t0
+        return a
+
+
+def _host(t):
+    return t.detach().cpu().float().numpy() if t.is_floating_point() else t.detach().cpu().numpy()
+
+
+def cpu_baseline(layer, cfg, sample_tokens, info):
+    """Time the oracle (the whole layer, routing included) on the first
+    `sample_tokens` tokens on the host cores; returns (record, oracle output)."""
     import threadpoolctl
     from oracle import moe_oracle as O
 
     S = min(sample_tokens, cfg.T)
-    f = lambda t: t.detach().float().cpu().numpy()
-    # the oracle takes each weight as the K x N matrix of x @ W
-    fw = (lambda t: np.ascontiguousarray(f(t).T)) if layer["layout"] == B.MOE_W_NK else f
-    log(f"cpu baseline: copying inputs for {S} tokens to the host")
-    x = f(layer["x"][:S])
-    wr = f(layer["w_router"])
+    contract = cfg.dtype == "bf16"
+    nk = layer["layout"] == B.MOE_W_NK
+    x = _host(layer["x"][:S])
+    wr = _host(layer["w_router"])
     mx = layer.get("mx")
-    if mx is not None:  # the oracle dequantizes the MXFP8 codes exactly, one expert when it is first used
-        u = lambda t: t.cpu().numpy()
-
-        class _Lazy:
-            def __init__(self, q, sc, axis):
-                self.q, self.sc, self.axis, self.cache = q, sc, axis, {}
-
-            def __len__(self):
-                return self.q.shape[0]
-
-            def __getitem__(self, e):
-                if e not in self.cache:
-                    d = O.mx_dequant(u(self.q[e]), u(self.sc[e]), axis=self.axis)
-                    self.cache[e] = np.ascontiguousarray(d.T.astype(np.float32))
-                return self.cache[e]
-
-        W1 = _Lazy(mx["W1q"], mx["W1s"], 0)
-        W2 = _Lazy(mx["W2q"], mx["W2s"], 1)
+    if mx is not None:
+        W1 = HostExperts(q=mx["W1q"], sc=mx["W1s"], axis=0)
+        W2 = HostExperts(q=mx["W2q"], sc=mx["W2s"], axis=1)
         shared = None
         if mx["shared"] is not None:
             q1, s1, q2, s2, wg = mx["shared"]
+            u = lambda t: t.cpu().numpy()
             shared = (np.ascontiguousarray(O.mx_dequant(u(q1), u(s1), axis=0).T.astype(np.float32)),
                       np.ascontiguousarray(O.mx_dequant(u(q2), u(s2), axis=1).T.astype(np.float32)),
-                      f(wg) if wg is not None else None)
+                      _host(wg) if wg is not None else None)
     else:
-        W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
-        W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
+        W1 = HostExperts(layer["W1"], layer["layout"])
+        W2 = HostExperts(layer["W2"], layer["layout"])
         shared = None
         if layer["shared"] is not None:
             ws1, ws2, wg = layer["shared"]
-            shared = (fw(ws1), fw(ws2), f(wg) if wg is not None else None)
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    log(f"cpu baseline: oracle over {S} tokens with {threads} BLAS threads")
-    runs = []
-    while True:  # repeat short runs (up to 5, about 10 s of CPU work) and take the median
-        t0 = time.perf_counter()
-        ref = O.moe_forward(x, wr, W1, W2, cfg.top_k, bias=layer["bias"], shared=shared, contract=True,
-                            dtype=np.float32)
-        runs.append(time.perf_counter() - t0)
-        if len(runs) >= 5 or sum(runs) >= 10.0:
-            break
+            fw = (lambda t: np.ascontiguousarray(_host(t).T)) if nk else _host
+            shared = (fw(ws1), fw(ws2), _host(wg) if wg is not None else None)
+    threads = info["threads"]
+    log(f"cpu baseline: oracle over {S} of {cfg.T} tokens, {threads} BLAS threads ({info['blas']}), "
+        f"{info['cpu_model']}")
+    runs, walls = [], []
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        while True:  # up to 3 runs within about 20 s of wall time; the median is reported
+            c0 = W1.copy_s + W2.copy_s
+            t0 = time.perf_counter()
+            ref = O.moe_forward(x, wr, W1, W2, cfg.top_k, bias=layer["bias"], shared=shared, contract=contract,
+                                dtype=np.float32)
+            wall = time.perf_counter() - t0
+            walls.append(wall)
+            runs.append(wall - (W1.copy_s + W2.copy_s - c0))
+            if len(runs) >= 3 or sum(walls) >= 20.0:
+                break
     dt = float(np.median(runs))
-    log(f"cpu baseline: {len(runs)} runs, median {dt:.2f} s")
-    # parity of the GPU run on the same tokens
-    ids_gpu = bufs.topk_ids[:S].cpu().numpy()
-    logits_gpu = bufs.logits[:S].cpu().numpy()
-    topk_exact = bool(np.array_equal(ids_gpu, O.topk_select(logits_gpu, cfg.top_k)))
-    same_route = (ids_gpu == ref["ids"]).all(1)
-    y_gpu = bufs.y[:S].cpu().numpy()[same_route]
-    y_ref = ref["y"][same_route]
-    d = y_gpu.astype(np.float64) - y_ref
-    max_err = float(np.abs(d).max()) if d.size else 0.0
-    rel = float(np.linalg.norm(d) / max(np.linalg.norm(y_ref), 1e-30)) if d.size else 0.0
-    ok = topk_exact and max_err <= 2e-2 and rel <= 1e-2 and np.isfinite(y_gpu).all()
-    parity = {"topk_bit_exact_on_gpu_logits": topk_exact, "tokens_compared": int(same_route.sum()),
-              "near_tie_tokens_excluded": int((~same_route).sum()), "max_abs_err": max_err,
-              "rel_fro_err": rel, "pass": bool(ok)}
-    cores = threads
-    base = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload, full layer (routing, scatter, "
-                      f"routed experts, combine, shared expert), NumPy float32 with bf16 activation rounding; "
-                      f"median of {len(runs)} runs ({', '.join(f'{r:.2f}' for r in runs)} s)"}
-    return base, parity
+    log(f"cpu baseline: {len(runs)} runs, median {dt:.2f} s of oracle time "
+        f"(+ {W1.copy_s + W2.copy_s:.1f} s moving weights to the host, not counted)")
+    base = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"first {S} of {cfg.T} tokens of the {cfg.name} workload, whole layer (routing, scatter, "
+                       f"routed experts, combine, shared expert), NumPy float32"
+                       f"{' with bf16 activation rounding' if contract else ''}; median of {len(runs)} runs "
+                       f"({', '.join(f'{r:.2f}' for r in runs)} s); expert weights are fetched from the device "
+                       f"one expert at a time and that transfer is not counted"),
+            "cpu_model": info["cpu_model"], "affinity_cpus": info["affinity_cpus"], "blas": info["blas"]}
+    return base, ref
+
+
+def parity_check(layer, cfg, bufs, bias_t, dev, side, ref, S):
+    """Parity of the run just timed, against the oracle:
+    * routing of all T tokens: GPU logits within the oracle's certified float32
+      bound, top-k bit-exact on the GPU's own logits, weights within 1e-6; tokens
+      whose oracle routes differ (certified near ties) at most 1% of T;
+    * the whole GPU layer run again with the oracle's routes fed in: scatter
+      structures bit-exact, every routed row and output finite, y on the first S
+      tokens within the tolerance of the oracle's y;
+    * the timed run's own y on the first S tokens whose routes agree with the
+      oracle's, within the same tolerance (and at least one token compared)."""
+    from oracle import moe_oracle as O
+
+    tol = {"max_abs": 2e-2, "rel_fro": 1e-2} if cfg.dtype == "bf16" else {"max_abs": 1e-4, "rel_fro": 1e-4}
+    T, k, E = cfg.T, cfg.top_k, cfg.E
+    xh, wrh = _host(layer["x"]), _host(layer["w_router"])
+    L_o = O.router_logits(xh, wrh, layer["bias"])
+    bound = O.router_logit_bound(xh, wrh, layer["bias"])
+    Lg = bufs.logits.cpu().numpy()
+    ids_g, w_g = bufs.topk_ids.cpu().numpy(), bufs.topk_weights.cpu().numpy()
+    ids_o = O.topk_select(L_o, k)
+    w_o = O.route_weights(L_o, ids_o)
+    near_tie = (ids_o != ids_g).any(1)
+    routing = {"tokens": T,
+               "logits_within_certified_bound": bool((np.abs(Lg.astype(np.float64) - L_o) <= bound).all()),
+               "topk_bit_exact_on_gpu_logits": bool(np.array_equal(ids_g, O.topk_select(Lg, k))),
+               "weights_max_abs_err": float(np.abs(w_g - O.route_weights(Lg, ids_g)).max()),
+               "near_tie_tokens": int(near_tie.sum())}
+    routing_ok = (routing["logits_within_certified_bound"] and routing["topk_bit_exact_on_gpu_logits"]
+                  and routing["weights_max_abs_err"] <= 1e-6 and near_tie.mean() <= 0.01)
+
+    def err(a, b):
+        d = a.astype(np.float64) - b
+        return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(b), 1e-30))
+
+    # the GPU layer with the oracle's routes fed in
+    fb = B.MoELayerBuffers(T, cfg.H, E, k, cfg.I, cfg.I_s, layer["x"].dtype, dev)
+    fb.y_rows.fill_(float("nan"))
+    fb.y.fill_(float("nan"))
+    run_step(layer, fb, cfg, bias_t, side=side,
+             routes=(torch.from_numpy(ids_o).to(dev), torch.from_numpy(w_o).to(dev)))
+    torch.cuda.synchronize()
+    sc = O.build_scatter(ids_o, E)
+    R = T * k
+    scatter_ok = (np.array_equal(fb.scatter_index.cpu().numpy(), sc["scatter_index"])
+                  and np.array_equal(fb.row_token.cpu().numpy(), sc["row_token"])
+                  and np.array_equal(fb.expert_offsets.cpu().numpy(), sc["offsets"])
+                  and fb.status_words.cpu().tolist() == [sc["max_group"], 0])
+    fed_finite = bool(torch.isfinite(fb.y_rows[:R]).all().item() and torch.isfinite(fb.y).all().item())
+    same_o = (ref["ids"] == ids_o[:S]).all(1)    # the oracle's routes of the sample, computed alone
+    y_fed = fb.y[:S].cpu().numpy()[same_o]
+    fmx, frel = err(y_fed, ref["y"][same_o]) if same_o.any() else (float("inf"), float("inf"))
+    fed = {"tokens_compared": int(same_o.sum()), "max_abs_err": fmx, "rel_fro_err": frel,
+           "scatter_bit_exact": bool(scatter_ok), "all_rows_finite": fed_finite}
+    fed_ok = (scatter_ok and fed_finite and same_o.sum() > 0 and (~same_o).mean() <= 0.01 and fmx <= tol["max_abs"]
+              and frel <= tol["rel_fro"])
+    del fb
+
+    # the timed run's own output
+    own_finite = bool(torch.isfinite(bufs.y_rows[:R]).all().item() and torch.isfinite(bufs.y).all().item())
+    same = (ids_g[:S] == ref["ids"]).all(1)
+    omx, orel = err(bufs.y[:S].cpu().numpy()[same], ref["y"][same]) if same.any() else (float("inf"),) * 2
+    own = {"tokens_compared": int(same.sum()), "tokens_excluded_near_tie": int((~same).sum()),
+           "max_abs_err": omx, "rel_fro_err": orel, "all_rows_finite": own_finite}
+    own_ok = own_finite and same.sum() > 0 and (~same).mean() <= 0.01 and omx <= tol["max_abs"] and \
+        orel <= tol["rel_fro"]
+    return {"routing": routing, "oracle_routes_fed": fed, "own_routes": own, "tolerance": tol,
+            "pass": bool(routing_ok and fed_ok and own_ok)}
 
 
 BWD_CALLS = ("scatter_grad", "fc2_backward", "fc1_backward")
@@ -306,7 +482,7 @@ def run_backward_step(layer, bufs, bwd, dy, events=None):
     rec(3)
 
 
-def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens):
+def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens, info):
     """Time the oracle's backward on the first `sample_tokens` tokens (their GPU
     routes) and check the GPU's d_x and route-weight gradients on them: both
     depend on a token's own rows only, so they are exact on a sample."""
@@ -314,25 +490,26 @@ def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens):
     from oracle import moe_oracle as O
 
     S = min(sample_tokens, cfg.T)
-    f = lambda t: t.detach().float().cpu().numpy()
-    fw = (lambda t: np.ascontiguousarray(f(t).T)) if layer["layout"] == B.MOE_W_NK else f
-    log(f"cpu baseline (backward): copying inputs for {S} tokens to the host")
+    f = _host
     x = f(layer["x"][:S])
-    W1 = [fw(layer["W1"][e]) for e in range(cfg.E)]
-    W2 = [fw(layer["W2"][e]) for e in range(cfg.E)]
+    W1 = HostExperts(layer["W1"], layer["layout"])
+    W2 = HostExperts(layer["W2"], layer["layout"])
     ids = bufs.topk_ids[:S].cpu().numpy()
     w = bufs.topk_weights[:S].cpu().numpy()
     dys = f(dy[:S])
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    log(f"cpu baseline (backward): oracle over {S} tokens with {threads} BLAS threads")
-    runs = []
-    while True:
-        t0 = time.perf_counter()
-        ref = O.moe_backward(x, W1, W2, (ids, w), dys, contract=True, dtype=np.float32)
-        runs.append(time.perf_counter() - t0)
-        if len(runs) >= 5 or sum(runs) >= 10.0:
-            break
+    threads = info["threads"]
+    log(f"cpu baseline (backward): oracle over {S} tokens with {threads} BLAS threads ({info['blas']})")
+    runs, walls = [], []
+    with threadpoolctl.threadpool_limits(limits=threads, user_api="blas"):
+        while True:
+            c0 = W1.copy_s + W2.copy_s
+            t0 = time.perf_counter()
+            ref = O.moe_backward(x, W1, W2, (ids, w), dys, contract=True, dtype=np.float32)
+            wall = time.perf_counter() - t0
+            walls.append(wall)
+            runs.append(wall - (W1.copy_s + W2.copy_s - c0))
+            if len(runs) >= 3 or sum(walls) >= 20.0:
+                break
     dt = float(np.median(runs))
     log(f"cpu baseline (backward): {len(runs)} runs, median {dt:.2f} s")
     parity = {}
@@ -349,7 +526,9 @@ def cpu_baseline_backward(layer, cfg, bufs, bwd, dy, sample_tokens):
     base = {"value": round(S / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {S} of {cfg.T} tokens of the {cfg.name} workload with their GPU routes: routed "
                       f"experts' training forward and backward (moe_backward, NumPy float32, bf16 storage "
-                      f"rounding); median of {len(runs)} runs ({', '.join(f'{r:.2f}' for r in runs)} s)"}
+                      f"rounding); median of {len(runs)} runs ({', '.join(f'{r:.2f}' for r in runs)} s); expert "
+                      f"weights are fetched from the device one expert at a time and that transfer is not counted",
+            "cpu_model": info["cpu_model"], "affinity_cpus": info["affinity_cpus"], "blas": info["blas"]}
     return base, parity
 
 
@@ -373,30 +552,37 @@ def backward_setup(cfg, layer, bias_t, dev):
     return bufs, bwd, dy
 
 
-def bench_backward(args, cfg, layer, bias_t, dev):
+def bench_backward(args, cfg, layer, bias_t, dev, evict, info):
     lay = layer["layout"]
     bufs, bwd, dy = backward_setup(cfg, layer, bias_t, dev)
     torch.cuda.synchronize()
     counts = np.diff(bufs.expert_offsets.cpu().numpy())
+    steps = args.steps or 50
     for _ in range(args.warmup):
         run_backward_step(layer, bufs, bwd, dy)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_CALLS) + 1)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(BWD_CALLS) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
+        evict()
         run_backward_step(layer, bufs, bwd, dy, ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+    step_ms = [ev[s][0].elapsed_time(ev[s][len(BWD_CALLS)]) for s in range(steps)]
+    stats = step_stats(step_ms)
+    ms_per_step = stats["median_ms"]
+    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
                 for i, c in enumerate(BWD_CALLS)}
     log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
     work = backward_work(cfg, counts)
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], per_call["fc1_backward"] / 1e3)
+    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    roof["algorithmic_flops"] = work["fc1_flops"]
     tr = committed_traffic(cfg.name, backward=True) if lay == B.MOE_W_KN else None
     roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per fc1_backward call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    add_profile_fraction(roof, committed_trace(cfg.name, backward=True) if lay == B.MOE_W_KN else None)
     roof["kernel"] = ("fc1_backward call = grouped_gemm_bf16_pipe<StoreF32, ROLE 2> (input gradient) + "
                       "gather_combine_k + grouped_wgrad_bf16<ROLE 1> (weight gradient)")
     step_s = ms_per_step / 1e3
@@ -406,7 +592,7 @@ def bench_backward(args, cfg, layer, bias_t, dev):
         "value": round(cfg.T / step_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
@@ -414,6 +600,10 @@ def bench_backward(args, cfg, layer, bias_t, dev):
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded normals; random-init weights of the layer shape; dy seeded normal / sqrt(H))",
+        "timing": {"step": stats, "cache": "evicted" if evict.buf is not None else "warm",
+                   "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+                   "note": "step = HIP events around the three calls; value uses the median; the wall time also "
+                           "covers the 1 GiB eviction fill before each step"},
         "config": {"workload": cfg.name, "pass": "backward of the routed experts (routes fixed)", "T": cfg.T,
                    "H": cfg.H, "E": cfg.E, "top_k": cfg.top_k, "I": cfg.I, "routing": cfg.skew or "natural",
                    "shared_expert": "not included", "realized_rows_per_expert": counts.tolist()},
@@ -428,7 +618,7 @@ def bench_backward(args, cfg, layer, bias_t, dev):
     }
     rc = 0
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline_backward(layer, cfg, bufs, bwd, dy, args.cpu_sample or 512)
+        base, parity = cpu_baseline_backward(layer, cfg, bufs, bwd, dy, args.cpu_sample or 512, info)
         result["cpu_baseline"] = base
         result["parity"] = parity
         if not parity["pass"]:
@@ -438,17 +628,29 @@ def bench_backward(args, cfg, layer, bias_t, dev):
     sys.exit(rc)
 
 
+def default_cpu_sample(cfg):
+    """Tokens in the CPU-baseline sample: all of a decode batch, at most 2048 of a
+    prefill batch (about 1-15 s of oracle time on 16 host threads)."""
+    return cfg.T if cfg.T <= 64 else min(cfg.T, 2048)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50 for prefill shapes, 200 for decode shapes, T <= 64)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="scout", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--workload", default="v3", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="tokens in the CPU-baseline sample (default 2048 for the forward, 512 for --backward)")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one step into a HIP graph and time graph replays (launch-bound decode shapes)")
+                    help="tokens in the CPU-baseline sample (default: all tokens of a decode batch, 2048 of a "
+                         "prefill batch; 512 for --backward)")
+    ap.add_argument("--launch", choices=("auto", "eager", "graph"), default="auto",
+                    help="eager launches, or replays of a HIP graph of one step; auto = graph for decode shapes "
+                         "(T <= 64), eager otherwise")
+    ap.add_argument("--graph", action="store_true", help="same as --launch graph")
+    ap.add_argument("--no-evict", action="store_true",
+                    help="do not evict the last-level cache before each timed step (warm-cache figures)")
     ap.add_argument("--shared", choices=("fused", "overlap"), default="fused",
                     help="shared expert inside the routed fc1/fc2 launches (fused, the default: measured faster "
                          "on every workload) or on a second stream concurrent with routing (overlap)")
@@ -456,8 +658,8 @@ def main():
                     help="expert weight format: bf16, or MXFP8 (e4m3 codes, one e8m0 scale per 8 along the "
                          "intermediate axis, dequantized exactly in the kernels; activations stay bf16)")
     ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
-                    help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default: measured "
-                         "as fast or faster on every workload), nk = [N, K] (torch.nn.Linear layout)")
+                    help="expert weight storage: kn = [K, N] per expert (the x @ W form, the default), "
+                         "nk = [N, K] (torch.nn.Linear layout)")
     ap.add_argument("--rows", choices=("gather", "copy"), default="gather",
                     help="routed rows for fc1: gathered from x through row_token on load (default), or copied to "
                          "x_scattered by the scatter build (the MXFP8 and overlap paths always copy)")
@@ -477,6 +679,12 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     cfg = wl.WORKLOADS[args.workload]
+    decode = cfg.T <= 64
+    launch = "graph" if args.graph else args.launch
+    if launch == "auto":
+        launch = "graph" if decode else "eager"
+    steps = args.steps or (200 if decode else 50)
+    info = host_info()
     log(f"workload {cfg}")
     layer = wl.make_layer(cfg, dev)
     layer["layout"] = B.MOE_W_NK if args.layout == "nk" else B.MOE_W_KN
@@ -497,6 +705,7 @@ def main():
             layer["shared"] = (t(ws1), t(ws2), wg)
     bias_t = torch.from_numpy(layer["bias"]).to(dev) if layer["bias"] is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, dev)
+    evict = Evictor(dev, enabled=not args.no_evict)
     torch.cuda.synchronize()
     if args.copy_reference_mb > 0:
         n = args.copy_reference_mb << 20
@@ -508,10 +717,10 @@ def main():
         del src, dst
 
     if args.backward:
-        if args.weights != "bf16" or args.graph:
+        if args.weights != "bf16" or args.graph or args.launch == "graph":
             print("--backward runs with bf16 weights and eager launches", file=sys.stderr)
             sys.exit(2)
-        bench_backward(args, cfg, layer, bias_t, dev)
+        bench_backward(args, cfg, layer, bias_t, dev, evict, info)
 
     mode = args.shared
     if not cfg.I_s:
@@ -528,11 +737,13 @@ def main():
         raise RuntimeError(f"router produced {status[1]} out-of-range expert ids")
     counts = np.diff(bufs.expert_offsets.cpu().numpy())
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    if args.graph:
-        # Per-call times come from an eager pass with events; the timed steps replay a captured graph.
-        for s in range(args.steps):
+    mk = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ev = [mk(len(CALLS) + 1) for _ in range(steps)]
+    if launch == "graph":
+        # Per-call times come from an eager pass (same eviction); the timed steps replay a captured graph.
+        torch.cuda.synchronize()
+        for s in range(steps):
+            evict()
             run_step(layer, bufs, cfg, bias_t, ev[s], side=side)
         torch.cuda.synchronize()
         capture_stream = torch.cuda.Stream()
@@ -544,33 +755,52 @@ def main():
         torch.cuda.current_stream().wait_stream(capture_stream)
         for _ in range(args.warmup):
             graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        step_fn = lambda e: (e[0].record(), graph.replay(), e[1].record())
     else:
-        t0 = time.perf_counter()
-        for s in range(args.steps):
-            run_step(layer, bufs, cfg, bias_t, ev[s], side=side)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+        step_fn = lambda e: run_step(layer, bufs, cfg, bias_t, e, side=side)
+    sev = [mk(2) for _ in range(steps)] if launch == "graph" else [(e[0], e[len(CALLS)]) for e in ev]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        evict()
+        step_fn(sev[s] if launch == "graph" else ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stats = step_stats([a.elapsed_time(b) for a, b in sev])
+    # warm cache, labelled: the same steps back to back with nothing evicted
+    wev = [mk(2) for _ in range(min(steps, 50))]
+    for e in wev:
+        if launch == "graph":
+            e[0].record()
+            graph.replay()
+            e[1].record()
+        else:
+            e[0].record()
+            run_step(layer, bufs, cfg, bias_t, side=side)
+            e[1].record()
+    torch.cuda.synchronize()
+    warm = step_stats([a.elapsed_time(b) for a, b in wev])
+    ms_per_step = stats["median_ms"]
+    per_call = {c: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
                 for i, c in enumerate(CALLS)}
-    log("per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
+    log(f"step ms median {stats['median_ms']:.4f} p10 {stats['p10_ms']:.4f} p90 {stats['p90_ms']:.4f} "
+        f"(warm {warm['median_ms']:.4f}); per-call ms: " + ", ".join(f"{k} {v:.4f}" for k, v in per_call.items()))
 
     work = algorithmic_work(cfg, counts, shared_in_gemms=(mode in ("fused", "mx")),
                             weight_bytes=1.125 if args.weights == "mxfp8" else None)
     fc1_s = per_call["fc1"] / 1e3
     fc2_s = per_call["fc2"] / 1e3
     roof = roofline(work["fc1_flops"], work["fc1_bytes"], fc1_s)
-    # the committed counters were taken in the default configuration (fused shared expert, [K, N], gathered rows)
-    tr = committed_traffic(cfg.name) if mode == "fused" and args.layout == "kn" and layer["gather"] else None
+    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    roof["algorithmic_flops"] = work["fc1_flops"]
+    roof["avg_us"] = round(per_call["fc1"] * 1e3, 2)
+    # the committed profiles were taken in the default configuration (fused shared expert, [K, N], gathered rows,
+    # bf16 weights, eviction before every step)
+    default_cfg = mode == "fused" and args.layout == "kn" and layer["gather"] and not args.no_evict
+    tr = committed_traffic(cfg.name) if default_cfg else None
     roof["traffic"] = round(tr["hbm_bytes_per_call"] / 1e9, 4) if tr else None
     roof["traffic_unit"] = "GB per fc1 call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-    roof["algorithmic_bytes"] = work["fc1_bytes"]
+    add_profile_fraction(roof, committed_trace(cfg.name) if default_cfg else None)
     one_launch = bool(cfg.I_s) and B.moe_and_shared_launches(layer["x"].dtype, cfg.R, cfg.H, cfg.E, cfg.I, cfg.T,
                                                                cfg.I_s) == 1
     if mode == "fused" and one_launch:
@@ -595,7 +825,7 @@ def main():
         "value": round(cfg.T / layer_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
@@ -607,9 +837,19 @@ def main():
                    "I_s": cfg.I_s, "shared_gate": cfg.gated, "routing": cfg.skew or "natural",
                    "realized_rows_per_expert": counts.tolist()},
         "roofline": roof,
+        "timing": {"launch": "hip graph replay" if launch == "graph" else "eager launches",
+                   "cache": "evicted" if evict.buf is not None else "warm",
+                   "step": stats, "warm_cache_step": warm,
+                   "wall_ms_per_step": round(wall * 1e3 / steps, 4),
+                   "note": ("value and ms_per_step use the median of the per-step HIP-event times; before every "
+                            "timed step a 1 GiB fill kernel (outside the events) evicts the 256 MiB last-level "
+                            "cache, so the wall time per step also covers it; warm_cache_step repeats the step "
+                            "back to back without eviction")},
         "grouped_gemm": {"tflops": round(gg_tflops, 2), "frac_mfma_peak": round(gg_tflops / PEAK_BF16_TFLOPS, 4),
                          "gbps": round(gg_gbps, 1), "frac_hbm_peak": round(gg_gbps / PEAK_HBM_GBPS, 4),
-                         "fc1_ms": round(per_call["fc1"], 4), "fc2_ms": round(per_call["fc2"], 4)},
+                         "fc1_ms": round(per_call["fc1"], 4), "fc2_ms": round(per_call["fc2"], 4),
+                         "fc1_frac": roof["frac"],
+                         "fc2": roofline(work["fc2_flops"], work["fc2_bytes"], fc2_s)},
         "layer": {"flops": work["layer_flops"], "bytes_alg": work["layer_bytes"],
                   "tflops": round(work["layer_flops"] / layer_s / 1e12, 2),
                   "gbps_alg": round(work["layer_bytes"] / layer_s / 1e9, 1),
@@ -618,7 +858,6 @@ def main():
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
         "per_call_note": ("fc1/fc2 carry the shared expert too (see shared_expert)" if mode in ("fused", "mx")
                           else "fc1/fc2 are the routed experts only"),
-        "timing": "hip graph replay" if args.graph else "eager launches",
         "weight_layout": "[N, K] per expert (torch.nn.Linear)" if args.layout == "nk" else "[K, N] per expert",
         "routed_rows": ("gathered from x through row_token by fc1" if layer["gather"]
                         else "copied to x_scattered by the scatter build"),
@@ -633,8 +872,10 @@ def main():
     }
     rc = 0
     if not args.no_cpu_baseline:
-        base, parity = cpu_baseline(layer, cfg, bufs, args.cpu_sample or 2048)
+        S = min(args.cpu_sample or default_cpu_sample(cfg), cfg.T)
+        base, ref = cpu_baseline(layer, cfg, S, info)
         result["cpu_baseline"] = base
+        parity = parity_check(layer, cfg, bufs, bias_t, dev, side, ref, S)
         result["parity"] = parity
         if not parity["pass"]:
             log(f"PARITY FAILURE: {parity}")

@@ -86,7 +86,11 @@ def trace(stats_csv: str, kernel_substr: str, out_md: str, command: str) -> None
             matched += float(r["AverageNs"]) / 1e3
             names.append(short(r["Name"]))
     lines += ["", f"Timed call (kernels containing `{kernel_substr}`: {'; '.join(names)}): "
-                  f"summed average duration {matched:.2f} us"]
+                  f"summed average duration {matched:.2f} us", "",
+              "Machine-readable record for the timed call (read by bench.py for the profile-based roofline "
+              "fraction):", "",
+              "TRACE_JSON " + json.dumps({"kernels": names, "avg_us_per_call": matched,
+                                          "gemm_source_hash": kernel_source_hash()})]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 

@@ -66,6 +66,7 @@ __all__ = [
     "topk_select",
     "route_weights",
     "route",
+    "router_logit_bound",
     "build_scatter",
     "scatter_rows",
     "silu",
@@ -207,6 +208,31 @@ def route(x, w_router, top_k: int, bias=None):
     L = router_logits(x, w_router, bias)
     ids = topk_select(L, top_k)
     return L, ids, route_weights(L, ids)
+
+
+def router_logit_bound(x, w_router, bias=None) -> np.ndarray:
+    """Largest distance [T,E] between router_logits and logits accumulated in float32.
+
+    The pages fix no precision for the router GEMM ([PLENA-C] section "Group E"
+    names it only), so a float32-accumulating implementation may sum the H
+    products in any order.  Every order obeys the forward error bound of a
+    summed dot product, |fl(sum_h x_h w_h) - sum_h x_h w_h| <= gamma_H *
+    sum_h |x_h| |w_h| with gamma_n = n u / (1 - n u) and u = 2^-24 (Higham,
+    "Accuracy and Stability of Numerical Algorithms", section 3.1; products of
+    bf16 or float32 inputs taken exactly or rounded once are covered by the
+    same gamma).  Returned: twice that term, plus four float32 units of
+    |value| + |bias| for the rounding of router_logits itself and of the bias
+    add on either side.  A near tie between the k-th and (k+1)-th logit closer
+    than this bound may legitimately order differently.
+    """
+    u = 2.0 ** -24
+    ax = np.abs(np.asarray(x, np.float64))
+    aw = np.abs(np.asarray(w_router, np.float64))
+    H = ax.shape[1]
+    gamma = H * u / (1.0 - H * u)
+    mag = ax @ aw
+    b = 0.0 if bias is None else np.abs(np.asarray(bias, np.float64))[None, :]
+    return 2.0 * gamma * mag + 4.0 * u * (mag + b) + 1e-30
 
 
 # ----------------------------------------------------------------------------

@@ -5,8 +5,6 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-U32 = 2.0 ** -24   # unit roundoff of float32
-
 # Output tolerances: bf16 workloads against the oracle in contract mode
 # (the SwiGLU output rounded to bf16 where the kernels round it), float32
 # workloads against the plain oracle.
@@ -36,25 +34,12 @@ def assert_output_close(y, ref, dtype: str, what: str = "y"):
     return mx, rel
 
 
-def logits_error_bound(x, w, bias=None):
-    """Bound on |fp32-accumulated logits - exact logits|, plus the oracle's own
-    rounding to float32 and the bias add: gamma_H * sum|x||w| (gamma_n =
-    n u / (1 - n u)) doubled for slack, plus two float32 ulps of the value."""
-    x = np.abs(np.asarray(x, np.float64))
-    w = np.abs(np.asarray(w, np.float64))
-    H = x.shape[1]
-    gamma = H * U32 / (1 - H * U32)
-    mag = x @ w
-    b = 0.0 if bias is None else np.abs(np.asarray(bias, np.float64))[None, :]
-    return 2.0 * gamma * mag + 4.0 * U32 * (mag + b) + 1e-30
-
-
 def check_routing(logits_gpu, ids_gpu, w_gpu, x, wr, bias, top_k, oracle):
     """Route parity: logits within the certified bound of the oracle's; top-k
     bit-exact against the oracle applied to the GPU's own logits; weights
     within 1e-6 of the oracle's softmax of those logits."""
     ref_logits = oracle.router_logits(x, wr, bias)
-    bound = logits_error_bound(x, wr, bias)
+    bound = oracle.router_logit_bound(x, wr, bias)
     excess = np.abs(logits_gpu.astype(np.float64) - ref_logits) - bound
     assert excess.max() <= 0, f"logits outside the certified bound by {excess.max():.3e}"
     ids_ref = oracle.topk_select(logits_gpu, top_k)

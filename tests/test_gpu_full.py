@@ -58,6 +58,7 @@ def test_full_size_layer(name, rows):
     bias_t = torch.from_numpy(bias).to(DEV) if bias is not None else None
     bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, x.dtype, DEV)
     bufs.y_rows.fill_(float("nan"))
+    bufs.y.fill_(float("nan"))
     B.moe_layer_forward(x, wr, bias_t, layer["W1"], layer["W2"], cfg.top_k, shared=layer["shared"], bufs=bufs,
                         fused_shared=True, fused_route=True, gather=rows == "gather")
     torch.cuda.synchronize()
@@ -79,6 +80,10 @@ def test_full_size_layer(name, rows):
         xs = host(bufs.x_scattered[torch.from_numpy(pick).to(DEV)])
         assert np.array_equal(xs.view(np.uint32), xh[sc["row_token"][pick]].view(np.uint32))
 
+    # every routed row and every output was written (the buffers were NaN-filled)
+    assert torch.isfinite(bufs.y_rows[:cfg.R]).all().item(), f"{name}: a routed row was not computed"
+    assert torch.isfinite(bufs.y).all().item(), f"{name}: non-finite output"
+
     # outputs on sampled tokens
     toks = _sample_tokens(cfg.T, 10 if cfg.E >= 256 else 24, seed=cfg.T)
     W1, W2 = layer["W1"], layer["W2"]
@@ -94,6 +99,141 @@ def test_full_size_layer(name, rows):
     per_slot = np.stack([Ys[sc["scatter_index"][t]] for t in toks])
     assert_output_close(per_slot.reshape(-1, cfg.H), ref["per_slot"].reshape(-1, cfg.H), "bf16", f"{name} Y_s")
     print(f"[full] {name}: y max|err| {mx:.3e} rel_fro {rel:.3e} over {len(toks)} tokens", flush=True)
+
+
+def _bench_layer(cfg):
+    layer = wl.make_layer(cfg, DEV)
+    layer["layout"] = B.MOE_W_KN
+    layer["gather"] = True
+    bias_t = torch.from_numpy(layer["bias"]).to(DEV) if layer["bias"] is not None else None
+    return layer, bias_t
+
+
+def _host_shared(layer):
+    if layer["shared"] is None:
+        return None
+    ws1, ws2, wg = layer["shared"]
+    return host(ws1), host(ws2), host(wg) if wg is not None else None
+
+
+def _check_sampled_outputs(name, cfg, layer, bufs, ids, w, toks):
+    """y and the sampled tokens' Y_s rows against the oracle's per-token layer equation."""
+    xh = host(layer["x"])
+    W1, W2 = layer["W1"], layer["W2"]
+    ref = O.token_outputs(xh[toks], ids[toks], w[toks], lambda e: (host(W1[e]), host(W2[e])),
+                          shared=_host_shared(layer), contract=True, dtype=np.float32)
+    mx, rel = assert_output_close(host(bufs.y)[toks], ref["y"], "bf16", f"{name} y")
+    si = host(bufs.scatter_index)
+    Ys = host(bufs.y_rows)
+    per_slot = np.stack([Ys[si[t]] for t in toks])
+    assert_output_close(per_slot.reshape(-1, cfg.H), ref["per_slot"].reshape(-1, cfg.H), "bf16", f"{name} Y_s")
+    return mx, rel
+
+
+# The end-to-end contract: the oracle's routes (computed on the host from the
+# oracle's own logits) fed into the GPU layer, in the benchmark's launch
+# configuration after routing (scatter build, fc1 gathering rows from x with the
+# shared expert, fc2 with the shared expert, combine).
+FED = ["scout", "qwen2", "v2l", "v3", "v2l_decode1", "v2l_decode16", "v3_decode64"]
+
+
+@pytest.mark.parametrize("name", FED)
+def test_full_size_layer_oracle_routes_fed(name):
+    import bench
+
+    cfg = wl.WORKLOADS[name]
+    print(f"[full-fed] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k} I={cfg.I} I_s={cfg.I_s}", flush=True)
+    layer, bias_t = _bench_layer(cfg)
+    _, ids, w = O.route(host(layer["x"]), host(layer["w_router"]), cfg.top_k, layer["bias"])
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, DEV)
+    bufs.y_rows.fill_(float("nan"))
+    bufs.y.fill_(float("nan"))
+    bench.run_step(layer, bufs, cfg, bias_t, routes=(torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)))
+    torch.cuda.synchronize()
+    sc = O.build_scatter(ids, cfg.E)
+    assert np.array_equal(host(bufs.scatter_index), sc["scatter_index"])
+    assert np.array_equal(host(bufs.row_token), sc["row_token"])
+    assert np.array_equal(host(bufs.expert_offsets), sc["offsets"])
+    assert host(bufs.status_words).tolist() == [sc["max_group"], 0]
+    assert torch.isfinite(bufs.y_rows[:cfg.R]).all().item(), f"{name}: a routed row was not computed"
+    assert torch.isfinite(bufs.y).all().item(), f"{name}: non-finite output"
+    toks = _sample_tokens(cfg.T, 10 if cfg.E >= 256 else 24, seed=cfg.T + 5)
+    mx, rel = _check_sampled_outputs(name, cfg, layer, bufs, ids, w, toks)
+    print(f"[full-fed] {name}: y max|err| {mx:.3e} rel_fro {rel:.3e} over {len(toks)} tokens", flush=True)
+
+
+# HIP-graph replay, the launch mode of the benchmark's decode lines: one step of
+# bench.run_step captured as bench.py captures it, replayed several times with
+# eager work and synchronisations in between; every replay must reproduce the
+# eager step bit for bit (all the kernels reduce in a fixed order), also after
+# x changes in place, and the replayed outputs must match the oracle.
+GRAPH = ["v2l_decode1", "v2l_decode16", "v2l_decode64", "v3_decode64"]
+
+
+@pytest.mark.parametrize("name", GRAPH)
+def test_graph_replay_decode(name):
+    import bench
+
+    cfg = wl.WORKLOADS[name]
+    print(f"[graph] {name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.top_k}", flush=True)
+    layer, bias_t = _bench_layer(cfg)
+    bufs = B.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.top_k, cfg.I, cfg.I_s, layer["x"].dtype, DEV)
+    outs = ("y", "y_rows", "topk_ids", "topk_weights", "logits", "scatter_index", "row_token", "expert_offsets",
+            "status_words", "act")
+
+    def eager():
+        bench.run_step(layer, bufs, cfg, bias_t)
+        torch.cuda.synchronize()
+        return {k: getattr(bufs, k).clone() for k in outs}
+
+    ref0 = eager()
+    capture_stream = torch.cuda.Stream()
+    capture_stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(capture_stream):
+        with torch.cuda.graph(graph, stream=capture_stream):
+            bench.run_step(layer, bufs, cfg, bias_t)
+    torch.cuda.current_stream().wait_stream(capture_stream)
+    torch.cuda.synchronize()
+
+    def replay_matches(ref, what):
+        for key in ("y", "y_rows", "act"):
+            getattr(bufs, key).fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            a, b = getattr(bufs, k), ref[k]
+            if a.is_floating_point():
+                assert torch.equal(a.view(torch.int16 if a.element_size() == 2 else torch.int32),
+                                   b.view(torch.int16 if b.element_size() == 2 else torch.int32)), f"{what}: {k}"
+            else:
+                assert torch.equal(a, b), f"{what}: {k}"
+
+    for rep in range(3):
+        replay_matches(ref0, f"{name} replay {rep}")
+        _ = torch.randn(1024, device=DEV).sum().item()   # eager work between replays
+
+    # new tokens in place: the next T rows of the prefill draw
+    base = wl.WORKLOADS[name.split("_")[0]]
+    x2 = wl.make_x(base, DEV)[cfg.T:2 * cfg.T]
+    layer["x"].copy_(x2)
+    ref1 = eager()
+    assert not torch.equal(ref1["y"], ref0["y"])
+    for rep in range(2):
+        replay_matches(ref1, f"{name} replay on new x {rep}")
+
+    xh = host(layer["x"])
+    ids, w = host(bufs.topk_ids), host(bufs.topk_weights)
+    check_routing(host(bufs.logits), ids, w, xh, host(layer["w_router"]), layer["bias"], cfg.top_k, O)
+    sc = O.build_scatter(ids, cfg.E)
+    assert np.array_equal(host(bufs.scatter_index), sc["scatter_index"])
+    assert np.array_equal(host(bufs.row_token), sc["row_token"])
+    assert np.array_equal(host(bufs.expert_offsets), sc["offsets"])
+    assert torch.isfinite(bufs.y_rows[:cfg.R]).all().item() and torch.isfinite(bufs.y).all().item()
+    toks = _sample_tokens(cfg.T, 6 if cfg.E >= 256 else 12, seed=cfg.T + 9)
+    mx, rel = _check_sampled_outputs(name, cfg, layer, bufs, ids, w, toks)
+    print(f"[graph] {name}: replays bitwise equal to eager; y max|err| {mx:.3e} rel_fro {rel:.3e} over "
+          f"{len(toks)} tokens", flush=True)
 
 
 MX_FULL = ["v2l_decode1", "v2l_decode64", "v3_decode64"]

@@ -121,6 +121,52 @@ def test_route_weights_properties():
         assert np.all(np.diff(w, axis=1) <= 0)     # slot order: weights non-increasing
 
 
+def _fp32_sums(x, w, order):
+    """x @ w accumulated in float32 one product at a time, in the given order of h."""
+    acc = np.zeros((x.shape[0], w.shape[1]), np.float32)
+    for h in order:
+        acc = (acc + (x[:, h:h + 1] * w[h:h + 1, :]).astype(np.float32)).astype(np.float32)
+    return acc
+
+
+def test_router_logit_bound_covers_float32_accumulation_orders():
+    # float32 sums in three orders (forward, reverse, and blocked partial sums
+    # added at the end, as split-K kernels do) against the float64 product:
+    # every error lies inside the bound, including under heavy cancellation.
+    rng = np.random.default_rng(11)
+    H, E = 512, 16
+    x = torch.from_numpy(rng.standard_normal((24, H)).astype(np.float32)).bfloat16().float().numpy()
+    w = torch.from_numpy((rng.standard_normal((H, E)) * 0.02).astype(np.float32)).bfloat16().float().numpy()
+    x[:4] = np.abs(x[:4]) * 1e3                     # large same-sign terms
+    w[:, :2] = np.abs(w[:, :2])
+    x[4:8, 1::2] = -x[4:8, 0::2]                    # exact cancellation pairs
+    bias = (rng.standard_normal(E) * 3).astype(np.float32)
+    exact = O.router_logits(x, w, bias).astype(np.float64)
+    bound = O.router_logit_bound(x, w, bias)
+    for order in (range(H), range(H - 1, -1, -1)):
+        got = (_fp32_sums(x, w, order) + bias[None, :]).astype(np.float32)
+        assert np.all(np.abs(got - exact) <= bound)
+    blocks = [_fp32_sums(x[:, b:b + 64], w[b:b + 64], range(64)) for b in range(0, H, 64)]
+    got = np.zeros_like(blocks[0])
+    for part in blocks:
+        got = (got + part).astype(np.float32)
+    got = (got + bias[None, :]).astype(np.float32)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_router_logit_bound_closed_form():
+    # one term: gamma_1 |x||w| doubled plus four units of |value| + |bias|
+    u = 2.0 ** -24
+    b = O.router_logit_bound(np.array([[3.0]]), np.array([[-2.0]]), np.array([5.0], np.float32))
+    gamma = u / (1 - u)
+    assert b[0, 0] == pytest.approx(2 * gamma * 6.0 + 4 * u * (6.0 + 5.0) + 1e-30, rel=1e-12)
+    # H equal terms: gamma_H grows with H and so does the magnitude
+    for H in (100, 200):
+        gH = H * u / (1 - H * u)
+        b = O.router_logit_bound(np.ones((1, H)), np.ones((H, 1)))
+        assert b[0, 0] == pytest.approx(2 * gH * H + 4 * u * H + 1e-30, rel=1e-12)
+
+
 # ----------------------------------------------------------------------------- scatter
 def _check_scatter_invariants(ids, E, sc):
     T, k = ids.shape
