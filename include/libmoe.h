@@ -53,7 +53,26 @@ typedef enum moe_status {
   MOE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* The *_RANGE_ markers of the enums below name no value a call accepts: they
+ * make each enum as wide as int32_t, so that whatever int32_t a caller passes
+ * is a representable value that validation then rejects (in C++ an enum
+ * holding a value outside its enumerators' range is undefined). */
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_DTYPE_RANGE_MIN = -0x7fffffff - 1,
+  MOE_DTYPE_RANGE_MAX = 0x7fffffff
+} moe_dtype;
+
+/* Tile configuration of a grouped-GEMM launch, as moe_grouped_gemm_tile reports it. */
+typedef enum moe_tile_config {
+  MOE_TILE_F32 = 0,       /* float32 path: one thread per output element */
+  MOE_TILE_GENERIC = 1,   /* bf16 with a reduction size not a multiple of 64: register-staged 128 x 128 tiles */
+  MOE_TILE_128x128 = 2,   /* pipelined: 128 rows x 128 staged weight columns x 64-deep slices, 4 waves */
+  MOE_TILE_256x256 = 3,   /* pipelined: 256 x 256 x 64, 8 waves (groups of >= 512 rows on average) */
+  MOE_TILE_128x256 = 4,   /* pipelined: 128 x 256 x 32, 8 waves, two workgroups per CU (mid-sized groups) */
+  MOE_TILE_32x128 = 5     /* pipelined: 32 x 128 x 64 with split-K waves (groups of <= 32 rows on average) */
+} moe_tile_config;
 
 /* Stage of a call, in the stage vocabulary of the PLENA pages (PLENA_Compiler
  * PR #69, sections "Group B" and "Group E": router_topk, expert_route_weight,
@@ -75,7 +94,12 @@ const char* moe_call_stage(const char* call, int32_t gated);
  *             tiles are read from LDS like activation tiles).
  * The values are the same matrix either way; results are identical up to
  * the fp32 accumulation order within a tile. */
-typedef enum moe_weight_layout { MOE_W_KN = 0, MOE_W_NK = 1 } moe_weight_layout;
+typedef enum moe_weight_layout {
+  MOE_W_KN = 0,
+  MOE_W_NK = 1,
+  MOE_W_RANGE_MIN = -0x7fffffff - 1,
+  MOE_W_RANGE_MAX = 0x7fffffff
+} moe_weight_layout;
 
 /* Name of a status code ("MOE_OK", ...).  Never NULL. */
 const char* moe_status_name(int status);
@@ -173,8 +197,26 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
                                  int32_t* status_words, void* x_scattered,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_grouped_gemm_tile -- which tile configuration (moe_tile_config) the routed
+ * experts' launch of a grouped-GEMM call takes for these sizes on the current
+ * device.  Host-only: launches nothing, reads the device's CU count.
+ *
+ * Source: VeOmni docs "Fused MoE Kernel Notes", section "Backward grouped-GEMM
+ * launch bound" (the launch is shaped from the sizes; the tile walk itself comes
+ * from expert_offsets on the device); PLENA_Simulator PR #97, section "Tests"
+ * (a test asserts which encoding a policy took, not only its result).
+ * call: 0 = fc1 (moe_grouped_swiglu_fc1 and its _gather / _and_shared variants),
+ * 1 = fc2.  R, H, E, I as in those calls; T and I_s > 0 ask about the
+ * *_and_shared call (routed and shared experts may then share one launch),
+ * I_s = 0 about the plain call.  Returns -1 for invalid arguments.
+ */
+int32_t moe_grouped_gemm_tile(moe_dtype dt, int32_t call, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T,
+                              int32_t I_s);
+
 /* Workspace bytes moe_route_and_scatter needs for (dt, T, H, E, top_k); 0 for invalid sizes. */
 size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E, int32_t top_k);
+
 
 /*
  * moe_grouped_swiglu_fc1 -- per-expert gate/up projection and SwiGLU.

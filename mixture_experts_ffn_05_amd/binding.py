@@ -70,6 +70,7 @@ _SIGNATURES = {
                                                 _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size,
                                                 _vp]),
     "moe_and_shared_launches": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_grouped_gemm_tile": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_grouped_swiglu_fc1_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                                    _vp, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_grouped_fc2_and_shared": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
@@ -97,11 +98,13 @@ def header_functions() -> list[str]:
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
-    """Load libmoe.so (once) and declare its signatures.  Raises if it is missing."""
+    """Load libmoe.so (once) and declare its signatures.  Raises if it is missing.
+    LIBMOE_LIBRARY in the environment names another build of the library (the
+    host-sanitized copy the ABI tests run against)."""
     global _lib
     if _lib is not None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LIBMOE_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libmoe.so not found at {p}: build it with "
                            "`python -m mixture_experts_ffn_05_amd.build` (there is no fallback path)")
@@ -383,6 +386,15 @@ def moe_grouped_fc2_and_shared_mx8(act, expert_offsets, w2q, w2s, y_rows, act_sh
             _ptr(y, "y", torch.float32, (T, H), dev), _ptr(workspace, "workspace", torch.uint8, None, dev),
             workspace.numel(), _stream(stream, dev))
     _check(lib.moe_grouped_fc2_and_shared_mx8(*args))
+
+
+MOE_TILE_F32, MOE_TILE_GENERIC, MOE_TILE_128x128, MOE_TILE_256x256, MOE_TILE_128x256, MOE_TILE_32x128 = range(6)
+
+
+def moe_grouped_gemm_tile(dtype, call, R, H, E, I, T=0, I_s=0) -> int:
+    """moe_tile_config of the routed experts' launch of fc1 (call 0) or fc2 (call 1) for these sizes."""
+    dt = MOE_BF16 if dtype == torch.bfloat16 else MOE_F32
+    return int(load().moe_grouped_gemm_tile(dt, int(call), int(R), int(H), int(E), int(I), int(T), int(I_s)))
 
 
 def moe_and_shared_launches(dtype, R, H, E, I, T, I_s) -> int:

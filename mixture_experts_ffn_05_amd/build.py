@@ -73,5 +73,49 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host-only sanitizers for the C-ABI layer (argument validation, error strings,
+# scratch bookkeeping): each -fsanitize= applies to the host pass only, so the
+# gfx950 code is built exactly as in the library.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "sanitized", "libmoe_sanitized.so")
+
+
+def asan_runtime() -> str:
+    """clang's shared AddressSanitizer runtime, which a process must preload to load SANITIZED_LIB."""
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("clang's AddressSanitizer runtime was not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A copy of libmoe whose C-ABI layer (moe_api.hip) is built with AddressSanitizer
+    and UndefinedBehaviorSanitizer on the host side, linked with the library's
+    other objects as built by build().  For host-side tests only (no GPU needed)."""
+    out_dir = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    others = [os.path.join(BUILD_DIR, os.path.basename(s).replace(".hip", ".o"))
+              for s in sorted(glob.glob(os.path.join(CSRC, "*.hip"))) if not s.endswith("moe_api.hip")]
+    if not all(os.path.exists(o) for o in others):
+        build(verbose)
+    api_obj = os.path.join(out_dir, "moe_api_sanitized.o")
+    cmd = [hipcc(), *COMMON_FLAGS, *SANITIZE_HOST, "-c", os.path.join(CSRC, "moe_api.hip"), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on moe_api.hip (sanitized):\n{res.stdout}\n{res.stderr}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_HOST, "-shared-libsan", api_obj,
+           *others, "-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib", "-o", SANITIZED_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{res.stdout}\n{res.stderr}")
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -230,13 +230,17 @@ size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H,
   return r > sc ? r : sc;
 }
 
-moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
-                                 int32_t T, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids,
-                                 float* topk_weights, float* logits, int32_t* scatter_index, int32_t* row_token,
-                                 int32_t* expert_offsets, int32_t* status_words, void* x_scattered, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  const char* fn = "moe_route_and_scatter";
-  StageRange stage_range(stage_of(fn));
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_route_and_scatter and its no-allocation variant
+// (everything but the workspace).
+moe_status check_route_and_scatter(const char* fn, moe_dtype dt, const void* x, const void* w_router, int32_t T,
+                                   int32_t H, int32_t E, int32_t top_k, const int32_t* topk_ids,
+                                   const float* topk_weights, const float* logits, const int32_t* scatter_index,
+                                   const int32_t* row_token, const int32_t* expert_offsets,
+                                   const int32_t* status_words) {
   MOE_CHECK(need_dtype(dt, fn));
   MOE_CHECK(need_ptr(x, fn, "x"));
   MOE_CHECK(need_ptr(w_router, fn, "w_router"));
@@ -256,10 +260,16 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
   MOE_CHECK(need_mult8(H, fn, "H"));
   MOE_CHECK(need_rows((int64_t)T * top_k, fn, "T*top_k"));
   MOE_CHECK(need_rows((int64_t)T * E / 8, fn, "T*E/8"));
-  const size_t need = moe_route_and_scatter_workspace_bytes(dt, T, H, E, top_k);
-  if (!workspace || workspace_bytes < need)
-    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, workspace_bytes,
-                workspace ? "" : ", NULL pointer");
+  return MOE_OK;
+}
+
+// The kernels of moe_route_and_scatter on a validated call, with `workspace`
+// holding at least moe_route_and_scatter_workspace_bytes bytes.
+moe_status run_route_and_scatter(const char* fn, moe_dtype dt, const void* x, const void* w_router,
+                                 const float* logit_bias, int32_t T, int32_t H, int32_t E, int32_t top_k,
+                                 int32_t* topk_ids, float* topk_weights, float* logits, int32_t* scatter_index,
+                                 int32_t* row_token, int32_t* expert_offsets, int32_t* status_words,
+                                 void* x_scattered, void* workspace, void* stream) {
   const hipStream_t s = (hipStream_t)stream;
   if (moe_launch::router_small((int)dt, T, E) && moe_launch::route_scatter_fusable(T, top_k, E)) {
     int nsplit = 0;
@@ -276,6 +286,28 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
     err = moe_launch::build_scatter((int)dt, x, topk_ids, T, H, E, top_k, scatter_index, row_token, expert_offsets,
                                     status_words, x_scattered, workspace, s);
   return hip_result(err, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                                 int32_t T, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids,
+                                 float* topk_weights, float* logits, int32_t* scatter_index, int32_t* row_token,
+                                 int32_t* expert_offsets, int32_t* status_words, void* x_scattered, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_route_and_scatter";
+  StageRange stage_range(stage_of(fn));
+  MOE_CHECK(check_route_and_scatter(fn, dt, x, w_router, T, H, E, top_k, topk_ids, topk_weights, logits,
+                                    scatter_index, row_token, expert_offsets, status_words));
+  const size_t need = moe_route_and_scatter_workspace_bytes(dt, T, H, E, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu%s)", fn, need, workspace_bytes,
+                workspace ? "" : ", NULL pointer");
+  return run_route_and_scatter(fn, dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
+                               scatter_index, row_token, expert_offsets, status_words, x_scattered, workspace,
+                               stream);
 }
 
 size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
@@ -574,6 +606,14 @@ moe_status moe_grouped_fc2_and_shared_mx8(const void* act, const int32_t* expert
   return hip_result(moe_launch::fused_fc2_mx8(act, expert_offsets, E, R, w2q, w2s, I, H, y_rows, act_shared, T, ws2q,
                                               ws2s, I_s, gate, accumulate, y, cu_count(), s),
                     fn);
+}
+
+int32_t moe_grouped_gemm_tile(moe_dtype dt, int32_t call, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T,
+                              int32_t I_s) {
+  if ((dt != MOE_F32 && dt != MOE_BF16) || (call != 0 && call != 1) || R < 1 || H < 1 || E < 1 || I < 1 ||
+      E > moe::kMaxExperts || I_s < 0 || (I_s > 0 && T < 1))
+    return -1;
+  return moe_launch::tile_config((int)dt, call, R, H, E, I, T, I_s, cu_count());
 }
 
 int32_t moe_and_shared_launches(moe_dtype dt, int32_t R, int32_t H, int32_t E, int32_t I, int32_t T, int32_t I_s) {

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "libmoe.h"
+
 namespace moe {
 
 // Raw 16-bit storage of a bfloat16 value.
@@ -144,6 +146,8 @@ hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, 
 // multiples of 64, and a shared expert that is light next to the routed
 // weights; fused_supported() decides from the shapes).
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T);
+// moe_tile_config of the routed experts' launch of fc1 (call 0) or fc2 (call 1); I_s > 0: the *_and_shared call.
+int tile_config(int dt, int call, int R, int H, int E, int I, int T, int I_s, int cu_count);
 hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,
                      void* act, const void* x, int T, const void* ws1, int I_s, void* act_s, int cu_count,
                      hipStream_t s, const int32_t* a_rows = nullptr);

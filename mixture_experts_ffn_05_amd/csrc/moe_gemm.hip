@@ -60,36 +60,6 @@
 
 #include <type_traits>
 
-// Build-time switches used when tuning (the defaults are the shipped
-// configuration; MOE_TUNING makes every numbered configuration reachable).
-#ifndef MOE_FRAG_PREFETCH
-#define MOE_FRAG_PREFETCH 1
-#endif
-#ifndef MOE_PIPE_VARIANT
-#define MOE_PIPE_VARIANT 0
-#endif
-#ifndef MOE_DECODE_FC1
-#define MOE_DECODE_FC1 13
-#endif
-#ifndef MOE_MID_FC1
-#define MOE_MID_FC1 23
-#endif
-#ifndef MOE_MID_FC2
-#define MOE_MID_FC2 23
-#endif
-#ifndef MOE_FUSE_POLICY
-#define MOE_FUSE_POLICY 0  // tuning: 0 by shape, 1 always, 2 never
-#endif
-#ifndef MOE_DENSE
-#define MOE_DENSE 8       // groups averaging >= 512 rows
-#endif
-#ifndef MOE_DECODE_FC2
-#define MOE_DECODE_FC2 13
-#endif
-#ifndef MOE_MID_DGRAD
-#define MOE_MID_DGRAD 1   // input-gradient GEMMs of the backward, mid-sized groups
-#endif
-
 namespace moe {
 namespace {
 
@@ -931,17 +901,13 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
 }
 
-#ifndef MOE_PIPE_LOOP
-#define MOE_PIPE_LOOP 1
-#endif
-
 // The loop with two fragment sets holds about 24-48 more VGPRs per lane; it is
 // used where each SIMD runs at most two waves of the kernel (256 VGPRs each).
 // With four waves per SIMD the extra registers would cost a workgroup per CU
 // (128x256x32 with 8 waves: 117 -> 140 VGPRs, 12-24% slower measured).
 template <class C>
 constexpr bool pipe_loop_v1() {
-  return MOE_PIPE_LOOP == 1 && C::kKSW % 2 == 0 && C::kWgsPerCu * C::kWaves <= 8;
+  return C::kKSW % 2 == 0 && C::kWgsPerCu * C::kWaves <= 8;
 }
 
 template <int EPI, class C, bool BT>
@@ -1054,22 +1020,12 @@ struct MxCfg {
   static_assert(BK == 128, "the scale tiles below assume 128-deep slices");
 };
 
-// 32-row tiles, 128 staged columns, 128-deep slices, 4-stage ring, 4 waves
-// (2 column positions x 2 split-K waves): the decode tile of the bf16 path.
-typedef MxCfg<32, 128, 128, 4, 1, 2, 2> MxCfg1;
-typedef MxCfg<32, 128, 128, 2, 1, 2, 2> MxCfg2;   // two workgroups per CU
-typedef MxCfg<32, 64, 128, 4, 1, 1, 4> MxCfg3;    // 64 columns, 4 split-K waves, two workgroups per CU
-#ifndef MOE_MX_VARIANT
-#define MOE_MX_VARIANT 2
-#endif
-typedef MxCfg<128, 128, 128, 2, 2, 2, 1> MxCfgP1;   // prefill: 128-row tiles, 4 waves
-typedef MxCfg<128, 256, 128, 2, 2, 4, 1> MxCfgP2;   // prefill: 128 x 256, 8 waves
-#ifndef MOE_MX_PREFILL
-#define MOE_MX_PREFILL 2
-#endif
-typedef typename std::conditional<MOE_MX_PREFILL == 2, MxCfgP2, MxCfgP1>::type MxCfgPrefill;
-typedef typename std::conditional<MOE_MX_VARIANT == 2, MxCfg2,
-                                  typename std::conditional<MOE_MX_VARIANT == 3, MxCfg3, MxCfg1>::type>::type MxCfgUsed;
+// Decode shapes: 32-row tiles, 128 staged columns, 128-deep slices, 2-stage
+// ring, 4 waves (2 column positions x 2 split-K waves), two workgroups per CU
+// (the best of three decode configurations measured).  Prefill shapes: 128 x
+// 256 tiles with 8 waves, which convert each weight fragment once per 128 rows.
+typedef MxCfg<32, 128, 128, 2, 1, 2, 2> MxCfgDecode;
+typedef MxCfg<128, 256, 128, 2, 2, 4, 1> MxCfgPrefill;
 
 template <int ROWBYTES>
 __device__ __forceinline__ int row_swizzle(int row) {
@@ -1383,18 +1339,7 @@ struct WgCfg {
 // 128x256 / 256x128 / 64x256 tiles, 8-byte stores of a swapped product,
 // non-temporal stores and an M-fastest tile order: all within a few percent or
 // slower.
-typedef WgCfg<128, 128, 32, 2, 2, 2> WgCfg1;
-typedef WgCfg<128, 128, 64, 2, 2, 2> WgCfg2;
-typedef WgCfg<128, 256, 64, 2, 2, 4> WgCfg3;   // 8 waves
-#ifndef MOE_WGRAD_VARIANT
-#define MOE_WGRAD_VARIANT 1
-#endif
-#ifndef MOE_WG_LDS_EPI
-#define MOE_WG_LDS_EPI 1   // output tiles through LDS (1) or straight from the accumulators (0)
-#endif
-typedef typename std::conditional<
-    MOE_WGRAD_VARIANT == 2, WgCfg2,
-    typename std::conditional<MOE_WGRAD_VARIANT == 3, WgCfg3, WgCfg1>::type>::type WgCfgUsed;
+typedef WgCfg<128, 128, 32, 2, 2, 2> WgCfgUsed;
 
 struct WgParams {
   const bf16_t* p;          // [rows, M]
@@ -1442,25 +1387,18 @@ __device__ __forceinline__ void wg_compute(const unsigned char* __restrict__ st,
 #pragma unroll
   for (int ks = 0; ks < C::kKS; ++ks) {
     if (ks + 1 < C::kKS) read(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-    // With the staged epilogue the product is taken swapped (the Q fragment as
-    // the MFMA's A operand), so that a lane holds four consecutive output
-    // columns of one output row.
+    // The product is taken swapped (the Q fragment as the MFMA's A operand),
+    // so that a lane holds four consecutive output columns of one output row
+    // for the LDS-staged epilogue.
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < C::kNB; ++nb)
-        acc[mb][nb] = MOE_WG_LDS_EPI ? mfma32(bf[ks & 1][nb], af[ks & 1][mb], acc[mb][nb])
-                                     : mfma32(af[ks & 1][mb], bf[ks & 1][nb], acc[mb][nb]);
+        acc[mb][nb] = mfma32(bf[ks & 1][nb], af[ks & 1][mb], acc[mb][nb]);
   }
 }
 
-#ifndef MOE_WG_BAND_M
-#define MOE_WG_BAND_M 8
-#endif
-#ifndef MOE_WG_BAND_N
-#define MOE_WG_BAND_N 16
-#endif
-constexpr int kBandM = MOE_WG_BAND_M, kBandN = MOE_WG_BAND_N;
+constexpr int kBandM = 8, kBandN = 16;   // tiles per group run in 8 x 16 blocks (L2 reuse)
 
 // Position of a workgroup in its stream of slices: tile id (>= total when the
 // stream is exhausted), the tile's group, row range and output corner, and the
@@ -1539,34 +1477,6 @@ __device__ __forceinline__ void wg_issue(unsigned char* __restrict__ st, const W
   }
 }
 
-template <class C>
-__device__ __forceinline__ void wg_store_tile(const WgParams& p, const WgCursor& c, f32x16 (&acc)[C::kMB][C::kNB],
-                                              int wm, int wn) {
-  // 32x32 accumulator layout: column = lane%32, row = 8*(i/4) + 4*(lane/32) + i%4.
-  const int lane = threadIdx.x & 63;
-  bf16_t* out = p.out + (int64_t)c.g * p.M * p.N;
-#pragma unroll
-  for (int mb = 0; mb < C::kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < C::kNB; ++nb) {
-      const int n = c.n0 + wn * (C::BN / C::WN) + 32 * nb + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = c.m0 + wm * (C::BM / C::WM) + 32 * mb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (m < p.M && n < p.N) out[(int64_t)m * p.N + n] = (bf16_t)f32_to_bf16_rne(acc[mb][nb][i]);
-        acc[mb][nb][i] = 0.f;
-      }
-    }
-}
-
-// Output tile through LDS (the ring stage just consumed, which every wave has
-// finished reading): each wave owns a 64x64 sub-tile and moves it in two
-// halves of 32 rows x 64 columns (4 KiB per wave).  The swapped product gives
-// a lane four consecutive columns of one row, written as 8 bytes; the 16-byte
-// chunks of a row are XOR-swizzled by (row / 2) % 8 so that both the writes and
-// the row reads are conflict-free; each lane then stores 16 bytes, 8 lanes per
-// 128-byte row.  Two-byte stores straight from the accumulators keep the
-// texture-address unit busy several times longer than the tile's loads do.
 template <class C>
 __device__ __forceinline__ void wg_store_tile_staged(const WgParams& p, const WgCursor& c,
                                                      f32x16 (&acc)[C::kMB][C::kNB], int wm, int wn,
@@ -1668,12 +1578,8 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_wgrad_bf16(WgPara
     wg_compute<C>(st, acc, wm, wn);
     --outstanding;
     if (++cc.kt == cc.nk) {
-      if (MOE_WG_LDS_EPI) {
-        lds_barrier();  // every wave is done reading `st`; the next iteration's barrier frees it again
-        wg_store_tile_staged<C>(p, cc, acc, wm, wn, st);
-      } else {
-        wg_store_tile<C>(p, cc, acc, wm, wn);
-      }
+      lds_barrier();  // every wave is done reading `st`; the next iteration's barrier frees it again
+      wg_store_tile_staged<C>(p, cc, acc, wm, wn, st);
       cc.id += gridDim.x;
       wg_seek<C, false>(p, per_group, total, cc);
     }
@@ -1794,8 +1700,8 @@ inline bool mx_decode_shape(const GemmParams<bf16_t>& p) {
 
 template <int EPI, int SAX, int ROLE>
 hipError_t launch_mx8(GemmParams<bf16_t> p, int cu_count, hipStream_t s) {
-  if (MOE_MX_PREFILL != 0 && !mx_decode_shape(p)) return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgPrefill>(p, cu_count, s);
-  return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgUsed>(p, cu_count, s);
+  if (!mx_decode_shape(p)) return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgPrefill>(p, cu_count, s);
+  return launch_mx8_cfg<EPI, SAX, ROLE, MxCfgDecode>(p, cu_count, s);
 }
 
 template <int EPI_R, int EPI_S, int SAX, class C>
@@ -1817,70 +1723,27 @@ hipError_t launch_mx8_fused_cfg(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, in
 
 template <int EPI_R, int EPI_S, int SAX>
 hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
-  if (MOE_MX_PREFILL != 0 && !(mx_decode_shape(pr) && ps.rows <= 64))
+  if (!(mx_decode_shape(pr) && ps.rows <= 64))
     return launch_mx8_fused_cfg<EPI_R, EPI_S, SAX, MxCfgPrefill>(pr, ps, cu_count, s);
-  return launch_mx8_fused_cfg<EPI_R, EPI_S, SAX, MxCfgUsed>(pr, ps, cu_count, s);
+  return launch_mx8_fused_cfg<EPI_R, EPI_S, SAX, MxCfgDecode>(pr, ps, cu_count, s);
 }
 
-// Pipelined configurations (BM, BN, BK, STAGES, WM, WN, KW), numbered for
-// tuning builds.
-typedef PipeCfg<128, 128, 64, 2> Cfg1;
-typedef PipeCfg<128, 128, 32, 4> Cfg2;
-typedef PipeCfg<256, 256, 32, 4> Cfg3;
-typedef PipeCfg<256, 256, 64, 2> Cfg4;
-typedef PipeCfg<128, 256, 64, 3> Cfg5;
-typedef PipeCfg<256, 128, 32, 4> Cfg6;
-typedef PipeCfg<256, 256, 32, 4, 4, 2> Cfg7;   // 8 waves
-typedef PipeCfg<256, 256, 64, 2, 4, 2> Cfg8;   // 8 waves
-typedef PipeCfg<256, 128, 64, 2, 4, 2> Cfg9;   // 8 waves
-typedef PipeCfg<128, 256, 64, 2, 2, 4> Cfg10;  // 8 waves
-// Few rows per group (decode): 32-row tiles, narrow columns, split-K waves.
-typedef PipeCfg<32, 64, 64, 5, 1, 1, 4> Cfg11;
-typedef PipeCfg<32, 64, 64, 8, 1, 1, 4> Cfg12;
-typedef PipeCfg<32, 128, 64, 4, 1, 2, 2> Cfg13;
-typedef PipeCfg<32, 64, 64, 3, 1, 1, 4> Cfg14;
-typedef PipeCfg<32, 64, 128, 4, 1, 1, 4> Cfg15;
-typedef PipeCfg<32, 128, 64, 6, 1, 2, 2> Cfg16;
-typedef PipeCfg<32, 128, 128, 3, 1, 2, 4> Cfg17;  // 8 waves
-typedef PipeCfg<32, 128, 64, 3, 1, 2, 2> Cfg18;
-typedef PipeCfg<128, 256, 32, 4, 2, 2> Cfg19;
-typedef PipeCfg<256, 128, 64, 3, 4, 2> Cfg20;  // 8 waves
-typedef PipeCfg<128, 128, 64, 3> Cfg21;
-typedef PipeCfg<128, 256, 64, 2, 2, 2> Cfg22;
-typedef PipeCfg<128, 256, 32, 2, 2, 4> Cfg23;  // 8 waves, 48 KiB ring: two workgroups per CU
-typedef PipeCfg<128, 256, 32, 2, 2, 2> Cfg24;  // 4 waves of 64x128, 48 KiB ring: two workgroups per CU
-typedef PipeCfg<128, 256, 32, 2, 1, 2> Cfg25;  // 2 waves of 128x128, 48 KiB ring: two workgroups per CU
+// The pipelined configurations (BM, BN, BK, STAGES, WM, WN, KW) the selection
+// below can return.
+typedef PipeCfg<128, 128, 64, 2> CfgSmall;          // 4 waves; narrow dense outputs, backward dgrad
+typedef PipeCfg<256, 256, 64, 2, 4, 2> CfgDense;    // 8 waves, one workgroup per CU
+typedef PipeCfg<128, 256, 32, 2, 2, 4> CfgMid;      // 8 waves, 48 KiB ring: two workgroups per CU
+typedef PipeCfg<32, 128, 64, 4, 1, 2, 2> CfgDecode; // 4 waves (2 column positions x 2 split-K waves)
 
-template <int V> struct CfgOf { typedef Cfg1 type; };
-#define MOE_CFG(V) template <> struct CfgOf<V> { typedef Cfg##V type; };
-MOE_CFG(2) MOE_CFG(3) MOE_CFG(4) MOE_CFG(5) MOE_CFG(6) MOE_CFG(7) MOE_CFG(8) MOE_CFG(9) MOE_CFG(10)
-MOE_CFG(11) MOE_CFG(12) MOE_CFG(13) MOE_CFG(14) MOE_CFG(15) MOE_CFG(16) MOE_CFG(17) MOE_CFG(18)
-MOE_CFG(19) MOE_CFG(20) MOE_CFG(21) MOE_CFG(22) MOE_CFG(23) MOE_CFG(24) MOE_CFG(25)
-#undef MOE_CFG
-
-// Calls f(Cfg{}) for configuration number v.  The shipped build instantiates
-// only the configurations that the selection below can return; a build with
-// MOE_TUNING instantiates all of them for sweeps.
+// Calls f(Cfg{}) for a pipelined configuration.
 template <class F>
 hipError_t with_cfg(int v, F&& f) {
-#ifdef MOE_TUNING
   switch (v) {
-#define MOE_CASE(V) case V: return f(typename CfgOf<V>::type{});
-    MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7) MOE_CASE(8) MOE_CASE(9)
-    MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13) MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
-    MOE_CASE(17) MOE_CASE(18) MOE_CASE(19) MOE_CASE(20) MOE_CASE(21) MOE_CASE(22) MOE_CASE(23)
-    MOE_CASE(24) MOE_CASE(25)
-#undef MOE_CASE
-    default: return f(Cfg1{});
+    case MOE_TILE_256x256: return f(CfgDense{});
+    case MOE_TILE_128x256: return f(CfgMid{});
+    case MOE_TILE_32x128: return f(CfgDecode{});
+    default: return f(CfgSmall{});
   }
-#else
-  if (v == MOE_DENSE) return f(typename CfgOf<MOE_DENSE>::type{});
-  if (v == MOE_MID_FC1) return f(typename CfgOf<MOE_MID_FC1>::type{});
-  if (v == MOE_MID_FC2) return f(typename CfgOf<MOE_MID_FC2>::type{});
-  if (v == MOE_DECODE_FC1) return f(typename CfgOf<MOE_DECODE_FC1>::type{});
-  if (v == MOE_DECODE_FC2) return f(typename CfgOf<MOE_DECODE_FC2>::type{});
-  return f(Cfg1{});
-#endif
 }
 
 // Configuration for a problem, from the host-known sizes only (measured on
@@ -1925,25 +1788,20 @@ double slot_fill(const GemmParams<bf16_t>& p, int cu_count) {
 
 constexpr int64_t kDecodeRows = 32;
 
-template <int EPI>
-constexpr int decode_variant() { return paired(EPI) ? MOE_DECODE_FC1 : MOE_DECODE_FC2; }
-
 template <int EPI, int ROLE>
 int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
-  if (MOE_PIPE_VARIANT != 0) return MOE_PIPE_VARIANT;
-  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return decode_variant<EPI>();
+  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return MOE_TILE_32x128;
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   if (rows_per_group >= 512)
-    return slot_fill<EPI, typename CfgOf<MOE_DENSE>::type>(p, cu_count) + 0.25 < slot_fill<EPI, Cfg1>(p, cu_count)
-               ? 1
-               : MOE_DENSE;
-  if (ROLE == 2) return MOE_MID_DGRAD;
-  return paired(EPI) ? MOE_MID_FC1 : MOE_MID_FC2;
+    return slot_fill<EPI, CfgDense>(p, cu_count) + 0.25 < slot_fill<EPI, CfgSmall>(p, cu_count) ? MOE_TILE_128x128
+                                                                                               : MOE_TILE_256x256;
+  if (ROLE == 2) return MOE_TILE_128x128;
+  return MOE_TILE_128x256;
 }
 
 template <int EPI_R, int EPI_S, class C, bool BT>
 hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
-  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, Cfg1, BT>(pr, ps, cu_count, s);
+  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, CfgSmall, BT>(pr, ps, cu_count, s);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -1963,20 +1821,18 @@ hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_cou
 // when the routed groups and the shared expert both average >= 512 rows, the
 // decode tile when the routed groups are small and the shared expert has at
 // most 64 rows.
+int pick_fused_variant(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps) {
+  const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
+  if (per_group >= 512 && ps.rows >= 512) return MOE_TILE_256x256;
+  if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 && ps.K % 128 == 0)
+    return MOE_TILE_32x128;
+  return MOE_TILE_128x256;
+}
+
 template <int EPI_R, int EPI_S>
 hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, int cu_count,
                              hipStream_t s) {
-  const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
-  int v = 1;
-  if (MOE_PIPE_VARIANT != 0)
-    v = MOE_PIPE_VARIANT;
-  else if (per_group >= 512 && ps.rows >= 512)
-    v = MOE_DENSE;
-  else if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 &&
-           ps.K % 128 == 0)
-    v = decode_variant<EPI_R>();
-  else
-    v = paired(EPI_R) ? MOE_MID_FC1 : MOE_MID_FC2;
+  const int v = pick_fused_variant(pr, ps);
   if (pr.bt)
     return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), true>(pr, ps, cu_count, s); });
   return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), false>(pr, ps, cu_count, s); });
@@ -2057,11 +1913,29 @@ hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, 
 // and ~16 (DeepSeek-V3-shaped prefill) and loses from ~128 (Scout-shaped).
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T) {
   if (!(dt == 1 && H % 64 == 0 && I % 64 == 0 && I_s % 64 == 0)) return false;
-  if (MOE_FUSE_POLICY == 1) return true;
-  if (MOE_FUSE_POLICY == 2) return false;
   const double routed_bytes = (double)(E < R ? E : R) * 3.0 * H * I * 2.0;
   const double shared_flops = 6.0 * T * H * I_s;
   return shared_flops < 50.0 * routed_bytes;
+}
+
+int tile_config(int dt, int call, int R, int H, int E, int I, int T, int I_s, int cu_count) {
+  using namespace moe;
+  if (dt != 1) return MOE_TILE_F32;
+  GemmParams<bf16_t> p{};
+  p.rows = R;
+  p.groups = E;
+  p.K = call == 0 ? H : I;
+  p.N = call == 0 ? I : H;
+  if (I_s > 0 && fused_supported(dt, H, I, I_s, E, R, T)) {
+    GemmParams<bf16_t> ps{};
+    ps.rows = T;
+    ps.groups = 1;
+    ps.K = call == 0 ? H : I_s;
+    ps.N = call == 0 ? I_s : H;
+    return pick_fused_variant(p, ps);
+  }
+  if (p.K % 64 != 0) return MOE_TILE_GENERIC;
+  return call == 0 ? pick_pipe_variant<kSwiGLU, 0>(p, cu_count) : pick_pipe_variant<kStoreF32, 0>(p, cu_count);
 }
 
 hipError_t fused_fc1(int bt, const void* xs, const int32_t* offsets, int E, int R, const void* w1, int H, int I,

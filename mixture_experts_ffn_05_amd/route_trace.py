@@ -266,6 +266,21 @@ def summarize(stage_ns: dict) -> dict:
     return {"total_profiled_ns": round(total), "stages": stages, "shared_vs_routed": split}
 
 
+def replay_gates(labels, per_rep, ys, status, rows, pairs) -> dict:
+    """The checks a replay must pass before its times are used: every stage label
+    in the pages' vocabulary, no negative interval, a finite output identical
+    over the repeats, and a scatter that placed every (token, slot) pair
+    (status = [largest group, out-of-range ids], rows = the last expert offset)."""
+    parts = {p for lab in labels for p in lab.split("+")}
+    return {
+        "stages_in_vocabulary": parts <= set(MOE_STAGES),
+        "times_non_negative": all(v >= 0 for r in per_rep for v in r),
+        "output_finite": bool(len(ys) > 0 and np.isfinite(ys[-1]).all()),
+        "output_identical_across_repeats": all(np.array_equal(ys[0], y) for y in ys[1:]),
+        "no_out_of_range_ids": status[1] == 0 and rows == pairs,
+    }
+
+
 def _layer_config(doc: dict, seed: int):
     from . import workloads as wl
     m = doc["model"]
@@ -355,14 +370,7 @@ def replay(doc: dict, repeats: int = 10, warmup: int = 3, include_router: bool =
     for i, lab in enumerate(labels):   # mean over repeats, summed per stage label
         stage_ns[lab] = stage_ns.get(lab, 0.0) + math.fsum(r[i] for r in per_rep) / repeats
     summary = summarize(stage_ns)
-    parts = {p for lab in labels for p in lab.split("+")}
-    gates = {
-        "stages_in_vocabulary": parts <= set(MOE_STAGES),
-        "times_non_negative": all(v >= 0 for r in per_rep for v in r),
-        "output_finite": bool(np.isfinite(ys[-1]).all()),
-        "output_identical_across_repeats": all(np.array_equal(ys[0], y) for y in ys[1:]),
-        "no_out_of_range_ids": status[1] == 0 and rows == T * k,
-    }
+    gates = replay_gates(labels, per_rep, ys, status, rows, T * k)
     m = doc["model"]
     result = {
         "trace": {"schema_version": doc["schema_version"], "model": m, "dtype": doc["dtype"], "tokens": T,

@@ -248,3 +248,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode == 2
     assert "one GPU only" in res.stderr
     assert res.stdout == ""
+
+
+def test_tile_configuration_choices():
+    """The host's choice of grouped-GEMM tile configuration (a host-only query): every
+    GPU parity case on the configuration its comment names, and the benchmark
+    workloads on theirs."""
+    from mixture_experts_ffn_05_amd import workloads as wl
+    from tests.test_gpu_parity import CASES, EXPECTED_TILES, tiles_of
+
+    for cfg in CASES:
+        assert tiles_of(cfg) == EXPECTED_TILES[cfg.name], cfg.name
+    D, M, DEC = B.MOE_TILE_256x256, B.MOE_TILE_128x256, B.MOE_TILE_32x128
+    bench = {"scout": (M, M, M, M), "qwen2": (M, M, M, M), "v2l": (D, D, D, D), "v3": (M, M, M, M),
+             "v2l_decode1": (DEC,) * 4, "v2l_decode16": (DEC,) * 4, "v2l_decode64": (DEC,) * 4,
+             "v3_decode64": (DEC,) * 4}
+    for name, want in bench.items():
+        assert tiles_of(wl.WORKLOADS[name]) == want, name
+    assert B.load().moe_grouped_gemm_tile(1, 2, 8, 64, 4, 64, 0, 0) == -1       # call must be 0 or 1
+    assert B.load().moe_grouped_gemm_tile(1, 0, 8, 64, 4, 64, 0, 64) == -1      # I_s needs T

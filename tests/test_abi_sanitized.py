@@ -1,0 +1,30 @@
+"""The C-ABI layer (argument validation, error strings, scratch bookkeeping)
+built with host-side AddressSanitizer and UndefinedBehaviorSanitizer: the ABI
+tests run against that build in a child process that preloads clang's
+sanitizer runtime, and any sanitizer report fails the run.  CPU only; the GPU
+code in that build is the library's own."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_abi_tests_pass_under_host_sanitizers():
+    from mixture_experts_ffn_05_amd import build
+
+    lib = build.build_sanitized()
+    preload = build.asan_runtime()
+    if os.environ.get("LD_PRELOAD"):
+        preload += ":" + os.environ["LD_PRELOAD"]
+    env = {**os.environ, "LIBMOE_LIBRARY": lib, "LD_PRELOAD": preload,
+           "ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1",
+           "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
+    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join("tests", "test_abi.py"), "-q", "-s",
+                          "-p", "no:cacheprovider", "-k", "not bench"],
+                         env=env, cwd=ROOT, capture_output=True, text=True, timeout=1200)
+    out = res.stdout + res.stderr
+    assert res.returncode == 0, out[-4000:]
+    assert "Sanitizer" not in out, out[-4000:]
+    assert " passed" in res.stdout

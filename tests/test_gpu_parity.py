@@ -33,6 +33,35 @@ CASES = [
 ]
 
 
+# The tile configuration (moe_tile_config) each case's routed launches take, as
+# the host chooses it from the sizes: fc1 / fc2 of the plain calls, and of the
+# *_and_shared calls where the case has a shared expert.  Asserted below, so a
+# change of the selection cannot silently move a case off the configuration it
+# exists to cover.
+_G, _S, _D, _M, _DEC, _F = (B.MOE_TILE_GENERIC, B.MOE_TILE_128x128, B.MOE_TILE_256x256, B.MOE_TILE_128x256,
+                            B.MOE_TILE_32x128, B.MOE_TILE_F32)
+EXPECTED_TILES = {
+    "tiny": (_F, _F, None, None),
+    "ragged_bf16": (_G, _G, None, None),
+    "gated_bf16": (_M, _G, _M, _G),
+    "decode1_bf16": (_DEC, _DEC, _DEC, _DEC),
+    "wide_bf16": (_DEC, _M, _M, _M),
+    "ragged_f32": (_F, _F, _F, _F),
+    "big_groups_bf16": (_D, _D, _D, _D),
+    "fused_big_bf16": (_D, _D, _D, _D),
+    "big_groups_short_k_bf16": (_D, _D, _D, _D),
+}
+
+
+def tiles_of(cfg):
+    """(fc1, fc2, fc1 with shared, fc2 with shared) tile configurations the host picks for cfg."""
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    plain = [B.moe_grouped_gemm_tile(dt, c, cfg.R, cfg.H, cfg.E, cfg.I) for c in (0, 1)]
+    shared = ([B.moe_grouped_gemm_tile(dt, c, cfg.R, cfg.H, cfg.E, cfg.I, cfg.T, cfg.I_s) for c in (0, 1)]
+              if cfg.I_s else [None, None])
+    return tuple(plain + shared)
+
+
 def _ids(c):
     return c.name
 
@@ -257,6 +286,7 @@ def test_route_and_scatter_matches_the_two_calls(T, H, E, k, with_bias):
 def test_grouped_gemms_per_call(cfg, layout):
     """fc1 on the oracle's scattered rows, then fc2 on the GPU's own activation,
     with the weights stored [K, N] or [N, K]."""
+    assert tiles_of(cfg) == EXPECTED_TILES[cfg.name]
     layer = _layer(cfg)
     W1d, W2d, _ = _device_weights(layer, layout)
     x = layer["x"]
@@ -301,6 +331,7 @@ def test_layer_end_to_end(cfg, mode, layout):
     the oracle fed the
     GPU's routes (which were themselves checked against the oracle's top-k of
     the GPU logits)."""
+    assert tiles_of(cfg) == EXPECTED_TILES[cfg.name]
     layer = _layer(cfg)
     x, wr = layer["x"], layer["w_router"]
     bias_t = torch.from_numpy(layer["bias"]).to(DEV) if layer["bias"] is not None else None

@@ -138,3 +138,24 @@ def test_golden_traces_validate():
     for name in ("route_trace_tiny_v1.json", "route_trace_small_v2_gated.json"):
         with open(os.path.join(GOLDEN, name)) as f:
             RT.validate_trace(json.load(f))
+
+
+def test_replay_gates_turn_false_on_bad_replays():
+    """Each replay gate passes on a good replay record and fails on the defect it guards."""
+    good = dict(labels=["router_topk+gather", "expert_projection", "scatter_combine"],
+                per_rep=[[1.0, 2.0, 3.0], [1.1, 2.1, 3.1]], ys=[np.ones((2, 4)), np.ones((2, 4))],
+                status=[3, 0], rows=8, pairs=8)
+    assert all(RT.replay_gates(**good).values())
+
+    def gates(**kw):
+        return RT.replay_gates(**{**good, **kw})
+
+    assert not gates(labels=["router_topk", "made_up_stage"])["stages_in_vocabulary"]
+    assert not gates(per_rep=[[1.0, -0.5, 3.0]])["times_non_negative"]
+    assert not gates(ys=[np.ones((2, 4)), np.array([[1.0, np.nan, 1, 1], [1, 1, 1, 1]])])["output_finite"]
+    assert not gates(ys=[])["output_finite"]
+    assert not gates(ys=[np.ones((2, 4)), np.ones((2, 4)) * 1.0000001])["output_identical_across_repeats"]
+    assert not gates(status=[3, 2])["no_out_of_range_ids"]
+    assert not gates(rows=7)["no_out_of_range_ids"]
+    for name, ok in gates(per_rep=[[1.0, -0.5, 3.0]]).items():
+        assert ok == (name != "times_non_negative")
