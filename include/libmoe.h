@@ -217,6 +217,32 @@ int32_t moe_grouped_gemm_tile(moe_dtype dt, int32_t call, int32_t R, int32_t H, 
 /* Workspace bytes moe_route_and_scatter needs for (dt, T, H, E, top_k); 0 for invalid sizes. */
 size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H, int32_t E, int32_t top_k);
 
+/*
+ * moe_route_and_scatter_noalloc -- moe_route_and_scatter without a workspace
+ * argument and without any allocation, for callers that cannot allocate device
+ * memory during the call: code being captured into a HIP graph, tight decode
+ * or serving loops, and harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus workspace), outputs (same bits), layouts, ownership and
+ * errors as moe_route_and_scatter.  The scratch the kernels need lives in a
+ * device array of the library, moe_route_and_scatter_noalloc_max_bytes() bytes
+ * (16 MiB) on every GPU the library runs on, allocated when the library's code
+ * loads on that GPU and held until the process ends; the call itself allocates
+ * nothing.  Sizes whose moe_route_and_scatter_workspace_bytes exceeds that
+ * return MOE_ERR_UNSUPPORTED before anything is launched.  Nothing in the
+ * scratch needs to start at zero.  Every call on one GPU shares that GPU's
+ * array: two calls that may run at the same time on one GPU (on different
+ * streams, or from different threads without ordering) race and must not be
+ * issued.
+ */
+moe_status moe_route_and_scatter_noalloc(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                                         int32_t T, int32_t H, int32_t E, int32_t top_k,
+                                         int32_t* topk_ids, float* topk_weights, float* logits,
+                                         int32_t* scatter_index, int32_t* row_token, int32_t* expert_offsets,
+                                         int32_t* status_words, void* x_scattered, void* stream);
+
+/* Bytes of device scratch moe_route_and_scatter_noalloc holds per GPU (its size limit). */
+size_t moe_route_and_scatter_noalloc_max_bytes(void);
 
 /*
  * moe_grouped_swiglu_fc1 -- per-expert gate/up projection and SwiGLU.

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "moe_route_and_scatter": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _c_size, _vp]),
     "moe_route_and_scatter_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "moe_route_and_scatter_noalloc": (_c_int, [_c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                               _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_and_scatter_noalloc_max_bytes": (_c_size, []),
     "moe_build_scatter": (_c_int, [_c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _c_size, _vp]),
     "moe_grouped_swiglu_fc1": (_c_int, [_c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
@@ -220,6 +223,30 @@ def moe_route_and_scatter(x, w_router, logit_bias, top_k, topk_ids, topk_weights
             _ptr(x_scattered, "x_scattered", x.dtype, (T * k, H), dev),
             _ptr(workspace, "workspace", torch.uint8, None, dev), workspace.numel(), _stream(stream, dev))
     _check(lib.moe_route_and_scatter(*args))
+
+
+def moe_route_and_scatter_noalloc_max_bytes() -> int:
+    return int(load().moe_route_and_scatter_noalloc_max_bytes())
+
+
+def moe_route_and_scatter_noalloc(x, w_router, logit_bias, top_k, topk_ids, topk_weights, logits, scatter_index,
+                                  row_token, expert_offsets, status_words, x_scattered, stream=None):
+    lib = load()
+    T, H = x.shape
+    E = w_router.shape[1]
+    k = int(top_k)
+    dev = x.device
+    args = (_dt(x), _ptr(x, "x"), _ptr(w_router, "w_router", x.dtype, (H, E), dev),
+            _ptr(logit_bias, "logit_bias", torch.float32, (E,), dev), T, H, E, k,
+            _ptr(topk_ids, "topk_ids", torch.int32, (T, k), dev),
+            _ptr(topk_weights, "topk_weights", torch.float32, (T, k), dev),
+            _ptr(logits, "logits", torch.float32, (T, E), dev),
+            _ptr(scatter_index, "scatter_index", torch.int32, (T, k), dev),
+            _ptr(row_token, "row_token", torch.int32, (T * k,), dev),
+            _ptr(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev),
+            _ptr(status_words, "status_words", torch.int32, (2,), dev),
+            _ptr(x_scattered, "x_scattered", x.dtype, (T * k, H), dev), _stream(stream, dev))
+    _check(lib.moe_route_and_scatter_noalloc(*args))
 
 
 def _fc1_sizes(w1, layout):

@@ -122,6 +122,7 @@ struct CallStage {
 constexpr CallStage kCallStages[] = {
     {"moe_route", "router_topk"},
     {"moe_route_and_scatter", "router_topk+gather"},
+    {"moe_route_and_scatter_noalloc", "router_topk+gather"},
     {"moe_build_scatter", "gather"},
     {"moe_grouped_swiglu_fc1", "expert_projection"},
     {"moe_grouped_fc2", "expert_projection"},
@@ -288,6 +289,40 @@ moe_status run_route_and_scatter(const char* fn, moe_dtype dt, const void* x, co
   return hip_result(err, fn);
 }
 
+// Scratch of the no-allocation entry point: one array per GPU, allocated
+// when the code object loads and held until the process ends.  Host code
+// must not pass `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in scratch_addr.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64] = {};
+
+moe_status scratch_address(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_result(err, fn);
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "%s: device ordinal %d is beyond 63", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_result(err, fn);
+    if (!p) return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress returned no address for the scratch array", fn);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +343,27 @@ moe_status moe_route_and_scatter(moe_dtype dt, const void* x, const void* w_rout
   return run_route_and_scatter(fn, dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
                                scatter_index, row_token, expert_offsets, status_words, x_scattered, workspace,
                                stream);
+}
+
+size_t moe_route_and_scatter_noalloc_max_bytes(void) { return kScratchBytes; }
+
+moe_status moe_route_and_scatter_noalloc(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
+                                         int32_t T, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids,
+                                         float* topk_weights, float* logits, int32_t* scatter_index,
+                                         int32_t* row_token, int32_t* expert_offsets, int32_t* status_words,
+                                         void* x_scattered, void* stream) {
+  const char* fn = "moe_route_and_scatter_noalloc";
+  StageRange stage_range(stage_of(fn));
+  MOE_CHECK(check_route_and_scatter(fn, dt, x, w_router, T, H, E, top_k, topk_ids, topk_weights, logits,
+                                    scatter_index, row_token, expert_offsets, status_words));
+  const size_t need = moe_route_and_scatter_workspace_bytes(dt, T, H, E, top_k);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: these sizes need %zu bytes of scratch, more than the %zu bytes the "
+                "library holds per device (use moe_route_and_scatter with a workspace)", fn, need, kScratchBytes);
+  void* ws = nullptr;
+  MOE_CHECK(scratch_address(fn, &ws));
+  return run_route_and_scatter(fn, dt, x, w_router, logit_bias, T, H, E, top_k, topk_ids, topk_weights, logits,
+                               scatter_index, row_token, expert_offsets, status_words, x_scattered, ws, stream);
 }
 
 size_t moe_build_scatter_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
