@@ -70,8 +70,9 @@ typedef enum moe_tile_config {
   MOE_TILE_GENERIC = 1,   /* bf16 with a reduction size not a multiple of 64: register-staged 128 x 128 tiles */
   MOE_TILE_128x128 = 2,   /* pipelined: 128 rows x 128 staged weight columns x 64-deep slices, 4 waves */
   MOE_TILE_256x256 = 3,   /* pipelined: 256 x 256 x 64, 8 waves (groups of >= 512 rows on average) */
-  MOE_TILE_128x256 = 4,   /* pipelined: 128 x 256 x 32, 8 waves, two workgroups per CU (mid-sized groups) */
-  MOE_TILE_32x128 = 5     /* pipelined: 32 x 128 x 64 with split-K waves (groups of <= 32 rows on average) */
+  MOE_TILE_128x256 = 4,   /* pipelined: 128 x 256 x 32, 8 waves, two workgroups per CU (193..511 rows) */
+  MOE_TILE_32x128 = 5,    /* pipelined: 32 x 128 x 64 with split-K waves (groups of <= 32 rows on average) */
+  MOE_TILE_128x512 = 6    /* pipelined: 128 x 512 x 32, 3-stage ring, 8 waves (weight-streaming groups, <= 192 rows) */
 } moe_tile_config;
 
 /* Stage of a call, in the stage vocabulary of the PLENA pages (PLENA_Compiler

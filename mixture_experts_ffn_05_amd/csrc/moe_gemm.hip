@@ -391,6 +391,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MOE_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 #define MOE_GLOBAL(T, ptr) ((const __attribute__((address_space(1))) T*)(ptr))
 
+// Cache policy of the direct loads of expert weights: non-temporal (the nt bit
+// of the instruction's cache-policy field).  A weight byte is read once per
+// call, so keeping it out of the cache lines the activations and the other
+// in-flight slices live in pays: measured on MI355X with the DeepSeek-V3-shaped
+// layer, the routed fc1 went from 2.96 to 2.82-2.85 ms and fc2 from 1.80 to
+// 1.78 ms; the DeepSeek-V2-Lite-shaped decode (T = 64) fc1 from 0.184 to
+// 0.128 ms; the dense 256x256 tile gains 3-4%.  Activation loads keep the
+// default policy (non-temporal activations measured 13% slower: they are
+// re-read by every column tile).
+constexpr int kWeightLoadPolicy = 2;
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -485,7 +496,8 @@ __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const
 #pragma unroll
   for (int i = 0; i < C::kBLoads; ++i)
     __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                     MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, 0);
+                                     MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
+                                     kWeightLoadPolicy);
 }
 
 // One pipeline step: start the loads of a future slice into `wst`, then run
@@ -508,7 +520,7 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
     for (int i = 0; i < C::kBLoads; ++i)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
                                        MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
-                                       0);
+                                       kWeightLoadPolicy);
   }
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
@@ -1117,12 +1129,12 @@ __device__ __forceinline__ void mx_step(unsigned char* __restrict__ wst, const u
     for (int i = 0; i < C::kBLoads; ++i)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
                                        MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
-                                       0);
+                                       kWeightLoadPolicy);
 #pragma unroll
     for (int i = 0; i < C::kSLoads; ++i)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
                                        MOE_LDS(void, wst + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256),
-                                       4, 0, 0);
+                                       4, 0, kWeightLoadPolicy);
   }
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
@@ -1227,12 +1239,13 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
       for (int i = 0; i < C::kBLoads; ++i)
         __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
                                          MOE_LDS(void, st + C::kAStage + (wave_ * C::kBLoads + i) * 1024), 16, 0,
-                                         0);
+                                         kWeightLoadPolicy);
 #pragma unroll
       for (int i = 0; i < C::kSLoads; ++i)
         __builtin_amdgcn_global_load_lds(
             MOE_GLOBAL(void, s_k + s_off[i]),
-            MOE_LDS(void, st + C::kAStage + C::kBStage + (wave_ * C::kSLoads + i) * 256), 4, 0, 0);
+            MOE_LDS(void, st + C::kAStage + C::kBStage + (wave_ * C::kSLoads + i) * 256), 4, 0,
+            kWeightLoadPolicy);
     }
   }
 
@@ -1731,8 +1744,9 @@ hipError_t launch_mx8_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu
 // The pipelined configurations (BM, BN, BK, STAGES, WM, WN, KW) the selection
 // below can return.
 typedef PipeCfg<128, 128, 64, 2> CfgSmall;          // 4 waves; narrow dense outputs, backward dgrad
-typedef PipeCfg<256, 256, 64, 2, 4, 2> CfgDense;    // 8 waves, one workgroup per CU
+typedef PipeCfg<256, 256, 64, 2, 2, 4> CfgDense;    // 8 waves (2 x 4, 128 x 64 each), one workgroup per CU
 typedef PipeCfg<128, 256, 32, 2, 2, 4> CfgMid;      // 8 waves, 48 KiB ring: two workgroups per CU
+typedef PipeCfg<128, 512, 32, 3, 1, 8> CfgWide;     // 8 waves (1 x 8, 128 x 64 each), 120 KiB 3-stage ring
 typedef PipeCfg<32, 128, 64, 4, 1, 2, 2> CfgDecode; // 4 waves (2 column positions x 2 split-K waves)
 
 // Calls f(Cfg{}) for a pipelined configuration.
@@ -1741,6 +1755,7 @@ hipError_t with_cfg(int v, F&& f) {
   switch (v) {
     case MOE_TILE_256x256: return f(CfgDense{});
     case MOE_TILE_128x256: return f(CfgMid{});
+    case MOE_TILE_128x512: return f(CfgWide{});
     case MOE_TILE_32x128: return f(CfgDecode{});
     default: return f(CfgSmall{});
   }
@@ -1787,6 +1802,12 @@ double slot_fill(const GemmParams<bf16_t>& p, int cu_count) {
 }
 
 constexpr int64_t kDecodeRows = 32;
+// Groups of at most this many rows on average stream their weights (fewer rows
+// than the ~312 FLOP per weight byte at which 2.5 PFLOP/s meets 8 TB/s) and take
+// the wide tile: measured on MI355X it wins at 128 rows per group (the Scout-
+// and DeepSeek-V3-shaped layers: routed fc1 0.69 -> 0.59 ms and 3.37 -> 2.85 ms)
+// and loses to the mid-size tile at 273 (Qwen2-shaped: 0.29 vs 0.42 ms).
+constexpr int64_t kWideRows = 192;
 
 template <int EPI, int ROLE>
 int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
@@ -1796,7 +1817,7 @@ int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
     return slot_fill<EPI, CfgDense>(p, cu_count) + 0.25 < slot_fill<EPI, CfgSmall>(p, cu_count) ? MOE_TILE_128x128
                                                                                                : MOE_TILE_256x256;
   if (ROLE == 2) return MOE_TILE_128x128;
-  return MOE_TILE_128x256;
+  return rows_per_active_group(p) <= kWideRows ? MOE_TILE_128x512 : MOE_TILE_128x256;
 }
 
 template <int EPI_R, int EPI_S, class C, bool BT>
@@ -1826,7 +1847,7 @@ int pick_fused_variant(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& p
   if (per_group >= 512 && ps.rows >= 512) return MOE_TILE_256x256;
   if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 && ps.K % 128 == 0)
     return MOE_TILE_32x128;
-  return MOE_TILE_128x256;
+  return rows_per_active_group(pr) <= kWideRows ? MOE_TILE_128x512 : MOE_TILE_128x256;
 }
 
 template <int EPI_R, int EPI_S>

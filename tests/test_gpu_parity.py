@@ -30,6 +30,15 @@ CASES = [
     # the 256x256 tile with one 64-deep slice (fc1, shared fc2) and two (fc2): the main loop's
     # shortest reductions, with no slice boundary and with one boundary that refills nothing
     wl.LayerConfig("big_groups_short_k_bf16", "bf16", T=1030, H=64, E=2, top_k=1, I=128, I_s=64),
+    # the wide 128x512 tile (3-stage ring) for weight-streaming groups: fc1 with two 32-deep slices
+    # (fewer slices than ring stages), fc2 with six and a 64-column output tail; group sizes
+    # around the 128-row tile boundary
+    wl.LayerConfig("wide_short_k_bf16", "bf16", T=300, H=64, E=6, top_k=2, I=192),
+    # the wide tile with ten slices, output columns past a tile (320 of 512 staged, 320 of 512
+    # outputs), and a gated shared expert in the same launch
+    wl.LayerConfig("wide_fused_bf16", "bf16", T=700, H=320, E=8, top_k=2, I=320, I_s=64, gated=True),
+    # the mid-size 128x256 tile (two workgroups per CU) for groups of 193..511 rows
+    wl.LayerConfig("mid_groups_bf16", "bf16", T=600, H=128, E=4, top_k=2, I=192),
 ]
 
 
@@ -38,18 +47,21 @@ CASES = [
 # *_and_shared calls where the case has a shared expert.  Asserted below, so a
 # change of the selection cannot silently move a case off the configuration it
 # exists to cover.
-_G, _S, _D, _M, _DEC, _F = (B.MOE_TILE_GENERIC, B.MOE_TILE_128x128, B.MOE_TILE_256x256, B.MOE_TILE_128x256,
-                            B.MOE_TILE_32x128, B.MOE_TILE_F32)
+_G, _S, _D, _M, _DEC, _F, _W = (B.MOE_TILE_GENERIC, B.MOE_TILE_128x128, B.MOE_TILE_256x256, B.MOE_TILE_128x256,
+                                B.MOE_TILE_32x128, B.MOE_TILE_F32, B.MOE_TILE_128x512)
 EXPECTED_TILES = {
     "tiny": (_F, _F, None, None),
     "ragged_bf16": (_G, _G, None, None),
-    "gated_bf16": (_M, _G, _M, _G),
+    "gated_bf16": (_W, _G, _W, _G),
     "decode1_bf16": (_DEC, _DEC, _DEC, _DEC),
-    "wide_bf16": (_DEC, _M, _M, _M),
+    "wide_bf16": (_DEC, _W, _W, _W),
     "ragged_f32": (_F, _F, _F, _F),
     "big_groups_bf16": (_D, _D, _D, _D),
     "fused_big_bf16": (_D, _D, _D, _D),
     "big_groups_short_k_bf16": (_D, _D, _D, _D),
+    "wide_short_k_bf16": (_W, _W, None, None),
+    "wide_fused_bf16": (_W, _W, _W, _W),
+    "mid_groups_bf16": (_M, _M, None, None),
 }
 
 
