@@ -14,8 +14,8 @@ E=256, top-8, I=2048, one shared expert), the largest layer that fits one GPU.
 
 Timing: W untimed warm-up steps, then exactly K steps (default 50 for prefill,
 200 for decode shapes) between two stream synchronisations.  Before every
-timed step, outside its events, an ordinary fill kernel writes 1 GiB so the
-256 MiB last-level cache holds none of the step's inputs (--no-evict skips
+timed step, outside its events, an ordinary reduction kernel reads 1 GiB so
+the 256 MiB last-level cache holds none of the step's inputs (--no-evict skips
 this).  HIP events on the launch stream bracket each step and each call; the
 line reports the median step time (value = T / median) with p10/p90, and the
 mean duration of the dominant call (the fc1 launch) for the roofline object.
@@ -149,16 +149,19 @@ def add_profile_fraction(roof, rec):
 
 
 class Evictor:
-    """Writes 1 GiB with an ordinary elementwise kernel (torch's add_), so the
-    256 MiB last-level cache (and every L2) holds none of the next step's
-    inputs.  Enqueued outside the timed events and outside any captured graph."""
+    """Reads 1 GiB with an ordinary reduction kernel (torch's sum), so the 256 MiB
+    last-level cache (and every L2) holds none of the next step's inputs, only
+    clean lines of this buffer: an eviction that wrote its buffer would leave
+    dirty lines whose write-back then competes with the step's reads.  Enqueued
+    outside the timed events and outside any captured graph."""
 
     def __init__(self, dev, enabled=True):
-        self.buf = torch.zeros((1 << 28,), dtype=torch.int32, device=dev) if enabled else None
+        self.buf = torch.ones((1 << 28,), dtype=torch.int32, device=dev) if enabled else None
+        self.sink = None
 
     def __call__(self):
         if self.buf is not None:
-            self.buf.add_(1)
+            self.sink = self.buf.sum(dtype=torch.int64)
 
 
 def step_stats(ms):
@@ -603,7 +606,7 @@ def bench_backward(args, cfg, layer, bias_t, dev, evict, info):
         "timing": {"step": stats, "cache": "evicted" if evict.buf is not None else "warm",
                    "wall_ms_per_step": round(wall * 1e3 / steps, 4),
                    "note": "step = HIP events around the three calls; value uses the median; the wall time also "
-                           "covers the 1 GiB eviction fill before each step"},
+                           "covers the 1 GiB eviction read before each step"},
         "config": {"workload": cfg.name, "pass": "backward of the routed experts (routes fixed)", "T": cfg.T,
                    "H": cfg.H, "E": cfg.E, "top_k": cfg.top_k, "I": cfg.I, "routing": cfg.skew or "natural",
                    "shared_expert": "not included", "realized_rows_per_expert": counts.tolist()},
@@ -842,9 +845,9 @@ def main():
                    "step": stats, "warm_cache_step": warm,
                    "wall_ms_per_step": round(wall * 1e3 / steps, 4),
                    "note": ("value and ms_per_step use the median of the per-step HIP-event times; before every "
-                            "timed step a 1 GiB fill kernel (outside the events) evicts the 256 MiB last-level "
-                            "cache, so the wall time per step also covers it; warm_cache_step repeats the step "
-                            "back to back without eviction")},
+                            "timed step a reduction kernel reading 1 GiB (outside the events) evicts the 256 MiB "
+                            "last-level cache, so the wall time per step also covers it; warm_cache_step repeats "
+                            "the step back to back without eviction")},
         "grouped_gemm": {"tflops": round(gg_tflops, 2), "frac_mfma_peak": round(gg_tflops / PEAK_BF16_TFLOPS, 4),
                          "gbps": round(gg_gbps, 1), "frac_hbm_peak": round(gg_gbps / PEAK_HBM_GBPS, 4),
                          "fc1_ms": round(per_call["fc1"], 4), "fc2_ms": round(per_call["fc2"], 4),

@@ -341,6 +341,7 @@ __device__ __forceinline__ int build_tile_prefix(const GemmParams<T>& p, int32_t
 
 struct TileCoord {
   int g, row0, row_end, ntile;
+  bool single;   // the group fits in one row tile (its weights are read once)
 };
 
 // Tile ids run expert-major, then column tile, then row tile.
@@ -359,6 +360,7 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t id, int G, int64_t nt, 
   c.ntile = (int)(local / mt);
   c.row0 = sOff[lo] + (int)(local % mt) * BM;
   c.row_end = sOff[lo + 1];
+  c.single = sOff[lo + 1] - sOff[lo] <= BM;
   return c;
 }
 
@@ -391,15 +393,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MOE_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
 #define MOE_GLOBAL(T, ptr) ((const __attribute__((address_space(1))) T*)(ptr))
 
-// Cache policy of the direct loads of expert weights: non-temporal (the nt bit
-// of the instruction's cache-policy field).  A weight byte is read once per
-// call, so keeping it out of the cache lines the activations and the other
-// in-flight slices live in pays: measured on MI355X with the DeepSeek-V3-shaped
-// layer, the routed fc1 went from 2.96 to 2.82-2.85 ms and fc2 from 1.80 to
-// 1.78 ms; the DeepSeek-V2-Lite-shaped decode (T = 64) fc1 from 0.184 to
-// 0.128 ms; the dense 256x256 tile gains 3-4%.  Activation loads keep the
-// default policy (non-temporal activations measured 13% slower: they are
-// re-read by every column tile).
+// Cache policy of the direct loads of expert weights for a group that fits in
+// one row tile: non-temporal (the nt bit of the instruction's cache-policy
+// field).  Each of those weight bytes is read once per call, so keeping it out
+// of the cache lines the activations and the other in-flight slices live in
+// pays: measured on MI355X, the DeepSeek-V3-shaped routed fc1 (groups of ~100
+// rows) went from 2.99 to 2.86 ms; the DeepSeek-V2-Lite-shaped decode (T = 64)
+// fc1 from 0.182 to 0.127 ms and fc2 from 0.110 to 0.069 ms.  A group spanning
+// several row tiles re-reads its weights once per row tile, and those re-reads
+// hit in L2 only under the default policy (Qwen2-shaped fc1, ~273-row groups
+// in 128-row tiles: 0.30 ms default, 0.40 ms non-temporal), so the policy is
+// chosen per tile.  Activation loads keep the default policy (non-temporal
+// activations measured 13% slower: every column tile re-reads them).
 constexpr int kWeightLoadPolicy = 2;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -483,21 +488,29 @@ __device__ __forceinline__ int pipe_col_base(int nb, int wn) {
              : (wn * (C::BN / C::WN) + 32 * nb);
 }
 
-// Direct loads of one reduction slice (activations, then weights) into a ring stage.
+// Direct loads of one reduction slice (activations, then weights) into a ring
+// stage; wnt: the weights are read once (non-temporal policy).
 template <class C>
 __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const bf16_t* a_k, const bf16_t* b_k,
-                                           const int64_t* a_off, const int* b_off) {
+                                           const int64_t* a_off, const int* b_off, bool wnt) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i)
     if (C::STAGES != 2 || a_off[i] >= 0)
       __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
                                        MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+  if (wnt) {
 #pragma unroll
-  for (int i = 0; i < C::kBLoads; ++i)
-    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                     MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
-                                     kWeightLoadPolicy);
+    for (int i = 0; i < C::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                       MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
+                                       kWeightLoadPolicy);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::kBLoads; ++i)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                       MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, 0);
+  }
 }
 
 // One pipeline step: start the loads of a future slice into `wst`, then run
@@ -507,21 +520,10 @@ __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
                                           bool issue, const bf16_t* a_k, const bf16_t* b_k, const int64_t* a_off,
-                                          const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw) {
+                                          const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw,
+                                          bool wnt) {
   const int lane = threadIdx.x & 63;
-  if (issue) {
-    const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < C::kALoads; ++i)
-      if (C::STAGES != 2 || a_off[i] >= 0)
-        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                         MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                       MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
-                                       kWeightLoadPolicy);
-  }
+  if (issue) pipe_issue<C>(wst, a_k, b_k, a_off, b_off, wnt);
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
   const int grp = lane >> 4, s16 = lane & 15;
@@ -646,7 +648,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
 
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
-                                              unsigned char* __restrict__ smem) {
+                                              unsigned char* __restrict__ smem, bool wnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
   const int wm = wpos / C::WN, wn = wpos % C::WN;
@@ -713,14 +715,14 @@ __device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, in
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
     if (s < nk)
-      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off);
+      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt);
 
   for (int kt = 0; kt < nk; ++kt) {
     if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
     lds_barrier();
     const int kn = kt + C::STAGES - 1;
     pipe_step<EPI, C, BT>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
-                          a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw);
+                          a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw, wnt);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
   finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
@@ -809,7 +811,7 @@ __device__ __forceinline__ void sched_substep() {
 // two fragment sets, so the number of substeps per slice must be even.
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
-                                                 unsigned char* __restrict__ smem) {
+                                                 unsigned char* __restrict__ smem, bool wnt) {
   static_assert(C::kKSW % 2 == 0, "substeps per slice alternate between two fragment sets");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
@@ -870,7 +872,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   const bf16_t* a_base = p.a;
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off);
+    if (s < nk) pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt);
   // slice 0 has landed in every wave (newer slices may still be in flight)
   if (nk - 1 >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
   lds_barrier();
@@ -878,7 +880,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   // at the slice boundaries below, STAGES slices ahead)
   if (C::STAGES - 1 < nk)
     pipe_issue<C>(smem + (C::STAGES - 1) * C::kStage, a_base + (C::STAGES - 1) * C::BK,
-                  bg + (C::STAGES - 1) * b_step, a_off, b_off);
+                  bg + (C::STAGES - 1) * b_step, a_off, b_off, wnt);
 
   PipeFrags<C> f0, f1;
   pipe_read<EPI, C, BT>(smem, kw, wm, wn, f0);
@@ -900,7 +902,8 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
         lds_barrier();
         const int kn = kt + C::STAGES;
         if (kn < nk)
-          pipe_issue<C>(smem + (kt % C::STAGES) * C::kStage, a_base + kn * C::BK, bg + kn * b_step, a_off, b_off);
+          pipe_issue<C>(smem + (kt % C::STAGES) * C::kStage, a_base + kn * C::BK, bg + kn * b_step, a_off, b_off,
+                        wnt);
         pipe_read<EPI, C, BT>(smem + ((kt + 1) % C::STAGES) * C::kStage, kw, wm, wn, nxt);
       }
       pipe_mfmas<C>(cur, acc);
@@ -924,11 +927,11 @@ constexpr bool pipe_loop_v1() {
 
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
-                                              unsigned char* __restrict__ smem) {
+                                              unsigned char* __restrict__ smem, bool wnt) {
   if constexpr (pipe_loop_v1<C>())
-    run_tile_pipe_v1<EPI, C, BT>(p, g, row0, row_end, n0, smem);
+    run_tile_pipe_v1<EPI, C, BT>(p, g, row0, row_end, n0, smem, wnt);
   else
-    run_tile_pipe_v0<EPI, C, BT>(p, g, row0, row_end, n0, smem);
+    run_tile_pipe_v0<EPI, C, BT>(p, g, row0, row_end, n0, smem, wnt);
 }
 
 template <int EPI, class C, int ROLE, bool BT>
@@ -943,7 +946,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
   const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
-    run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
+    run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem, c.single);
   }
 }
 
@@ -953,29 +956,43 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
 // (MFMA-bound).  Tile ids of the two problems are interleaved evenly
 // (position p is a shared tile when floor((p+1)*Ts/total) > floor(p*Ts/total)),
 // so every CU works on both kinds at once and each hides the other's stalls.
-template <int EPI_R, int EPI_S, class C, bool BT>
-__global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_fused(GemmParams<bf16_t> pr,
-                                                                                GemmParams<bf16_t> ps) {
+// The two problems may use different tile configurations CR and CS (same
+// thread count; the LDS ring is sized for the larger of the two), so the
+// shared expert can take the dense tile while the routed groups take the
+// weight-streaming one.
+template <class CR, class CS>
+constexpr int fused_lds() {
+  return CR::kLds > CS::kLds ? CR::kLds : CS::kLds;
+}
+template <class CR, class CS>
+constexpr int fused_wgs() {
+  return CR::kWgsPerCu < CS::kWgsPerCu ? CR::kWgsPerCu : CS::kWgsPerCu;
+}
+
+template <int EPI_R, int EPI_S, class CR, class CS, bool BT>
+__global__ __launch_bounds__(CR::NT, (fused_wgs<CR, CS>())) void grouped_gemm_bf16_fused(GemmParams<bf16_t> pr,
+                                                                                          GemmParams<bf16_t> ps) {
+  static_assert(CR::NT == CS::NT, "both configurations run in the same workgroups");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int32_t sOff[kMaxExperts + 1];
   __shared__ int32_t sPre[kMaxExperts + 1];
-  __shared__ int32_t sWave[C::kWaves];
-  const int mtiles = build_tile_prefix<C::BM, C::NT>(pr, sOff, sPre, sWave);
+  __shared__ int32_t sWave[CR::kWaves];
+  const int mtiles = build_tile_prefix<CR::BM, CR::NT>(pr, sOff, sPre, sWave);
   const int64_t ntr = pr.n_tiles;
   const int64_t tiles_r = (int64_t)mtiles * ntr;
-  const int64_t mts = (ps.rows + C::BM - 1) / C::BM;
+  const int64_t mts = (ps.rows + CS::BM - 1) / CS::BM;
   const int64_t tiles_s = mts * ps.n_tiles;
   const int64_t total = tiles_r + tiles_s;
-  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
-  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? CR::BN / 2 : CR::BN;
+  const int out_s = paired(EPI_S) ? CS::BN / 2 : CS::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const int64_t s_before = id * tiles_s / total;
     if ((id + 1) * tiles_s / total != s_before) {
       const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
-      run_tile_pipe<EPI_S, C, BT>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
+      run_tile_pipe<EPI_S, CS, BT>(ps, 0, mtile * CS::BM, ps.rows, ntile * out_s, smem, ps.rows <= CS::BM);
     } else {
-      const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
-      run_tile_pipe<EPI_R, C, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
+      const TileCoord c = decode_tile<CR::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
+      run_tile_pipe<EPI_R, CR, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem, c.single);
     }
   }
 }
@@ -1113,29 +1130,46 @@ __device__ __forceinline__ void mx_read(const unsigned char* __restrict__ As, co
 // fragments of the next substep while the current one is converted and
 // multiplied.  The __restrict__ stage pointers let the compiler skip waiting
 // for the in-flight direct loads before the LDS reads.
+// Direct loads of one slice (activations, codes, scales) into a ring stage;
+// wnt: the weights are read once (non-temporal policy, as in the bf16 path).
+template <class C, int POL>
+__device__ __forceinline__ void mx_issue_pol(unsigned char* __restrict__ st, const bf16_t* a_k,
+                                             const unsigned char* b_k, const unsigned char* s_k, const int64_t* a_off,
+                                             const int* b_off, const int* s_off) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < C::kALoads; ++i)
+    if (C::STAGES != 2 || a_off[i] >= 0)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
+                                       MOE_LDS(void, st + (wave * C::kALoads + i) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::kBLoads; ++i)
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
+                                     MOE_LDS(void, st + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0, POL);
+#pragma unroll
+  for (int i = 0; i < C::kSLoads; ++i)
+    __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
+                                     MOE_LDS(void, st + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256), 4,
+                                     0, POL);
+}
+
+template <class C>
+__device__ __forceinline__ void mx_issue(unsigned char* __restrict__ st, const bf16_t* a_k, const unsigned char* b_k,
+                                         const unsigned char* s_k, const int64_t* a_off, const int* b_off,
+                                         const int* s_off, bool wnt) {
+  if (wnt)
+    mx_issue_pol<C, kWeightLoadPolicy>(st, a_k, b_k, s_k, a_off, b_off, s_off);
+  else
+    mx_issue_pol<C, 0>(st, a_k, b_k, s_k, a_off, b_off, s_off);
+}
+
 template <int EPI, class C, int SAX>
 __device__ __forceinline__ void mx_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
                                         bool issue, const bf16_t* a_k, const unsigned char* b_k,
                                         const unsigned char* s_k, const int64_t* a_off, const int* b_off,
-                                        const int* s_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw) {
-  const int wave = threadIdx.x >> 6;
-  if (issue) {
-#pragma unroll
-    for (int i = 0; i < C::kALoads; ++i)
-      if (C::STAGES != 2 || a_off[i] >= 0)
-        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                         MOE_LDS(void, wst + (wave * C::kALoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                       MOE_LDS(void, wst + C::kAStage + (wave * C::kBLoads + i) * 1024), 16, 0,
-                                       kWeightLoadPolicy);
-#pragma unroll
-    for (int i = 0; i < C::kSLoads; ++i)
-      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, s_k + s_off[i]),
-                                       MOE_LDS(void, wst + C::kAStage + C::kBStage + (wave * C::kSLoads + i) * 256),
-                                       4, 0, kWeightLoadPolicy);
-  }
+                                        const int* s_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw,
+                                        bool wnt) {
+  if (issue) mx_issue<C>(wst, a_k, b_k, s_k, a_off, b_off, s_off, wnt);
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
   const unsigned char* Ss = rst + C::kAStage + C::kBStage;
@@ -1159,7 +1193,7 @@ __device__ __forceinline__ void mx_step(unsigned char* __restrict__ wst, const u
 
 template <int EPI, class C, int SAX>
 __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
-                                            unsigned char* __restrict__ smem) {
+                                            unsigned char* __restrict__ smem, bool wnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
   const int wm = wpos / C::WN, wn = wpos % C::WN;
@@ -1223,31 +1257,10 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
   // Prologue: the first STAGES - 1 slices (the second stage pointer of each
   // call is unused because nothing is computed yet).
 #pragma unroll
-  for (int s = 0; s < C::STAGES - 1; ++s) {
-    if (s < nk) {
-      unsigned char* st = smem + s * C::kStage;
-      const int wave_ = wave;
-      const bf16_t* a_k = p.a + (int64_t)s * C::BK;
-      const unsigned char* b_k = bq + (int64_t)s * C::BK;
-      const unsigned char* s_k = bs + (int64_t)s * kSStep;
-#pragma unroll
-      for (int i = 0; i < C::kALoads; ++i)
-        if (C::STAGES != 2 || a_off[i] >= 0)
-          __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, a_k + a_off[i]),
-                                           MOE_LDS(void, st + (wave_ * C::kALoads + i) * 1024), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < C::kBLoads; ++i)
-        __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, b_k + b_off[i]),
-                                         MOE_LDS(void, st + C::kAStage + (wave_ * C::kBLoads + i) * 1024), 16, 0,
-                                         kWeightLoadPolicy);
-#pragma unroll
-      for (int i = 0; i < C::kSLoads; ++i)
-        __builtin_amdgcn_global_load_lds(
-            MOE_GLOBAL(void, s_k + s_off[i]),
-            MOE_LDS(void, st + C::kAStage + C::kBStage + (wave_ * C::kSLoads + i) * 256), 4, 0,
-            kWeightLoadPolicy);
-    }
-  }
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk)
+      mx_issue<C>(smem + s * C::kStage, p.a + (int64_t)s * C::BK, bq + (int64_t)s * C::BK,
+                  bs + (int64_t)s * kSStep, a_off, b_off, s_off, wnt);
 
   for (int kt = 0; kt < nk; ++kt) {
     if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
@@ -1255,7 +1268,7 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
     const int kn = kt + C::STAGES - 1;
     mx_step<EPI, C, SAX>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
                          p.a + (int64_t)kn * C::BK, bq + (int64_t)kn * C::BK, bs + (int64_t)kn * kSStep, a_off,
-                         b_off, s_off, acc, wn, wm, kw);
+                         b_off, s_off, acc, wn, wm, kw, wnt);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
   finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
@@ -1273,7 +1286,7 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8(GemmPara
   const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
     const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
-    run_tile_mx<EPI, C, SAX>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem);
+    run_tile_mx<EPI, C, SAX>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem, c.single);
   }
 }
 
@@ -1298,10 +1311,10 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_mx8_fused(Ge
     const int64_t s_before = id * tiles_s / total;
     if ((id + 1) * tiles_s / total != s_before) {
       const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
-      run_tile_mx<EPI_S, C, SAX>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem);
+      run_tile_mx<EPI_S, C, SAX>(ps, 0, mtile * C::BM, ps.rows, ntile * out_s, smem, ps.rows <= C::BM);
     } else {
       const TileCoord c = decode_tile<C::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
-      run_tile_mx<EPI_R, C, SAX>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem);
+      run_tile_mx<EPI_R, C, SAX>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem, c.single);
     }
   }
 }
@@ -1820,28 +1833,28 @@ int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
   return rows_per_active_group(p) <= kWideRows ? MOE_TILE_128x512 : MOE_TILE_128x256;
 }
 
-template <int EPI_R, int EPI_S, class C, bool BT>
+template <int EPI_R, int EPI_S, class CR, class CS, bool BT>
 hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_count, hipStream_t s) {
-  if (pr.K % C::BK != 0 || ps.K % C::BK != 0) return launch_fused<EPI_R, EPI_S, CfgSmall, BT>(pr, ps, cu_count, s);
+  if (pr.K % CR::BK != 0 || ps.K % CS::BK != 0)
+    return launch_fused<EPI_R, EPI_S, CfgSmall, CfgSmall, BT>(pr, ps, cu_count, s);
+  constexpr int lds = fused_lds<CR, CS>();
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+      reinterpret_cast<const void*>(&grouped_gemm_bf16_fused<EPI_R, EPI_S, CR, CS, BT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  const int out_r = paired(EPI_R) ? C::BN / 2 : C::BN;
-  const int out_s = paired(EPI_S) ? C::BN / 2 : C::BN;
+  const int out_r = paired(EPI_R) ? CR::BN / 2 : CR::BN;
+  const int out_s = paired(EPI_S) ? CS::BN / 2 : CS::BN;
   pr.n_tiles = (pr.N + out_r - 1) / out_r;
   ps.n_tiles = (ps.N + out_s - 1) / out_s;
-  const int64_t ub_r = ((int64_t)pr.rows / C::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
-  const int64_t tiles_s = (int64_t)((ps.rows + C::BM - 1) / C::BM) * ps.n_tiles;
-  const int grid = persistent_grid(ub_r + tiles_s, cu_count * C::kWgsPerCu);
-  hipLaunchKernelGGL((grouped_gemm_bf16_fused<EPI_R, EPI_S, C, BT>), dim3(grid), dim3(C::NT), C::kLds, s, pr, ps);
+  const int64_t ub_r = ((int64_t)pr.rows / CR::BM + (pr.groups < pr.rows ? pr.groups : pr.rows)) * pr.n_tiles;
+  const int64_t tiles_s = (int64_t)((ps.rows + CS::BM - 1) / CS::BM) * ps.n_tiles;
+  const int grid = persistent_grid(ub_r + tiles_s, cu_count * fused_wgs<CR, CS>());
+  hipLaunchKernelGGL((grouped_gemm_bf16_fused<EPI_R, EPI_S, CR, CS, BT>), dim3(grid), dim3(CR::NT), lds, s, pr, ps);
   return hipGetLastError();
 }
 
-// One configuration for both problems of a fused launch: the large tile only
-// when the routed groups and the shared expert both average >= 512 rows, the
-// decode tile when the routed groups are small and the shared expert has at
-// most 64 rows.
+constexpr int kFusedDenseSharedRows = 512;
+
 int pick_fused_variant(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps) {
   const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
   if (per_group >= 512 && ps.rows >= 512) return MOE_TILE_256x256;
@@ -1854,9 +1867,19 @@ template <int EPI_R, int EPI_S>
 hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, int cu_count,
                              hipStream_t s) {
   const int v = pick_fused_variant(pr, ps);
+  // The weight-streaming routed tile runs the shared expert with the dense
+  // tile when the shared expert has rows enough to fill it.
+  if (v == MOE_TILE_128x512 && ps.rows >= kFusedDenseSharedRows) {
+    if (pr.bt) return launch_fused<EPI_R, EPI_S, CfgWide, CfgDense, true>(pr, ps, cu_count, s);
+    return launch_fused<EPI_R, EPI_S, CfgWide, CfgDense, false>(pr, ps, cu_count, s);
+  }
   if (pr.bt)
-    return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), true>(pr, ps, cu_count, s); });
-  return with_cfg(v, [&](auto c) { return launch_fused<EPI_R, EPI_S, decltype(c), false>(pr, ps, cu_count, s); });
+    return with_cfg(v, [&](auto c) {
+      return launch_fused<EPI_R, EPI_S, decltype(c), decltype(c), true>(pr, ps, cu_count, s);
+    });
+  return with_cfg(v, [&](auto c) {
+    return launch_fused<EPI_R, EPI_S, decltype(c), decltype(c), false>(pr, ps, cu_count, s);
+  });
 }
 
 template <int EPI, int ROLE>
@@ -1926,15 +1949,21 @@ hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, 
 }
 
 // One launch for both problems pays off when the shared expert's MFMA work is
-// small next to the routed weight stream (decode, many large experts): its
-// tiles then fill the gaps of the weight-bound routed tiles.  A large shared
-// expert (prefill with a wide shared MLP) runs faster in a launch of its own
-// with the large tile.  Measured on MI355X: one launch wins at a ratio of
-// shared FLOPs to routed weight bytes of ~2 (DeepSeek-V2-Lite-shaped decode)
-// and ~16 (DeepSeek-V3-shaped prefill) and loses from ~128 (Scout-shaped).
+// small next to the routed weight stream (decode, many large experts), or when
+// the routed groups stream their weights through the wide tile while the
+// shared expert takes the dense one: its tiles then fill the gaps of the
+// weight-bound routed tiles.  With mid-size or dense routed groups a large
+// shared expert runs faster in a launch of its own (measured on MI355X:
+// Qwen2-shaped fc2 0.30 ms in two launches against 0.36 ms in one).
 bool fused_supported(int dt, int H, int I, int I_s, int E, int R, int T) {
+  using namespace moe;
   if (!(dt == 1 && H % 64 == 0 && I % 64 == 0 && I_s % 64 == 0)) return false;
-  const double routed_bytes = (double)(E < R ? E : R) * 3.0 * H * I * 2.0;
+  // Weight-streaming routed groups (the wide tile) leave the MFMAs idle most of
+  // the time; the shared expert's dense tiles fill them in the same launch
+  // (Scout-shaped layer: fc1 0.93 -> 0.91 ms, fc2 0.57 -> 0.52 ms).
+  const int64_t active = E < R ? E : R;
+  if ((int64_t)R / (active > 0 ? active : 1) <= kWideRows && R / (active > 0 ? active : 1) > kDecodeRows) return true;
+  const double routed_bytes = (double)active * 3.0 * H * I * 2.0;
   const double shared_flops = 6.0 * T * H * I_s;
   return shared_flops < 50.0 * routed_bytes;
 }

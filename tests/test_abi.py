@@ -171,9 +171,11 @@ def test_combine_and_shared_validation(lib):
 
 
 def test_and_shared_launch_count_query(lib):
-    # Scout-shaped: a wide shared expert next to 16 routed experts -> two launches;
+    # Qwen2-shaped: a wide gated shared expert next to mid-size routed groups -> two launches;
+    # Scout-shaped: weight-streaming routed groups (128 rows each) -> one launch, whatever the shared width;
     # DeepSeek-V3-shaped prefill: a light shared expert next to 256 experts -> one launch
-    assert lib.moe_and_shared_launches(1, 2048, 5120, 16, 8192, 2048, 8192) == 2
+    assert lib.moe_and_shared_launches(1, 16384, 2048, 60, 1408, 4096, 5632) == 2
+    assert lib.moe_and_shared_launches(1, 2048, 5120, 16, 8192, 2048, 8192) == 1
     assert lib.moe_and_shared_launches(1, 32768, 7168, 256, 2048, 4096, 2048) == 1
     assert lib.moe_and_shared_launches(0, 32768, 7168, 256, 2048, 4096, 2048) == 2   # f32: never one launch
     assert lib.moe_and_shared_launches(1, 0, 7168, 256, 2048, 4096, 2048) == 0
