@@ -156,12 +156,13 @@ class Evictor:
     outside the timed events and outside any captured graph."""
 
     def __init__(self, dev, enabled=True):
-        self.buf = torch.ones((1 << 28,), dtype=torch.int32, device=dev) if enabled else None
+        # float32, so the sum reads the buffer in place (an integer sum would first widen it to a new buffer)
+        self.buf = torch.ones((1 << 28,), dtype=torch.float32, device=dev) if enabled else None
         self.sink = None
 
     def __call__(self):
         if self.buf is not None:
-            self.sink = self.buf.sum(dtype=torch.int64)
+            self.sink = self.buf.sum()
 
 
 def step_stats(ms):
