@@ -297,15 +297,19 @@ class HostExperts:
     time.  With MXFP8 codes the oracle's exact dequantization runs on access (its
     own arithmetic, so it is not counted in `copy_s`)."""
 
-    def __init__(self, w=None, layout=None, q=None, sc=None, axis=None):
-        self.w, self.layout, self.q, self.sc, self.axis = w, layout, q, sc, axis
+    def __init__(self, w=None, layout=None, q=None, sc=None, axis=None, name="W"):
+        self.w, self.layout, self.q, self.sc, self.axis, self.name = w, layout, q, sc, axis, name
         self.copy_s = 0.0
+        self.fetched = 0
 
     def __len__(self):
         return (self.w if self.w is not None else self.q).shape[0]
 
     def __getitem__(self, e):
         from oracle import moe_oracle as O
+        self.fetched += 1
+        if self.fetched % 64 == 0:
+            log(f"cpu baseline: {self.name} of {self.fetched} experts fetched so far")
         t0 = time.perf_counter()
         if self.q is not None:
             q, sc = self.q[e].cpu().numpy(), self.sc[e].cpu().numpy()
@@ -335,8 +339,8 @@ def cpu_baseline(layer, cfg, sample_tokens, info):
     wr = _host(layer["w_router"])
     mx = layer.get("mx")
     if mx is not None:
-        W1 = HostExperts(q=mx["W1q"], sc=mx["W1s"], axis=0)
-        W2 = HostExperts(q=mx["W2q"], sc=mx["W2s"], axis=1)
+        W1 = HostExperts(q=mx["W1q"], sc=mx["W1s"], axis=0, name="W1")
+        W2 = HostExperts(q=mx["W2q"], sc=mx["W2s"], axis=1, name="W2")
         shared = None
         if mx["shared"] is not None:
             q1, s1, q2, s2, wg = mx["shared"]
@@ -345,8 +349,8 @@ def cpu_baseline(layer, cfg, sample_tokens, info):
                       np.ascontiguousarray(O.mx_dequant(u(q2), u(s2), axis=1).T.astype(np.float32)),
                       _host(wg) if wg is not None else None)
     else:
-        W1 = HostExperts(layer["W1"], layer["layout"])
-        W2 = HostExperts(layer["W2"], layer["layout"])
+        W1 = HostExperts(layer["W1"], layer["layout"], name="W1")
+        W2 = HostExperts(layer["W2"], layer["layout"], name="W2")
         shared = None
         if layer["shared"] is not None:
             ws1, ws2, wg = layer["shared"]
@@ -632,9 +636,14 @@ def bench_backward(args, cfg, layer, bias_t, dev, evict, info):
     sys.exit(rc)
 
 
-def default_cpu_sample(cfg):
+def default_cpu_sample(cfg, mxfp8=False):
     """Tokens in the CPU-baseline sample: all of a decode batch, at most 2048 of a
-    prefill batch (about 1-15 s of oracle time on 16 host threads)."""
+    prefill batch (about 1-15 s of oracle time on 16 host threads).  With MXFP8
+    weights the oracle decodes every expert it touches in float64 (about 1 s per
+    DeepSeek-V3-sized expert), so 256-expert layers sample 4 tokens (at most 32
+    experts) and the others at most 256 tokens."""
+    if mxfp8:
+        return min(cfg.T, 4 if cfg.E >= 256 else 256)
     return cfg.T if cfg.T <= 64 else min(cfg.T, 2048)
 
 
@@ -876,7 +885,7 @@ def main():
     }
     rc = 0
     if not args.no_cpu_baseline:
-        S = min(args.cpu_sample or default_cpu_sample(cfg), cfg.T)
+        S = min(args.cpu_sample or default_cpu_sample(cfg, args.weights == "mxfp8"), cfg.T)
         base, ref = cpu_baseline(layer, cfg, S, info)
         result["cpu_baseline"] = base
         parity = parity_check(layer, cfg, bufs, bias_t, dev, side, ref, S)
