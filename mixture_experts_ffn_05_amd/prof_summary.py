@@ -13,6 +13,9 @@ rocprofv3 marker trace.
 `sq` tabulates SQ/TA/TD counter runs per kernel (MFMA busy share, waiting
 shares, texture-data unit busy and stalled shares, implied clock).
 
+`bandwidth` reads the kernel trace of a bench run with --copy-reference-mb and
+reports the copy, read (the cache-eviction reduction) and fill bandwidths.
+
 `pmc` reads two counter-collection runs
 (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), calibrates both against the
 device copy of <copy_mib> MiB that the profiled command performed first (its
@@ -185,6 +188,36 @@ def sq(out_md: str, command: str, dirs: list, cus: int = 256, xcds: int = 8) -> 
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def bandwidth(trace_csv: str, out_md: str, command: str, mib: float = 1024.0) -> None:
+    """Reference bandwidths from one kernel trace of a bench run with --copy-reference-mb: the
+    device copy of `mib` MiB (read + write), and the cache-eviction pass's 1 GiB reduction (read)
+    and 1 GiB fill (write) that the bench runs."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    nbytes = mib * 2 ** 20
+
+    def durs(pred, min_us):
+        out = []
+        for r in rows:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            if pred(r["Kernel_Name"]) and d >= min_us:
+                out.append(d)
+        return out
+
+    copy = durs(lambda n: "copyBuffer" in n, 100.0)
+    read = durs(lambda n: "reduce_kernel" in n, 50.0)
+    fill = durs(lambda n: "FillFunctor" in n, 50.0)
+    med = lambda xs: sorted(xs)[len(xs) // 2] if xs else float("nan")
+    lines = ["# Reference bandwidths on the box", "", f"Command: `{command}`", "",
+             f"Each kernel moves {nbytes / 1e9:.3f} GB of payload (1 GiB); GB/s = bytes moved / median duration.", "",
+             "| kernel | what it moves | dispatches | median us | GB/s |", "|---|---|---|---|---|"]
+    for name, what, xs, factor in (("device copy (copyBuffer)", "1 GiB read + 1 GiB written", copy, 2.0),
+                                   ("reduction (torch sum, the cache eviction)", "1 GiB read", read, 1.0),
+                                   ("fill (torch ones)", "1 GiB written", fill, 1.0)):
+        m = med(xs)
+        lines.append(f"| {name} | {what} | {len(xs)} | {m:.1f} | {factor * nbytes / (m * 1e-6) / 1e9:.0f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def replay(out_md: str, command: str, results: list) -> None:
     lines = ["# Route-trace replay: per-stage GPU time", "", f"Command (per trace): `{command}`", "",
              "Times are means over the repeats of HIP-event intervals around each libmoe call, in microseconds; "
@@ -230,6 +263,9 @@ if __name__ == "__main__":
     if mode == "sq":  # sq <out.md> <dir> [<dir> ...] -- <command...>
         cut = sys.argv.index("--")
         sq(sys.argv[2], " ".join(sys.argv[cut + 1:]), sys.argv[3:cut])
+        sys.exit(0)
+    if mode == "bandwidth":  # bandwidth <kernel_trace.csv> <out.md> <command...>
+        bandwidth(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
         sys.exit(0)
     if mode == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
