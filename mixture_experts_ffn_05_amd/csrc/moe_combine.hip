@@ -32,9 +32,22 @@ __global__ __launch_bounds__(256) void gather_combine_k(const f32x4* __restrict_
   const int hv = H / 4;
   for (int c = threadIdx.x; c < hv; c += 256) {
     f32x4 sum = accumulate ? y[(int64_t)t * hv + c] : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = s_idx[j];
-      if (r >= 0) sum += s_w[j] * y_rows[(int64_t)r * hv + c];
+    // Slots in batches of 8: the batch's loads are all issued before its
+    // adds, which still run in slot order.  Each routed row is read once
+    // (non-temporal loads).
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const int r = j < k ? s_idx[j] : -1;
+        v[u] = r >= 0 ? __builtin_nontemporal_load(y_rows + (int64_t)r * hv + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < k && s_idx[j] >= 0) sum += s_w[j] * v[u];
+      }
     }
     y[(int64_t)t * hv + c] = sum;
   }

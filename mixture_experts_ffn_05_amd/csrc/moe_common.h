@@ -74,6 +74,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// NV independent fixed-order sums, v[j] = sum over z = 0 .. n-1 of
+// p[j][z * stride] (0 where valid[j] is false).  Each batch of B slices issues
+// the loads of every sum before adding them, so the NV sums cost about the load
+// latency of one; each sum still adds its slices in the order z = 0, 1, ...
+template <int NV, int B>
+__device__ __forceinline__ void sum_slices_n(const float* const (&p)[NV], const bool (&valid)[NV], int64_t stride,
+                                             int n, float (&v)[NV]) {
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = 0.f;
+  for (int z = 0; z < n; z += B) {
+    float a[NV][B];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < B; ++u) a[j][u] = (valid[j] && z + u < n) ? p[j][(int64_t)(z + u) * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (z + u < n) v[j] += a[j][u];
+  }
+}
+
 // Fixed-order sum over z of p[z * stride], z = 0 .. n-1, eight loads in flight.
 __device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t stride, int n) {
   float v = 0.f;

@@ -285,7 +285,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
-            *o = v;
+            __builtin_nontemporal_store(v, o);  // read once, by the next call
           } else {
             const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
             *o = (p.accumulate ? *o : 0.0f) + sc * v;
@@ -635,7 +635,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
-            *o = v;
+            __builtin_nontemporal_store(v, o);  // read once, by the next call
           } else {
             const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
             *o = (p.accumulate ? *o : 0.0f) + sc * v;

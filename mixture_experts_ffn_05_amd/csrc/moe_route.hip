@@ -206,6 +206,10 @@ __global__ __launch_bounds__(256) void router_logits_valu(const bf16_t* __restri
 // One wave64 per token.  With `partial` set, the logits are first assembled
 // as the fixed-order sum of `nsplit` partial products (+ bias) and written to
 // `logits`; otherwise `logits` already holds them.
+// Q logits per lane (E <= 64 Q).  The partial sums of all Q logits of a lane
+// are added together, a batch of slices at a time, so that the lane waits for
+// about nsplit / B load latencies rather than Q times as many.
+template <int Q>
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ partial, int nsplit, int stride_e,
                                                     const float* __restrict__ bias, float* __restrict__ logits,
                                                     int T, int E, int k, int32_t* __restrict__ ids,
@@ -214,22 +218,30 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ pa
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float* row = logits + (int64_t)t * E;
-  float raw[kTopkPer];
+  float raw[Q];
+  bool ok[Q];
 #pragma unroll
-  for (int q = 0; q < kTopkPer; ++q) {
-    const int e = lane + kWave * q;
-    float v = -INFINITY;
-    if (e < E) {
-      if (partial) {
-        v = sum_slices(partial + (int64_t)t * stride_e + e, (int64_t)T * stride_e, nsplit);
-        if (bias) v += bias[e];
-        row[e] = v;
-      } else {
-        v = row[e];
+  for (int q = 0; q < Q; ++q) ok[q] = lane + kWave * q < E;
+  if (partial) {
+    const float* ptr[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) ptr[q] = partial + (int64_t)t * stride_e + lane + kWave * q;
+    sum_slices_n<Q, (Q >= 8 ? 2 : 16 / Q)>(ptr, ok, (int64_t)T * stride_e, nsplit, raw);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int e = lane + kWave * q;
+      if (ok[q]) {
+        if (bias) raw[q] += bias[e];
+        row[e] = raw[q];
       }
     }
-    raw[q] = v;
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) raw[q] = ok[q] ? row[lane + kWave * q] : 0.f;
   }
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    if (!ok[q]) raw[q] = -INFINITY;
   int id;
   float wgt;
   topk_wave(raw, E, k, id, wgt);
@@ -304,6 +316,21 @@ hipError_t route_partials_small(const void* x, const void* w_router, int T, int 
   return hipGetLastError();
 }
 
+// topk_softmax with the logits-per-lane specialization for E.
+hipError_t launch_topk(const float* partial, int nsplit, int stride_e, const float* bias, float* logits, int T, int E,
+                       int k, int32_t* ids, float* weights, hipStream_t s) {
+  using namespace moe;
+  const dim3 grid((T + 3) / 4), block(256);
+  switch (topk_per_lane(E)) {
+    case 1: hipLaunchKernelGGL(topk_softmax<1>, grid, block, 0, s, partial, nsplit, stride_e, bias, logits, T, E, k, ids, weights); break;
+    case 2: hipLaunchKernelGGL(topk_softmax<2>, grid, block, 0, s, partial, nsplit, stride_e, bias, logits, T, E, k, ids, weights); break;
+    case 4: hipLaunchKernelGGL(topk_softmax<4>, grid, block, 0, s, partial, nsplit, stride_e, bias, logits, T, E, k, ids, weights); break;
+    case 8: hipLaunchKernelGGL(topk_softmax<8>, grid, block, 0, s, partial, nsplit, stride_e, bias, logits, T, E, k, ids, weights); break;
+    default: hipLaunchKernelGGL(topk_softmax<kTopkPer>, grid, block, 0, s, partial, nsplit, stride_e, bias, logits, T, E, k, ids, weights); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t route(int dt, const void* x, const void* w_router, const float* bias, int T, int H, int E,
                  int top_k, int32_t* ids, float* weights, float* logits, void* workspace, hipStream_t s) {
   using namespace moe;
@@ -311,9 +338,7 @@ hipError_t route(int dt, const void* x, const void* w_router, const float* bias,
   if (router_small(dt, T, E)) {
     int nz = 0;
     if ((err = route_partials_small(x, w_router, T, H, E, workspace, &nz, s)) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)workspace, nz, E, bias,
-                       logits, T, E, top_k, ids, weights);
-    return hipGetLastError();
+    return launch_topk((const float*)workspace, nz, E, bias, logits, T, E, top_k, ids, weights, s);
   }
   if (dt == 1) {
     const int E_pad = padded_experts(E);
@@ -332,17 +357,13 @@ hipError_t route(int dt, const void* x, const void* w_router, const float* bias,
       hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
                          E_pad, sp.kslice, partial);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)partial, sp.nz, E_pad, bias,
-                       logits, T, E, top_k, ids, weights);
-    return hipGetLastError();
+    return launch_topk((const float*)partial, sp.nz, E_pad, bias, logits, T, E, top_k, ids, weights, s);
   }
   const int64_t n = (int64_t)T * E;
   hipLaunchKernelGGL(route_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      (const float*)x, (const float*)w_router, bias, T, H, E, logits);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, (const float*)nullptr, 0, E, nullptr, logits,
-                     T, E, top_k, ids, weights);
-  return hipGetLastError();
+  return launch_topk(nullptr, 0, E, nullptr, logits, T, E, top_k, ids, weights, s);
 }
 
 }  // namespace moe_launch

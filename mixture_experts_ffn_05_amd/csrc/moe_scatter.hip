@@ -27,6 +27,8 @@
 #include "moe_common.h"
 #include "moe_topk.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(NW * 64) void scatter_small(const int32_t* __restri
 constexpr int kRsTokens = 16;
 constexpr int kRsLogits = 4096;
 
-template <int NW>
+template <int NW, int Q>
 __global__ __launch_bounds__(NW * 64) void route_scatter_small(
     const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, float* __restrict__ logits,
     int T, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int nbits, int nchunks,
@@ -323,17 +325,32 @@ __global__ __launch_bounds__(NW * 64) void route_scatter_small(
   __shared__ int32_t s_ids[kRsTokens * kMaxTopK];
   __shared__ float s_logits[kRsLogits];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < T * E; i += NW * kWave) {
-    float v = sum_slices(partial + i, (int64_t)T * E, nsplit);
-    if (bias) v += bias[i % E];
-    logits[i] = v;
-    s_logits[i] = v;
+  // four logits per thread at a time, their slice loads issued together
+  constexpr int kNT = NW * kWave;
+  for (int i0 = tid; i0 < T * E; i0 += 4 * kNT) {
+    const float* ptr[4];
+    bool ok[4];
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = i0 + j * kNT < T * E;
+      ptr[j] = partial + i0 + j * kNT;
+    }
+    sum_slices_n<4, 8>(ptr, ok, (int64_t)T * E, nsplit, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kNT;
+      if (!ok[j]) continue;
+      if (bias) v[j] += bias[i % E];
+      logits[i] = v[j];
+      s_logits[i] = v[j];
+    }
   }
   __syncthreads();
   for (int t = w; t < T; t += NW) {
-    float raw[kTopkPer];
+    float raw[Q];
 #pragma unroll
-    for (int q = 0; q < kTopkPer; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       raw[q] = e < E ? s_logits[t * E + e] : -INFINITY;
     }
@@ -446,14 +463,25 @@ hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const f
   const int row_vecs = (int)((int64_t)H * elem / 16);
   const int fold = x_scattered && R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
   const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
+  auto launch = [&](auto nw, auto q) {
+    constexpr int NW = decltype(nw)::value, Q = decltype(q)::value;
+    hipLaunchKernelGGL((route_scatter_small<NW, Q>), dim3(1), dim3(NW * 64), lds, s, partial, nsplit, bias, logits,
+                       T, E, top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets, status_words,
+                       fold, (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
+  };
+  auto with_q = [&](auto nw) {
+    switch (topk_per_lane(E)) {
+      case 1: launch(nw, std::integral_constant<int, 1>{}); break;
+      case 2: launch(nw, std::integral_constant<int, 2>{}); break;
+      case 4: launch(nw, std::integral_constant<int, 4>{}); break;
+      case 8: launch(nw, std::integral_constant<int, 8>{}); break;
+      default: launch(nw, std::integral_constant<int, kTopkPer>{}); break;
+    }
+  };
   if (T <= 4)  // one token per wave
-    hipLaunchKernelGGL(route_scatter_small<4>, dim3(1), dim3(256), lds, s, partial, nsplit, bias, logits, T, E,
-                       top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets, status_words, fold,
-                       (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
+    with_q(std::integral_constant<int, 4>{});
   else
-    hipLaunchKernelGGL(route_scatter_small<kSmallWaves>, dim3(1), dim3(kSmallWaves * 64), lds, s, partial, nsplit,
-                       bias, logits, T, E, top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets,
-                       status_words, fold, (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
+    with_q(std::integral_constant<int, kSmallWaves>{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || fold || !x_scattered) return err;  // rows copied, or not wanted
   hipLaunchKernelGGL(scatter_copy, dim3((R + kCopyRows - 1) / kCopyRows), dim3(256), 0, s, (const u32x4*)x,

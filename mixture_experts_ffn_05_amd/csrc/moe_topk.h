@@ -13,7 +13,15 @@ __device__ __forceinline__ bool ranks_before(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
-constexpr int kTopkPer = kMaxExperts / kWave;  // logits per lane of one token
+constexpr int kTopkPer = kMaxExperts / kWave;  // logits per lane of one token, at most
+
+// Logits per lane for E experts (a power of two up to kTopkPer), the template
+// argument of topk_wave and of the kernels that call it.
+inline int topk_per_lane(int E) {
+  int q = 1;
+  while (q * kWave < E) q <<= 1;
+  return q;
+}
 
 // One exchange of a wave arg-max through DPP (lanes of one 16-lane row; no LDS):
 // take the partner's (key, index) if it ranks first.  CTRL is a DPP control
@@ -33,11 +41,13 @@ __device__ __forceinline__ void argmax_dpp_step(float& bv, int& be) {
 // the key (logit descending, index ascending, NaN lowest), then a softmax over
 // the k selected logits.  Lane j < k returns the j-th selection in slot order
 // (id, weight); the other lanes return id -1.
-__device__ __forceinline__ void topk_wave(const float (&raw)[kTopkPer], int E, int k, int& my_id, float& my_w) {
+template <int Q>
+__device__ __forceinline__ void topk_wave(const float (&raw)[Q], int E, int k, int& my_id, float& my_w) {
+  static_assert(Q >= 1 && Q <= kTopkPer && (Q & (Q - 1)) == 0, "logits per lane: a power of two up to kTopkPer");
   const int lane = lane_id();
-  float key[kTopkPer];
+  float key[Q];
 #pragma unroll
-  for (int q = 0; q < kTopkPer; ++q) key[q] = (raw[q] != raw[q]) ? -INFINITY : raw[q];
+  for (int q = 0; q < Q; ++q) key[q] = (raw[q] != raw[q]) ? -INFINITY : raw[q];
   uint32_t taken = 0;
   float my_sel = 0.f;
   my_id = -1;
@@ -45,7 +55,7 @@ __device__ __forceinline__ void topk_wave(const float (&raw)[kTopkPer], int E, i
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < kTopkPer; ++q) {
+    for (int q = 0; q < Q; ++q) {
       const int e = lane + kWave * q;
       if (e < E && !((taken >> q) & 1u) && ranks_before(key[q], e, bv, be)) {
         bv = key[q];
@@ -72,7 +82,7 @@ __device__ __forceinline__ void topk_wave(const float (&raw)[kTopkPer], int E, i
     // the winner's raw logit (a NaN stays NaN): lane be % 64 holds it in slot be / 64
     float cand = raw[0];
 #pragma unroll
-    for (int q = 1; q < kTopkPer; ++q)
+    for (int q = 1; q < Q; ++q)
       if ((be >> 6) == q) cand = raw[q];
     const float br = __shfl(cand, be & 63, kWave);
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
