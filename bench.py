@@ -636,6 +636,55 @@ def bench_backward(args, cfg, layer, bias_t, dev, evict, info):
     sys.exit(rc)
 
 
+def library_reference(cfg, layer, counts, evict, dev, reps=20):
+    """The same GEMM shapes through torch's bf16 bmm/matmul (the vendor GEMM library), as a reference for the
+    grouped GEMMs: every active expert gets the mean group size (a uniform routing, no partial tiles), fc1 without
+    the SwiGLU epilogue and fc2 with a bf16 output (libmoe's fc2 writes fp32).  Each call is timed after the same
+    1 GiB eviction; median of `reps`."""
+    active = np.flatnonzero(counts > 0)
+    ea = len(active)
+    m = max(1, int(round(cfg.R / max(ea, 1))))
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    sel = lambda w: w if ea == cfg.E else w[torch.from_numpy(active).to(dev)].contiguous()
+
+    def timed(fn, flops, name, shape):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            evict()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts))
+        tf = flops / (ms / 1e3) / 1e12
+        log(f"library reference {name} {shape}: {ms:.4f} ms, {tf:.1f} TFLOP/s ({tf / PEAK_BF16_TFLOPS:.1%} of peak)")
+        return {"shape": shape, "ms": round(ms, 4), "tflops": round(tf, 1),
+                "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    out = {"note": "torch bf16 bmm/matmul (hipBLASLt) on the layer's own [K, N] weights, every active expert with "
+                   f"the mean group size {m} (uniform routing); fc1 without SwiGLU, bf16 outputs"}
+    for name, w, K, N in (("routed_fc1", layer["W1"], cfg.H, 2 * cfg.I), ("routed_fc2", layer["W2"], cfg.I, cfg.H)):
+        wb = sel(w)
+        x = torch.randn((ea, m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        y = torch.empty((ea, m, N), device=dev, dtype=torch.bfloat16)
+        out[name] = timed(lambda: torch.bmm(x, wb, out=y), 2.0 * ea * m * K * N, name, [ea, m, K, N])
+        del wb, x, y
+    if layer["shared"] is not None:
+        ws1, ws2, _ = layer["shared"]
+        for name, w, K, N in (("shared_fc1", ws1, cfg.H, 2 * cfg.I_s), ("shared_fc2", ws2, cfg.I_s, cfg.H)):
+            x = torch.randn((cfg.T, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            y = torch.empty((cfg.T, N), device=dev, dtype=torch.bfloat16)
+            out[name] = timed(lambda: torch.matmul(x, w, out=y), 2.0 * cfg.T * K * N, name, [cfg.T, K, N])
+            del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def default_cpu_sample(cfg, mxfp8=False):
     """Tokens in the CPU-baseline sample: all of a decode batch, at most 2048 of a
     prefill batch (about 1-15 s of oracle time on 16 host threads).  With MXFP8
@@ -679,6 +728,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the routed experts (for the routes a forward realized) instead of "
                          "the forward")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="also time the same GEMM shapes through torch's bf16 bmm/matmul (the vendor GEMM library) "
+                         "at uniform group sizes, as a reference (bf16 weights in the [K, N] layout)")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -883,6 +935,11 @@ def main():
                           "none": "layer has no shared expert"}[mode],
         "cpu_baseline": None,
     }
+    if args.library_reference:
+        if args.weights != "bf16" or args.layout != "kn" or cfg.dtype != "bf16":
+            print("--library-reference needs bf16 weights in the [K, N] layout", file=sys.stderr)
+            sys.exit(2)
+        result["library_reference"] = library_reference(cfg, layer, counts, evict, dev)
     rc = 0
     if not args.no_cpu_baseline:
         S = min(args.cpu_sample or default_cpu_sample(cfg, args.weights == "mxfp8"), cfg.T)
