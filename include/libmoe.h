@@ -72,7 +72,9 @@ typedef enum moe_tile_config {
   MOE_TILE_256x256 = 3,   /* pipelined: 256 x 256 x 64, 8 waves (groups of >= 512 rows on average) */
   MOE_TILE_128x256 = 4,   /* pipelined: 128 x 256 x 32, 8 waves, two workgroups per CU (193..511 rows) */
   MOE_TILE_32x128 = 5,    /* pipelined: 32 x 128 x 64 with split-K waves (groups of <= 32 rows on average) */
-  MOE_TILE_128x512 = 6    /* pipelined: 128 x 512 x 32, 3-stage ring, 8 waves (weight-streaming groups, <= 192 rows) */
+  MOE_TILE_128x512 = 6,   /* pipelined: 128 x 512 x 32, 3-stage ring, 8 waves (weight-streaming groups, <= 192 rows) */
+  MOE_TILE_32x64 = 7      /* pipelined: 32 x 64 x 64 with split-K waves, two workgroups per CU (fc2 at decode sizes whose
+                             32 x 128 tiles would leave CUs idle) */
 } moe_tile_config;
 
 /* Stage of a call, in the stage vocabulary of the PLENA pages (PLENA_Compiler

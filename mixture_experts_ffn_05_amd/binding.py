@@ -416,7 +416,7 @@ def moe_grouped_fc2_and_shared_mx8(act, expert_offsets, w2q, w2s, y_rows, act_sh
 
 
 (MOE_TILE_F32, MOE_TILE_GENERIC, MOE_TILE_128x128, MOE_TILE_256x256, MOE_TILE_128x256, MOE_TILE_32x128,
- MOE_TILE_128x512) = range(7)
+ MOE_TILE_128x512, MOE_TILE_32x64) = range(8)
 
 
 def moe_grouped_gemm_tile(dtype, call, R, H, E, I, T=0, I_s=0) -> int:

@@ -1761,6 +1761,7 @@ typedef PipeCfg<256, 256, 64, 2, 2, 4> CfgDense;    // 8 waves (2 x 4, 128 x 64 
 typedef PipeCfg<128, 256, 32, 2, 2, 4> CfgMid;      // 8 waves, 48 KiB ring: two workgroups per CU
 typedef PipeCfg<128, 512, 32, 3, 1, 8> CfgWide;     // 8 waves (1 x 8, 128 x 64 each), 120 KiB 3-stage ring
 typedef PipeCfg<32, 128, 64, 4, 1, 2, 2> CfgDecode; // 4 waves (2 column positions x 2 split-K waves)
+typedef PipeCfg<32, 64, 64, 4, 1, 1, 2> CfgDecodeNarrow;  // 2 waves (split-K), two workgroups per CU
 
 // Calls f(Cfg{}) for a pipelined configuration.
 template <class F>
@@ -1770,6 +1771,7 @@ hipError_t with_cfg(int v, F&& f) {
     case MOE_TILE_128x256: return f(CfgMid{});
     case MOE_TILE_128x512: return f(CfgWide{});
     case MOE_TILE_32x128: return f(CfgDecode{});
+    case MOE_TILE_32x64: return f(CfgDecodeNarrow{});
     default: return f(CfgSmall{});
   }
 }
@@ -1822,9 +1824,25 @@ constexpr int64_t kDecodeRows = 32;
 // and loses to the mid-size tile at 273 (Qwen2-shaped: 0.29 vs 0.42 ms).
 constexpr int64_t kWideRows = 192;
 
+// Decode sizes whose 32 x 128 tiles (routed, plus the shared expert's in a
+// fused launch) would leave CUs idle take the 32 x 64 tile, which doubles the
+// tiles streaming the weights: measured on MI355X, the DeepSeek-V2-Lite-shaped
+// fc2 at one token (112 tiles of 32 x 128 for 256 CUs) 26.1 -> 20.5 us.  Not
+// for fc1: its paired gate/up columns would be fetched in 64-byte pieces
+// (24.9 -> 35 us measured), and not once the 32 x 128 tiles fill the CUs
+// (T = 64: 3-5% slower).
+bool decode_narrow(bool paired_epi, const GemmParams<bf16_t>& p, int shared_rows, int shared_n, int cu_count) {
+  if (paired_epi) return false;
+  const int64_t active = p.groups < p.rows ? p.groups : p.rows;
+  int64_t tiles = active * ((p.N + 127) / 128);
+  if (shared_rows > 0) tiles += (int64_t)((shared_rows + 31) / 32) * ((shared_n + 127) / 128);
+  return tiles < cu_count;
+}
+
 template <int EPI, int ROLE>
 int pick_pipe_variant(const GemmParams<bf16_t>& p, int cu_count) {
-  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0) return MOE_TILE_32x128;
+  if (rows_per_active_group(p) <= kDecodeRows && p.K % 128 == 0)
+    return decode_narrow(paired(EPI), p, 0, 0, cu_count) ? MOE_TILE_32x64 : MOE_TILE_32x128;
   const int64_t rows_per_group = (int64_t)p.rows / (p.groups > 0 ? p.groups : 1);
   if (rows_per_group >= 512)
     return slot_fill<EPI, CfgDense>(p, cu_count) + 0.25 < slot_fill<EPI, CfgSmall>(p, cu_count) ? MOE_TILE_128x128
@@ -1855,18 +1873,18 @@ hipError_t launch_fused(GemmParams<bf16_t> pr, GemmParams<bf16_t> ps, int cu_cou
 
 constexpr int kFusedDenseSharedRows = 512;
 
-int pick_fused_variant(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps) {
+int pick_fused_variant(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, bool paired_epi, int cu_count) {
   const int64_t per_group = (int64_t)pr.rows / (pr.groups > 0 ? pr.groups : 1);
   if (per_group >= 512 && ps.rows >= 512) return MOE_TILE_256x256;
   if (rows_per_active_group(pr) <= kDecodeRows && ps.rows <= 2 * kDecodeRows && pr.K % 128 == 0 && ps.K % 128 == 0)
-    return MOE_TILE_32x128;
+    return decode_narrow(paired_epi, pr, ps.rows, ps.N, cu_count) ? MOE_TILE_32x64 : MOE_TILE_32x128;
   return rows_per_active_group(pr) <= kWideRows ? MOE_TILE_128x512 : MOE_TILE_128x256;
 }
 
 template <int EPI_R, int EPI_S>
 hipError_t launch_fused_bf16(const GemmParams<bf16_t>& pr, const GemmParams<bf16_t>& ps, int cu_count,
                              hipStream_t s) {
-  const int v = pick_fused_variant(pr, ps);
+  const int v = pick_fused_variant(pr, ps, paired(EPI_R), cu_count);
   // The weight-streaming routed tile runs the shared expert's fc2 with the
   // dense tile when the shared expert has rows enough to fill it.  Its fc1
   // (SwiGLU) keeps the weight-streaming tile for both: measured on MI355X,
@@ -1986,7 +2004,7 @@ int tile_config(int dt, int call, int R, int H, int E, int I, int T, int I_s, in
     ps.groups = 1;
     ps.K = call == 0 ? H : I_s;
     ps.N = call == 0 ? I_s : H;
-    return pick_fused_variant(p, ps);
+    return pick_fused_variant(p, ps, call == 0, cu_count);
   }
   if (p.K % 64 != 0) return MOE_TILE_GENERIC;
   return call == 0 ? pick_pipe_variant<kSwiGLU, 0>(p, cu_count) : pick_pipe_variant<kStoreF32, 0>(p, cu_count);

@@ -284,9 +284,10 @@ def test_tile_configuration_choices():
 
     for cfg in CASES:
         assert tiles_of(cfg) == EXPECTED_TILES[cfg.name], cfg.name
-    D, M, DEC, W = B.MOE_TILE_256x256, B.MOE_TILE_128x256, B.MOE_TILE_32x128, B.MOE_TILE_128x512
+    D, M, DEC, W, N = (B.MOE_TILE_256x256, B.MOE_TILE_128x256, B.MOE_TILE_32x128, B.MOE_TILE_128x512,
+                       B.MOE_TILE_32x64)
     bench = {"scout": (W, W, W, W), "qwen2": (M, M, M, M), "v2l": (D, D, D, D), "v3": (W, W, W, W),
-             "v2l_decode1": (DEC,) * 4, "v2l_decode16": (DEC,) * 4, "v2l_decode64": (DEC,) * 4,
+             "v2l_decode1": (DEC, N, DEC, N), "v2l_decode16": (DEC,) * 4, "v2l_decode64": (DEC,) * 4,
              "v3_decode64": (DEC,) * 4}
     for name, want in bench.items():
         assert tiles_of(wl.WORKLOADS[name]) == want, name

@@ -20,7 +20,10 @@ CASES = [
     wl.TINY,
     wl.LayerConfig("ragged_bf16", "bf16", T=300, H=264, E=7, top_k=2, I=200),
     wl.LayerConfig("gated_bf16", "bf16", T=517, H=512, E=16, top_k=4, I=136, I_s=96, gated=True),
+    # one token: fc2's 32x128 tiles would leave CUs idle, so fc2 takes the 32x64 tile
     wl.LayerConfig("decode1_bf16", "bf16", T=1, H=256, E=64, top_k=6, I=128, I_s=128),
+    # 16 tokens with enough fc2 columns to fill the CUs with 32x128 tiles
+    wl.LayerConfig("decode16_bf16", "bf16", T=16, H=1024, E=64, top_k=6, I=128, I_s=128),
     wl.LayerConfig("wide_bf16", "bf16", T=96, H=384, E=256, top_k=8, I=64, I_s=64),
     wl.LayerConfig("ragged_f32", "f32", T=77, H=136, E=5, top_k=3, I=40, I_s=24, gated=True, fan_in_init=True),
     # groups of >= 512 rows take the 256x256 tile configuration (routed and shared)
@@ -47,13 +50,14 @@ CASES = [
 # *_and_shared calls where the case has a shared expert.  Asserted below, so a
 # change of the selection cannot silently move a case off the configuration it
 # exists to cover.
-_G, _S, _D, _M, _DEC, _F, _W = (B.MOE_TILE_GENERIC, B.MOE_TILE_128x128, B.MOE_TILE_256x256, B.MOE_TILE_128x256,
-                                B.MOE_TILE_32x128, B.MOE_TILE_F32, B.MOE_TILE_128x512)
+_G, _S, _D, _M, _DEC, _F, _W, _N = (B.MOE_TILE_GENERIC, B.MOE_TILE_128x128, B.MOE_TILE_256x256, B.MOE_TILE_128x256,
+                                    B.MOE_TILE_32x128, B.MOE_TILE_F32, B.MOE_TILE_128x512, B.MOE_TILE_32x64)
 EXPECTED_TILES = {
     "tiny": (_F, _F, None, None),
     "ragged_bf16": (_G, _G, None, None),
     "gated_bf16": (_W, _G, _W, _G),
-    "decode1_bf16": (_DEC, _DEC, _DEC, _DEC),
+    "decode1_bf16": (_DEC, _N, _DEC, _N),
+    "decode16_bf16": (_DEC, _DEC, _DEC, _DEC),
     "wide_bf16": (_DEC, _W, _W, _W),
     "ragged_f32": (_F, _F, _F, _F),
     "big_groups_bf16": (_D, _D, _D, _D),
