@@ -25,6 +25,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -87,30 +89,91 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restri
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = kbeg; k < kend; k += 128) {
-    u32x4 a[MB][4], b[4][4];
+  // Steps of 64 k.  Full steps load unconditionally (a row past T reads row 0
+  // and a column block past E_pad reads the last router row; neither result
+  // is stored), so the only wait before a step's MFMAs is for that step's own
+  // loads; the last, partial step masks k past the slice end with zeros.  The
+  // MFMAs run in k order in every form below.
+  struct Step {
+    u32x4 a[MB][2], b[2][4];
+  };
+  auto load = [&](Step& st, int k, auto masked) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int kk = k + 32 * u + koff;
       const bool k_ok = kk < kend;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        a[mb][u] = (row_ok[mb] && k_ok) ? *(const u32x4*)(xr[mb] + kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (decltype(masked)::value)
+          st.a[mb][u] = (row_ok[mb] && k_ok) ? *(const u32x4*)(xr[mb] + kk) : u32x4{0u, 0u, 0u, 0u};
+        else
+          st.a[mb][u] = *(const u32x4*)(xr[mb] + kk);
+      }
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int e = e0 + nb * 16 + (lane & 15);
-        b[u][nb] = (k_ok && nb < nblk) ? *(const u32x4*)(wt + (int64_t)e * H + kk) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (decltype(masked)::value)
+          st.b[u][nb] = (k_ok && nb < nblk) ? *(const u32x4*)(wt + (int64_t)e * H + kk) : u32x4{0u, 0u, 0u, 0u};
+        else
+          st.b[u][nb] = *(const u32x4*)(wt + (int64_t)min(e, E_pad - 1) * H + kk);
       }
     }
+  };
+  auto mfmas = [&](const Step& st) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][u]),
-                                                                __builtin_bit_cast(bf16x8, b[u][nb]), acc[mb][nb],
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.a[mb][u]),
+                                                                __builtin_bit_cast(bf16x8, st.b[u][nb]), acc[mb][nb],
                                                                 0, 0, 0);
+  };
+  const int nfull = kend > kbeg ? (kend - kbeg) / 64 : 0;
+  Step s0;
+  if constexpr (MB == 1) {
+    // One row block: two register sets in turn, so one step's loads are in flight while the
+    // other set's MFMAs run.  The loop's loads are unconditional (the last one or two steps
+    // are peeled off), so the waits before each MFMA group cover only the older set; the
+    // scheduling barriers keep each phase where it is written.  With four row blocks a second
+    // set would halve the waves each SIMD holds, and those waves hide the load latency better.
+    Step s1;
+    if (nfull > 0) {
+      load(s0, kbeg, std::false_type{});
+      int i = 0;
+      for (; i + 3 <= nfull; i += 2) {
+        load(s1, kbeg + 64 * (i + 1), std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(s0, kbeg + 64 * (i + 2), std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i + 2 == nfull) {
+        load(s1, kbeg + 64 * (i + 1), std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s1);
+      } else {
+        mfmas(s0);
+      }
+    }
+  } else {
+    for (int i = 0; i < nfull; ++i) {
+      load(s0, kbeg + 64 * i, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);   // all of the step's loads in flight before the first wait
+      mfmas(s0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const int ktail = kbeg + 64 * nfull;
+  if (ktail < kend) {
+    load(s0, ktail, std::true_type{});
+    mfmas(s0);
   }
   // 16x16 accumulator layout: row = 4*(lane/16) + r, column = lane%16.
 #pragma unroll
