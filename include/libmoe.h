@@ -131,9 +131,9 @@ int moe_version(void);
  * topk_ids [T, top_k] int32 out, topk_weights [T, top_k] fp32 out,
  * logits [T, E] fp32 out (required): the logits exactly as top-k saw them.
  * workspace: device scratch of at least moe_route_workspace_bytes(dt, T, H, E)
- * bytes (it receives the router weight transposed to [E rounded up to 16, H]
- * and partial sums over slices of H; may be NULL when that size is 0),
- * contents undefined on entry and exit.
+ * bytes (it receives partial sums over slices of H and, for an odd E, a copy
+ * of the router weight with a zero column appended; may be NULL when that size
+ * is 0), contents undefined on entry and exit.
  */
 moe_status moe_route(moe_dtype dt, const void* x, const void* w_router, const float* logit_bias,
                      int32_t T, int32_t H, int32_t E, int32_t top_k,

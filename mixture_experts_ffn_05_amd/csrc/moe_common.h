@@ -112,6 +112,37 @@ __device__ __forceinline__ float sum_slices(const float* __restrict__ p, int64_t
   return v;
 }
 
+// ---- LDS rings fed by direct loads (global_load_lds: HBM -> LDS, no register round trip) ----
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define MOE_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+#define MOE_GLOBAL(T, ptr) ((const __attribute__((address_space(1))) T*)(ptr))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for an LDS ring.  __syncthreads() (and a fence on LDS
+// alone) makes the compiler wait for every outstanding direct load first --
+// they count as vector-memory operations -- which would drain the ring.  The
+// ring's loads are waited for explicitly with wait_vmcnt before this barrier;
+// the "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The 8 consecutive-k bf16 values of an MFMA B fragment from two
+// ds_read_b64_tr_b16 reads (k 0-3 and k 4-7).
+__device__ __forceinline__ u32x4 pack_tr_pair(i16x4 lo, i16x4 hi) {
+  return u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+}
+
 }  // namespace moe
 
 // Host-side launchers implemented in the kernel translation units.  Each

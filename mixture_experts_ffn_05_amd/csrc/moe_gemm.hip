@@ -389,10 +389,6 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_generic(GemmPar
 // ------------------------------------------------------------------------------------------
 // Pipelined bf16 path
 // ------------------------------------------------------------------------------------------
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-#define MOE_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
-#define MOE_GLOBAL(T, ptr) ((const __attribute__((address_space(1))) T*)(ptr))
-
 // Cache policy of the direct loads of expert weights for a group that fits in
 // one row tile: non-temporal (the nt bit of the instruction's cache-policy
 // field).  Each of those weight bytes is read once per call, so keeping it out
@@ -406,22 +402,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // chosen per tile.  Activation loads keep the default policy (non-temporal
 // activations measured 13% slower: every column tile re-reads them).
 constexpr int kWeightLoadPolicy = 2;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the LDS ring.  __syncthreads() (and a fence on LDS
-// alone) makes the compiler wait for every outstanding direct load first --
-// they count as vector-memory operations -- which would drain the ring.  The
-// ring's loads are waited for explicitly with wait_vmcnt before this barrier;
-// the "memory" clobber keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Shape of one pipelined configuration: workgroup tile BM x BN (staged weight
 // columns), reduction slice BK, STAGES-deep LDS ring; WM x WN x KW waves.
@@ -552,10 +532,7 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
       const unsigned char* ptr = Bs + row * (2 * C::BN) + chunk * 16 + b_byte;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * (2 * C::BN)));
-      bfr[nb] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      bfr[nb] = pack_tr_pair(lo, hi);
     }
   };
   // This wave's substeps are kw, kw+KW, ...; the fragments of the next one
@@ -765,10 +742,7 @@ __device__ __forceinline__ void pipe_read(const unsigned char* __restrict__ rst,
       const unsigned char* ptr = Bs + row * (2 * C::BN) + chunk * 16 + (s16 & 1) * 8;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * (2 * C::BN)));
-      f.b[nb] = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                      (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                      (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                      (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      f.b[nb] = pack_tr_pair(lo, hi);
     }
   }
 }
@@ -1391,10 +1365,7 @@ __device__ __forceinline__ u32x4 kn_frag(const unsigned char* __restrict__ tile,
   const unsigned char* ptr = tile + row * (16 * CHUNKS) + chunk * 16 + (s16 & 1) * 8;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, ptr + 4 * 16 * CHUNKS));
-  return u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-               (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-               (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-               (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+  return pack_tr_pair(lo, hi);
 }
 
 template <class C>

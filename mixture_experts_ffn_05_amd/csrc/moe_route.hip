@@ -8,12 +8,13 @@
 //   router_logits_valu     up to 16 tokens (bf16, E a multiple of 8): x @ W_r on the
 //                          vector ALUs straight from W_r's [H,E] layout, H split
 //                          across workgroups; partial sums land in the workspace.
-//   router_transpose_bf16  W_r [H,E] -> [E_pad,H] in the caller's workspace, so that
-//                          both operands of the router product are K-contiguous.
-//   router_logits_mfma     x[T,H] @ W_r on MFMA (16x16x32 bf16, fp32 accumulate),
-//                          16 (or 64 for T >= 256) tokens x 64 experts per workgroup, H split across
-//                          workgroups (grid.z) and across each workgroup's 4 waves;
-//                          partial sums land in the workspace.
+//   router_pad_bf16        odd E only: W_r [H,E] -> [H,E+1] with a zero column in the
+//                          caller's workspace (the ring kernel loads W_r 4 bytes a lane).
+//   router_logits_ring     x[T,H] @ W_r on MFMA (16x16x32 bf16, fp32 accumulate) from
+//                          W_r's own [H,E] layout: 64 tokens x 64 experts per
+//                          workgroup, both operands streamed through an LDS ring by
+//                          direct loads, H split across workgroups; partial sums
+//                          land in the workspace.
 //   route_logits_f32       the same product for float32 inputs, one thread per logit.
 //   topk_softmax           one wave64 per token: adds the partial sums in a fixed
 //                          order (+ bias) into the logits, then topk_wave: k rounds
@@ -30,166 +31,175 @@
 namespace moe {
 namespace {
 
-constexpr int kRtTok = 16;   // tokens per MFMA row block
-constexpr int kRtExp = 64;   // experts per workgroup (4 MFMA column blocks of 16)
+constexpr int kRtExp = 64;    // experts per workgroup tile
+constexpr int kRtBK = 64;     // k per ring step
+constexpr int kRtStages = 4;  // ring depth: three steps in flight while one is multiplied
 
 int padded_experts(int E) { return (E + 15) / 16 * 16; }
+// The ring kernel reads W_r with 4-byte loads, so an odd E first gets a zero column.
+int ring_experts(int E) { return (E + 1) & ~1; }
 
-// W_r [H, E] (E contiguous) -> wt [E_pad, H] (H contiguous), zero rows for e >= E.
-__global__ __launch_bounds__(256) void router_transpose_bf16(const bf16_t* __restrict__ w, int H, int E, int E_pad,
-                                                             bf16_t* __restrict__ wt) {
-  __shared__ bf16_t tile[64][65];
-  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int hh = i >> 6, ee = i & 63;
-    const int h = h0 + hh, e = e0 + ee;
-    tile[hh][ee] = (h < H && e < E) ? w[(int64_t)h * E + e] : (bf16_t)0;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ee = i >> 6, hh = i & 63;
-    const int h = h0 + hh, e = e0 + ee;
-    if (h < H && e < E_pad) wt[(int64_t)e * H + h] = tile[hh][ee];
-  }
+// W_r [H, E] -> [H, E + 1] with a zero last column (odd E only).
+__global__ __launch_bounds__(256) void router_pad_bf16(const bf16_t* __restrict__ w, int H, int E,
+                                                       bf16_t* __restrict__ wp) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int Ep = E + 1;
+  if (i >= (int64_t)H * Ep) return;
+  const int64_t h = i / Ep;
+  const int e = (int)(i - h * Ep);
+  wp[i] = e < E ? w[h * E + e] : (bf16_t)0;
 }
 
-// Partial logits over one slice of H for 16*MB tokens x 64 experts per
-// workgroup.  Both MFMA operands are K-contiguous (x rows and the transposed
-// router rows), so each lane loads its 16x16x32 fragments straight from global
-// memory, four k-substeps (128 k) at a time so that many loads are in flight;
-// each router fragment feeds the MB 16-token row blocks (MB = 4 for many tokens
-// cuts the router-row traffic per MFMA by 2.5x; the product is bound by those
-// loads).  The 4 waves split the workgroup's slice; their sums are added in a
-// fixed order through LDS.  grid.z splits H into `ksplit` slices;
-// partial[z][t][e] is summed over z in a fixed order by topk_softmax, so the
-// result does not depend on scheduling.
-template <int MB>
-__global__ __launch_bounds__(256) void router_logits_mfma(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ wt, int T, int H, int E_pad,
-                                                          int kslice, float* __restrict__ partial) {
-  constexpr int kTok = 16 * MB;
-  __shared__ float red[4][kTok][kRtExp + 1];
+// Swizzle of a 128-byte W_r row in LDS: the 32-byte slot (16 experts) s of row
+// r sits at slot s ^ rt_wslot(r).  A transposing B-fragment read covers 4 rows
+// x 16 experts per 16 lanes, and a half-wave the rows {0-3, 8-11} (+4, +16,
+// +32) of one slot; with bit 1 and bit 3 of the row in the slot, those 8 rows
+// land in 8 different 32-byte bank windows.
+__device__ __forceinline__ int rt_wslot(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
+
+// Partial router logits over one slice of H for a tile of BM tokens x 64
+// experts, from x [T, H] and W_r in its own [H, E] layout (E even).
+//
+// The slice streams through an LDS ring of kRtStages steps of 64 k, filled
+// with direct loads (HBM -> LDS, no register round trip), so three steps'
+// loads are in flight while one step is multiplied:
+//  * x rows as 128-byte LDS rows, the 16-byte chunk c of row m at chunk
+//    c ^ ((m >> 1) & 7): an A-fragment read (one chunk of 16 consecutive rows)
+//    is then conflict-free;
+//  * W_r rows (E-contiguous) as 128-byte LDS rows of 64 experts, swizzled by
+//    rt_wslot, loaded 4 bytes a lane (E need only be even).  A B fragment (8
+//    consecutive k of one expert) is assembled from two ds_read_b64_tr_b16
+//    reads: within each 16-lane group, lane c receives element c % 4 of the
+//    8-byte rows read by lanes c/4, c/4 + 4, c/4 + 8 and c/4 + 12, so lanes that
+//    read a 4 (k) x 16 (expert) block get 4 consecutive k of their own expert.
+// 4 waves in a 2x2 arrangement each own (BM/2) x 32 outputs as 16x16 blocks
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulate in k order).  Rows past T and
+// experts past E are fetched from clamped addresses and feed only outputs
+// that are never stored or read; k past H (the last slice of an H that is not
+// a multiple of 64) is zeroed in LDS.  partial[z][t][e] is summed over z in a
+// fixed order by topk_softmax, so the logits do not depend on scheduling.
+//
+// The grid is 1-D.  Workgroups are dealt to the 8 XCDs in turn, so the id is
+// remapped: the expert tiles of one (token tile, slice) pair are consecutive
+// workgroups of one XCD and share the x tile through its L2.  Ids past the last
+// pair (the grid is padded to a multiple of 8 pairs) exit at once.
+template <int BM>
+__global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ w, int T, int H, int E,
+                                                          int E_pad, int kslice, int n_t, int n_e, int nz,
+                                                          float* __restrict__ partial) {
+  constexpr int S = kRtStages, BK = kRtBK;
+  constexpr int kXStage = BM * BK * 2, kWStage = BK * kRtExp * 2, kStage = kXStage + kWStage;
+  constexpr int kXLoads = kXStage / 1024 / 4;  // 16-byte loads (1 KiB per wave) per wave and step
+  constexpr int kWLoads = kWStage / 256 / 4;   // 4-byte loads (256 B per wave) per wave and step
+  constexpr int kLoads = kXLoads + kWLoads;
+  constexpr int MB = BM / 32;                  // 16-row blocks per wave
+  static_assert(kXLoads >= 1 && (S - 2) * kLoads < 64, "ring shape");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[S * kStage];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * kTok, e0 = blockIdx.y * kRtExp;
-  const int nblk = min(4, (E_pad - e0) / 16);
-  const int zbeg = blockIdx.z * kslice, zend = min(H, zbeg + kslice);
-  const int kq = ((kslice + 127) / 128) * 32;   // per-wave share of the slice, a multiple of 32
-  const int kbeg = zbeg + wave * kq, kend = min(zend, kbeg + kq);
-  const int koff = (lane >> 4) * 8;
-  const bf16_t* xr[MB];
-  bool row_ok[MB];
+  const int slot = (int)(blockIdx.x >> 3);
+  const int pair = (slot / n_e) * 8 + (int)(blockIdx.x & 7);
+  if (pair >= n_t * nz) return;  // whole workgroup, before any barrier
+  const int zb = pair / n_t;
+  const int t0 = (pair - zb * n_t) * BM, e0 = (slot % n_e) * kRtExp;
+  const int kbeg = zb * kslice, kend = min(H, kbeg + kslice);
+  const int nsteps = (kend - kbeg + BK - 1) / BK;
+
+  // Per-lane sources of the direct loads (fixed over the slice but for k).
+  int64_t xsrc[kXLoads];
+  int xk[kXLoads];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int row = t0 + 16 * mb + (lane & 15);
-    row_ok[mb] = row < T;
-    xr[mb] = x + (int64_t)(row_ok[mb] ? row : 0) * H;
+  for (int j = 0; j < kXLoads; ++j) {
+    const int m = (wave * kXLoads + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((m >> 1) & 7);
+    xsrc[j] = (int64_t)min(t0 + m, T - 1) * H;
+    xk[j] = 8 * c;
   }
-  f32x4 acc[MB][4];
+  int wrow[kWLoads];
+  int wcol[kWLoads];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int j = 0; j < kWLoads; ++j) {
+    const int r = (wave * kWLoads + j) * 2 + (lane >> 5);
+    const int d = lane & 31;
+    wrow[j] = r;
+    wcol[j] = min(e0 + 16 * ((d >> 3) ^ rt_wslot(r)) + 2 * (d & 7), E - 2);
+  }
+  auto issue = [&](int step) {
+    unsigned char* st = ring + (step % S) * kStage;
+    const int k0 = kbeg + step * BK;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Steps of 64 k.  Full steps load unconditionally (a row past T reads row 0
-  // and a column block past E_pad reads the last router row; neither result
-  // is stored), so the only wait before a step's MFMAs is for that step's own
-  // loads; the last, partial step masks k past the slice end with zeros.  The
-  // MFMAs run in k order in every form below.
-  struct Step {
-    u32x4 a[MB][2], b[2][4];
+    for (int j = 0; j < kXLoads; ++j)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, x + xsrc[j] + min(k0 + xk[j], H - 8)),
+                                       MOE_LDS(void, st + (wave * kXLoads + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kWLoads; ++j)
+      __builtin_amdgcn_global_load_lds(MOE_GLOBAL(void, w + (int64_t)min(k0 + wrow[j], H - 1) * E + wcol[j]),
+                                       MOE_LDS(void, st + kXStage + (wave * kWLoads + j) * 256), 4, 0, 0);
   };
-  auto load = [&](Step& st, int k, auto masked) {
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4, s16 = lane & 15;
+  f32x4 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < S - 1 && s < nsteps; ++s) issue(s);
+  for (int kt = 0; kt < nsteps; ++kt) {
+    if (nsteps - 1 - kt >= S - 2) wait_vmcnt<(S - 2) * kLoads>(); else wait_vmcnt<0>();
+    lds_barrier();
+    unsigned char* st = ring + (kt % S) * kStage;
+    const int kvalid = kend - (kbeg + kt * BK);
+    if (kvalid < BK) {  // the last step of a ragged H: zero k >= H in both operands
+      for (int i = tid; i < BM * 8; i += 256) {
+        const int m = i >> 3, c = i & 7;
+        if (8 * c >= kvalid) *(u32x4*)(st + m * 128 + 16 * (c ^ ((m >> 1) & 7))) = u32x4{0u, 0u, 0u, 0u};
+      }
+      for (int i = tid; i < (BK - kvalid) * 8; i += 256)
+        *(u32x4*)(st + kXStage + (kvalid + (i >> 3)) * 128 + 16 * (i & 7)) = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier();
+    }
+    if (kt + S - 1 < nsteps) issue(kt + S - 1);  // refills the stage every wave finished with in step kt - 1
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int kk = k + 32 * u + koff;
-      const bool k_ok = kk < kend;
+      u32x4 a[MB], b[2];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (decltype(masked)::value)
-          st.a[mb][u] = (row_ok[mb] && k_ok) ? *(const u32x4*)(xr[mb] + kk) : u32x4{0u, 0u, 0u, 0u};
-        else
-          st.a[mb][u] = *(const u32x4*)(xr[mb] + kk);
+        const int m = wm * (BM / 2) + 16 * mb + s16;
+        const int c = 4 * u + g;
+        a[mb] = *(const u32x4*)(st + m * 128 + 16 * (c ^ ((m >> 1) & 7)));
       }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int e = e0 + nb * 16 + (lane & 15);
-        if constexpr (decltype(masked)::value)
-          st.b[u][nb] = (k_ok && nb < nblk) ? *(const u32x4*)(wt + (int64_t)e * H + kk) : u32x4{0u, 0u, 0u, 0u};
-        else
-          st.b[u][nb] = *(const u32x4*)(wt + (int64_t)min(e, E_pad - 1) * H + kk);
+      for (int nb = 0; nb < 2; ++nb) {
+        const int r = 32 * u + 8 * g + (s16 >> 2);
+        const int sl = 2 * wn + nb;
+        const unsigned char* p_lo = st + kXStage + r * 128 + 32 * (sl ^ rt_wslot(r)) + 8 * (s16 & 3);
+        const unsigned char* p_hi = st + kXStage + (r + 4) * 128 + 32 * (sl ^ rt_wslot(r + 4)) + 8 * (s16 & 3);
+        b[nb] = pack_tr_pair(__builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, p_lo)),
+                             __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, p_hi)));
       }
-    }
-  };
-  auto mfmas = [&](const Step& st) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.a[mb][u]),
-                                                                __builtin_bit_cast(bf16x8, st.b[u][nb]), acc[mb][nb],
-                                                                0, 0, 0);
-  };
-  const int nfull = kend > kbeg ? (kend - kbeg) / 64 : 0;
-  Step s0;
-  if constexpr (MB == 1) {
-    // One row block: two register sets in turn, so one step's loads are in flight while the
-    // other set's MFMAs run.  The loop's loads are unconditional (the last one or two steps
-    // are peeled off), so the waits before each MFMA group cover only the older set; the
-    // scheduling barriers keep each phase where it is written.  With four row blocks a second
-    // set would halve the waves each SIMD holds, and those waves hide the load latency better.
-    Step s1;
-    if (nfull > 0) {
-      load(s0, kbeg, std::false_type{});
-      int i = 0;
-      for (; i + 3 <= nfull; i += 2) {
-        load(s1, kbeg + 64 * (i + 1), std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(s0);
-        __builtin_amdgcn_sched_barrier(0);
-        load(s0, kbeg + 64 * (i + 2), std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(s1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (i + 2 == nfull) {
-        load(s1, kbeg + 64 * (i + 1), std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(s0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(s1);
-      } else {
-        mfmas(s0);
-      }
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb]),
+                                                                __builtin_bit_cast(bf16x8, b[nb]), acc[mb][nb], 0,
+                                                                0, 0);
     }
-  } else {
-    for (int i = 0; i < nfull; ++i) {
-      load(s0, kbeg + 64 * i, std::false_type{});
-      __builtin_amdgcn_sched_barrier(0);   // all of the step's loads in flight before the first wait
-      mfmas(s0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  const int ktail = kbeg + 64 * nfull;
-  if (ktail < kend) {
-    load(s0, ktail, std::true_type{});
-    mfmas(s0);
   }
   // 16x16 accumulator layout: row = 4*(lane/16) + r, column = lane%16.
+  float* out = partial + (int64_t)zb * T * E_pad;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      const int e = e0 + 32 * wn + 16 * nb + s16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][16 * mb + 4 * (lane >> 4) + r][nb * 16 + (lane & 15)] = acc[mb][nb][r];
-  __syncthreads();
-  float* out = partial + (int64_t)blockIdx.z * T * E_pad;
-  for (int i = tid; i < kTok * kRtExp; i += 256) {
-    const int tt = i / kRtExp, ee = i % kRtExp;
-    const int t = t0 + tt, e = e0 + ee;
-    if (t < T && e < E_pad)
-      out[(int64_t)t * E_pad + e] = ((red[0][tt][ee] + red[1][tt][ee]) + red[2][tt][ee]) + red[3][tt][ee];
-  }
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wm * (BM / 2) + 16 * mb + 4 * g + r;
+        if (t < T && e < E_pad) out[(int64_t)t * E_pad + e] = acc[mb][nb][r];
+      }
+    }
 }
 
 __global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict__ x,
@@ -340,32 +350,34 @@ Split router_valu_split(int T, int H) {
   return Split{(H + kslice - 1) / kslice, kslice};
 }
 
-// Tokens per workgroup of the MFMA router: 64 (four 16-token row blocks per
-// router fragment) once there are enough tokens to fill the grid, else 16.
-int router_mfma_tokens(int T) { return T >= 256 ? 4 * moe::kRtTok : moe::kRtTok; }
+// Tokens per workgroup tile of the ring router.
+int router_ring_tokens(int T) { (void)T; return 64; }
 
-// MFMA router: slices of H (multiples of 128) so that the grid covers about
-// 512 workgroups.
-Split router_mfma_split(int T, int H, int E) {
+// Ring router: slices of H (multiples of 64, at least two steps each) so that the grid covers about
+// 512 workgroups -- two per CU, the most the ring's LDS allows -- with at most 32 slices.
+Split router_ring_split(int T, int H, int E) {
   using namespace moe;
-  const int tok = router_mfma_tokens(T);
-  const int tiles = ((T + tok - 1) / tok) * ((padded_experts(E) + kRtExp - 1) / kRtExp);
-  int ks = (512 + tiles - 1) / tiles;
-  const int max_ks = (H + 127) / 128;
-  if (ks > max_ks) ks = max_ks;
-  if (ks < 1) ks = 1;
-  const int kslice = ((H + ks - 1) / ks + 127) / 128 * 128;
+  const int bm = router_ring_tokens(T);
+  const int tiles = ((T + bm - 1) / bm) * ((ring_experts(E) + kRtExp - 1) / kRtExp);
+  int nz = (512 + tiles - 1) / tiles;
+  int max_nz = H / (2 * kRtBK);
+  if (max_nz > 32) max_nz = 32;
+  if (nz > max_nz) nz = max_nz;
+  if (nz < 1) nz = 1;
+  const int kslice = ((H + nz - 1) / nz + kRtBK - 1) / kRtBK * kRtBK;
   return Split{(H + kslice - 1) / kslice, kslice};
 }
 
-size_t wt_bytes(int H, int E) {
-  return ((size_t)moe::padded_experts(E) * H * sizeof(moe::bf16_t) + 255) & ~(size_t)255;
+// Bytes of the zero-padded router copy an odd E needs (none for an even E).
+size_t pad_bytes(int H, int E) {
+  if (moe::ring_experts(E) == E) return 0;
+  return ((size_t)H * moe::ring_experts(E) * sizeof(moe::bf16_t) + 255) & ~(size_t)255;
 }
 
 size_t route_workspace_bytes(int dt, int T, int H, int E) {
   if (dt != 1) return 0;
   if (router_small(dt, T, E)) return (size_t)router_valu_split(T, H).nz * T * E * sizeof(float);
-  return wt_bytes(H, E) + (size_t)router_mfma_split(T, H, E).nz * T * moe::padded_experts(E) * sizeof(float);
+  return pad_bytes(H, E) + (size_t)router_ring_split(T, H, E).nz * T * moe::padded_experts(E) * sizeof(float);
 }
 
 hipError_t route_partials_small(const void* x, const void* w_router, int T, int H, int E, void* workspace,
@@ -404,21 +416,21 @@ hipError_t route(int dt, const void* x, const void* w_router, const float* bias,
     return launch_topk((const float*)workspace, nz, E, bias, logits, T, E, top_k, ids, weights, s);
   }
   if (dt == 1) {
-    const int E_pad = padded_experts(E);
-    const Split sp = router_mfma_split(T, H, E);
-    bf16_t* wt = (bf16_t*)workspace;
-    float* partial = (float*)((char*)workspace + wt_bytes(H, E));
-    hipLaunchKernelGGL(router_transpose_bf16, dim3((H + 63) / 64, (E_pad + 63) / 64), dim3(256), 0, s,
-                       (const bf16_t*)w_router, H, E, E_pad, wt);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int tok = router_mfma_tokens(T);
-    dim3 grid((T + tok - 1) / tok, (E_pad + kRtExp - 1) / kRtExp, sp.nz);
-    if (tok == 4 * kRtTok)
-      hipLaunchKernelGGL(router_logits_mfma<4>, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
-                         E_pad, sp.kslice, partial);
-    else
-      hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, (const bf16_t*)x, (const bf16_t*)wt, T, H,
-                         E_pad, sp.kslice, partial);
+    const int E_pad = padded_experts(E), Er = ring_experts(E);
+    const bf16_t* wr = (const bf16_t*)w_router;
+    if (Er != E) {
+      hipLaunchKernelGGL(router_pad_bf16, dim3((unsigned)(((int64_t)H * Er + 255) / 256)), dim3(256), 0, s,
+                         (const bf16_t*)w_router, H, E, (bf16_t*)workspace);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      wr = (const bf16_t*)workspace;
+    }
+    float* partial = (float*)((char*)workspace + pad_bytes(H, E));
+    const Split sp = router_ring_split(T, H, E);
+    const int bm = router_ring_tokens(T);
+    const int n_t = (T + bm - 1) / bm, n_e = (Er + kRtExp - 1) / kRtExp;
+    const dim3 grid((unsigned)((n_t * sp.nz + 7) / 8 * 8 * n_e));
+    hipLaunchKernelGGL(router_logits_ring<64>, grid, dim3(256), 0, s, (const bf16_t*)x, wr, T, H, Er, E_pad,
+                       sp.kslice, n_t, n_e, sp.nz, partial);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     return launch_topk((const float*)partial, sp.nz, E_pad, bias, logits, T, E, top_k, ids, weights, s);
   }

@@ -54,7 +54,8 @@ def test_route_validation(lib):
     assert call(dt=7) == 1 and "dt must be" in _err(lib)
     assert call(logits=None) == 1 and "logits" in _err(lib)
     assert lib.moe_route_workspace_bytes(1, 4, 16, 8) >= 4 * 8 * 4                  # partial sums
-    assert lib.moe_route_workspace_bytes(1, 32, 16, 8) >= 16 * 16 * 2 + 32 * 16 * 4  # W_r^T, E rounded up to 16
+    assert lib.moe_route_workspace_bytes(1, 32, 16, 8) >= 32 * 16 * 4               # partial sums, E rounded up to 16
+    assert lib.moe_route_workspace_bytes(1, 32, 16, 7) >= 16 * 8 * 2 + 32 * 16 * 4  # + W_r with a zero column (odd E)
     assert lib.moe_route_workspace_bytes(0, 4, 16, 8) == 0
     assert call(ws=None) == 3 and "workspace needs" in _err(lib)
     assert call(ws_bytes=16) == 3
