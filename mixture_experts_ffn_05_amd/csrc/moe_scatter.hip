@@ -9,16 +9,17 @@
 // The layout is a stable counting sort of the pairs p = t*k + j by expert id,
 // computed without atomics so that it is deterministic:
 //   scatter_count  each wave64 takes a chunk of 1024 consecutive pairs and counts
-//                  them per expert.  Lanes holding the same expert are found
-//                  with ceil(log2 E) ballots; one leader per expert adds the
-//                  group's popcount to an LDS histogram.
+//                  them per expert with LDS atomic adds (integer counts do not
+//                  depend on the order of the adds).
 //   scatter_scan   one workgroup: per expert, an exclusive scan of the chunk
 //                  counts (chunk bases); across experts, an exclusive scan of the
 //                  totals (expert_offsets), the largest group and the number of
 //                  out-of-range ids.
 //   scatter_rank   each wave replays its chunk; a pair's row is its chunk base
 //                  plus offsets[e] plus the number of lower lanes with the same
-//                  expert; a running per-expert cursor lives in LDS.
+//                  expert; a running per-expert cursor lives in LDS.  Lanes
+//                  holding the same expert are found with ceil(log2 E) ballots,
+//                  for all 16 rounds of the chunk at once so that they overlap.
 //   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies (skipped when
 //                  x_scattered is NULL: the fc1 call then gathers the rows on load).
 // Up to 16 chunks (decode, and prefill up to 16384 pairs) take scatter_small,
@@ -36,16 +37,30 @@ constexpr int kChunk = 1024;              // pairs per wave
 constexpr int kIters = kChunk / kWave;    // ballot rounds per chunk
 constexpr int kWavesPerBlock = 4;
 
-// Lanes (bitmask) whose expert id equals the calling lane's.  All lanes of the
-// wave must call it; lanes with in_range == false get 0.
-__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool in_range, int nbits) {
-  uint64_t m = __ballot(in_range);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t on = __ballot(in_range && bit);
-    m &= bit ? on : ~on;
+// Lanes (bitmask) whose expert id equals the calling lane's, for every round of
+// a chunk's pairs p0 + it * 64 + lane; 0 for lanes whose pair is past R or whose
+// id is outside [0, E).  All lanes of the wave must call it.  The bit loop is
+// outermost, so the ballots of the kIters rounds do not depend on each other
+// and overlap instead of forming one long chain per round.
+__device__ __forceinline__ void chunk_masks(const int (&ev)[kIters], int64_t p0, int R, int E, int nbits, int lane,
+                                            uint64_t (&m)[kIters]) {
+  bool in_range[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    in_range[it] = p0 + it * kWave + lane < R && ev[it] >= 0 && ev[it] < E;
+    m[it] = __ballot(in_range[it]);
   }
-  return in_range ? m : 0ull;
+  for (int b = 0; b < nbits; ++b) {
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const bool bit = (ev[it] >> b) & 1;
+      const uint64_t on = __ballot(in_range[it] && bit);
+      m[it] &= bit ? on : ~on;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it)
+    if (!in_range[it]) m[it] = 0ull;
 }
 
 // The expert ids of one chunk, kIters per lane, all loads issued before any is used.
@@ -64,21 +79,24 @@ __device__ __forceinline__ void load_chunk(const int32_t* ids, int R, int c, int
 __device__ __forceinline__ void rank_chunk(const int (&ev)[kIters], int R, int E, int k, int nbits, int c, int lane,
                                            int32_t* cursor, int32_t* __restrict__ scatter_index,
                                            int32_t* __restrict__ row_token, int32_t* lds_row_token = nullptr) {
+  const int64_t p0 = (int64_t)c * kChunk;
+  uint64_t m[kIters];
+  chunk_masks(ev, p0, R, E, nbits, lane, m);
   const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
+  const uint64_t below = lanemask_lt();
+#pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    if ((int64_t)c * kChunk + it * kWave >= R) break;  // the rest of the chunk is past R
-    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
-    const bool live = p < R;
+    if (p0 + it * kWave >= R) break;  // the rest of the chunk is past R
+    const int64_t p = p0 + it * kWave + lane;
     const int e = ev[it];
-    const bool in_range = live && e >= 0 && e < E;
-    const uint64_t m = same_expert_lanes(e, in_range, nbits);
+    const bool in_range = m[it] != 0ull;  // a lane in range always finds itself
     int r = -1;
     if (in_range) {
       const int b = cursor[e];
-      r = b + __popcll(m & lanemask_lt());
-      if ((m & above) == 0ull) cursor[e] = b + __popcll(m);
+      r = b + __popcll(m[it] & below);
+      if ((m[it] & above) == 0ull) cursor[e] = b + __popcll(m[it]);
     }
-    if (live) scatter_index[p] = r;
+    if (p < R) scatter_index[p] = r;
     if (in_range) {
       row_token[r] = (int)(p / k);
       if (lds_row_token) lds_row_token[r] = (int)(p / k);
@@ -86,8 +104,22 @@ __device__ __forceinline__ void rank_chunk(const int (&ev)[kIters], int R, int E
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__ ids, int R, int E, int nbits,
-                                                     int nchunks, int32_t* __restrict__ cnt,
+// Per-expert counts of one chunk into the LDS histogram h; returns the number of
+// the chunk's pairs whose id is outside [0, E).
+__device__ __forceinline__ int count_chunk(const int (&ev)[kIters], int64_t p0, int R, int E, int lane, int32_t* h) {
+  int nbad = 0;
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const bool live = p0 + it * kWave + lane < R;
+    const int e = ev[it];
+    const bool in_range = live && e >= 0 && e < E;
+    nbad += __popcll(__ballot(live && !in_range));
+    if (in_range) atomicAdd(h + e, 1);
+  }
+  return nbad;
+}
+
+__global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__ ids, int R, int E, int nchunks, int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ bad) {
   extern __shared__ int32_t hist[];  // [4][E]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -96,18 +128,9 @@ __global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__
   const int c = blockIdx.x * kWavesPerBlock + w;
   int nbad = 0;
   if (c < nchunks) {
-    int32_t* h = hist + w * E;
     int ev[kIters];
     load_chunk(ids, R, c, lane, ev);
-    for (int it = 0; it < kIters; ++it) {
-      const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
-      const bool live = p < R;
-      const int e = ev[it];
-      const bool in_range = live && e >= 0 && e < E;
-      nbad += __popcll(__ballot(live && !in_range));
-      const uint64_t m = same_expert_lanes(e, in_range, nbits);
-      if (in_range && lane == __ffsll((unsigned long long)m) - 1) h[e] += __popcll(m);
-    }
+    nbad = count_chunk(ev, (int64_t)c * kChunk, R, E, lane, hist + w * E);
   }
   __syncthreads();
   if (c < nchunks) {
@@ -220,17 +243,7 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
   int nbad = 0;
   if (has) {
     load_chunk(ids, R, w, lane, ev);
-    int32_t* h = L.hist + w * E;
-    for (int it = 0; it < kIters; ++it) {
-      if ((int64_t)w * kChunk + it * kWave >= R) break;  // the rest of the chunk is past R
-      const int64_t p = (int64_t)w * kChunk + it * kWave + lane;
-      const bool live = p < R;
-      const int e = ev[it];
-      const bool in_range = live && e >= 0 && e < E;
-      nbad += __popcll(__ballot(live && !in_range));
-      const uint64_t m = same_expert_lanes(e, in_range, nbits);
-      if (in_range && lane == __ffsll((unsigned long long)m) - 1) h[e] += __popcll(m);
-    }
+    nbad = count_chunk(ev, (int64_t)w * kChunk, R, E, lane, L.hist + w * E);
   }
   if (lane == 0) L.wbad[w] = nbad;
   __syncthreads();
@@ -428,7 +441,7 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
     int32_t* cnt = (int32_t*)workspace;
     int32_t* bad = cnt + (int64_t)nchunks * E;
     const size_t lds = (size_t)kWavesPerBlock * E * sizeof(int32_t);
-    hipLaunchKernelGGL(scatter_count, dim3(nblk), dim3(256), lds, s, ids, R, E, nbits, nchunks, cnt, bad);
+    hipLaunchKernelGGL(scatter_count, dim3(nblk), dim3(256), lds, s, ids, R, E, nchunks, cnt, bad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, cnt, (const int32_t*)bad, nchunks, E, R, offsets,
                        status_words, row_token);
