@@ -37,56 +37,57 @@ constexpr int kChunk = 1024;              // pairs per wave
 constexpr int kIters = kChunk / kWave;    // ballot rounds per chunk
 constexpr int kWavesPerBlock = 4;
 
-// Lanes (bitmask) whose expert id equals the calling lane's, for every round of
-// a chunk's pairs p0 + it * 64 + lane; 0 for lanes whose pair is past R or whose
+// Lanes (bitmask) whose expert id equals the calling lane's, for each of N
+// rounds of pairs p0 + it * 64 + lane; 0 for lanes whose pair is past R or whose
 // id is outside [0, E).  All lanes of the wave must call it.  The bit loop is
-// outermost, so the ballots of the kIters rounds do not depend on each other
-// and overlap instead of forming one long chain per round.
-__device__ __forceinline__ void chunk_masks(const int (&ev)[kIters], int64_t p0, int R, int E, int nbits, int lane,
-                                            uint64_t (&m)[kIters]) {
-  bool in_range[kIters];
+// outermost, so the ballots of the N rounds do not depend on each other and
+// overlap instead of forming one long chain per round.
+template <int N>
+__device__ __forceinline__ void round_masks(const int (&ev)[N], int64_t p0, int R, int E, int nbits, int lane,
+                                            uint64_t (&m)[N]) {
+  bool in_range[N];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
+  for (int it = 0; it < N; ++it) {
     in_range[it] = p0 + it * kWave + lane < R && ev[it] >= 0 && ev[it] < E;
     m[it] = __ballot(in_range[it]);
   }
   for (int b = 0; b < nbits; ++b) {
 #pragma unroll
-    for (int it = 0; it < kIters; ++it) {
+    for (int it = 0; it < N; ++it) {
       const bool bit = (ev[it] >> b) & 1;
       const uint64_t on = __ballot(in_range[it] && bit);
       m[it] &= bit ? on : ~on;
     }
   }
 #pragma unroll
-  for (int it = 0; it < kIters; ++it)
+  for (int it = 0; it < N; ++it)
     if (!in_range[it]) m[it] = 0ull;
 }
 
-// The expert ids of one chunk, kIters per lane, all loads issued before any is used.
-__device__ __forceinline__ void load_chunk(const int32_t* ids, int R, int c, int lane,
-                                           int (&ev)[kIters]) {
+// The expert ids of N rounds of pairs p0 + it * 64 + lane, all loads issued before any is used.
+template <int N>
+__device__ __forceinline__ void load_rounds(const int32_t* ids, int R, int64_t p0, int lane, int (&ev)[N]) {
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t p = (int64_t)c * kChunk + it * kWave + lane;
+  for (int it = 0; it < N; ++it) {
+    const int64_t p = p0 + it * kWave + lane;
     ev[it] = p < R ? ids[p] : -1;
   }
 }
 
-// Rows of one chunk's pairs: a pair's row is the running cursor of its expert
-// plus the number of lower lanes with the same expert; the highest such lane
-// advances the cursor.
-__device__ __forceinline__ void rank_chunk(const int (&ev)[kIters], int R, int E, int k, int nbits, int c, int lane,
-                                           int32_t* cursor, int32_t* __restrict__ scatter_index,
-                                           int32_t* __restrict__ row_token, int32_t* lds_row_token = nullptr) {
-  const int64_t p0 = (int64_t)c * kChunk;
-  uint64_t m[kIters];
-  chunk_masks(ev, p0, R, E, nbits, lane, m);
+// Rows of N rounds of pairs p0 + it * 64 + lane: a pair's row is the running
+// cursor of its expert plus the number of lower lanes with the same expert; the
+// highest such lane advances the cursor.
+template <int N>
+__device__ __forceinline__ void rank_rounds(const int (&ev)[N], int64_t p0, int R, int E, int k, int nbits, int lane,
+                                            int32_t* cursor, int32_t* __restrict__ scatter_index,
+                                            int32_t* __restrict__ row_token, int32_t* lds_row_token = nullptr) {
+  uint64_t m[N];
+  round_masks<N>(ev, p0, R, E, nbits, lane, m);
   const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
   const uint64_t below = lanemask_lt();
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    if (p0 + it * kWave >= R) break;  // the rest of the chunk is past R
+  for (int it = 0; it < N; ++it) {
+    if (p0 + it * kWave >= R) break;  // the remaining rounds are past R
     const int64_t p = p0 + it * kWave + lane;
     const int e = ev[it];
     const bool in_range = m[it] != 0ull;  // a lane in range always finds itself
@@ -104,12 +105,13 @@ __device__ __forceinline__ void rank_chunk(const int (&ev)[kIters], int R, int E
   }
 }
 
-// Per-expert counts of one chunk into the LDS histogram h; returns the number of
-// the chunk's pairs whose id is outside [0, E).
-__device__ __forceinline__ int count_chunk(const int (&ev)[kIters], int64_t p0, int R, int E, int lane, int32_t* h) {
+// Per-expert counts of N rounds of pairs p0 + it * 64 + lane into the LDS
+// histogram h; returns the number of those pairs whose id is outside [0, E).
+template <int N>
+__device__ __forceinline__ int count_rounds(const int (&ev)[N], int64_t p0, int R, int E, int lane, int32_t* h) {
   int nbad = 0;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
+  for (int it = 0; it < N; ++it) {
     const bool live = p0 + it * kWave + lane < R;
     const int e = ev[it];
     const bool in_range = live && e >= 0 && e < E;
@@ -129,8 +131,8 @@ __global__ __launch_bounds__(256) void scatter_count(const int32_t* __restrict__
   int nbad = 0;
   if (c < nchunks) {
     int ev[kIters];
-    load_chunk(ids, R, c, lane, ev);
-    nbad = count_chunk(ev, (int64_t)c * kChunk, R, E, lane, hist + w * E);
+    load_rounds<kIters>(ids, R, (int64_t)c * kChunk, lane, ev);
+    nbad = count_rounds<kIters>(ev, (int64_t)c * kChunk, R, E, lane, hist + w * E);
   }
   __syncthreads();
   if (c < nchunks) {
@@ -193,20 +195,37 @@ __global__ __launch_bounds__(1024) void scatter_scan(int32_t* __restrict__ cnt, 
   for (int r = s_total + tid; r < R; r += 1024) row_token[r] = -1;
 }
 
+// Workgroup c ranks chunk c; wave w takes its quarter, pairs c * 1024 + 256 w
+// onward.  The waves recount their quarters per expert (LDS atomics), and wave
+// w's cursor for expert e starts at the chunk's base plus the counts of waves
+// 0 .. w-1, so every pair gets the row a single pass over the chunk would give.
 __global__ __launch_bounds__(256) void scatter_rank(const int32_t* __restrict__ ids, int R, int E, int k, int nbits,
                                                     int nchunks, const int32_t* __restrict__ chunk_base,
                                                     const int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ scatter_index,
                                                     int32_t* __restrict__ row_token) {
-  extern __shared__ int32_t cursor_all[];  // [4][E]
+  constexpr int kQ = kIters / kWavesPerBlock;  // rounds per wave
+  extern __shared__ int32_t cursor_all[];  // [4][E]: quarter counts, then cursors
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = blockIdx.x * kWavesPerBlock + w;
-  if (c >= nchunks) return;  // whole wave; no workgroup barrier follows
-  int32_t* cursor = cursor_all + w * E;
-  int ev[kIters];
-  load_chunk(ids, R, c, lane, ev);
-  for (int e = lane; e < E; e += kWave) cursor[e] = chunk_base[(int64_t)c * E + e] + offsets[e];
-  rank_chunk(ev, R, E, k, nbits, c, lane, cursor, scatter_index, row_token);
+  const int c = blockIdx.x;
+  for (int i = tid; i < kWavesPerBlock * E; i += 256) cursor_all[i] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)c * kChunk + (int64_t)w * kQ * kWave;
+  int ev[kQ];
+  load_rounds<kQ>(ids, R, p0, lane, ev);
+  count_rounds<kQ>(ev, p0, R, E, lane, cursor_all + w * E);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int run = chunk_base[(int64_t)c * E + e] + offsets[e];
+#pragma unroll
+    for (int q = 0; q < kWavesPerBlock; ++q) {
+      const int v = cursor_all[q * E + e];
+      cursor_all[q * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  rank_rounds<kQ>(ev, p0, R, E, k, nbits, lane, cursor_all + w * E, scatter_index, row_token);
 }
 
 // Pairs up to 16 chunks (16384 pairs) in one workgroup of 4 waves (up to 4
@@ -242,8 +261,8 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
   int ev[kIters];
   int nbad = 0;
   if (has) {
-    load_chunk(ids, R, w, lane, ev);
-    nbad = count_chunk(ev, (int64_t)w * kChunk, R, E, lane, L.hist + w * E);
+    load_rounds<kIters>(ids, R, (int64_t)w * kChunk, lane, ev);
+    nbad = count_rounds<kIters>(ev, (int64_t)w * kChunk, R, E, lane, L.hist + w * E);
   }
   if (lane == 0) L.wbad[w] = nbad;
   __syncthreads();
@@ -291,7 +310,8 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
   const int total = carry;
   for (int r = total + tid; r < R; r += NT) row_token[r] = -1;
   if (has)
-    rank_chunk(ev, R, E, k, nbits, w, lane, L.hist + w * E, scatter_index, row_token, fold ? L.row_token : nullptr);
+    rank_rounds<kIters>(ev, (int64_t)w * kChunk, R, E, k, nbits, lane, L.hist + w * E, scatter_index, row_token,
+                        fold ? L.row_token : nullptr);
   if (fold) {
     __syncthreads();
     const int n = total * row_vecs;
@@ -446,7 +466,7 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
     hipLaunchKernelGGL(scatter_scan, dim3(1), dim3(1024), 0, s, cnt, (const int32_t*)bad, nchunks, E, R, offsets,
                        status_words, row_token);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(scatter_rank, dim3(nblk), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
+    hipLaunchKernelGGL(scatter_rank, dim3(nchunks), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
                        (const int32_t*)cnt, (const int32_t*)offsets, scatter_index, row_token);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
