@@ -22,9 +22,10 @@
 //                  for all 16 rounds of the chunk at once so that they overlap.
 //   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies (skipped when
 //                  x_scattered is NULL: the fc1 call then gathers the rows on load).
-// Up to 16 chunks (decode, and prefill up to 16384 pairs) take scatter_small,
-// which runs count, scan and rank in one workgroup of 16 waves, and for at
-// most 256 rows of at most 256 KiB in all also the row copy.
+// Up to 4 chunks (decode, and prefill up to 4096 pairs) take scatter_small,
+// which runs count, scan and rank in one workgroup of 4 waves (the pairs split
+// evenly between them), and for at most 256 rows of at most 256 KiB in all
+// also the row copy.
 #include "moe_common.h"
 #include "moe_topk.h"
 
@@ -38,25 +39,28 @@ constexpr int kIters = kChunk / kWave;    // ballot rounds per chunk
 constexpr int kWavesPerBlock = 4;
 
 // Lanes (bitmask) whose expert id equals the calling lane's, for each of N
-// rounds of pairs p0 + it * 64 + lane; 0 for lanes whose pair is past R or whose
+// rounds of pairs p0 + it * 64 + lane; 0 for lanes whose pair is at or past end, or whose
 // id is outside [0, E).  All lanes of the wave must call it.  The bit loop is
 // outermost, so the ballots of the N rounds do not depend on each other and
 // overlap instead of forming one long chain per round.
 template <int N>
-__device__ __forceinline__ void round_masks(const int (&ev)[N], int64_t p0, int R, int E, int nbits, int lane,
+__device__ __forceinline__ void round_masks(const int (&ev)[N], int64_t p0, int end, int E, int nbits, int lane,
                                             uint64_t (&m)[N]) {
+  const int64_t live = end - p0;  // rounds from live / 64 on hold no pair and are skipped
   bool in_range[N];
 #pragma unroll
   for (int it = 0; it < N; ++it) {
-    in_range[it] = p0 + it * kWave + lane < R && ev[it] >= 0 && ev[it] < E;
-    m[it] = __ballot(in_range[it]);
+    in_range[it] = it * kWave + lane < live && ev[it] >= 0 && ev[it] < E;
+    m[it] = it * kWave < live ? __ballot(in_range[it]) : 0ull;
   }
   for (int b = 0; b < nbits; ++b) {
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-      const bool bit = (ev[it] >> b) & 1;
-      const uint64_t on = __ballot(in_range[it] && bit);
-      m[it] &= bit ? on : ~on;
+      if (it * kWave < live) {  // wave-uniform
+        const bool bit = (ev[it] >> b) & 1;
+        const uint64_t on = __ballot(in_range[it] && bit);
+        m[it] &= bit ? on : ~on;
+      }
     }
   }
 #pragma unroll
@@ -64,30 +68,31 @@ __device__ __forceinline__ void round_masks(const int (&ev)[N], int64_t p0, int 
     if (!in_range[it]) m[it] = 0ull;
 }
 
-// The expert ids of N rounds of pairs p0 + it * 64 + lane, all loads issued before any is used.
+// The expert ids of N rounds of pairs p0 + it * 64 + lane below end (-1 from
+// end on), all loads issued before any is used.
 template <int N>
-__device__ __forceinline__ void load_rounds(const int32_t* ids, int R, int64_t p0, int lane, int (&ev)[N]) {
+__device__ __forceinline__ void load_rounds(const int32_t* ids, int end, int64_t p0, int lane, int (&ev)[N]) {
 #pragma unroll
   for (int it = 0; it < N; ++it) {
     const int64_t p = p0 + it * kWave + lane;
-    ev[it] = p < R ? ids[p] : -1;
+    ev[it] = p < end ? ids[p] : -1;
   }
 }
 
-// Rows of N rounds of pairs p0 + it * 64 + lane: a pair's row is the running
+// Rows of N rounds of pairs p0 + it * 64 + lane below end: a pair's row is the running
 // cursor of its expert plus the number of lower lanes with the same expert; the
 // highest such lane advances the cursor.
 template <int N>
-__device__ __forceinline__ void rank_rounds(const int (&ev)[N], int64_t p0, int R, int E, int k, int nbits, int lane,
+__device__ __forceinline__ void rank_rounds(const int (&ev)[N], int64_t p0, int end, int E, int k, int nbits, int lane,
                                             int32_t* cursor, int32_t* __restrict__ scatter_index,
                                             int32_t* __restrict__ row_token, int32_t* lds_row_token = nullptr) {
   uint64_t m[N];
-  round_masks<N>(ev, p0, R, E, nbits, lane, m);
+  round_masks<N>(ev, p0, end, E, nbits, lane, m);
   const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int it = 0; it < N; ++it) {
-    if (p0 + it * kWave >= R) break;  // the remaining rounds are past R
+    if (p0 + it * kWave >= end) break;  // the remaining rounds are past end
     const int64_t p = p0 + it * kWave + lane;
     const int e = ev[it];
     const bool in_range = m[it] != 0ull;  // a lane in range always finds itself
@@ -97,7 +102,7 @@ __device__ __forceinline__ void rank_rounds(const int (&ev)[N], int64_t p0, int 
       r = b + __popcll(m[it] & below);
       if ((m[it] & above) == 0ull) cursor[e] = b + __popcll(m[it]);
     }
-    if (p < R) scatter_index[p] = r;
+    if (p < end) scatter_index[p] = r;
     if (in_range) {
       row_token[r] = (int)(p / k);
       if (lds_row_token) lds_row_token[r] = (int)(p / k);
@@ -105,18 +110,79 @@ __device__ __forceinline__ void rank_rounds(const int (&ev)[N], int64_t p0, int 
   }
 }
 
-// Per-expert counts of N rounds of pairs p0 + it * 64 + lane into the LDS
-// histogram h; returns the number of those pairs whose id is outside [0, E).
-template <int N>
-__device__ __forceinline__ int count_rounds(const int (&ev)[N], int64_t p0, int R, int E, int lane, int32_t* h) {
+// Compact forms for the one-workgroup path.  It runs once per call, with cold
+// instruction caches, so its loops are not unrolled: one iteration per 64-pair
+// round, the id reloaded each round (ids may be in global memory or LDS).
+//
+// Lanes (bitmask) whose expert id equals the calling lane's; 0 for a lane with
+// in_range false.  All lanes of the wave must call it.
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool in_range, int nbits) {
+  uint64_t m = __ballot(in_range);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t on = __ballot(in_range && bit);
+    m &= bit ? on : ~on;
+  }
+  return in_range ? m : 0ull;
+}
+
+// Per-expert counts of the pairs [p0, end) into h (LDS atomic adds); returns how
+// many of them have an id outside [0, E).
+__device__ __forceinline__ int count_segment(const int32_t* ids, int64_t p0, int end, int E, int lane, int32_t* h) {
   int nbad = 0;
-#pragma unroll
-  for (int it = 0; it < N; ++it) {
-    const bool live = p0 + it * kWave + lane < R;
-    const int e = ev[it];
+#pragma unroll 1
+  for (int64_t q = p0; q < end; q += kWave) {
+    const int64_t p = q + lane;
+    const bool live = p < end;
+    const int e = live ? ids[p] : -1;
     const bool in_range = live && e >= 0 && e < E;
     nbad += __popcll(__ballot(live && !in_range));
     if (in_range) atomicAdd(h + e, 1);
+  }
+  return nbad;
+}
+
+// Rows of the pairs [p0, end), in pair order from the per-expert cursors.
+__device__ __forceinline__ void rank_segment(const int32_t* ids, int64_t p0, int end, int E, int k, int nbits,
+                                             int lane, int32_t* cursor, int32_t* __restrict__ scatter_index,
+                                             int32_t* __restrict__ row_token, int32_t* lds_row_token) {
+  const uint64_t above = lane == 63 ? 0ull : (~0ull << (lane + 1));
+  const uint64_t below = lanemask_lt();
+#pragma unroll 1
+  for (int64_t q = p0; q < end; q += kWave) {
+    const int64_t p = q + lane;
+    const bool live = p < end;
+    const int e = live ? ids[p] : -1;
+    const bool in_range = live && e >= 0 && e < E;
+    const uint64_t m = same_expert_lanes(e, in_range, nbits);
+    int r = -1;
+    if (in_range) {
+      const int b = cursor[e];
+      r = b + __popcll(m & below);
+      if ((m & above) == 0ull) cursor[e] = b + __popcll(m);
+    }
+    if (live) scatter_index[p] = r;
+    if (in_range) {
+      row_token[r] = (int)(p / k);
+      if (lds_row_token) lds_row_token[r] = (int)(p / k);
+    }
+  }
+}
+
+// Per-expert counts of N rounds of pairs p0 + it * 64 + lane below end into the
+// LDS histogram h; returns the number of those pairs whose id is outside [0, E).
+template <int N>
+__device__ __forceinline__ int count_rounds(const int (&ev)[N], int64_t p0, int end, int E, int lane, int32_t* h) {
+  int nbad = 0;
+#pragma unroll
+  for (int it = 0; it < N; ++it) {
+    if (p0 + it * kWave < end) {  // wave-uniform: rounds past end hold no pair
+      const bool live = p0 + it * kWave + lane < end;
+      const int e = ev[it];
+      const bool in_range = live && e >= 0 && e < E;
+      nbad += __popcll(__ballot(live && !in_range));
+      if (in_range) atomicAdd(h + e, 1);
+    }
   }
   return nbad;
 }
@@ -228,45 +294,56 @@ __global__ __launch_bounds__(256) void scatter_rank(const int32_t* __restrict__ 
   rank_rounds<kQ>(ev, p0, R, E, k, nbits, lane, cursor_all + w * E, scatter_index, row_token);
 }
 
-// Pairs up to 16 chunks (16384 pairs) in one workgroup of 4 waves (up to 4
-// chunks) or 16 waves: count, scan and rank in one launch, with each wave's
-// chunk held in registers between the count and the rank.  hist holds
-// nchunks x E counts, then cursors.  With fold set (at most kFoldRows rows),
-// the same workgroup also copies the rows, reading row_token from LDS.
+// The whole scatter build in one workgroup of NW waves: count, scan and rank in
+// one launch.  The pairs are split into nseg contiguous segments of whole
+// 64-pair rounds (at most 16 rounds each), one per wave, counted and then
+// ranked with the compact loops above; segment w's cursor for expert e starts at
+// offsets[e] plus the counts of segments 0 .. w-1, so the rows are those of one
+// pass in pair order.  hist holds nseg x E counts, then cursors.  With fold set
+// (at most kFoldRows rows), the same workgroup also copies the rows, reading
+// row_token from LDS.
 constexpr int kSmallWaves = 16;
 constexpr int kFoldRows = 256;
 constexpr int64_t kFoldBytes = 256 * 1024;
+constexpr int kSmallHist = 8192;  // LDS counters of the one-workgroup path (32 KiB)
+
+// Segments of the one-workgroup path for R pairs: one per wave, as many as kSmallHist holds, and no more
+// than there are 64-pair rounds (each segment adds a step to the per-expert scan).
+int block_segments(int NW, int E, int R) {
+  int n = NW < kSmallHist / E ? NW : kSmallHist / E;
+  const int rounds = (R + kWave - 1) / kWave;
+  if (n > rounds) n = rounds;
+  return n < 1 ? 1 : n;
+}
 
 struct BlockLds {
-  int32_t* hist;        // [nchunks][E]
+  int32_t* hist;        // [nseg][E]
   int32_t* wsum;        // [NW]
   int32_t* wmax;        // [NW]
   int32_t* wbad;        // [NW]
   int32_t* row_token;   // [kFoldRows]
 };
 
-// The whole scatter build of R <= NW * 1024 pairs (one chunk per wave) by one
-// workgroup of NW waves; ids may point to global memory or to LDS.
+// The scatter build of R <= nseg * 1024 pairs; ids may point to global memory or to LDS.
 template <int NW>
-__device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, int k, int nbits, int nchunks,
+__device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, int k, int nbits, int nseg,
                                               int32_t* __restrict__ scatter_index, int32_t* __restrict__ row_token,
                                               int32_t* __restrict__ offsets, int32_t* __restrict__ status,
                                               int fold, const u32x4* __restrict__ x, int row_vecs,
                                               u32x4* __restrict__ xs, const BlockLds& L) {
   constexpr int NT = NW * kWave;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int i = tid; i < nchunks * E; i += NT) L.hist[i] = 0;
+  for (int i = tid; i < nseg * E; i += NT) L.hist[i] = 0;
   __syncthreads();
-  const bool has = w < nchunks;
-  int ev[kIters];
+  const int seg = ((R + nseg - 1) / nseg + kWave - 1) / kWave * kWave;  // pairs per segment, whole rounds
+  const int64_t p0 = (int64_t)w * seg;
+  const int pend = (int)min((int64_t)R, p0 + seg);
+  const bool has = w < nseg && p0 < R;
   int nbad = 0;
-  if (has) {
-    load_rounds<kIters>(ids, R, (int64_t)w * kChunk, lane, ev);
-    nbad = count_rounds<kIters>(ev, (int64_t)w * kChunk, R, E, lane, L.hist + w * E);
-  }
+  if (has) nbad = count_segment(ids, p0, pend, E, lane, L.hist + w * E);
   if (lane == 0) L.wbad[w] = nbad;
   __syncthreads();
-  // Per expert: chunk bases, then the exclusive scan of the totals.  Thread
+  // Per expert: segment bases, then the exclusive scan of the totals.  Thread
   // tid owns experts tid, tid + NT, ...; the scan runs over the experts in
   // index order, one block of NT experts after the other.
   int carry = 0, maxg = 0;
@@ -275,7 +352,7 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
     int total_e = 0;
     if (e < E) {
       int run = 0;
-      for (int c = 0; c < nchunks; ++c) {
+      for (int c = 0; c < nseg; ++c) {
         const int v = L.hist[c * E + e];
         L.hist[c * E + e] = run;
         run += v;
@@ -292,7 +369,7 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
     if (e < E) {
       const int excl = base + incl - total_e;
       offsets[e] = excl;
-      for (int c = 0; c < nchunks; ++c) L.hist[c * E + e] += excl;
+      for (int c = 0; c < nseg; ++c) L.hist[c * E + e] += excl;
     }
     for (int i = 0; i < NW; ++i) {
       carry += L.wsum[i];
@@ -310,8 +387,8 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
   const int total = carry;
   for (int r = total + tid; r < R; r += NT) row_token[r] = -1;
   if (has)
-    rank_rounds<kIters>(ev, (int64_t)w * kChunk, R, E, k, nbits, lane, L.hist + w * E, scatter_index, row_token,
-                        fold ? L.row_token : nullptr);
+    rank_segment(ids, p0, pend, E, k, nbits, lane, L.hist + w * E, scatter_index, row_token,
+                 fold ? L.row_token : nullptr);
   if (fold) {
     __syncthreads();
     const int n = total * row_vecs;
@@ -330,14 +407,13 @@ __device__ __forceinline__ void scatter_block(const int32_t* ids, int R, int E, 
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void scatter_small(const int32_t* __restrict__ ids, int R, int E, int k,
-                                                         int nbits, int nchunks, int32_t* __restrict__ scatter_index,
+                                                         int nbits, int nseg, int32_t* __restrict__ scatter_index,
                                                          int32_t* __restrict__ row_token,
                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ status,
                                                          int fold, const u32x4* __restrict__ x, int row_vecs,
                                                          u32x4* __restrict__ xs) {
   MOE_BLOCK_LDS(NW)
-  scatter_block<NW>(ids, R, E, k, nbits, nchunks, scatter_index, row_token, offsets, status, fold, x, row_vecs, xs,
-                    lds);
+  scatter_block<NW>(ids, R, E, k, nbits, nseg, scatter_index, row_token, offsets, status, fold, x, row_vecs, xs, lds);
 }
 
 // Routing and scatter of at most kRsTokens tokens (and kRsLogits logits) in
@@ -351,7 +427,7 @@ constexpr int kRsLogits = 4096;
 template <int NW, int Q>
 __global__ __launch_bounds__(NW * 64) void route_scatter_small(
     const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, float* __restrict__ logits,
-    int T, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int nbits, int nchunks,
+    int T, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int nbits, int nseg,
     int32_t* __restrict__ scatter_index, int32_t* __restrict__ row_token, int32_t* __restrict__ offsets,
     int32_t* __restrict__ status, int fold, const u32x4* __restrict__ x, int row_vecs, u32x4* __restrict__ xs) {
   MOE_BLOCK_LDS(NW)
@@ -397,8 +473,8 @@ __global__ __launch_bounds__(NW * 64) void route_scatter_small(
     }
   }
   __syncthreads();
-  scatter_block<NW>(s_ids, T * k, E, k, nbits, nchunks, scatter_index, row_token, offsets, status, fold, x,
-                          row_vecs, xs, lds);
+  scatter_block<NW>(s_ids, T * k, E, k, nbits, nseg, scatter_index, row_token, offsets, status, fold, x, row_vecs,
+                    xs, lds);
 }
 
 constexpr int kCopyRows = 8;
@@ -419,7 +495,6 @@ __global__ __launch_bounds__(256) void scatter_copy(const u32x4* __restrict__ x,
 }
 
 int num_chunks(int R) { return (R + kChunk - 1) / kChunk; }
-constexpr int kSmallHist = 8192;  // LDS counters of the one-workgroup path (32 KiB)
 
 }  // namespace
 }  // namespace moe
@@ -444,17 +519,13 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
   hipError_t err;
   const int elem = dt == 1 ? 2 : 4;
   const int row_vecs = (int)((int64_t)H * elem / 16);
-  if (nchunks <= kSmallWaves && nchunks * E <= kSmallHist) {
+  const int nseg = block_segments(4, E, R);
+  if ((int64_t)nseg * kChunk >= R) {
     const int fold = x_scattered && R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
-    const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
-    if (nchunks <= 4)
-      hipLaunchKernelGGL(scatter_small<4>, dim3(1), dim3(256), lds, s, ids, R, E, top_k, nbits, nchunks,
-                         scatter_index, row_token, offsets, status_words, fold, (const u32x4*)x, row_vecs,
-                         (u32x4*)x_scattered);
-    else
-      hipLaunchKernelGGL(scatter_small<kSmallWaves>, dim3(1), dim3(kSmallWaves * 64), lds, s, ids, R, E, top_k,
-                         nbits, nchunks, scatter_index, row_token, offsets, status_words, fold, (const u32x4*)x,
-                         row_vecs, (u32x4*)x_scattered);
+    const size_t lds = (size_t)nseg * E * sizeof(int32_t);
+    hipLaunchKernelGGL(scatter_small<4>, dim3(1), dim3(256), lds, s, ids, R, E, top_k, nbits, nseg,
+                       scatter_index, row_token, offsets, status_words, fold, (const u32x4*)x, row_vecs,
+                       (u32x4*)x_scattered);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (fold) return hipSuccess;
   } else {
@@ -479,8 +550,9 @@ hipError_t build_scatter(int dt, const void* x, const int32_t* ids, int T, int H
 bool route_scatter_fusable(int T, int top_k, int E) {
   using namespace moe;
   const int R = T * top_k;
-  return T <= kRsTokens && T * E <= kRsLogits && top_k <= kMaxTopK && num_chunks(R) <= 4 &&
-         num_chunks(R) * E <= kSmallHist;
+  // the launch takes 4 waves up to 4 tokens, else 16, and R <= 16 * 32 pairs always fit its segments
+  return T <= kRsTokens && T * E <= kRsLogits && top_k <= kMaxTopK &&
+         (int64_t)block_segments(T <= 4 ? 4 : kSmallWaves, E, R) * kChunk >= R;
 }
 
 hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const float* bias, float* logits, int T,
@@ -489,17 +561,17 @@ hipError_t route_scatter_fused(int dt, const float* partial, int nsplit, const f
                                void* x_scattered, hipStream_t s) {
   using namespace moe;
   const int R = T * top_k;
-  const int nchunks = num_chunks(R);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const int elem = dt == 1 ? 2 : 4;
   const int row_vecs = (int)((int64_t)H * elem / 16);
   const int fold = x_scattered && R <= kFoldRows && (int64_t)R * row_vecs * 16 <= kFoldBytes;
-  const size_t lds = (size_t)nchunks * E * sizeof(int32_t);
   auto launch = [&](auto nw, auto q) {
     constexpr int NW = decltype(nw)::value, Q = decltype(q)::value;
+    const int nseg = block_segments(NW, E, R);
+    const size_t lds = (size_t)nseg * E * sizeof(int32_t);
     hipLaunchKernelGGL((route_scatter_small<NW, Q>), dim3(1), dim3(NW * 64), lds, s, partial, nsplit, bias, logits,
-                       T, E, top_k, ids, weights, nbits, nchunks, scatter_index, row_token, offsets, status_words,
+                       T, E, top_k, ids, weights, nbits, nseg, scatter_index, row_token, offsets, status_words,
                        fold, (const u32x4*)x, row_vecs, (u32x4*)x_scattered);
   };
   auto with_q = [&](auto nw) {
