@@ -17,9 +17,6 @@
 namespace moe {
 namespace {
 
-// NT: read the routed rows with non-temporal loads (rows that fc2 wrote
-// non-temporally: an output too large for the caches; see fc2's store policy).
-template <bool NT>
 __global__ __launch_bounds__(256) void gather_combine_k(const f32x4* __restrict__ y_rows,
                                                         const int32_t* __restrict__ scatter_index,
                                                         const float* __restrict__ weights, int T, int H, int k,
@@ -36,15 +33,15 @@ __global__ __launch_bounds__(256) void gather_combine_k(const f32x4* __restrict_
   for (int c = threadIdx.x; c < hv; c += 256) {
     f32x4 sum = accumulate ? y[(int64_t)t * hv + c] : f32x4{0.f, 0.f, 0.f, 0.f};
     // Slots in batches of 8: the batch's loads are all issued before its
-    // adds, which still run in slot order.  Each routed row is read once.
+    // adds, which still run in slot order.  Each routed row is read once
+    // (non-temporal loads).
     for (int j0 = 0; j0 < k; j0 += 8) {
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
         const int r = j < k ? s_idx[j] : -1;
-        const f32x4* src = y_rows + (int64_t)r * hv + c;
-        v[u] = r < 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : NT ? __builtin_nontemporal_load(src) : *src;
+        v[u] = r >= 0 ? __builtin_nontemporal_load(y_rows + (int64_t)r * hv + c) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -76,13 +73,8 @@ namespace moe_launch {
 hipError_t gather_combine(const float* y_rows, const int32_t* scatter_index, const float* weights, int T, int H,
                           int top_k, int accumulate, float* y, hipStream_t s) {
   using namespace moe;
-  // the same size rule as fc2's store policy (32 MiB of fp32 routed rows)
-  if ((int64_t)T * top_k * H * 4 >= ((int64_t)32 << 20))
-    hipLaunchKernelGGL(gather_combine_k<true>, dim3(T), dim3(256), 0, s, (const f32x4*)y_rows, scatter_index, weights,
-                       T, H, top_k, accumulate, (f32x4*)y);
-  else
-    hipLaunchKernelGGL(gather_combine_k<false>, dim3(T), dim3(256), 0, s, (const f32x4*)y_rows, scatter_index,
-                       weights, T, H, top_k, accumulate, (f32x4*)y);
+  hipLaunchKernelGGL(gather_combine_k, dim3(T), dim3(256), 0, s, (const f32x4*)y_rows, scatter_index, weights, T, H,
+                     top_k, accumulate, (f32x4*)y);
   return hipGetLastError();
 }
 

@@ -101,15 +101,7 @@ struct GemmParams {
   void* out2;               // kSwiGLUSave: fc1 pre-activation out, T [rows, 2N]
   const int32_t* a_rows;    // optional: row r of A is row a_rows[r] of `a` ([a_src_rows, K]), else row r
   int a_src_rows;           // rows of `a` when a_rows is set (indices are clamped to [0, a_src_rows))
-  int nt_store;             // kStoreF32: non-temporal stores (see nt_output)
 };
-
-// fp32 outputs stored with kStoreF32 (fc2's routed rows, fc1's input gradient)
-// are read once, by the next call.  From 32 MiB on they are far larger than
-// what the caches keep for that call, so they are written non-temporally;
-// smaller ones (decode) stay in the cache for the reader.
-constexpr int64_t kNtOutputBytes = (int64_t)32 << 20;
-inline int nt_output(int64_t rows, int64_t n) { return rows * n * 4 >= kNtOutputBytes; }
 
 // Source row of A for row r (gather-on-load when a_rows is set).
 template <typename T>
@@ -293,8 +285,7 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
-            if (p.nt_store) __builtin_nontemporal_store(v, o);
-            else *o = v;
+            __builtin_nontemporal_store(v, o);  // read once, by the next call
           } else {
             const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
             *o = (p.accumulate ? *o : 0.0f) + sc * v;
@@ -621,8 +612,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
           float* o = (float*)p.out + (int64_t)row * p.N + col;
           const float v = acc[mb][nb][i];
           if (EPI == kStoreF32) {
-            if (p.nt_store) __builtin_nontemporal_store(v, o);
-            else *o = v;
+            __builtin_nontemporal_store(v, o);  // read once, by the next call
           } else {
             const float sc = p.row_scale ? p.row_scale[row] : 1.0f;
             *o = (p.accumulate ? *o : 0.0f) + sc * v;
@@ -1937,7 +1927,6 @@ hipError_t grouped_fc2(int dt, int bt, const void* act, const int32_t* offsets, 
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)act, offsets, groups, rows, K, N, (const bf16_t*)w2, w2_group_stride,
                          ldb, 0, out, row_scale, accumulate, 0, bt};
-    p.nt_store = nt_output(rows, N);
     if (plain_store) return role ? launch_bf16<kStoreF32, 1>(p, cu_count, s) : launch_bf16<kStoreF32, 0>(p, cu_count, s);
     return role ? launch_bf16<kScaleAdd, 1>(p, cu_count, s) : launch_bf16<kScaleAdd, 0>(p, cu_count, s);
   }
@@ -2011,7 +2000,6 @@ hipError_t fused_fc2(int bt, const void* act, const int32_t* offsets, int E, int
   using namespace moe;
   GemmParams<bf16_t> pr{(const bf16_t*)act, offsets, E, R, I, H, (const bf16_t*)w2, (int64_t)I * H,
                         bt ? I : H, 0, y_rows, nullptr, 0, 0, bt};
-  pr.nt_store = nt_output(R, H);
   GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2, 0,
                         bt ? I_s : H, 0, y, gate, accumulate, 0, bt};
   return launch_fused_bf16<kStoreF32, kScaleAdd>(pr, ps, cu_count, s);
@@ -2033,7 +2021,6 @@ hipError_t grouped_fc2_mx8(const void* act, const int32_t* offsets, int groups, 
   using namespace moe;
   GemmParams<bf16_t> p{(const bf16_t*)act, offsets, groups, rows, K, N, (const bf16_t*)w2q, (int64_t)N * K,
                        K, 0, out, row_scale, accumulate, 0, 1, (const uint8_t*)w2s, (int64_t)N * (K / 8)};
-  p.nt_store = nt_output(rows, N);
   if (plain_store)
     return role ? launch_mx8<kStoreF32, kScaleK, 1>(p, cu_count, s) : launch_mx8<kStoreF32, kScaleK, 0>(p, cu_count, s);
   return role ? launch_mx8<kScaleAdd, kScaleK, 1>(p, cu_count, s) : launch_mx8<kScaleAdd, kScaleK, 0>(p, cu_count, s);
@@ -2056,7 +2043,6 @@ hipError_t fused_fc2_mx8(const void* act, const int32_t* offsets, int E, int R, 
   using namespace moe;
   GemmParams<bf16_t> pr{(const bf16_t*)act, offsets, E, R, I, H, (const bf16_t*)w2q, (int64_t)H * I,
                         I, 0, y_rows, nullptr, 0, 0, 1, (const uint8_t*)w2s, (int64_t)H * (I / 8)};
-  pr.nt_store = nt_output(R, H);
   GemmParams<bf16_t> ps{(const bf16_t*)act_s, nullptr, 1, T, I_s, H, (const bf16_t*)ws2q, 0,
                         I_s, 0, y, gate, accumulate, 0, 1, (const uint8_t*)ws2s, 0};
   return launch_mx8_fused<kStoreF32, kScaleAdd, kScaleK>(pr, ps, cu_count, s);
@@ -2117,7 +2103,6 @@ hipError_t grouped_fc1_dgrad(int dt, int wt_nk, const void* d_h, const int32_t* 
   if (dt == 1) {
     GemmParams<bf16_t> p{(const bf16_t*)d_h, offsets, groups, rows, 2 * I, H, (const bf16_t*)w1,
                          (int64_t)2 * I * H, ldb, 0, d_xs, nullptr, 0, 0, bt};
-    p.nt_store = nt_output(rows, H);
     return launch_bf16<kStoreF32, 2>(p, cu_count, s);
   }
   GemmParams<float> p{(const float*)d_h, offsets, groups, rows, 2 * I, H, (const float*)w1, (int64_t)2 * I * H,
