@@ -12,9 +12,10 @@
 //                          caller's workspace (the ring kernel loads W_r 4 bytes a lane).
 //   router_logits_ring     x[T,H] @ W_r on MFMA (16x16x32 bf16, fp32 accumulate) from
 //                          W_r's own [H,E] layout: 64 tokens x 64 experts per
-//                          workgroup, both operands streamed through an LDS ring by
-//                          direct loads, H split across workgroups; partial sums
-//                          land in the workspace.
+//                          workgroup (128 x 256 for many tokens and experts), both
+//                          operands streamed through an LDS ring by direct loads,
+//                          H split across workgroups; partial sums land in the
+//                          workspace.
 //   route_logits_f32       the same product for float32 inputs, one thread per logit.
 //   topk_softmax           one wave64 per token: adds the partial sums in a fixed
 //                          order (+ bias) into the logits, then topk_wave: k rounds
@@ -31,9 +32,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRtExp = 64;    // experts per workgroup tile
 constexpr int kRtBK = 64;     // k per ring step
-constexpr int kRtStages = 4;  // ring depth: three steps in flight while one is multiplied
 
 int padded_experts(int E) { return (E + 15) / 16 * 16; }
 // The ring kernel reads W_r with 4-byte loads, so an odd E first gets a zero column.
@@ -50,29 +49,36 @@ __global__ __launch_bounds__(256) void router_pad_bf16(const bf16_t* __restrict_
   wp[i] = e < E ? w[h * E + e] : (bf16_t)0;
 }
 
-// Swizzle of a 128-byte W_r row in LDS: the 32-byte slot (16 experts) s of row
-// r sits at slot s ^ rt_wslot(r).  A transposing B-fragment read covers 4 rows
-// x 16 experts per 16 lanes, and a half-wave the rows {0-3, 8-11} (+4, +16,
-// +32) of one slot; with bit 1 and bit 3 of the row in the slot, those 8 rows
-// land in 8 different 32-byte bank windows.
-__device__ __forceinline__ int rt_wslot(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
+// Swizzle of a W_r row of BN experts in LDS: the 32-byte slot (16 experts) s of
+// row r sits at slot s ^ rt_wslot<BN>(r).  A transposing B-fragment read covers
+// 4 rows x 16 experts per 16 lanes, and a half-wave the rows {0-3, 8-11} (+4,
+// +16, +32) of one slot; the swizzle sends those 8 rows to 8 different 32-byte
+// windows of the 256-byte bank space.  128-byte rows (BN = 64) alternate
+// between two halves of it, so bits 1 and 3 of the row pick the slot; 512-byte
+// rows (BN = 256) all start at offset 0, so bits 0, 1 and 3 do.
+template <int BN>
+__device__ __forceinline__ int rt_wslot(int r) {
+  static_assert(BN == 64 || BN == 256, "W_r tile widths of 64 or 256 experts");
+  if constexpr (BN == 64) return ((r >> 1) & 1) | ((r >> 2) & 2);
+  else return (r & 3) | ((r >> 1) & 4);
+}
 
-// Partial router logits over one slice of H for a tile of BM tokens x 64
+// Partial router logits over one slice of H for a tile of BM tokens x BN
 // experts, from x [T, H] and W_r in its own [H, E] layout (E even).
 //
-// The slice streams through an LDS ring of kRtStages steps of 64 k, filled
-// with direct loads (HBM -> LDS, no register round trip), so three steps'
-// loads are in flight while one step is multiplied:
+// The slice streams through an LDS ring of S steps of 64 k, filled with direct
+// loads (HBM -> LDS, no register round trip), so S - 1 steps' loads are in
+// flight while one step is multiplied:
 //  * x rows as 128-byte LDS rows, the 16-byte chunk c of row m at chunk
 //    c ^ ((m >> 1) & 7): an A-fragment read (one chunk of 16 consecutive rows)
 //    is then conflict-free;
-//  * W_r rows (E-contiguous) as 128-byte LDS rows of 64 experts, swizzled by
-//    rt_wslot, loaded 4 bytes a lane (E need only be even).  A B fragment (8
-//    consecutive k of one expert) is assembled from two ds_read_b64_tr_b16
-//    reads: within each 16-lane group, lane c receives element c % 4 of the
-//    8-byte rows read by lanes c/4, c/4 + 4, c/4 + 8 and c/4 + 12, so lanes that
-//    read a 4 (k) x 16 (expert) block get 4 consecutive k of their own expert.
-// 4 waves in a 2x2 arrangement each own (BM/2) x 32 outputs as 16x16 blocks
+//  * W_r rows (E-contiguous) as LDS rows of BN experts, swizzled by rt_wslot,
+//    loaded 4 bytes a lane (E need only be even).  A B fragment (8 consecutive
+//    k of one expert) is assembled from two ds_read_b64_tr_b16 reads: within
+//    each 16-lane group, lane c receives element c % 4 of the 8-byte rows read
+//    by lanes c/4, c/4 + 4, c/4 + 8 and c/4 + 12, so lanes that read a 4 (k) x
+//    16 (expert) block get 4 consecutive k of their own expert.
+// WM x WN waves each own (BM/WM) x (BN/WN) outputs as 16x16 blocks
 // (v_mfma_f32_16x16x32_bf16, fp32 accumulate in k order).  Rows past T and
 // experts past E are fetched from clamped addresses and feed only outputs
 // that are never stored or read; k past H (the last slice of an H that is not
@@ -83,18 +89,20 @@ __device__ __forceinline__ int rt_wslot(int r) { return ((r >> 1) & 1) | ((r >> 
 // remapped: the expert tiles of one (token tile, slice) pair are consecutive
 // workgroups of one XCD and share the x tile through its L2.  Ids past the last
 // pair (the grid is padded to a multiple of 8 pairs) exit at once.
-template <int BM>
-__global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ w, int T, int H, int E,
-                                                          int E_pad, int kslice, int n_t, int n_e, int nz,
-                                                          float* __restrict__ partial) {
-  constexpr int S = kRtStages, BK = kRtBK;
-  constexpr int kXStage = BM * BK * 2, kWStage = BK * kRtExp * 2, kStage = kXStage + kWStage;
-  constexpr int kXLoads = kXStage / 1024 / 4;  // 16-byte loads (1 KiB per wave) per wave and step
-  constexpr int kWLoads = kWStage / 256 / 4;   // 4-byte loads (256 B per wave) per wave and step
+template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(WM * WN * 64) void router_logits_ring(const bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ w, int T, int H, int E,
+                                                                   int E_pad, int kslice, int n_t, int n_e, int nz,
+                                                                   float* __restrict__ partial) {
+  constexpr int BK = kRtBK, NW = WM * WN, NT = NW * 64;
+  constexpr int kWRow = BN * 2;                // bytes of one W_r row in LDS
+  constexpr int kXStage = BM * BK * 2, kWStage = BK * kWRow, kStage = kXStage + kWStage;
+  constexpr int kXLoads = kXStage / 1024 / NW;  // 16-byte loads (1 KiB per wave) per wave and step
+  constexpr int kWLoads = kWStage / 256 / NW;   // 4-byte loads (256 B per wave) per wave and step
   constexpr int kLoads = kXLoads + kWLoads;
-  constexpr int MB = BM / 32;                  // 16-row blocks per wave
-  static_assert(kXLoads >= 1 && (S - 2) * kLoads < 64, "ring shape");
+  constexpr int MB = BM / WM / 16, NB = BN / WN / 16;  // 16x16 blocks per wave
+  static_assert(kXLoads >= 1 && kXStage % (1024 * NW) == 0 && kWStage % (256 * NW) == 0, "loads per wave");
+  static_assert(S >= 2 && (S - 2) * kLoads < 64 && S * kStage <= 160 * 1024, "ring shape");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[S * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restri
   const int pair = (slot / n_e) * 8 + (int)(blockIdx.x & 7);
   if (pair >= n_t * nz) return;  // whole workgroup, before any barrier
   const int zb = pair / n_t;
-  const int t0 = (pair - zb * n_t) * BM, e0 = (slot % n_e) * kRtExp;
+  const int t0 = (pair - zb * n_t) * BM, e0 = (slot % n_e) * BN;
   const int kbeg = zb * kslice, kend = min(H, kbeg + kslice);
   const int nsteps = (kend - kbeg + BK - 1) / BK;
 
@@ -120,10 +128,10 @@ __global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restri
   int wcol[kWLoads];
 #pragma unroll
   for (int j = 0; j < kWLoads; ++j) {
-    const int r = (wave * kWLoads + j) * 2 + (lane >> 5);
-    const int d = lane & 31;
+    const int b = (wave * kWLoads + j) * 256 + 4 * lane;  // byte inside the stage's W_r tile
+    const int r = b / kWRow, d = (b % kWRow) / 4;        // row, 4-byte word in the row
     wrow[j] = r;
-    wcol[j] = min(e0 + 16 * ((d >> 3) ^ rt_wslot(r)) + 2 * (d & 7), E - 2);
+    wcol[j] = min(e0 + 16 * ((d >> 3) ^ rt_wslot<BN>(r)) + 2 * (d & 7), E - 2);
   }
   auto issue = [&](int step) {
     unsigned char* st = ring + (step % S) * kStage;
@@ -138,11 +146,13 @@ __global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restri
                                        MOE_LDS(void, st + kXStage + (wave * kWLoads + j) * 256), 4, 0, 0);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 4, s16 = lane & 15;
-  f32x4 acc[MB][2];
+  f32x4 acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int s = 0; s < S - 1 && s < nsteps; ++s) issue(s);
   for (int kt = 0; kt < nsteps; ++kt) {
@@ -151,37 +161,39 @@ __global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restri
     unsigned char* st = ring + (kt % S) * kStage;
     const int kvalid = kend - (kbeg + kt * BK);
     if (kvalid < BK) {  // the last step of a ragged H: zero k >= H in both operands
-      for (int i = tid; i < BM * 8; i += 256) {
+      for (int i = tid; i < BM * 8; i += NT) {
         const int m = i >> 3, c = i & 7;
         if (8 * c >= kvalid) *(u32x4*)(st + m * 128 + 16 * (c ^ ((m >> 1) & 7))) = u32x4{0u, 0u, 0u, 0u};
       }
-      for (int i = tid; i < (BK - kvalid) * 8; i += 256)
-        *(u32x4*)(st + kXStage + (kvalid + (i >> 3)) * 128 + 16 * (i & 7)) = u32x4{0u, 0u, 0u, 0u};
+      for (int i = tid; i < (BK - kvalid) * (kWRow / 16); i += NT)
+        *(u32x4*)(st + kXStage + (kvalid + i / (kWRow / 16)) * kWRow + 16 * (i % (kWRow / 16))) =
+            u32x4{0u, 0u, 0u, 0u};
       lds_barrier();
     }
     if (kt + S - 1 < nsteps) issue(kt + S - 1);  // refills the stage every wave finished with in step kt - 1
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      u32x4 a[MB], b[2];
+      u32x4 a[MB], b[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int m = wm * (BM / 2) + 16 * mb + s16;
+        const int m = wm * (BM / WM) + 16 * mb + s16;
         const int c = 4 * u + g;
         a[mb] = *(const u32x4*)(st + m * 128 + 16 * (c ^ ((m >> 1) & 7)));
       }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const int r = 32 * u + 8 * g + (s16 >> 2);
-        const int sl = 2 * wn + nb;
-        const unsigned char* p_lo = st + kXStage + r * 128 + 32 * (sl ^ rt_wslot(r)) + 8 * (s16 & 3);
-        const unsigned char* p_hi = st + kXStage + (r + 4) * 128 + 32 * (sl ^ rt_wslot(r + 4)) + 8 * (s16 & 3);
+        const int sl = wn * NB + nb;
+        const unsigned char* p_lo = st + kXStage + r * kWRow + 32 * (sl ^ rt_wslot<BN>(r)) + 8 * (s16 & 3);
+        const unsigned char* p_hi =
+            st + kXStage + (r + 4) * kWRow + 32 * (sl ^ rt_wslot<BN>(r + 4)) + 8 * (s16 & 3);
         b[nb] = pack_tr_pair(__builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, p_lo)),
                              __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS(i16x4, p_hi)));
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb]),
                                                                 __builtin_bit_cast(bf16x8, b[nb]), acc[mb][nb], 0,
                                                                 0, 0);
@@ -192,15 +204,23 @@ __global__ __launch_bounds__(256) void router_logits_ring(const bf16_t* __restri
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int e = e0 + 32 * wn + 16 * nb + s16;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = e0 + wn * (BN / WN) + 16 * nb + s16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = t0 + wm * (BM / 2) + 16 * mb + 4 * g + r;
+        const int t = t0 + wm * (BM / WM) + 16 * mb + 4 * g + r;
         if (t < T && e < E_pad) out[(int64_t)t * E_pad + e] = acc[mb][nb][r];
       }
     }
 }
+
+// The two ring configurations: 64 tokens x 64 experts, 4 waves, 4 stages (two
+// workgroups per CU), and for many tokens and more than 64 experts 128 tokens x
+// 256 experts, 8 waves, 3 stages (one workgroup per CU): every expert of a
+// token tile in one workgroup, so each x tile is staged once rather than once
+// per 64 experts, which keeps more of x's HBM reads in flight.
+struct RingSmall { static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, S = 4, kWgsPerCu = 2; };
+struct RingWide { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, S = 3, kWgsPerCu = 1; };
 
 __global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict__ x,
                                                         const float* __restrict__ w,
@@ -350,22 +370,30 @@ Split router_valu_split(int T, int H) {
   return Split{(H + kslice - 1) / kslice, kslice};
 }
 
-// Tokens per workgroup tile of the ring router.
-int router_ring_tokens(int T) { (void)T; return 64; }
+// Ring configuration for (T, E): the wide tile once there are more than 64 experts and at least 1024
+// tokens, so that eight 128-token tiles or more keep the chip busy; f receives the configuration.
+template <class F>
+auto with_ring(int T, int E, F&& f) {
+  if (moe::ring_experts(E) > 64 && T >= 1024) return f(moe::RingWide{});
+  return f(moe::RingSmall{});
+}
 
-// Ring router: slices of H (multiples of 64, at least two steps each) so that the grid covers about
-// 512 workgroups -- two per CU, the most the ring's LDS allows -- with at most 32 slices.
+// Ring router: slices of H (multiples of 64, at least two steps each) so that the grid covers about one
+// round of the workgroups the ring's LDS lets each CU hold, with at most 32 slices.
 Split router_ring_split(int T, int H, int E) {
   using namespace moe;
-  const int bm = router_ring_tokens(T);
-  const int tiles = ((T + bm - 1) / bm) * ((ring_experts(E) + kRtExp - 1) / kRtExp);
-  int nz = (512 + tiles - 1) / tiles;
-  int max_nz = H / (2 * kRtBK);
-  if (max_nz > 32) max_nz = 32;
-  if (nz > max_nz) nz = max_nz;
-  if (nz < 1) nz = 1;
-  const int kslice = ((H + nz - 1) / nz + kRtBK - 1) / kRtBK * kRtBK;
-  return Split{(H + kslice - 1) / kslice, kslice};
+  return with_ring(T, E, [&](auto cfg) {
+    using C = decltype(cfg);
+    const int tiles = ((T + C::BM - 1) / C::BM) * ((ring_experts(E) + C::BN - 1) / C::BN);
+    const int target = 256 * C::kWgsPerCu;
+    int nz = (target + tiles - 1) / tiles;
+    int max_nz = H / (2 * kRtBK);
+    if (max_nz > 32) max_nz = 32;
+    if (nz > max_nz) nz = max_nz;
+    if (nz < 1) nz = 1;
+    const int kslice = ((H + nz - 1) / nz + kRtBK - 1) / kRtBK * kRtBK;
+    return Split{(H + kslice - 1) / kslice, kslice};
+  });
 }
 
 // Bytes of the zero-padded router copy an odd E needs (none for an even E).
@@ -426,11 +454,14 @@ hipError_t route(int dt, const void* x, const void* w_router, const float* bias,
     }
     float* partial = (float*)((char*)workspace + pad_bytes(H, E));
     const Split sp = router_ring_split(T, H, E);
-    const int bm = router_ring_tokens(T);
-    const int n_t = (T + bm - 1) / bm, n_e = (Er + kRtExp - 1) / kRtExp;
-    const dim3 grid((unsigned)((n_t * sp.nz + 7) / 8 * 8 * n_e));
-    hipLaunchKernelGGL(router_logits_ring<64>, grid, dim3(256), 0, s, (const bf16_t*)x, wr, T, H, Er, E_pad,
-                       sp.kslice, n_t, n_e, sp.nz, partial);
+    with_ring(T, E, [&](auto cfg) {
+      using C = decltype(cfg);
+      const int n_t = (T + C::BM - 1) / C::BM, n_e = (Er + C::BN - 1) / C::BN;
+      const dim3 grid((unsigned)((n_t * sp.nz + 7) / 8 * 8 * n_e));
+      hipLaunchKernelGGL((router_logits_ring<C::BM, C::BN, C::WM, C::WN, C::S>), grid, dim3(C::WM * C::WN * 64), 0,
+                         s, (const bf16_t*)x, wr, T, H, Er, E_pad, sp.kslice, n_t, n_e, sp.nz, partial);
+      return 0;
+    });
     if ((err = hipGetLastError()) != hipSuccess) return err;
     return launch_topk((const float*)partial, sp.nz, E_pad, bias, logits, T, E, top_k, ids, weights, s);
   }

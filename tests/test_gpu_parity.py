@@ -171,6 +171,25 @@ def test_route_small_token_paths(T, H, E, k, with_bias):
     check_routing(host(bufs.logits), host(bufs.topk_ids), host(bufs.topk_weights), host(x), host(wr), bias, k, O)
 
 
+@pytest.mark.parametrize("T,H,E,k,with_bias", [
+    (1100, 264, 130, 6, True),    # 128-token x 256-expert ring tile: ragged T, H tail of 8, partial expert tile
+    (1030, 200, 258, 8, False),   # two expert tiles, the second holding 2 experts; one H slice with a tail
+    (2048, 1024, 256, 8, False),  # several H slices of whole 64-deep steps
+    (1024, 136, 255, 4, True),    # odd E (zero column appended) on the wide tile
+])
+def test_route_wide_ring_tile(T, H, E, k, with_bias):
+    cfg = wl.LayerConfig("route_wide", "bf16", T=T, H=H, E=E, top_k=k, I=8)
+    print(f"[route-wide] T={T} H={H} E={E} k={k} bias={with_bias}", flush=True)
+    x = wl.make_x(cfg, DEV)
+    wr = wl.make_router(cfg, DEV)
+    bias = np.linspace(-0.5, 0.5, E).astype(np.float32) if with_bias else None
+    bias_t = torch.from_numpy(bias).to(DEV) if with_bias else None
+    bufs = B.MoELayerBuffers(T, H, E, k, 8, 0, x.dtype, DEV)
+    B.moe_route(x, wr, bias_t, k, bufs.topk_ids, bufs.topk_weights, bufs.logits, bufs.route_ws)
+    torch.cuda.synchronize()
+    check_routing(host(bufs.logits), host(bufs.topk_ids), host(bufs.topk_weights), host(x), host(wr), bias, k, O)
+
+
 @pytest.mark.parametrize("T", [4, 64])
 def test_topk_ties_on_integer_logits(T):
     """Exact integer router products at both router paths: logits and ties bit-exact."""
