@@ -30,26 +30,36 @@ __global__ __launch_bounds__(256) void gather_combine_k(const f32x4* __restrict_
   }
   __syncthreads();
   const int hv = H / 4;
-  for (int c = threadIdx.x; c < hv; c += 256) {
-    f32x4 sum = accumulate ? y[(int64_t)t * hv + c] : f32x4{0.f, 0.f, 0.f, 0.f};
-    // Slots in batches of 8: the batch's loads are all issued before its
-    // adds, which still run in slot order.  Each routed row is read once
-    // (non-temporal loads).
+  // Two 16-byte columns per thread at a time (c and c + 256), and for each the
+  // slots in batches of 8: all loads of a batch, for both columns, are issued
+  // before its adds, which still run in slot order.  Each routed row is read
+  // once (non-temporal loads).
+  for (int c0 = threadIdx.x; c0 < hv; c0 += 512) {
+    const int c1 = c0 + 256;
+    const bool has1 = c1 < hv;
+    f32x4 sum0 = accumulate ? y[(int64_t)t * hv + c0] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sum1 = accumulate && has1 ? y[(int64_t)t * hv + c1] : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += 8) {
-      f32x4 v[8];
+      f32x4 v0[8], v1[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
         const int r = j < k ? s_idx[j] : -1;
-        v[u] = r >= 0 ? __builtin_nontemporal_load(y_rows + (int64_t)r * hv + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4* row = y_rows + (int64_t)r * hv;
+        v0[u] = r >= 0 ? __builtin_nontemporal_load(row + c0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v1[u] = r >= 0 && has1 ? __builtin_nontemporal_load(row + c1) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
-        if (j < k && s_idx[j] >= 0) sum += s_w[j] * v[u];
+        if (j < k && s_idx[j] >= 0) {
+          sum0 += s_w[j] * v0[u];
+          sum1 += s_w[j] * v1[u];
+        }
       }
     }
-    y[(int64_t)t * hv + c] = sum;
+    y[(int64_t)t * hv + c0] = sum0;
+    if (has1) y[(int64_t)t * hv + c1] = sum1;
   }
 }
 
