@@ -229,7 +229,7 @@ size_t moe_route_and_scatter_workspace_bytes(moe_dtype dt, int32_t T, int32_t H,
  * Same arguments (minus workspace), outputs (same bits), layouts, ownership and
  * errors as moe_route_and_scatter.  The scratch the kernels need lives in a
  * device array of the library, moe_route_and_scatter_noalloc_max_bytes() bytes
- * (16 MiB) on every GPU the library runs on, allocated when the library's code
+ * (64 MiB) on every GPU the library runs on, allocated when the library's code
  * loads on that GPU and held until the process ends; the call itself allocates
  * nothing.  Sizes whose moe_route_and_scatter_workspace_bytes exceeds that
  * return MOE_ERR_UNSUPPORTED before anything is launched.  Nothing in the

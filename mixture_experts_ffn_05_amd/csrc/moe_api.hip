@@ -295,7 +295,7 @@ moe_status run_route_and_scatter(const char* fn, moe_dtype dt, const void* x, co
 // stand-in, not device memory); it uses the device address that
 // hipGetSymbolAddress returns, looked up once per device with that device
 // current and kept in scratch_addr.
-constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 
 }  // namespace
 

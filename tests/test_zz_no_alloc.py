@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 
-CALLS = [("v2l", 512), ("v2l", 16), ("v3", 64)]
+CALLS = [("v3", 4096), ("v2l", 512), ("v2l", 16), ("v3", 64)]   # the first: the largest benchmark layer
 
 
 def _outputs(T, H, E, k, dtype):
