@@ -6,20 +6,22 @@
 // top-k routes": one token may send several slots to one expert, so a group can
 // hold more than T rows -- nothing below assumes a bound of T.
 //
-// The layout is a stable counting sort of the pairs p = t*k + j by expert id,
-// computed without atomics so that it is deterministic:
+// The layout is a stable counting sort of the pairs p = t*k + j by expert id.
+// It is deterministic: the only atomics are integer count increments, whose
+// result does not depend on their order, and every row comes from a fixed scan.
 //   scatter_count  each wave64 takes a chunk of 1024 consecutive pairs and counts
-//                  them per expert with LDS atomic adds (integer counts do not
-//                  depend on the order of the adds).
+//                  them per expert with LDS atomic adds.
 //   scatter_scan   one workgroup: per expert, an exclusive scan of the chunk
 //                  counts (chunk bases); across experts, an exclusive scan of the
 //                  totals (expert_offsets), the largest group and the number of
 //                  out-of-range ids.
-//   scatter_rank   each wave replays its chunk; a pair's row is its chunk base
-//                  plus offsets[e] plus the number of lower lanes with the same
-//                  expert; a running per-expert cursor lives in LDS.  Lanes
-//                  holding the same expert are found with ceil(log2 E) ballots,
-//                  for all 16 rounds of the chunk at once so that they overlap.
+//   scatter_rank   one workgroup per chunk, one quarter of it per wave; a pair's
+//                  row is offsets[e] plus its chunk's base, the counts of the
+//                  earlier quarters and the number of earlier pairs of the
+//                  quarter with the same expert, kept as a running per-expert
+//                  cursor in LDS.  Lanes holding the same expert are found with
+//                  ceil(log2 E) ballots, for all rounds of the quarter at once so
+//                  that they overlap.
 //   scatter_copy   x_scattered[r] = x[row_token[r]], 16-byte vector copies (skipped when
 //                  x_scattered is NULL: the fc1 call then gathers the rows on load).
 // Up to 4 chunks (decode, and prefill up to 4096 pairs) take scatter_small,
