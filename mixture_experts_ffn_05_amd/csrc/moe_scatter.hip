@@ -436,9 +436,22 @@ __global__ __launch_bounds__(NW * 64) void route_scatter_small(
   __shared__ int32_t s_ids[kRsTokens * kMaxTopK];
   __shared__ float s_logits[kRsLogits];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // four logits per thread at a time, their slice loads issued together
+  // Logits: each the fixed-order sum of its slices (+ bias).  With at most one
+  // logit per thread, all of its slice loads go out together (32 at a time);
+  // otherwise four logits per thread at a time, 8 slices each.
   constexpr int kNT = NW * kWave;
-  for (int i0 = tid; i0 < T * E; i0 += 4 * kNT) {
+  if (T * E <= kNT) {
+    if (tid < T * E) {
+      const float* ptr[1] = {partial + tid};
+      const bool ok[1] = {true};
+      float v[1];
+      sum_slices_n<1, 32>(ptr, ok, (int64_t)T * E, nsplit, v);
+      if (bias) v[0] += bias[tid % E];
+      logits[tid] = v[0];
+      s_logits[tid] = v[0];
+    }
+  }
+  for (int i0 = tid; T * E > kNT && i0 < T * E; i0 += 4 * kNT) {
     const float* ptr[4];
     bool ok[4];
     float v[4];
