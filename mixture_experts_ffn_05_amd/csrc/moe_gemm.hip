@@ -298,10 +298,12 @@ __device__ __forceinline__ void run_tile_bf16(const GemmParams<bf16_t>& p, int g
 
 // Group bounds (clamped to [0, rows], so that no tile can leave the buffers)
 // and the exclusive prefix of row tiles per group, built in LDS by the whole
-// workgroup of NT threads.  Returns the number of row tiles.
+// workgroup of NT threads.  Returns the number of row tiles.  With sAct set,
+// also the exclusive prefix of groups that fill exactly one row tile
+// (sAct[G] = their number).
 template <int BM, int NT, typename T>
 __device__ __forceinline__ int build_tile_prefix(const GemmParams<T>& p, int32_t* sOff, int32_t* sPre,
-                                                 int32_t* sWave) {
+                                                 int32_t* sWave, int32_t* sAct = nullptr) {
   constexpr int kPer = (kMaxExperts + NT - 1) / NT;  // consecutive groups per thread
   constexpr int kWaves = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -336,6 +338,31 @@ __device__ __forceinline__ int build_tile_prefix(const GemmParams<T>& p, int32_t
     sPre[G] = total;
   }
   __syncthreads();
+  if (sAct) {  // the same scan over "group has exactly one row tile"
+    int la[kPer], a = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int g = tid * kPer + q;
+      la[q] = a;
+      a += (g < G && sPre[g + 1] - sPre[g] == 1) ? 1 : 0;
+    }
+    const int ia = wave_inclusive_scan(a);
+    if (lane == 63) sWave[wave] = ia;
+    __syncthreads();
+    int ab = 0;
+    for (int i = 0; i < wave; ++i) ab += sWave[i];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int g = tid * kPer + q;
+      if (g < G) sAct[g] = ab + ia - a + la[q];
+    }
+    if (tid == 0) {
+      int total = 0;
+      for (int i = 0; i < kWaves; ++i) total += sWave[i];
+      sAct[G] = total;
+    }
+    __syncthreads();
+  }
   return sPre[G];
 }
 
@@ -359,6 +386,51 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t id, int G, int64_t nt, 
   c.g = lo;
   c.ntile = (int)(local / mt);
   c.row0 = sOff[lo] + (int)(local % mt) * BM;
+  c.row_end = sOff[lo + 1];
+  c.single = sOff[lo + 1] - sOff[lo] <= BM;
+  return c;
+}
+
+// The weight-streaming tile's order.  A group that fits in one row tile
+// streams each weight slab from HBM once (HBM-bound); a group of m > 1 row
+// tiles reads each slab once and re-reads it from L2 m - 1 times (MFMA-bound).
+// In expert-major order a few large groups (skewed routing) would run all
+// together, with HBM idle, and the single-tile groups after them with the
+// MFMAs idle.  Here the tiles of single-tile groups come in expert-major, then
+// column order, and the tiles of multi-tile groups (expert, column, row: the
+// row tiles of one slab stay adjacent so that they share it in L2) are spread
+// evenly among them: id is a multi-tile group's tile when
+// floor((id+1)*B/N) > floor(id*B/N), for B such tiles out of N.
+template <int BM>
+__device__ __forceinline__ TileCoord decode_tile_spread(int64_t id, int G, int64_t nt, int64_t total,
+                                                        const int32_t* sOff, const int32_t* sPre,
+                                                        const int32_t* sAct) {
+  const int64_t nb = total - (int64_t)sAct[G] * nt;  // tiles of multi-tile groups
+  const int64_t b_before = id * nb / total;
+  const bool further = (id + 1) * nb / total != b_before;
+  int lo = 0, hi = G - 1;
+  TileCoord c;
+  if (further) {  // largest g with (sPre[g] - sAct[g]) * nt <= b: a multi-tile group
+    const int64_t b = b_before;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)(sPre[mid] - sAct[mid]) * nt <= b) lo = mid; else hi = mid - 1;
+    }
+    const int64_t local = b - (int64_t)(sPre[lo] - sAct[lo]) * nt;
+    const int mt = sPre[lo + 1] - sPre[lo];
+    c.ntile = (int)(local / mt);
+    c.row0 = sOff[lo] + (int)(local % mt) * BM;
+  } else {  // largest g with sAct[g] <= a / nt: the single-tile group of that rank
+    const int64_t a = id - b_before;
+    const int rank = (int)(a / nt);
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sAct[mid] <= rank) lo = mid; else hi = mid - 1;
+    }
+    c.ntile = (int)(a % nt);
+    c.row0 = sOff[lo];
+  }
+  c.g = lo;
   c.row_end = sOff[lo + 1];
   c.single = sOff[lo + 1] - sOff[lo] <= BM;
   return c;
@@ -468,12 +540,23 @@ __device__ __forceinline__ int pipe_col_base(int nb, int wn) {
              : (wn * (C::BN / C::WN) + 32 * nb);
 }
 
+// threadIdx.x passed through an empty asm statement.  A persistent kernel
+// runs many tiles; values derived from the thread index (load and LDS
+// offsets) are then recomputed at the start of each tile instead of being
+// hoisted out of the tile loop, where they would stay live, and spill, across
+// the code of the other tile configuration in a fused launch.
+__device__ __forceinline__ int tile_thread() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Direct loads of one reduction slice (activations, then weights) into a ring
 // stage; wnt: the weights are read once (non-temporal policy).
 template <class C>
 __device__ __forceinline__ void pipe_issue(unsigned char* __restrict__ st, const bf16_t* a_k, const bf16_t* b_k,
-                                           const int64_t* a_off, const int* b_off, bool wnt) {
-  const int wave = threadIdx.x >> 6;
+                                           const int64_t* a_off, const int* b_off, bool wnt, int tid) {
+  const int wave = tid >> 6;
 #pragma unroll
   for (int i = 0; i < C::kALoads; ++i)
     if (C::STAGES != 2 || a_off[i] >= 0)
@@ -501,9 +584,9 @@ template <int EPI, class C, bool BT>
 __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const unsigned char* __restrict__ rst,
                                           bool issue, const bf16_t* a_k, const bf16_t* b_k, const int64_t* a_off,
                                           const int* b_off, f32x16 (&acc)[C::kMB][C::kNB], int wn, int wm, int kw,
-                                          bool wnt) {
-  const int lane = threadIdx.x & 63;
-  if (issue) pipe_issue<C>(wst, a_k, b_k, a_off, b_off, wnt);
+                                          bool wnt, int tid) {
+  const int lane = tid & 63;
+  if (issue) pipe_issue<C>(wst, a_k, b_k, a_off, b_off, wnt, tid);
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
   const int grp = lane >> 4, s16 = lane & 15;
@@ -553,8 +636,8 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
 // waves hold; the ring must be idle (every wave past its last LDS read).
 template <int EPI, class C>
 __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 (&acc)[C::kMB][C::kNB], int row0,
-                                            int row_end, int n0, unsigned char* __restrict__ smem) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                            int row_end, int n0, unsigned char* __restrict__ smem, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
   const int wm = wpos / C::WN, wn = wpos % C::WN;
   if constexpr (C::KW > 1) {
@@ -626,7 +709,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem, bool wnt) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_thread(), lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
   const int wm = wpos / C::WN, wn = wpos % C::WN;
   const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
@@ -692,17 +775,17 @@ __device__ __forceinline__ void run_tile_pipe_v0(const GemmParams<bf16_t>& p, in
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
     if (s < nk)
-      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt);
+      pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt, tid);
 
   for (int kt = 0; kt < nk; ++kt) {
     if (nk - 1 - kt >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
     lds_barrier();
     const int kn = kt + C::STAGES - 1;
     pipe_step<EPI, C, BT>(smem + (kn % C::STAGES) * C::kStage, smem + (kt % C::STAGES) * C::kStage, kn < nk,
-                          a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw, wnt);
+                          a_base + kn * C::BK, bg + kn * b_step, a_off, b_off, acc, wn, wm, kw, wnt, tid);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
-  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem, tid);
 }
 
 
@@ -717,8 +800,8 @@ struct PipeFrags {
 // Reads the fragments of substep `ks` of the slice held in ring stage `rst`.
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void pipe_read(const unsigned char* __restrict__ rst, int ks, int wm, int wn,
-                                          PipeFrags<C>& f) {
-  const int lane = threadIdx.x & 63;
+                                          PipeFrags<C>& f, int tid) {
+  const int lane = tid & 63;
   const unsigned char* As = rst;
   const unsigned char* Bs = rst + C::kAStage;
   const int grp = lane >> 4, s16 = lane & 15;
@@ -787,7 +870,7 @@ template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                                  unsigned char* __restrict__ smem, bool wnt) {
   static_assert(C::kKSW % 2 == 0, "substeps per slice alternate between two fragment sets");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_thread(), lane = tid & 63, wave = tid >> 6;
   const int kw = wave / C::kPos, wpos = wave % C::kPos;
   const int wm = wpos / C::WN, wn = wpos % C::WN;
   const bf16_t* __restrict__ bg = p.b + (int64_t)g * p.b_stride;
@@ -846,7 +929,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   const bf16_t* a_base = p.a;
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt);
+    if (s < nk) pipe_issue<C>(smem + s * C::kStage, a_base + s * C::BK, bg + s * b_step, a_off, b_off, wnt, tid);
   // slice 0 has landed in every wave (newer slices may still be in flight)
   if (nk - 1 >= C::STAGES - 2) wait_vmcnt<(C::STAGES - 2) * C::kLoads>(); else wait_vmcnt<0>();
   lds_barrier();
@@ -854,10 +937,10 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   // at the slice boundaries below, STAGES slices ahead)
   if (C::STAGES - 1 < nk)
     pipe_issue<C>(smem + (C::STAGES - 1) * C::kStage, a_base + (C::STAGES - 1) * C::BK,
-                  bg + (C::STAGES - 1) * b_step, a_off, b_off, wnt);
+                  bg + (C::STAGES - 1) * b_step, a_off, b_off, wnt, tid);
 
   PipeFrags<C> f0, f1;
-  pipe_read<EPI, C, BT>(smem, kw, wm, wn, f0);
+  pipe_read<EPI, C, BT>(smem, kw, wm, wn, f0, tid);
   // One slice; the last one (LAST) has no boundary.  The last slice is peeled
   // off the loop so that no branch separates a boundary's reads from the
   // MFMAs that hide them.
@@ -868,7 +951,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
       PipeFrags<C>& cur = (j & 1) ? f1 : f0;
       PipeFrags<C>& nxt = (j & 1) ? f0 : f1;
       if (j + 1 < C::kKSW) {
-        pipe_read<EPI, C, BT>(rst, kw + (j + 1) * C::KW, wm, wn, nxt);
+        pipe_read<EPI, C, BT>(rst, kw + (j + 1) * C::KW, wm, wn, nxt, tid);
       } else if constexpr (!decltype(last)::value) {
         // the previous substep's MFMAs all issue before this wave waits at the barrier
         __builtin_amdgcn_sched_barrier(0);
@@ -877,8 +960,8 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
         const int kn = kt + C::STAGES;
         if (kn < nk)
           pipe_issue<C>(smem + (kt % C::STAGES) * C::kStage, a_base + kn * C::BK, bg + kn * b_step, a_off, b_off,
-                        wnt);
-        pipe_read<EPI, C, BT>(smem + ((kt + 1) % C::STAGES) * C::kStage, kw, wm, wn, nxt);
+                        wnt, tid);
+        pipe_read<EPI, C, BT>(smem + ((kt + 1) % C::STAGES) * C::kStage, kw, wm, wn, nxt, tid);
       }
       pipe_mfmas<C>(cur, acc);
       sched_substep<C, BT>();
@@ -887,7 +970,7 @@ __device__ __forceinline__ void run_tile_pipe_v1(const GemmParams<bf16_t>& p, in
   for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::false_type{});
   slice(nk - 1, std::true_type{});
   lds_barrier();  // every wave is done with the ring before the next tile refills it
-  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem, tid);
 }
 
 // The loop with two fragment sets holds about 24-48 more VGPRs per lane; it is
@@ -908,18 +991,24 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
     run_tile_pipe_v0<EPI, C, BT>(p, g, row0, row_end, n0, smem, wnt);
 }
 
+// The weight-streaming configuration walks its tiles in decode_tile_spread's order.
+template <class C>
+constexpr bool spread_walk() { return C::BN == 512; }
+
 template <int EPI, class C, int ROLE, bool BT>
 __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(GemmParams<bf16_t> p) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int32_t sOff[kMaxExperts + 1];
   __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sAct[spread_walk<C>() ? kMaxExperts + 1 : 1];
   __shared__ int32_t sWave[C::kWaves];
-  const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave);
+  const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave, spread_walk<C>() ? sAct : nullptr);
   const int64_t nt = p.n_tiles;
   const int64_t total = (int64_t)mtiles * nt;
   const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
   for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
-    const TileCoord c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
+    const TileCoord c = spread_walk<C>() ? decode_tile_spread<C::BM>(id, p.groups, nt, total, sOff, sPre, sAct)
+                                         : decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
     run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem, c.single);
   }
 }
@@ -950,8 +1039,9 @@ __global__ __launch_bounds__(CR::NT, (fused_wgs<CR, CS>())) void grouped_gemm_bf
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int32_t sOff[kMaxExperts + 1];
   __shared__ int32_t sPre[kMaxExperts + 1];
+  __shared__ int32_t sAct[spread_walk<CR>() ? kMaxExperts + 1 : 1];
   __shared__ int32_t sWave[CR::kWaves];
-  const int mtiles = build_tile_prefix<CR::BM, CR::NT>(pr, sOff, sPre, sWave);
+  const int mtiles = build_tile_prefix<CR::BM, CR::NT>(pr, sOff, sPre, sWave, spread_walk<CR>() ? sAct : nullptr);
   const int64_t ntr = pr.n_tiles;
   const int64_t tiles_r = (int64_t)mtiles * ntr;
   const int64_t mts = (ps.rows + CS::BM - 1) / CS::BM;
@@ -965,7 +1055,9 @@ __global__ __launch_bounds__(CR::NT, (fused_wgs<CR, CS>())) void grouped_gemm_bf
       const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
       run_tile_pipe<EPI_S, CS, BT>(ps, 0, mtile * CS::BM, ps.rows, ntile * out_s, smem, ps.rows <= CS::BM);
     } else {
-      const TileCoord c = decode_tile<CR::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
+      const TileCoord c = spread_walk<CR>()
+                              ? decode_tile_spread<CR::BM>(id - s_before, pr.groups, ntr, tiles_r, sOff, sPre, sAct)
+                              : decode_tile<CR::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
       run_tile_pipe<EPI_R, CR, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem, c.single);
     }
   }
@@ -1245,7 +1337,7 @@ __device__ __forceinline__ void run_tile_mx(const GemmParams<bf16_t>& p, int g, 
                          b_off, s_off, acc, wn, wm, kw, wnt);
   }
   lds_barrier();  // every wave is done with the ring before the next tile refills it
-  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem);
+  finish_tile<EPI, C>(p, acc, row0, row_end, n0, smem, tid);
 }
 
 template <int EPI, class C, int SAX, int ROLE>
