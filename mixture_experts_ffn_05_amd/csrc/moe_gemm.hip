@@ -982,13 +982,57 @@ constexpr bool pipe_loop_v1() {
   return C::kKSW % 2 == 0 && C::kWgsPerCu * C::kWaves <= 8;
 }
 
+// Configuration C with a wave's MFMA rows cut to its first MB 32-row blocks.
+// The ring (loads, stages, barriers) is C's; only the fragment reads, MFMAs,
+// accumulators and epilogue rows of the wave shrink.
+template <class C, int MB>
+struct RowBlocks : C {
+  static constexpr int kMB = MB;
+};
+
+// Runs the tile with the wave's MFMA rows cut to nmb 32-row blocks (1 <= nmb
+// <= kMB): one loop instance per block count, chosen by a wave-uniform branch.
+// Every instance issues the same loads and barriers, so the waves of one
+// workgroup may take different instances.
+template <int EPI, class C, bool BT, int MB>
+__device__ __forceinline__ void run_tile_rows(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
+                                              unsigned char* __restrict__ smem, bool wnt, int nmb) {
+  if constexpr (MB > 1) {
+    if (nmb < MB) {
+      run_tile_rows<EPI, C, BT, MB - 1>(p, g, row0, row_end, n0, smem, wnt, nmb);
+      return;
+    }
+  }
+  using R = std::conditional_t<MB == C::kMB, C, RowBlocks<C, MB>>;
+  if constexpr (pipe_loop_v1<C>())
+    run_tile_pipe_v1<EPI, R, BT>(p, g, row0, row_end, n0, smem, wnt);
+  else
+    run_tile_pipe_v0<EPI, R, BT>(p, g, row0, row_end, n0, smem, wnt);
+}
+
+// Configurations whose partial row tiles run with fewer row blocks.  In the
+// 256 x 256 tile (two wave rows of four blocks) the wave row that still holds
+// all its blocks sets the pace and the other waits at the barriers: cutting
+// its blocks measured no faster there, and only adds code.
+template <class C>
+constexpr bool row_variants() {
+  return C::kMB > 1 && (C::WM == 1 || C::kMB <= 2);
+}
+
+// A partial row tile: a wave whose rows end inside the tile runs only the
+// 32-row blocks that hold rows of the group (at least one, so that every wave
+// keeps the same control flow); blocks wholly past the group end are neither
+// read from LDS nor multiplied.
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem, bool wnt) {
-  if constexpr (pipe_loop_v1<C>())
-    run_tile_pipe_v1<EPI, C, BT>(p, g, row0, row_end, n0, smem, wnt);
-  else
-    run_tile_pipe_v0<EPI, C, BT>(p, g, row0, row_end, n0, smem, wnt);
+  int nmb = C::kMB;
+  if constexpr (row_variants<C>()) {
+    const int wm = ((int)(threadIdx.x >> 6) % C::kPos) / C::WN;
+    const int live = row_end - row0 - wm * (C::BM / C::WM);
+    nmb = __builtin_amdgcn_readfirstlane(min(max((live + 31) / 32, 1), C::kMB));
+  }
+  run_tile_rows<EPI, C, BT, C::kMB>(p, g, row0, row_end, n0, smem, wnt, nmb);
 }
 
 // The weight-streaming configuration walks its tiles in decode_tile_spread's order.
