@@ -396,22 +396,47 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t id, int G, int64_t nt, 
 // tiles reads each slab once and re-reads it from L2 m - 1 times (MFMA-bound).
 // In expert-major order a few large groups (skewed routing) would run all
 // together, with HBM idle, and the single-tile groups after them with the
-// MFMAs idle.  Here the tiles of single-tile groups come in expert-major, then
-// column order, and the tiles of multi-tile groups (expert, column, row: the
-// row tiles of one slab stay adjacent so that they share it in L2) are spread
-// evenly among them: id is a multi-tile group's tile when
-// floor((id+1)*B/N) > floor(id*B/N), for B such tiles out of N.
+// MFMAs idle.  Here the tiles of single-tile groups (expert-major, then
+// column) and those of multi-tile groups (expert, column, row) are cut into
+// chunks of one XCD's share of the grid, and the two kinds of chunk are
+// spread evenly: chunk j is a multi-tile chunk when
+// floor((j+1)*CB/CC) > floor(j*CB/CC), for CB such chunks out of CC.  The row
+// tiles of one slab stay adjacent inside a chunk, so they run at the same
+// time on one XCD and share the slab in its L2.  The last chunk of each kind
+// is padded; its padding ids decode to no tile.
+struct SpreadWalk {
+  int64_t nt;     // column tiles
+  int64_t ns;     // tiles of single-tile groups
+  int64_t nb;     // tiles of multi-tile groups
+  int64_t chunk;  // ids per chunk
+  int64_t cb;     // chunks of multi-tile groups
+  int64_t cc;     // chunks in all
+  __device__ int64_t ids() const { return cc * chunk; }
+};
+
+__device__ __forceinline__ SpreadWalk make_spread_walk(int G, int64_t nt, int64_t total, const int32_t* sAct) {
+  SpreadWalk w;
+  w.nt = nt;
+  w.ns = (int64_t)sAct[G] * nt;
+  w.nb = total - w.ns;
+  w.chunk = max((int)gridDim.x / kXcds, 1);
+  w.cb = (w.nb + w.chunk - 1) / w.chunk;
+  w.cc = w.cb + (w.ns + w.chunk - 1) / w.chunk;
+  return w;
+}
+
+// Tile of walk id `id` (0 <= id < w.ids()); false for a padding id.
 template <int BM>
-__device__ __forceinline__ TileCoord decode_tile_spread(int64_t id, int G, int64_t nt, int64_t total,
-                                                        const int32_t* sOff, const int32_t* sPre,
-                                                        const int32_t* sAct) {
-  const int64_t nb = total - (int64_t)sAct[G] * nt;  // tiles of multi-tile groups
-  const int64_t b_before = id * nb / total;
-  const bool further = (id + 1) * nb / total != b_before;
+__device__ __forceinline__ bool decode_tile_spread(int64_t id, int G, const SpreadWalk& w, const int32_t* sOff,
+                                                   const int32_t* sPre, const int32_t* sAct, TileCoord& c) {
+  const int64_t j = id / w.chunk, r = id - j * w.chunk;
+  const int64_t cb_before = j * w.cb / w.cc;  // multi-tile chunks before chunk j
+  const int64_t nt = w.nt;
   int lo = 0, hi = G - 1;
-  TileCoord c;
-  if (further) {  // largest g with (sPre[g] - sAct[g]) * nt <= b: a multi-tile group
-    const int64_t b = b_before;
+  if ((j + 1) * w.cb / w.cc != cb_before) {
+    const int64_t b = cb_before * w.chunk + r;
+    if (b >= w.nb) return false;
+    // largest g with (sPre[g] - sAct[g]) * nt <= b: a multi-tile group
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if ((int64_t)(sPre[mid] - sAct[mid]) * nt <= b) lo = mid; else hi = mid - 1;
@@ -420,8 +445,10 @@ __device__ __forceinline__ TileCoord decode_tile_spread(int64_t id, int G, int64
     const int mt = sPre[lo + 1] - sPre[lo];
     c.ntile = (int)(local / mt);
     c.row0 = sOff[lo] + (int)(local % mt) * BM;
-  } else {  // largest g with sAct[g] <= a / nt: the single-tile group of that rank
-    const int64_t a = id - b_before;
+  } else {
+    const int64_t a = (j - cb_before) * w.chunk + r;
+    if (a >= w.ns) return false;
+    // largest g with sAct[g] <= a / nt: the single-tile group of that rank
     const int rank = (int)(a / nt);
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -433,7 +460,7 @@ __device__ __forceinline__ TileCoord decode_tile_spread(int64_t id, int G, int64
   c.g = lo;
   c.row_end = sOff[lo + 1];
   c.single = sOff[lo + 1] - sOff[lo] <= BM;
-  return c;
+  return true;
 }
 
 // Consecutive slots run on one XCD (workgroups are dealt to the 8 XCDs round-robin).
@@ -1049,10 +1076,17 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
   const int mtiles = build_tile_prefix<C::BM, C::NT>(p, sOff, sPre, sWave, spread_walk<C>() ? sAct : nullptr);
   const int64_t nt = p.n_tiles;
   const int64_t total = (int64_t)mtiles * nt;
+  SpreadWalk sw{};
+  if constexpr (spread_walk<C>()) sw = make_spread_walk(p.groups, nt, total, sAct);
+  const int64_t ids = spread_walk<C>() ? sw.ids() : total;
   const int out_cols = paired(EPI) ? C::BN / 2 : C::BN;
-  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
-    const TileCoord c = spread_walk<C>() ? decode_tile_spread<C::BM>(id, p.groups, nt, total, sOff, sPre, sAct)
-                                         : decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
+  for (int64_t id = xcd_slot(); id < ids; id += gridDim.x) {
+    TileCoord c;
+    if constexpr (spread_walk<C>()) {
+      if (!decode_tile_spread<C::BM>(id, p.groups, sw, sOff, sPre, sAct, c)) continue;
+    } else {
+      c = decode_tile<C::BM>(id, p.groups, nt, sOff, sPre);
+    }
     run_tile_pipe<EPI, C, BT>(p, c.g, c.row0, c.row_end, c.ntile * out_cols, smem, c.single);
   }
 }
@@ -1060,9 +1094,13 @@ __global__ __launch_bounds__(C::NT, C::kWgsPerCu) void grouped_gemm_bf16_pipe(Ge
 // Routed expert groups and the shared expert in one persistent launch.  The
 // routed tiles stream expert weights that are read once (HBM-bound when
 // groups are small); the shared-expert tiles reuse one weight over all T rows
-// (MFMA-bound).  Tile ids of the two problems are interleaved evenly
-// (position p is a shared tile when floor((p+1)*Ts/total) > floor(p*Ts/total)),
+// (MFMA-bound).  Tile ids of the two problems are interleaved evenly in units
+// of U ids (unit j is shared when floor((j+1)*Us/Utotal) > floor(j*Us/Utotal)),
 // so every CU works on both kinds at once and each hides the other's stalls.
+// U is one tile, or with the weight-streaming walk one XCD's share of the grid:
+// consecutive shared tiles are the row tiles of one weight slab, which then
+// run together on one XCD and share the slab in its L2.  A unit past the end
+// of its problem's tiles is padding and decodes to no tile.
 // The two problems may use different tile configurations CR and CS (same
 // thread count; the LDS ring is sized for the larger of the two), so the
 // shared expert can take the dense tile while the routed groups take the
@@ -1087,21 +1125,33 @@ __global__ __launch_bounds__(CR::NT, (fused_wgs<CR, CS>())) void grouped_gemm_bf
   __shared__ int32_t sWave[CR::kWaves];
   const int mtiles = build_tile_prefix<CR::BM, CR::NT>(pr, sOff, sPre, sWave, spread_walk<CR>() ? sAct : nullptr);
   const int64_t ntr = pr.n_tiles;
-  const int64_t tiles_r = (int64_t)mtiles * ntr;
+  SpreadWalk sw{};
+  if constexpr (spread_walk<CR>()) sw = make_spread_walk(pr.groups, ntr, (int64_t)mtiles * ntr, sAct);
+  const int64_t tiles_r = spread_walk<CR>() ? sw.ids() : (int64_t)mtiles * ntr;  // routed ids, padding included
   const int64_t mts = (ps.rows + CS::BM - 1) / CS::BM;
   const int64_t tiles_s = mts * ps.n_tiles;
-  const int64_t total = tiles_r + tiles_s;
+  const int64_t unit = spread_walk<CR>() ? sw.chunk : 1;
+  const int64_t units_s = (tiles_s + unit - 1) / unit;
+  const int64_t units = units_s + (tiles_r + unit - 1) / unit;
   const int out_r = paired(EPI_R) ? CR::BN / 2 : CR::BN;
   const int out_s = paired(EPI_S) ? CS::BN / 2 : CS::BN;
-  for (int64_t id = xcd_slot(); id < total; id += gridDim.x) {
-    const int64_t s_before = id * tiles_s / total;
-    if ((id + 1) * tiles_s / total != s_before) {
-      const int ntile = (int)(s_before / mts), mtile = (int)(s_before % mts);
+  for (int64_t id = xcd_slot(); id < units * unit; id += gridDim.x) {
+    const int64_t j = id / unit, r = id - j * unit;
+    const int64_t s_before = j * units_s / units;  // shared units before unit j
+    if ((j + 1) * units_s / units != s_before) {
+      const int64_t st = s_before * unit + r;
+      if (st >= tiles_s) continue;
+      const int ntile = (int)(st / mts), mtile = (int)(st % mts);
       run_tile_pipe<EPI_S, CS, BT>(ps, 0, mtile * CS::BM, ps.rows, ntile * out_s, smem, ps.rows <= CS::BM);
     } else {
-      const TileCoord c = spread_walk<CR>()
-                              ? decode_tile_spread<CR::BM>(id - s_before, pr.groups, ntr, tiles_r, sOff, sPre, sAct)
-                              : decode_tile<CR::BM>(id - s_before, pr.groups, ntr, sOff, sPre);
+      const int64_t rt = (j - s_before) * unit + r;
+      if (rt >= tiles_r) continue;
+      TileCoord c;
+      if constexpr (spread_walk<CR>()) {
+        if (!decode_tile_spread<CR::BM>(rt, pr.groups, sw, sOff, sPre, sAct, c)) continue;
+      } else {
+        c = decode_tile<CR::BM>(rt, pr.groups, ntr, sOff, sPre);
+      }
       run_tile_pipe<EPI_R, CR, BT>(pr, c.g, c.row0, c.row_end, c.ntile * out_r, smem, c.single);
     }
   }
