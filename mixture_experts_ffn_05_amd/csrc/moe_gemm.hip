@@ -578,6 +578,15 @@ __device__ __forceinline__ int tile_thread() {
   return t;
 }
 
+// First tile row of 32-row block mb of the waves in wave row wm.  With
+// several wave rows the blocks are dealt out alternately (block b belongs to
+// wave row b mod WM), so that in a partial row tile every wave row holds about
+// the same number of live blocks.
+template <class C>
+__device__ __forceinline__ int block_row(int wm, int mb) {
+  return (mb * C::WM + wm) * 32;
+}
+
 // Direct loads of one reduction slice (activations, then weights) into a ring
 // stage; wnt: the weights are read once (non-temporal policy).
 template <class C>
@@ -624,7 +633,7 @@ __device__ __forceinline__ void pipe_step(unsigned char* __restrict__ wst, const
   auto load_frags = [&](int ks, u32x4 (&af)[C::kMB], u32x4 (&bfr)[C::kNB]) {
 #pragma unroll
     for (int mb = 0; mb < C::kMB; ++mb) {
-      const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+      const int m = block_row<C>(wm, mb) + (lane & 31);
       const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(m);
       af[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
     }
@@ -702,7 +711,7 @@ __device__ __forceinline__ void finish_tile(const GemmParams<bf16_t>& p, f32x16 
   for (int mb = 0; mb < C::kMB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = row0 + wm * (C::BM / C::WM) + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const int row = row0 + block_row<C>(wm, mb) + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (row >= row_end) continue;
       if (paired(EPI)) {
 #pragma unroll
@@ -834,7 +843,7 @@ __device__ __forceinline__ void pipe_read(const unsigned char* __restrict__ rst,
   const int grp = lane >> 4, s16 = lane & 15;
 #pragma unroll
   for (int mb = 0; mb < C::kMB; ++mb) {
-    const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+    const int m = block_row<C>(wm, mb) + (lane & 31);
     const int chunk = (2 * ks + (lane >> 5)) ^ a_swizzle<C>(m);
     f.a[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
   }
@@ -1037,13 +1046,10 @@ __device__ __forceinline__ void run_tile_rows(const GemmParams<bf16_t>& p, int g
     run_tile_pipe_v0<EPI, R, BT>(p, g, row0, row_end, n0, smem, wnt);
 }
 
-// Configurations whose partial row tiles run with fewer row blocks.  In the
-// 256 x 256 tile (two wave rows of four blocks) the wave row that still holds
-// all its blocks sets the pace and the other waits at the barriers: cutting
-// its blocks measured no faster there, and only adds code.
+// Configurations whose partial row tiles run with fewer row blocks.
 template <class C>
 constexpr bool row_variants() {
-  return C::kMB > 1 && (C::WM == 1 || C::kMB <= 2);
+  return C::kMB > 1;
 }
 
 // A partial row tile: a wave whose rows end inside the tile runs only the
@@ -1056,8 +1062,8 @@ __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g
   int nmb = C::kMB;
   if constexpr (row_variants<C>()) {
     const int wm = ((int)(threadIdx.x >> 6) % C::kPos) / C::WN;
-    const int live = row_end - row0 - wm * (C::BM / C::WM);
-    nmb = __builtin_amdgcn_readfirstlane(min(max((live + 31) / 32, 1), C::kMB));
+    const int blocks = (row_end - row0 + 31) / 32;  // live blocks of the tile
+    nmb = __builtin_amdgcn_readfirstlane(min(max((blocks - wm + C::WM - 1) / C::WM, 1), C::kMB));
   }
   run_tile_rows<EPI, C, BT, C::kMB>(p, g, row0, row_end, n0, smem, wnt, nmb);
 }
@@ -1268,7 +1274,7 @@ __device__ __forceinline__ void mx_read(const unsigned char* __restrict__ As, co
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int mb = 0; mb < C::kMB; ++mb) {
-    const int m = wm * (C::BM / C::WM) + mb * 32 + (lane & 31);
+    const int m = block_row<C>(wm, mb) + (lane & 31);
     const int chunk = (2 * ks + (lane >> 5)) ^ row_swizzle<C::kARow>(m);
     f.a[mb] = *(const u32x4*)(As + m * C::kARow + chunk * 16);
   }
