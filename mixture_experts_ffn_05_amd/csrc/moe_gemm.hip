@@ -1046,25 +1046,16 @@ __device__ __forceinline__ void run_tile_rows(const GemmParams<bf16_t>& p, int g
     run_tile_pipe_v0<EPI, R, BT>(p, g, row0, row_end, n0, smem, wnt);
 }
 
-// Configurations whose partial row tiles run with fewer row blocks.
-template <class C>
-constexpr bool row_variants() {
-  return C::kMB > 1;
-}
-
-// A partial row tile: a wave whose rows end inside the tile runs only the
-// 32-row blocks that hold rows of the group (at least one, so that every wave
-// keeps the same control flow); blocks wholly past the group end are neither
-// read from LDS nor multiplied.
+// A partial row tile: each wave runs only its 32-row blocks that hold rows of
+// the group (at least one, so that every wave keeps the same control flow);
+// blocks wholly past the group end are neither read from LDS nor multiplied.
+// The tile's live blocks are dealt to the wave rows as block_row deals them.
 template <int EPI, class C, bool BT>
 __device__ __forceinline__ void run_tile_pipe(const GemmParams<bf16_t>& p, int g, int row0, int row_end, int n0,
                                               unsigned char* __restrict__ smem, bool wnt) {
-  int nmb = C::kMB;
-  if constexpr (row_variants<C>()) {
-    const int wm = ((int)(threadIdx.x >> 6) % C::kPos) / C::WN;
-    const int blocks = (row_end - row0 + 31) / 32;  // live blocks of the tile
-    nmb = __builtin_amdgcn_readfirstlane(min(max((blocks - wm + C::WM - 1) / C::WM, 1), C::kMB));
-  }
+  const int wm = ((int)(threadIdx.x >> 6) % C::kPos) / C::WN;
+  const int blocks = (row_end - row0 + 31) / 32;  // live blocks of the tile
+  const int nmb = __builtin_amdgcn_readfirstlane(min(max((blocks - wm + C::WM - 1) / C::WM, 1), C::kMB));
   run_tile_rows<EPI, C, BT, C::kMB>(p, g, row0, row_end, n0, smem, wnt, nmb);
 }
 
