@@ -323,13 +323,19 @@ def test_grouped_gemms_per_call(cfg, layout):
     with the weights stored [K, N] or [N, K]."""
     assert tiles_of(cfg) == EXPECTED_TILES[cfg.name]
     layer = _layer(cfg)
-    W1d, W2d, _ = _device_weights(layer, layout)
-    x = layer["x"]
     rng = np.random.default_rng(5)
     ids = rng.integers(0, cfg.E, (cfg.T, cfg.top_k)).astype(np.int32)
     ids[: min(cfg.T, 5)] = 0                                # a fat group
     if cfg.E > 3:
         ids[ids == 2] = 1                                   # an empty expert
+    _check_grouped_gemms(cfg, layer, ids, layout)
+
+
+def _check_grouped_gemms(cfg, layer, ids, layout):
+    """fc1 and fc2 through the C ABI on the rows the oracle scatters for `ids`,
+    element by element against the oracle (fc2 on the GPU's own activation)."""
+    W1d, W2d, _ = _device_weights(layer, layout)
+    x = layer["x"]
     sc = O.build_scatter(ids, cfg.E)
     W1, W2 = _np_weights(layer)
     Xs = O.scatter_rows(host(x), sc["row_token"])
@@ -353,6 +359,29 @@ def test_grouped_gemms_per_call(cfg, layout):
     assert_output_close(Y, Y_ref, "f32" if cfg.dtype == "f32" else "bf16", "Y_s")
     mx = np.abs(Y - Y_ref).max() / max(np.abs(Y_ref).max(), 1e-30)
     assert mx <= 1e-5, f"fc2 relative max error {mx:.3e} against the oracle on the same activation"
+
+
+# Group sizes whose last row tiles hold every count of live 32-row blocks
+# (1 .. BM/32, dealt to the wave rows alternately), in groups of one and of
+# several row tiles in one launch, for each tile configuration that cuts a
+# partial row tile to its live blocks.
+_WIDE_SIZES = [1, 32, 33, 64, 65, 96, 97, 127, 128, 129, 160, 161, 192, 193, 255, 256]
+_MID_SIZES = [193, 224, 225, 256, 257, 288, 289, 320, 321, 352, 353, 384]
+_DENSE_SIZES = [513, 544, 545, 576, 577, 608, 609, 640, 641, 672, 673, 704, 705, 736, 737, 768]
+ROW_BLOCK_CASES = [("wide", 256, 192, _WIDE_SIZES, _W), ("mid", 256, 192, _MID_SIZES, _M),
+                   ("dense", 256, 192, _DENSE_SIZES, _D), ("small", 512, 256, _DENSE_SIZES, _S)]
+
+
+@pytest.mark.parametrize("name,H,I,sizes,tile", ROW_BLOCK_CASES, ids=[c[0] for c in ROW_BLOCK_CASES])
+def test_partial_row_tiles_every_block_count(name, H, I, sizes, tile):
+    E, T = len(sizes), sum(sizes)
+    cfg = wl.LayerConfig(f"row_blocks_{name}", "bf16", T=T, H=H, E=E, top_k=1, I=I)
+    assert tuple(B.moe_grouped_gemm_tile(torch.bfloat16, c, T, H, E, I) for c in (0, 1)) == (tile, tile)
+    layer = _layer(cfg)
+    rng = np.random.default_rng(11)
+    ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), sizes)).reshape(T, 1)
+    assert np.array_equal(np.bincount(ids[:, 0], minlength=E), sizes)
+    _check_grouped_gemms(cfg, layer, ids, B.MOE_W_KN)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
